@@ -1,0 +1,236 @@
+// C ABI of the batched logits sampler: argument checks, workspace, planning
+// and kernel launches.  The operation itself is defined in sampler.h.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "sampler.h"
+#include "sampler_internal.h"
+
+using namespace smp;
+
+struct sampler_s {
+    int32_t max_batch;
+    int32_t vocab;
+    int32_t dtype;
+    int32_t guess;
+    int32_t chunks;
+    int device;
+    KWork ws;
+    void *ws_base;
+    hipEvent_t ev[5];
+    bool events_ok;
+    bool prof_pending;
+    bool launched[4];
+};
+
+namespace {
+
+constexpr int32_t DEFAULT_GUESS = 256;
+constexpr int32_t DEFAULT_CHUNKS = 8;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+KPlan make_plan(const sampler_s *h) {
+    KPlan l;
+    const int64_t V = h->vocab;
+    int64_t tiles = (V + TILE - 1) / TILE;
+    int64_t nch = h->chunks;
+    if (nch > tiles) nch = tiles;
+    if (nch < 1) nch = 1;
+    int64_t per = (V + nch - 1) / nch;
+    l.chunk_len = (per + TILE - 1) / TILE * TILE;
+    l.nch = (int32_t)((V + l.chunk_len - 1) / l.chunk_len);
+    l.nt4 = (int32_t)((V + TILE4 - 1) / TILE4);
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sampler_strerror(int code) {
+    switch (code) {
+        case SAMPLER_OK: return "ok";
+        case SAMPLER_EINVAL: return "invalid argument";
+        case SAMPLER_ENOMEM: return "device workspace allocation failed";
+        case SAMPLER_EHIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtype,
+                   const sampler_opts *opts) {
+    if (h == nullptr) return SAMPLER_EINVAL;
+    *h = nullptr;
+    if (max_batch < 1 || vocab < 1 || vocab > SAMPLER_VOCAB_MAX) return SAMPLER_EINVAL;
+    if (dtype != SAMPLER_F32 && dtype != SAMPLER_BF16) return SAMPLER_EINVAL;
+    int32_t guess = DEFAULT_GUESS, chunks = DEFAULT_CHUNKS;
+    if (opts) {
+        if (opts->topk_guess < 0 || opts->topk_guess > SAMPLER_TOPK_MAX) return SAMPLER_EINVAL;
+        if (opts->chunks_per_row < 0 || opts->chunks_per_row > NCH_MAX) return SAMPLER_EINVAL;
+        if (opts->topk_guess) guess = opts->topk_guess;
+        if (opts->chunks_per_row) chunks = opts->chunks_per_row;
+    }
+
+    sampler_s *s = new (std::nothrow) sampler_s();
+    if (!s) return SAMPLER_ENOMEM;
+    s->max_batch = max_batch;
+    s->vocab = vocab;
+    s->dtype = dtype;
+    s->guess = guess;
+    s->chunks = chunks;
+    if (hipGetDevice(&s->device) != hipSuccess) {
+        delete s;
+        return SAMPLER_EHIP;
+    }
+    const size_t B = (size_t)max_batch;
+    size_t off = 0;
+    const size_t o_cand = off;
+    off = align_up(off + B * NCH_MAX * KMAX * sizeof(uint64_t), 256);
+    const size_t o_ccnt = off;
+    off = align_up(off + B * NCH_MAX * sizeof(int32_t), 256);
+    const size_t o_cstat = off;
+    off = align_up(off + B * NCH_MAX * sizeof(ChunkStat), 256);
+    const size_t o_info = off;
+    off = align_up(off + B * sizeof(RowInfo), 256);
+    const size_t o_klist = off;
+    off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
+    void *base = nullptr;
+    hipError_t e = hipMalloc(&base, off);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete s;
+        return e == hipErrorOutOfMemory ? SAMPLER_ENOMEM : SAMPLER_EHIP;
+    }
+    char *c = (char *)base;
+    s->ws_base = base;
+    s->ws.cand = (uint64_t *)(c + o_cand);
+    s->ws.ccnt = (int32_t *)(c + o_ccnt);
+    s->ws.cstat = (ChunkStat *)(c + o_cstat);
+    s->ws.info = (RowInfo *)(c + o_info);
+    s->ws.klist = (uint64_t *)(c + o_klist);
+    s->events_ok = true;
+    for (int i = 0; i < 5; ++i)
+        if (hipEventCreate(&s->ev[i]) != hipSuccess) s->events_ok = false;
+    s->prof_pending = false;
+    *h = s;
+    return SAMPLER_OK;
+}
+
+int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
+    if (h == nullptr || a == nullptr) return SAMPLER_EINVAL;
+    if (batch < 0 || batch > h->max_batch) return SAMPLER_EINVAL;
+    if (batch == 0) return SAMPLER_OK;
+    if (a->logits == nullptr || a->out_idx == nullptr) return SAMPLER_EINVAL;
+    if (a->ld < h->vocab) return SAMPLER_EINVAL;
+    if (!(a->temperature > 0.0f) || !isfinite(a->temperature)) return SAMPLER_EINVAL;
+    if (!(a->repetition_penalty > 0.0f) || !isfinite(a->repetition_penalty))
+        return SAMPLER_EINVAL;
+    if (!(a->eps >= 0.0f) || !isfinite(a->eps)) return SAMPLER_EINVAL;
+    const uint32_t known = SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_PROFILE;
+    if (a->flags & ~known) return SAMPLER_EINVAL;
+    if ((a->flags & SAMPLER_NEED_LOGITS) && a->out_logits == nullptr) return SAMPLER_EINVAL;
+    if ((a->flags & SAMPLER_NEED_PROBS) && a->out_probs == nullptr) return SAMPLER_EINVAL;
+    if ((a->penalty_ids == nullptr) != (a->penalty_offsets == nullptr)) return SAMPLER_EINVAL;
+    if (a->row_flags == nullptr && a->q == nullptr) return SAMPLER_EINVAL;
+    return SAMPLER_OK;
+}
+
+int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream) {
+    int rc = sampler_check(h, batch, a);
+    if (rc != SAMPLER_OK) return rc;
+    if (batch == 0) return SAMPLER_OK;
+    hipStream_t st = (hipStream_t)stream;
+
+    KParams p;
+    memset(&p, 0, sizeof p);
+    p.logits = a->logits;
+    p.ld = a->ld;
+    p.top_k = a->top_k;
+    p.top_p = a->top_p;
+    p.q = a->q;
+    p.ids = a->penalty_ids;
+    p.offsets = a->penalty_offsets;
+    p.row_flags = a->row_flags;
+    p.out_idx = a->out_idx;
+    p.out_logits = (a->flags & SAMPLER_NEED_LOGITS) ? a->out_logits : nullptr;
+    p.out_probs = (a->flags & SAMPLER_NEED_PROBS) ? a->out_probs : nullptr;
+    p.eps = a->eps;
+    p.temperature = a->temperature;
+    p.rho = a->repetition_penalty;
+    p.flags = a->flags & (SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS);
+    p.B = batch;
+    p.V = h->vocab;
+    p.guess = h->guess;
+    p.pen = (a->repetition_penalty != 1.0f && a->penalty_ids != nullptr) ? 1 : 0;
+
+    const KPlan l = make_plan(h);
+    const int esize = h->dtype == SAMPLER_BF16 ? 2 : 4;
+    const bool al = aligned16(a->logits) && ((a->ld * esize) % 16) == 0 &&
+                    (h->vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
+                    (p.out_logits == nullptr || aligned16(p.out_logits)) &&
+                    (p.out_probs == nullptr || aligned16(p.out_probs));
+
+    const bool prof = (a->flags & SAMPLER_PROFILE) && h->events_ok;
+    for (int i = 0; i < 4; ++i) h->launched[i] = false;
+    auto mark = [&](int i) {
+        if (prof) (void)hipEventRecord(h->ev[i], st);
+    };
+
+    hipError_t e;
+    mark(0);
+    e = launch_chunk(p, l, h->ws, h->dtype, al, st);
+    if (e != hipSuccess) return SAMPLER_EHIP;
+    h->launched[0] = true;
+    mark(1);
+    e = launch_rows(p, l, h->ws, st);
+    if (e != hipSuccess) return SAMPLER_EHIP;
+    h->launched[1] = true;
+    mark(2);
+    if (a->top_p != nullptr) {
+        e = launch_fallback(p, l, h->ws, h->dtype, al, st);
+        if (e != hipSuccess) return SAMPLER_EHIP;
+        h->launched[2] = true;
+    }
+    mark(3);
+    if (p.out_logits || p.out_probs) {
+        e = launch_dense(p, l, h->ws, h->dtype, al, st);
+        if (e != hipSuccess) return SAMPLER_EHIP;
+        h->launched[3] = true;
+    }
+    mark(4);
+    h->prof_pending = prof;
+    return SAMPLER_OK;
+}
+
+int sampler_last_profile(sampler_t *h, float *ms, int32_t n) {
+    if (h == nullptr || ms == nullptr || n < 0) return SAMPLER_EINVAL;
+    if (!h->prof_pending) return SAMPLER_EINVAL;
+    if (hipEventSynchronize(h->ev[4]) != hipSuccess) return SAMPLER_EHIP;
+    int w = n < 4 ? n : 4;
+    for (int i = 0; i < w; ++i) {
+        float t = 0.0f;
+        if (h->launched[i] && hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]) != hipSuccess)
+            return SAMPLER_EHIP;
+        ms[i] = h->launched[i] ? t : 0.0f;
+    }
+    return w;
+}
+
+int sampler_destroy(sampler_t *h) {
+    if (h == nullptr) return SAMPLER_OK;
+    int rc = SAMPLER_OK;
+    if (h->ws_base && hipFree(h->ws_base) != hipSuccess) rc = SAMPLER_EHIP;
+    for (int i = 0; i < 5; ++i)
+        if (h->events_ok) (void)hipEventDestroy(h->ev[i]);
+    delete h;
+    return rc;
+}
+
+}  // extern "C"

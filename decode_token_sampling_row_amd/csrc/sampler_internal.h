@@ -1,0 +1,100 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smp {
+
+// Streaming-pass geometry (chunk kernel): 256 threads x 8 elements per tile.
+constexpr int K1_THREADS = 256;
+constexpr int VEC = 8;
+constexpr int TILE = K1_THREADS * VEC;  // 2048 elements
+constexpr int NCH_MAX = 8;              // chunks per row
+constexpr int KMAX = 1024;              // largest k / guess
+constexpr int CAP = 4096;               // LDS candidate buffer entries
+// Row kernels.
+constexpr int K2_THREADS = 1024;
+constexpr int K3_THREADS = 1024;
+constexpr int K3_BINS = 2048;           // value-space histogram bins
+constexpr int K3_COLLECT = 4096;        // bucket members sorted in LDS
+constexpr int K3_SEG = 65536;           // penalty-bitmap segment
+// Dense writer: 256 threads x 32 elements.
+constexpr int K4_THREADS = 256;
+constexpr int TILE4 = 8192;
+
+// Row kinds written by the merge kernel.
+enum RowKind : int32_t {
+    KIND_UNFILTERED = 0,  // K = whole row; dense logits already written
+    KIND_LIST = 1,        // K listed in klist[b][0..nK)
+    KIND_FALLBACK = 2,    // guess failed; full-row cutoff search pending
+    KIND_THRESH = 3,      // K = { comp >= T } (after the full-row search)
+};
+
+struct ChunkStat {
+    float m;       // max transformed logit of the chunk (-inf if none)
+    float xmin;    // min finite transformed logit (+inf if none)
+    double z;      // sum exp(x - m) over the chunk
+    float rx;      // race winner: logit
+    float rqe;     // race winner: q + eps
+    uint32_t ridx; // race winner: vocab id (0xffffffff = none)
+    uint32_t pad;
+};
+
+struct RowInfo {
+    int32_t kind;
+    int32_t nK;
+    uint64_t T;    // threshold composite key (KIND_THRESH)
+    double ZK;     // sum exp(x - m) over K
+    float m;       // row max (transformed)
+    float xmin;    // row min finite
+    uint32_t idx0; // id of the row maximum (first in order)
+    uint32_t pad;
+};
+
+struct KParams {
+    const void *logits;
+    int64_t ld;
+    const int32_t *top_k;
+    const float *top_p;
+    const float *q;
+    const int32_t *ids;
+    const int64_t *offsets;
+    const uint8_t *row_flags;
+    int64_t *out_idx;
+    float *out_logits;
+    float *out_probs;
+    float eps;
+    float temperature;
+    float rho;
+    uint32_t flags;
+    int32_t B;
+    int32_t V;
+    int32_t guess;
+    int32_t pen;  // penalty stage active for the call
+};
+
+struct KPlan {
+    int32_t nch;        // chunks per row
+    int64_t chunk_len;  // elements per chunk (multiple of TILE)
+    int32_t nt4;        // dense-writer tiles per row
+};
+
+struct KWork {
+    uint64_t *cand;   // [maxB][NCH_MAX][KMAX]
+    int32_t *ccnt;    // [maxB][NCH_MAX]
+    ChunkStat *cstat; // [maxB][NCH_MAX]
+    RowInfo *info;    // [maxB]
+    uint64_t *klist;  // [maxB][KMAX]
+};
+
+// Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_chunk(const KParams &p, const KPlan &l, const KWork &w, int dtype,
+                        bool aligned, hipStream_t s);
+hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);
+hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype,
+                           bool aligned, hipStream_t s);
+hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype,
+                        bool aligned, hipStream_t s);
+
+}  // namespace smp

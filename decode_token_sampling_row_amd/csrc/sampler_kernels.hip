@@ -1,0 +1,1410 @@
+// HIP kernels of the batched logits sampler (gfx950, wave64).
+//
+// Pipeline of one call (all on the caller's stream):
+//
+//   k_chunk     grid = B x nch.  One workgroup streams one chunk of one row
+//               once from HBM: widen bf16 -> fp32, repetition penalty (LDS
+//               bitmap of the chunk's history ids), temperature.  Depending on
+//               the row's stages it then
+//                 - keeps the chunk's top-kk candidates in an LDS buffer
+//                   filtered by a rising threshold (the rolling top-k of the
+//                   Ascend npu_top_k_top_p_sample page, topK section: each
+//                   batch of elements is prefiltered by the k-th value of
+//                   what came before, the buffer is cut back to exactly kk by
+//                   a radix select when it fills);
+//                 - accumulates the chunk's max / sum-exp for top-p rows
+//                   without top-k (the softmax of that page's topP section);
+//                 - runs the exponential race over the whole chunk for rows
+//                   that only sample (streams q in the same pass);
+//                 - writes the dense output of unfiltered rows.
+//   k_rows      grid = B.  Merges the <= 8 chunk results of a row: exact
+//               top-kk by radix select, bitonic sort, softmax in double,
+//               inclusive scan, shortest prefix reaching p, exponential race
+//               over the kept set (gather of q at the kept ids), output id.
+//               Rows whose guess does not settle top-p are flagged.
+//   k_fallback  grid = B (flagged rows only).  Full-row top-p cutoff: a
+//               value-space mass histogram, then key-space refinement, then
+//               an exact sort of the boundary bucket in LDS (or a rank among
+//               ties by vocab id), then the race over the kept set.  This is
+//               the page's full-sort fallback reached without a full sort.
+//   k_dense     grid = B x tiles.  Writes the dense filtered logits (and the
+//               optional probabilities) of filtered rows with full-line
+//               stores, composing each tile in LDS from the kept list.
+//
+// Order and keys: a transformed logit x and its vocab id j form the 64-bit
+// composite  (orderkey(x) << 32) | ~j ; larger composite = earlier in the
+// row's order (larger value, then smaller id).  All composites of a row are
+// distinct, so every selection below is exact and deterministic.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "sampler_internal.h"
+
+namespace smp {
+namespace {
+
+constexpr uint32_t NONE = 0xffffffffu;
+constexpr uint32_t NEED_LOGITS = 1u;
+constexpr uint32_t NEED_PROBS = 2u;
+// top-p decisions taken from a guess must clear the cutoff by this much
+// (relative to the row's total mass); the row's total is accumulated from
+// fp32 exponentials, good to a few 1e-7.
+constexpr double GUESS_MARGIN = 2e-6;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- keys
+
+__device__ __forceinline__ uint32_t f2key(float x) {
+    uint32_t b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+    uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(b);
+}
+__device__ __forceinline__ uint64_t mkcomp(float x, uint32_t j) {
+    return ((uint64_t)f2key(x) << 32) | (uint64_t)(~j);
+}
+__device__ __forceinline__ uint32_t cidx(uint64_t c) { return ~(uint32_t)c; }
+__device__ __forceinline__ float cval(uint64_t c) { return key2f((uint32_t)(c >> 32)); }
+
+// ---------------------------------------------------------------- row mode
+
+struct Mode {
+    bool tk, tp, sm;
+    int k;
+    float p;
+};
+
+__device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
+    Mode md;
+    uint32_t rf = P.row_flags ? (uint32_t)P.row_flags[b] : 7u;
+    int kmax = P.V < KMAX ? P.V : KMAX;
+    md.k = 0;
+    md.p = 1.0f;
+    md.tk = false;
+    if ((rf & 1u) && P.top_k) {
+        int k = P.top_k[b];
+        if (k >= 1 && k <= kmax) {
+            md.tk = true;
+            md.k = k;
+        }
+    }
+    md.tp = false;
+    if ((rf & 2u) && P.top_p) {
+        float p = P.top_p[b];
+        if (p < 1.0f) {  // NaN compares false: stage off
+            md.tp = true;
+            md.p = p;
+        }
+    }
+    md.sm = (rf & 4u) && P.q;
+    return md;
+}
+
+// Penalty, temperature, -0 -> +0.  Division is IEEE correctly rounded.
+__device__ __forceinline__ float xform(float x, bool hit, const KParams &P) {
+    if (hit) x = (x > 0.0f) ? x / P.rho : x * P.rho;
+    if (P.temperature != 1.0f) x = x / P.temperature;
+    return (x == 0.0f) ? 0.0f : x;
+}
+
+// Row index of workgroup i in a grid of n row-workgroups: consecutive
+// workgroups go round-robin to the 8 XCDs; give each XCD a contiguous block
+// of rows so row-dependent work (stage mixes often cycle with the row) is
+// spread evenly over the XCDs.
+__device__ __forceinline__ int xcd_row(int i, int n) {
+    int x = i & 7, pos = i >> 3;
+    int q = n >> 3, r = n & 7;
+    return x * q + (x < r ? x : r) + pos;
+}
+
+// ---------------------------------------------------------------- loads
+
+template <int DT>
+__device__ __forceinline__ float ld1(const void *p, int64_t j) {
+    if (DT == 1) {
+        uint32_t h = ((const uint16_t *)p)[j];
+        return __uint_as_float(h << 16);
+    }
+    return ((const float *)p)[j];
+}
+
+// x[0..8) = elements j..j+8 of the row (nv valid).  Vector path when the
+// row is 16-byte aligned and the group is whole.
+template <int DT, bool AL>
+__device__ __forceinline__ void load8(const void *p, int64_t j, int nv, float (&x)[8]) {
+    if (AL && nv == 8) {
+        if (DT == 1) {
+            u32x4 u = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)p + j));
+            x[0] = __uint_as_float(u.x << 16);
+            x[1] = __uint_as_float(u.x & 0xffff0000u);
+            x[2] = __uint_as_float(u.y << 16);
+            x[3] = __uint_as_float(u.y & 0xffff0000u);
+            x[4] = __uint_as_float(u.z << 16);
+            x[5] = __uint_as_float(u.z & 0xffff0000u);
+            x[6] = __uint_as_float(u.w << 16);
+            x[7] = __uint_as_float(u.w & 0xffff0000u);
+        } else {
+            const f32x4 *q = (const f32x4 *)((const float *)p + j);
+            f32x4 a = __builtin_nontemporal_load(q);
+            f32x4 c = __builtin_nontemporal_load(q + 1);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (i < nv) ? ld1<DT>(p, j + i) : 0.0f;
+    }
+}
+
+template <bool AL>
+__device__ __forceinline__ void store8(float *p, int64_t j, int nv, const float (&x)[8]) {
+    if (AL && nv == 8) {
+        f32x4 a = {x[0], x[1], x[2], x[3]};
+        f32x4 c = {x[4], x[5], x[6], x[7]};
+        __builtin_nontemporal_store(a, (f32x4 *)(p + j));
+        __builtin_nontemporal_store(c, (f32x4 *)(p + j) + 1);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nv) p[j + i] = x[i];
+    }
+}
+
+// ---------------------------------------------------------------- wave / WG primitives
+
+__device__ __forceinline__ uint32_t shx(uint32_t v, int m) {
+    return (uint32_t)__shfl_xor((int)v, m, 64);
+}
+__device__ __forceinline__ uint64_t shx64(uint64_t v, int m) {
+    uint32_t lo = shx((uint32_t)v, m), hi = shx((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float shxf(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ double shxd(double v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t t = (uint32_t)__shfl_up((int)v, d, 64);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        double t = __shfl_up(v, d, 64);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix over the workgroup (thread order); total via `total`.
+// sc: >= 16 LDS words.  Ends with a barrier so sc can be reused at once.
+template <int NT>
+__device__ __forceinline__ uint32_t wg_excl_scan_u32(uint32_t v, uint32_t *sc, uint32_t &total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t inc = wave_incl_scan_u32(v, lane);
+    if (lane == 63) sc[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        uint32_t s = sc[i];
+        before += (i < w) ? s : 0u;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return before + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ double wg_excl_scan_f64(double v, double *sc, double &total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double inc = wave_incl_scan_f64(v, lane);
+    if (lane == 63) sc[w] = inc;
+    __syncthreads();
+    double before = 0.0, tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        double s = sc[i];
+        if (i < w) before += s;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return before + (inc - v);
+}
+
+template <int NT>
+__device__ __forceinline__ double wg_sum_f64(double v, double *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shxd(v, m);
+    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += sc[i];
+    __syncthreads();
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ uint64_t wg_max_u64(uint64_t v, uint64_t *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shx64(v, m);
+        v = o > v ? o : v;
+    }
+    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t = sc[i] > t ? sc[i] : t;
+    __syncthreads();
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ uint64_t wg_min_u64(uint64_t v, uint64_t *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shx64(v, m);
+        v = o < v ? o : v;
+    }
+    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t t = ~0ull;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t = sc[i] < t ? sc[i] : t;
+    __syncthreads();
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t wg_min_u32(uint32_t v, uint32_t *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, shx(v, m));
+    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t t = NONE;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t = min(t, sc[i]);
+    __syncthreads();
+    return t;
+}
+
+// Exponential race: is candidate a (logit xa, q+eps qa) ahead of b?
+// e_a / qa > e_b / qb  <=>  exp(xa - xb) * qb > qa.  Equal -> smaller id.
+struct Race {
+    float x, qe;
+    uint32_t idx;
+};
+__device__ __forceinline__ bool race_ahead(const Race &a, const Race &b) {
+    if (a.idx == NONE) return false;
+    if (b.idx == NONE) return true;
+    float f = expf(a.x - b.x) * b.qe;
+    if (f > a.qe) return true;
+    if (f < a.qe) return false;
+    return a.idx < b.idx;
+}
+__device__ __forceinline__ void race_offer(Race &best, float x, float qe, uint32_t j) {
+    if (!(x > -INFINITY)) return;  // probability 0: never drawn
+    if (best.idx == NONE || expf(x - best.x) * best.qe > qe) {
+        best.x = x;
+        best.qe = qe;
+        best.idx = j;
+    }
+}
+template <int NT>
+__device__ __forceinline__ Race wg_race(Race r, float *scx, float *scq, uint32_t *sci) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        Race o;
+        o.x = shxf(r.x, m);
+        o.qe = shxf(r.qe, m);
+        o.idx = shx(r.idx, m);
+        if (race_ahead(o, r)) r = o;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        scx[w] = r.x;
+        scq[w] = r.qe;
+        sci[w] = r.idx;
+    }
+    __syncthreads();
+    Race t;
+    t.x = scx[0];
+    t.qe = scq[0];
+    t.idx = sci[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) {
+        Race o;
+        o.x = scx[i];
+        o.qe = scq[i];
+        o.idx = sci[i];
+        if (race_ahead(o, t)) t = o;
+    }
+    __syncthreads();
+    return t;
+}
+
+// Radix select over distinct 64-bit composites held in registers.  Finds
+// (prefix, pmask) such that exactly kk of the valid entries satisfy
+// (v & pmask) >= prefix, i.e. the kk largest.  8-bit digits from the top,
+// stopping as soon as the boundary bucket is taken whole.  Needs
+// 1 <= kk <= number of valid entries.
+template <int NT, int R>
+__device__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t kk,
+                                uint32_t *hist, uint32_t *sel, uint64_t &prefix_out,
+                                uint64_t &pmask_out) {
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t need = kk;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (((vmask >> r) & 1u) && (v[r] & pmask) == prefix)
+                atomicAdd(&hist[(uint32_t)(v[r] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+            uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+            uint32_t s = h0 + h1 + h2 + h3;
+            uint32_t S = s;  // suffix sum over lanes >= lane
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                uint32_t t = (uint32_t)__shfl_down((int)S, d, 64);
+                if (lane + d < 64) S += t;
+            }
+            uint32_t above = S - s;
+            if (above < need && S >= need) {
+                uint32_t acc = above;
+                uint32_t d = 4 * lane, c = h0;
+                if (acc + h3 >= need) {
+                    d = 4 * lane + 3; c = h3;
+                } else if (acc + h3 + h2 >= need) {
+                    acc += h3; d = 4 * lane + 2; c = h2;
+                } else if (acc + h3 + h2 + h1 >= need) {
+                    acc += h3 + h2; d = 4 * lane + 1; c = h1;
+                } else {
+                    acc += h3 + h2 + h1; d = 4 * lane; c = h0;
+                }
+                sel[0] = d;
+                sel[1] = acc;
+                sel[2] = c;
+            }
+        }
+        __syncthreads();
+        uint32_t d = sel[0], above = sel[1], cntd = sel[2];
+        need -= above;
+        prefix |= (uint64_t)d << shift;
+        pmask |= (uint64_t)0xff << shift;
+        if (cntd == need) break;
+    }
+    prefix_out = prefix;
+    pmask_out = pmask;
+}
+
+// Descending bitonic sort of s[0..n), n a power of two.  Callers barrier
+// before; ends with a barrier.
+template <int NT>
+__device__ void bitonic_desc(uint64_t *s, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += NT) {
+                int ixj = i ^ j;
+                if (ixj > i) {
+                    uint64_t a = s[i], c = s[ixj];
+                    bool desc = (i & k) == 0;
+                    if (desc ? (a < c) : (a > c)) {
+                        s[i] = c;
+                        s[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ int pow2_ceil(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+// Chunk/segment-local bitmap of a row's history ids (duplicates collapse,
+// ids outside [seg0, seg0 + len) ignored).  Begins and ends with barriers.
+template <int NT>
+__device__ void build_bitmap(uint32_t *bm, int64_t seg0, int64_t len, const KParams &P, int b) {
+    const int nw = (int)((len + 31) >> 5);
+    __syncthreads();
+    for (int w = threadIdx.x; w < nw; w += NT) bm[w] = 0u;
+    __syncthreads();
+    const int64_t i0 = P.offsets[b], i1 = P.offsets[b + 1];
+    for (int64_t t = i0 + threadIdx.x; t < i1; t += NT) {
+        int64_t r = (int64_t)P.ids[t] - seg0;
+        if (r >= 0 && r < len) atomicOr(&bm[r >> 5], 1u << (r & 31));
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ const void *row_ptr(const KParams &P, int dt, int b) {
+    return (const char *)P.logits + (int64_t)b * P.ld * (dt == 1 ? 2 : 4);
+}
+
+// ================================================================== k_chunk
+
+constexpr int U = 4;  // tiles per batch
+
+struct ChunkShared {
+    uint64_t buf[CAP];
+    uint32_t hist[256];
+    uint32_t sel[4];
+    uint32_t sc[16];
+    uint64_t sc64[16];
+    double scd[16];
+    float scx[16], scq[16];
+    uint32_t sci[16];
+};
+
+// Cut buf[0..cnt) back to its kk largest (cnt > kk); returns the smallest
+// kept composite, the new admission threshold.
+__device__ uint64_t chunk_reduce(ChunkShared &S, uint32_t cnt, uint32_t kk) {
+    constexpr int R = CAP / K1_THREADS;
+    uint64_t v[R];
+    uint32_t vm = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t i = threadIdx.x + r * K1_THREADS;
+        v[r] = (i < cnt) ? S.buf[i] : 0ull;
+        if (i < cnt) vm |= 1u << r;
+    }
+    uint64_t prefix, pmask;
+    wg_radix_select<K1_THREADS, R>(v, vm, kk, S.hist, S.sel, prefix, pmask);
+    uint32_t km = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
+    uint32_t tot;
+    uint32_t off = wg_excl_scan_u32<K1_THREADS>(__popc(km), S.sc, tot);
+    uint64_t mn = ~0ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if ((km >> r) & 1u) {
+            S.buf[off++] = v[r];
+            mn = v[r] < mn ? v[r] : mn;
+        }
+    return wg_min_u64<K1_THREADS>(mn, S.sc64);
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(K1_THREADS) void k_chunk(KParams P, KPlan L, KWork W) {
+    __shared__ ChunkShared S;
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
+
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
+    const int64_t V = P.V;
+    const int64_t c0 = (int64_t)c * L.chunk_len;
+    const int64_t c1 = min(c0 + L.chunk_len, V);
+    const int slot = b * NCH_MAX + c;
+    const Mode md = row_mode(P, b);
+
+    const bool filtered = md.tk || md.tp;
+    const bool do_sel = filtered;
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    const bool do_stats = (md.tp && !md.tk) || (!filtered && (P.flags & NEED_PROBS));
+    const bool do_race = !filtered && md.sm;
+    const bool do_argmax = !filtered && !md.sm;
+    const bool do_dense = !filtered && (P.flags & NEED_LOGITS);
+
+    if (c0 >= c1) {  // empty chunk (only when V < nch * chunk_len)
+        if (tid == 0) {
+            W.ccnt[slot] = 0;
+            ChunkStat cs;
+            cs.m = -INFINITY; cs.xmin = INFINITY; cs.z = 0.0;
+            cs.rx = -INFINITY; cs.rqe = 1.0f; cs.ridx = NONE; cs.pad = 0;
+            W.cstat[slot] = cs;
+        }
+        return;
+    }
+    if (P.pen) build_bitmap<K1_THREADS>(bm, c0, c1 - c0, P, b);
+
+    const void *rowp = row_ptr(P, DT, b);
+    const float *rowq = P.q ? P.q + (int64_t)b * V : nullptr;
+    float *rowo = P.out_logits ? P.out_logits + (int64_t)b * V : nullptr;
+
+    uint64_t T = 0;    // admission threshold (uniform)
+    uint32_t cnt = 0;  // buffer fill (uniform)
+    float st_m = -INFINITY, st_min = INFINITY;
+    double st_z = 0.0;
+    Race rc;
+    rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
+    uint64_t am = 0;
+
+    for (int64_t base = c0; base < c1; base += (int64_t)TILE * U) {
+        float x[U][8];
+        int nv[U];
+        int64_t jb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            jb[u] = base + (int64_t)u * TILE + (int64_t)tid * VEC;
+            int64_t rem = c1 - jb[u];
+            nv[u] = rem <= 0 ? 0 : (rem >= 8 ? 8 : (int)rem);
+            load8<DT, AL>(rowp, jb[u], nv[u], x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint32_t bits = 0;
+            if (P.pen && nv[u] > 0) {
+                int64_t r = jb[u] - c0;
+                bits = (bm[r >> 5] >> (r & 31)) & 0xffu;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[u][i] = xform(x[u][i], (bits >> i) & 1u, P);
+        }
+        if (do_dense) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (nv[u] > 0) store8<AL>(rowo, jb[u], nv[u], x[u]);
+        }
+        if (do_stats) {
+            float tm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i < nv[u]) {
+                        tm = fmaxf(tm, x[u][i]);
+                        if (x[u][i] > -INFINITY) st_min = fminf(st_min, x[u][i]);
+                    }
+            if (tm > st_m) {
+                if (st_z != 0.0) st_z *= exp((double)st_m - (double)tm);
+                st_m = tm;
+            }
+            if (st_m > -INFINITY) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i < nv[u]) st_z += (double)expf(x[u][i] - st_m);
+            }
+        }
+        if (do_race) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float qv[8];
+                load8<0, AL>(rowq, jb[u], nv[u], qv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i < nv[u]) race_offer(rc, x[u][i], qv[i] + P.eps, (uint32_t)(jb[u] + i));
+            }
+        }
+        if (do_argmax) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i < nv[u]) {
+                        uint64_t cv = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
+                        am = cv > am ? cv : am;
+                    }
+        }
+        if (do_sel) {
+            uint32_t pm = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T)
+                        pm |= 1u << (u * 8 + i);
+            uint32_t tot;
+            uint32_t off = wg_excl_scan_u32<K1_THREADS>(__popc(pm), S.sc, tot);
+            if (cnt + tot <= (uint32_t)CAP) {
+                uint32_t pos = cnt + off;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if ((pm >> (u * 8 + i)) & 1u)
+                            S.buf[pos++] = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
+                cnt += tot;
+            } else {
+                // Tile by tile; cut the buffer back when a tile would overflow.
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    uint32_t m8 = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T) m8 |= 1u << i;
+                    uint32_t t8;
+                    uint32_t o8 = wg_excl_scan_u32<K1_THREADS>(__popc(m8), S.sc, t8);
+                    if (cnt + t8 > (uint32_t)CAP) {
+                        T = chunk_reduce(S, cnt, kk);
+                        cnt = kk;
+                        m8 = 0;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T)
+                                m8 |= 1u << i;
+                        o8 = wg_excl_scan_u32<K1_THREADS>(__popc(m8), S.sc, t8);
+                    }
+                    uint32_t pos = cnt + o8;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if ((m8 >> i) & 1u) S.buf[pos++] = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
+                    cnt += t8;
+                }
+            }
+        }
+    }
+
+    if (do_sel) {
+        __syncthreads();
+        if (cnt > kk) {
+            T = chunk_reduce(S, cnt, kk);
+            cnt = kk;
+        }
+        uint64_t *dst = W.cand + (int64_t)slot * KMAX;
+        for (uint32_t i = tid; i < cnt; i += K1_THREADS) dst[i] = S.buf[i];
+        if (tid == 0) W.ccnt[slot] = (int32_t)cnt;
+    }
+    if (do_argmax) {
+        am = wg_max_u64<K1_THREADS>(am, S.sc64);
+        if (tid == 0) {
+            W.cand[(int64_t)slot * KMAX] = am;
+            W.ccnt[slot] = 1;
+        }
+    }
+    ChunkStat cs;
+    cs.m = -INFINITY; cs.xmin = INFINITY; cs.z = 0.0;
+    cs.rx = -INFINITY; cs.rqe = 1.0f; cs.ridx = NONE; cs.pad = 0;
+    if (do_stats) {
+        // merge (m, z) pairs: max first, then rescaled sums
+        float m = st_m;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, shxf(m, s));
+        if ((tid & 63) == 0) S.scx[tid >> 6] = m;
+        __syncthreads();
+        float M = S.scx[0];
+#pragma unroll
+        for (int i = 1; i < K1_THREADS / 64; ++i) M = fmaxf(M, S.scx[i]);
+        __syncthreads();
+        double z = (st_z != 0.0) ? st_z * exp((double)st_m - (double)M) : 0.0;
+        z = wg_sum_f64<K1_THREADS>(z, S.scd);
+        float mn = st_min;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) mn = fminf(mn, shxf(mn, s));
+        if ((tid & 63) == 0) S.scq[tid >> 6] = mn;
+        __syncthreads();
+        float MN = S.scq[0];
+#pragma unroll
+        for (int i = 1; i < K1_THREADS / 64; ++i) MN = fminf(MN, S.scq[i]);
+        __syncthreads();
+        cs.m = M;
+        cs.z = z;
+        cs.xmin = MN;
+    }
+    if (do_race) {
+        Race r = wg_race<K1_THREADS>(rc, S.scx, S.scq, S.sci);
+        cs.rx = r.x;
+        cs.rqe = r.qe;
+        cs.ridx = r.idx;
+    }
+    if (tid == 0) W.cstat[slot] = cs;
+}
+
+// ================================================================== k_rows
+
+struct RowsShared {
+    uint64_t srt[KMAX];
+    double ev[KMAX];
+    double cs[KMAX];
+    uint32_t hist[256];
+    uint32_t sel[4];
+    uint32_t sc[16];
+    uint64_t sc64[16];
+    double scd[16];
+    uint32_t sci[16];
+};
+
+template <int NT>
+__device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double *scd,
+                                                  uint32_t *sci) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        double ro = shxd(r, m);
+        uint32_t io = shx(idx, m);
+        if (ro > r || (ro == r && io < idx)) {
+            r = ro;
+            idx = io;
+        }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        scd[w] = r;
+        sci[w] = idx;
+    }
+    __syncthreads();
+    double br = scd[0];
+    uint32_t bi = sci[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i)
+        if (scd[i] > br || (scd[i] == br && sci[i] < bi)) {
+            br = scd[i];
+            bi = sci[i];
+        }
+    __syncthreads();
+    return bi;
+}
+
+__global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W) {
+    __shared__ RowsShared S;
+    const int tid = threadIdx.x;
+    const int b = xcd_row(blockIdx.x, gridDim.x);
+    const Mode md = row_mode(P, b);
+    const bool filtered = md.tk || md.tp;
+    const int nch = L.nch;
+    const int slot0 = b * NCH_MAX;
+
+    // merged chunk statistics (identical in every thread)
+    float M = -INFINITY, XMIN = INFINITY;
+    for (int c = 0; c < nch; ++c) {
+        M = fmaxf(M, W.cstat[slot0 + c].m);
+        XMIN = fminf(XMIN, W.cstat[slot0 + c].xmin);
+    }
+    double Z = 0.0;
+    for (int c = 0; c < nch; ++c) {
+        ChunkStat cs = W.cstat[slot0 + c];
+        if (cs.z != 0.0) Z += cs.z * exp((double)cs.m - (double)M);
+    }
+
+    RowInfo info;
+    info.kind = KIND_UNFILTERED;
+    info.nK = P.V;
+    info.T = 0;
+    info.ZK = Z;
+    info.m = M;
+    info.xmin = XMIN;
+    info.idx0 = NONE;
+    info.pad = 0;
+
+    if (!filtered) {
+        uint32_t idx;
+        if (!md.sm) {
+            uint64_t am = 0;
+            for (int c = 0; c < nch; ++c)
+                if (W.ccnt[slot0 + c] > 0) {
+                    uint64_t v = W.cand[(int64_t)(slot0 + c) * KMAX];
+                    am = v > am ? v : am;
+                }
+            idx = cidx(am);
+        } else {
+            float xr = -INFINITY;
+            for (int c = 0; c < nch; ++c)
+                if (W.cstat[slot0 + c].ridx != NONE) xr = fmaxf(xr, W.cstat[slot0 + c].rx);
+            double br = -1.0;
+            idx = NONE;
+            for (int c = 0; c < nch; ++c) {
+                ChunkStat cs = W.cstat[slot0 + c];
+                if (cs.ridx == NONE) continue;
+                double r = exp((double)cs.rx - (double)xr) / (double)cs.rqe;
+                if (r > br || (r == br && cs.ridx < idx)) {
+                    br = r;
+                    idx = cs.ridx;
+                }
+            }
+        }
+        info.idx0 = idx;
+        if (tid == 0) {
+            P.out_idx[b] = (int64_t)idx;
+            W.info[b] = info;
+        }
+        return;
+    }
+
+    // ---- candidates: exact top-kk over the row
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    uint32_t N = 0;
+    for (int c = 0; c < nch; ++c) N += (uint32_t)W.ccnt[slot0 + c];
+    constexpr int R2 = NCH_MAX * KMAX / K2_THREADS;  // 8
+    uint64_t v[R2];
+    uint32_t vm = 0;
+#pragma unroll
+    for (int r = 0; r < R2; ++r) {
+        uint32_t s = tid + r * K2_THREADS;
+        uint32_t c = s / kk, i = s - c * kk;
+        bool ok = c < (uint32_t)nch && i < (uint32_t)W.ccnt[slot0 + min(c, (uint32_t)nch - 1)];
+        v[r] = ok ? W.cand[(int64_t)(slot0 + c) * KMAX + i] : 0ull;
+        if (ok) vm |= 1u << r;
+    }
+    const uint32_t nsel = min(kk, N);
+    uint32_t km = vm;
+    if (N > kk) {
+        uint64_t prefix, pmask;
+        wg_radix_select<K2_THREADS, R2>(v, vm, kk, S.hist, S.sel, prefix, pmask);
+        km = 0;
+#pragma unroll
+        for (int r = 0; r < R2; ++r)
+            if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
+    }
+    {
+        uint32_t tot;
+        uint32_t off = wg_excl_scan_u32<K2_THREADS>(__popc(km), S.sc, tot);
+#pragma unroll
+        for (int r = 0; r < R2; ++r)
+            if ((km >> r) & 1u) S.srt[off++] = v[r];
+    }
+    const int npad = pow2_ceil((int)nsel);
+    for (int i = nsel + tid; i < npad; i += K2_THREADS) S.srt[i] = 0ull;
+    __syncthreads();
+    bitonic_desc<K2_THREADS>(S.srt, npad);
+
+    // ---- softmax over the sorted candidates, in double
+    const float x0 = cval(S.srt[0]);
+    double e = 0.0;
+    if ((uint32_t)tid < nsel) e = exp((double)cval(S.srt[tid]) - (double)x0);
+    double tot_e;
+    double incl = wg_excl_scan_f64<K2_THREADS>(e, S.scd, tot_e) + e;
+    if ((uint32_t)tid < nsel) {
+        S.ev[tid] = e;
+        S.cs[tid] = incl;
+    }
+    __syncthreads();
+    double Zc;
+    if (md.tk) Zc = S.cs[nsel - 1];
+    else Zc = (Z != 0.0) ? Z * exp((double)M - (double)x0) : tot_e;
+
+    uint32_t nK = nsel;
+    bool settled = true;
+    if (md.tp) {
+        const double pZ = (double)md.p * Zc;
+        uint32_t first = NONE;
+        if ((uint32_t)tid < nsel && S.cs[tid] >= pZ) first = (uint32_t)tid;
+        first = wg_min_u32<K2_THREADS>(first, S.sc);
+        if (md.tk) {
+            nK = (first == NONE) ? nsel : first + 1;
+        } else {
+            // top-k guess (Ascend page, topP section): settled only when the
+            // cutoff lies inside the guess with a safe margin on both sides.
+            if (first == NONE) {
+                settled = false;
+            } else {
+                double hi = S.cs[first] - pZ;
+                double lo = (first == 0) ? INFINITY : pZ - S.cs[first - 1];
+                settled = hi > GUESS_MARGIN * Zc && lo > GUESS_MARGIN * Zc;
+                if (md.p <= 0.0f) settled = true;
+                nK = first + 1;
+            }
+        }
+    }
+    info.m = x0;
+    info.idx0 = cidx(S.srt[0]);
+    if (!settled) {
+        info.kind = KIND_FALLBACK;
+        if (tid == 0) W.info[b] = info;
+        return;
+    }
+
+    // ---- exponential race over K (or greedy)
+    uint32_t idx = cidx(S.srt[0]);
+    if (md.sm) {
+        double r = -1.0;
+        uint32_t id = NONE;
+        if ((uint32_t)tid < nK) {
+            id = cidx(S.srt[tid]);
+            double den = (double)P.q[(int64_t)b * P.V + id] + (double)P.eps;
+            double ei = S.ev[tid];
+            r = (ei == 0.0) ? 0.0 : ei / den;
+        }
+        idx = wg_best_ratio<K2_THREADS>(r, id, S.scd, S.sci);
+    }
+    for (uint32_t i = tid; i < nK; i += K2_THREADS) W.klist[(int64_t)b * KMAX + i] = S.srt[i];
+    info.kind = KIND_LIST;
+    info.nK = (int32_t)nK;
+    info.ZK = S.cs[nK - 1];
+    if (tid == 0) {
+        P.out_idx[b] = (int64_t)idx;
+        W.info[b] = info;
+    }
+}
+
+// ================================================================== k_fallback
+
+struct FallbackShared {
+    double hm[K3_BINS];
+    uint32_t hc[K3_BINS];
+    uint32_t hlo[K3_BINS];
+    uint32_t hhi[K3_BINS];
+    uint64_t coll[K3_COLLECT];
+    uint32_t bm[K3_SEG / 32];
+    // refinement levels: level 0 bins by value, later levels by key
+    float lv_lo, lv_scale;
+    uint32_t lv_bin[8];
+    uint32_t lv_klo[8];
+    uint64_t lv_span[8];
+    uint32_t sc[16];
+    uint64_t sc64[16];
+    double scd[16];
+    float scx[16], scq[16];
+    uint32_t sci[16];
+    uint32_t counter;
+    uint32_t found[4];
+    double fd[4];
+    double lane_sum[64];
+};
+
+__device__ __forceinline__ uint32_t bin_value(float x, float lo, float scale) {
+    float t = (x - lo) * scale;
+    if (!(t >= 0.0f)) return 0u;
+    if (t >= (float)(K3_BINS - 1)) return K3_BINS - 1;
+    return (uint32_t)t;
+}
+__device__ __forceinline__ uint32_t bin_key(uint32_t key, uint32_t klo, uint64_t span) {
+    uint64_t bi = ((uint64_t)(key - klo) * (uint64_t)K3_BINS) / span;
+    return bi < (uint64_t)K3_BINS ? (uint32_t)bi : (uint32_t)(K3_BINS - 1);
+}
+
+// Boundary bucket of a mass histogram: walking the bins from the top, the
+// bin where the running mass first reaches `need`.  Wave 0 sums 32 bins per
+// lane; lane 0 then walks lane sums and that lane's bins with one running
+// accumulator, so exactly one bin is chosen whatever the rounding.  Writes
+// found[0] = bin, fd[0] = mass of the bins above it.  If rounding leaves
+// `need` beyond the total, the lowest non-empty bin is chosen.
+__device__ void find_bucket(const double *hm, const uint32_t *hc, double need, double *lane_sum,
+                            uint32_t *found, double *fd) {
+    constexpr int PER = K3_BINS / 64;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        double s = 0.0;
+        for (int t = 0; t < PER; ++t) s += hm[K3_BINS - 1 - lane * PER - t];
+        lane_sum[lane] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double acc = 0.0;
+        int l = 0;
+        for (; l < 63; ++l) {
+            if (acc + lane_sum[l] >= need) break;
+            acc += lane_sum[l];
+        }
+        uint32_t pick = NONE, last_nonempty = NONE;
+        double pick_above = 0.0, last_above = 0.0;
+        for (int ll = l; ll < 64 && pick == NONE; ++ll) {
+            for (int t = 0; t < PER; ++t) {
+                const int bin = K3_BINS - 1 - ll * PER - t;
+                const double mbin = hm[bin];
+                if (hc[bin] > 0) {
+                    last_nonempty = (uint32_t)bin;
+                    last_above = acc;
+                }
+                if (mbin > 0.0 && acc + mbin >= need) {
+                    pick = (uint32_t)bin;
+                    pick_above = acc;
+                    break;
+                }
+                acc += mbin;
+            }
+        }
+        if (pick == NONE) {
+            pick = (last_nonempty == NONE) ? 0u : last_nonempty;
+            pick_above = last_above;
+        }
+        found[0] = pick;
+        fd[0] = pick_above;
+    }
+    __syncthreads();
+}
+
+// Is x (key k) inside the selected bucket of every level < nlev?
+__device__ __forceinline__ bool in_play(const FallbackShared &S, float x, uint32_t k, int nlev) {
+    if (nlev == 0) return true;
+    if (bin_value(x, S.lv_lo, S.lv_scale) != S.lv_bin[0]) return false;
+    for (int l = 1; l < nlev; ++l)
+        if (bin_key(k, S.lv_klo[l], S.lv_span[l]) != S.lv_bin[l]) return false;
+    return true;
+}
+
+// Visit every element (x transformed, id j) of row b; f(x, j).
+template <int DT, bool AL, class F>
+__device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
+    const void *rowp = row_ptr(P, DT, b);
+    const int64_t V = P.V;
+    for (int64_t s0 = 0; s0 < V; s0 += K3_SEG) {
+        const int64_t s1 = min(s0 + (int64_t)K3_SEG, V);
+        if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
+        for (int64_t j = s0 + (int64_t)threadIdx.x * VEC; j < s1; j += (int64_t)K3_THREADS * VEC) {
+            int64_t rem = s1 - j;
+            int nv = rem >= 8 ? 8 : (int)rem;
+            float x[8];
+            load8<DT, AL>(rowp, j, nv, x);
+            uint32_t bits = 0;
+            if (P.pen) {
+                int64_t r = j - s0;
+                bits = (bm[r >> 5] >> (r & 31)) & 0xffu;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < nv) f(xform(x[i], (bits >> i) & 1u, P), (uint32_t)(j + i));
+        }
+    }
+    __syncthreads();
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
+    __shared__ FallbackShared S;
+    const int tid = threadIdx.x;
+    const int b = xcd_row(blockIdx.x, gridDim.x);
+    RowInfo info = W.info[b];
+    if (info.kind != KIND_FALLBACK) return;
+    const Mode md = row_mode(P, b);
+    const double m = (double)info.m;
+
+    uint64_t Tstar;
+    double ZK;
+    if (md.p <= 0.0f) {
+        Tstar = mkcomp(info.m, info.idx0);
+        ZK = 1.0;
+    } else {
+        double above = 0.0, target = 0.0;
+        int nlev = 0;
+        int path = 0;  // 1 collect, 2 ties
+        uint32_t bsel = 0, bcnt = 0, bklo = 0;
+        for (int level = 0; level < 6; ++level) {
+            // bin function of this level
+            float lo = 0.0f, scale = 0.0f;
+            uint32_t klo = 0;
+            uint64_t span = 1;
+            if (level == 0) {
+                lo = info.xmin;
+                scale = (info.m > info.xmin) ? (float)K3_BINS / (info.m - info.xmin) : 0.0f;
+            } else {
+                klo = S.lv_klo[level];
+                span = S.lv_span[level];
+            }
+            for (int i = tid; i < K3_BINS; i += K3_THREADS) {
+                S.hm[i] = 0.0;
+                S.hc[i] = 0u;
+                S.hlo[i] = NONE;
+                S.hhi[i] = 0u;
+            }
+            __syncthreads();
+            double zt = 0.0;
+            row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+                if (!(x > -INFINITY)) return;
+                uint32_t k = f2key(x);
+                if (!in_play(S, x, k, nlev)) return;
+                double e = exp((double)x - m);
+                if (level == 0) zt += e;
+                uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, span);
+                atomicAdd(&S.hm[bi], e);
+                atomicAdd(&S.hc[bi], 1u);
+                atomicMin(&S.hlo[bi], k);
+                atomicMax(&S.hhi[bi], k);
+            });
+            if (level == 0) {
+                double Z = wg_sum_f64<K3_THREADS>(zt, S.scd);
+                target = (double)md.p * Z;
+            }
+            find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
+            const uint32_t fb = S.found[0];
+            const double bbefore = S.fd[0];
+            __syncthreads();
+            above += bbefore;
+            bsel = fb;
+            bcnt = S.hc[fb];
+            bklo = S.hlo[fb];
+            const uint32_t bkhi = S.hhi[fb];
+            __syncthreads();
+            if (tid == 0) {
+                if (level == 0) {
+                    S.lv_lo = lo;
+                    S.lv_scale = scale;
+                }
+                S.lv_bin[level] = fb;
+                if (level + 1 < 8) {
+                    S.lv_klo[level + 1] = bklo;
+                    S.lv_span[level + 1] = (uint64_t)(bkhi - bklo) + 1ull;
+                }
+            }
+            __syncthreads();
+            nlev = level + 1;
+            if (bcnt <= (uint32_t)K3_COLLECT) {
+                path = 1;
+                break;
+            }
+            if (bklo == bkhi) {
+                path = 2;
+                break;
+            }
+        }
+        (void)bsel;
+        if (path == 0) path = 1;  // unreachable: a key range of 1 is reached by level 4
+        if (path == 1) {
+            if (tid == 0) S.counter = 0;
+            __syncthreads();
+            row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+                if (!(x > -INFINITY)) return;
+                uint32_t k = f2key(x);
+                if (!in_play(S, x, k, nlev)) return;
+                uint32_t pos = atomicAdd(&S.counter, 1u);
+                if (pos < (uint32_t)K3_COLLECT) S.coll[pos] = mkcomp(x, j);
+            });
+            const int n = (int)min(S.counter, (uint32_t)K3_COLLECT);
+            const int npad = pow2_ceil(n < 1 ? 1 : n);
+            for (int i = n + tid; i < npad; i += K3_THREADS) S.coll[i] = 0ull;
+            __syncthreads();
+            bitonic_desc<K3_THREADS>(S.coll, npad);
+            // masses of the sorted bucket members, 4 per thread
+            constexpr int PER = K3_COLLECT / K3_THREADS;
+            double ei[PER];
+            double loc = 0.0;
+#pragma unroll
+            for (int t = 0; t < PER; ++t) {
+                int i = tid * PER + t;
+                ei[t] = (i < n) ? exp((double)cval(S.coll[i]) - m) : 0.0;
+                loc += ei[t];
+            }
+            double tot;
+            double run = above + wg_excl_scan_f64<K3_THREADS>(loc, S.scd, tot);
+            uint32_t first = NONE;
+#pragma unroll
+            for (int t = 0; t < PER; ++t) {
+                int i = tid * PER + t;
+                run += ei[t];
+                if (i < n && first == NONE && run >= target) first = (uint32_t)i;
+            }
+            uint32_t fi = wg_min_u32<K3_THREADS>(first, S.sc);
+            if (fi == NONE) fi = (uint32_t)(n > 0 ? n - 1 : 0);  // rounding: whole bucket
+            Tstar = (n > 0) ? S.coll[fi] : mkcomp(info.m, info.idx0);
+            // ZK: mass of every kept element = above + bucket prefix through fi
+            double s = 0.0;
+#pragma unroll
+            for (int t = 0; t < PER; ++t) {
+                int i = tid * PER + t;
+                if (i <= (int)fi && i < n) s += ei[t];
+            }
+            ZK = above + wg_sum_f64<K3_THREADS>(s, S.scd);
+        } else {
+            // every bucket member has the same value: take the c members with
+            // the smallest vocab ids
+            const float xt = key2f(bklo);
+            const double et = exp((double)xt - m);
+            double cnt_need = ceil((target - above) / et);
+            uint32_t cneed = (cnt_need < 1.0) ? 1u : (cnt_need > (double)bcnt ? bcnt : (uint32_t)cnt_need);
+            // c-th smallest index among elements equal to xt: scan in index order
+            const void *rowp = row_ptr(P, DT, b);
+            uint32_t seen = 0;  // uniform running count
+            if (tid == 0) S.found[1] = NONE;
+            __syncthreads();
+            for (int64_t s0 = 0; s0 < P.V && S.found[1] == NONE; s0 += K3_SEG) {
+                const int64_t s1 = min(s0 + (int64_t)K3_SEG, (int64_t)P.V);
+                if (P.pen) build_bitmap<K3_THREADS>(S.bm, s0, s1 - s0, P, b);
+                for (int64_t t0 = s0; t0 < s1; t0 += (int64_t)K3_THREADS * VEC) {
+                    int64_t j = t0 + (int64_t)tid * VEC;
+                    int64_t rem = s1 - j;
+                    int nv = rem <= 0 ? 0 : (rem >= 8 ? 8 : (int)rem);
+                    float x[8];
+                    load8<DT, AL>(rowp, j, nv, x);
+                    uint32_t bits = 0;
+                    if (P.pen && nv > 0) {
+                        int64_t r = j - s0;
+                        bits = (S.bm[r >> 5] >> (r & 31)) & 0xffu;
+                    }
+                    uint32_t mm = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i < nv && xform(x[i], (bits >> i) & 1u, P) == xt) mm |= 1u << i;
+                    uint32_t tot;
+                    uint32_t off = wg_excl_scan_u32<K3_THREADS>(__popc(mm), S.sc, tot);
+                    if (seen + off < cneed && cneed <= seen + off + __popc(mm)) {
+                        uint32_t r = cneed - (seen + off);  // r-th set bit (1-based)
+                        for (int i = 0; i < 8; ++i)
+                            if ((mm >> i) & 1u) {
+                                if (--r == 0) {
+                                    S.found[1] = (uint32_t)(j + i);
+                                    break;
+                                }
+                            }
+                    }
+                    seen += tot;
+                    __syncthreads();
+                    if (S.found[1] != NONE) break;
+                }
+                __syncthreads();
+            }
+            Tstar = mkcomp(xt, S.found[1]);
+            ZK = above + (double)cneed * et;
+        }
+    }
+
+    // ---- exponential race over K = { comp >= T* }, or greedy
+    uint32_t idx = info.idx0;
+    if (md.sm) {
+        Race rc;
+        rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
+        const float *rowq = P.q + (int64_t)b * P.V;
+        row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+            if (mkcomp(x, j) >= Tstar) race_offer(rc, x, rowq[j] + P.eps, j);
+        });
+        Race r = wg_race<K3_THREADS>(rc, S.scx, S.scq, S.sci);
+        idx = r.idx;
+    }
+    if (tid == 0) {
+        P.out_idx[b] = (int64_t)idx;
+        info.kind = KIND_THRESH;
+        info.T = Tstar;
+        info.ZK = ZK;
+        W.info[b] = info;
+    }
+}
+
+// ================================================================== k_dense
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(K4_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
+    __shared__ float tv[TILE4];
+    __shared__ uint32_t tb[TILE4 / 32];
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / L.nt4, t = blockIdx.x % L.nt4;
+    const int64_t V = P.V;
+    const int64_t t0 = (int64_t)t * TILE4, t1 = min(t0 + (int64_t)TILE4, V);
+    const RowInfo info = W.info[b];
+    const bool want_l = (P.flags & NEED_LOGITS) && P.out_logits;
+    const bool want_p = (P.flags & NEED_PROBS) && P.out_probs;
+    if (info.kind == KIND_UNFILTERED && !want_p) return;
+    float *ol = want_l ? P.out_logits + (int64_t)b * V : nullptr;
+    float *op = want_p ? P.out_probs + (int64_t)b * V : nullptr;
+    const double m = (double)info.m, ZK = info.ZK;
+
+    if (info.kind == KIND_LIST) {
+        for (int w = tid; w < TILE4 / 32; w += K4_THREADS) tb[w] = 0u;
+        __syncthreads();
+        const uint64_t *kl = W.klist + (int64_t)b * KMAX;
+        for (int i = tid; i < info.nK; i += K4_THREADS) {
+            uint64_t cv = kl[i];
+            int64_t j = cidx(cv);
+            if (j >= t0 && j < t1) {
+                int r = (int)(j - t0);
+                tv[r] = cval(cv);
+                atomicOr(&tb[r >> 5], 1u << (r & 31));
+            }
+        }
+        __syncthreads();
+        for (int g = 0; g < TILE4 / (K4_THREADS * VEC); ++g) {
+            const int r0 = (g * K4_THREADS + tid) * VEC;
+            const int64_t j = t0 + r0;
+            int64_t rem = t1 - j;
+            if (rem <= 0) continue;
+            const int nv = rem >= 8 ? 8 : (int)rem;
+            const uint32_t bits = (tb[r0 >> 5] >> (r0 & 31)) & 0xffu;
+            if (want_l) {
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = ((bits >> i) & 1u) ? tv[r0 + i] : -INFINITY;
+                store8<AL>(ol, j, nv, o);
+            }
+            if (want_p) {
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    o[i] = ((bits >> i) & 1u) ? (float)(exp((double)tv[r0 + i] - m) / ZK) : 0.0f;
+                store8<AL>(op, j, nv, o);
+            }
+        }
+        return;
+    }
+    if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
+    // K = { comp >= T }: re-read the tile
+    if (P.pen) build_bitmap<K4_THREADS>(bm, t0, t1 - t0, P, b);
+    const void *rowp = row_ptr(P, DT, b);
+    const uint64_t T = info.T;
+    for (int g = 0; g < TILE4 / (K4_THREADS * VEC); ++g) {
+        const int r0 = (g * K4_THREADS + tid) * VEC;
+        const int64_t j = t0 + r0;
+        int64_t rem = t1 - j;
+        if (rem <= 0) continue;
+        const int nv = rem >= 8 ? 8 : (int)rem;
+        float x[8];
+        load8<DT, AL>(rowp, j, nv, x);
+        uint32_t bits = P.pen ? ((bm[r0 >> 5] >> (r0 & 31)) & 0xffu) : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = xform(x[i], (bits >> i) & 1u, P);
+        if (want_l && info.kind == KIND_THRESH) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                o[i] = (mkcomp(x[i], (uint32_t)(j + i)) >= T) ? x[i] : -INFINITY;
+            store8<AL>(ol, j, nv, o);
+        }
+        if (want_p) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                o[i] = (mkcomp(x[i], (uint32_t)(j + i)) >= T)
+                           ? (float)(exp((double)x[i] - m) / ZK)
+                           : 0.0f;
+            store8<AL>(op, j, nv, o);
+        }
+    }
+}
+
+template <class K>
+hipError_t launch(K kern, dim3 grid, dim3 block, size_t shmem, hipStream_t s, const KParams &p,
+                  const KPlan &l, const KWork &w) {
+    if (grid.x == 0) return hipSuccess;
+    hipLaunchKernelGGL(kern, grid, block, shmem, s, p, l, w);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                        hipStream_t s) {
+    dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(K1_THREADS);
+    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
+    if (dtype == 1)
+        return al ? launch(k_chunk<1, true>, grid, block, sh, s, p, l, w)
+                  : launch(k_chunk<1, false>, grid, block, sh, s, p, l, w);
+    return al ? launch(k_chunk<0, true>, grid, block, sh, s, p, l, w)
+              : launch(k_chunk<0, false>, grid, block, sh, s, p, l, w);
+}
+
+hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {
+    return launch(k_rows, dim3((unsigned)p.B), dim3(K2_THREADS), 0, s, p, l, w);
+}
+
+hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                           hipStream_t s) {
+    dim3 grid((unsigned)p.B), block(K3_THREADS);
+    if (dtype == 1)
+        return al ? launch(k_fallback<1, true>, grid, block, 0, s, p, l, w)
+                  : launch(k_fallback<1, false>, grid, block, 0, s, p, l, w);
+    return al ? launch(k_fallback<0, true>, grid, block, 0, s, p, l, w)
+              : launch(k_fallback<0, false>, grid, block, 0, s, p, l, w);
+}
+
+hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                        hipStream_t s) {
+    dim3 grid((unsigned)((int64_t)p.B * l.nt4)), block(K4_THREADS);
+    size_t sh = p.pen ? (size_t)(TILE4 / 32) * 4 : 0;
+    if (dtype == 1)
+        return al ? launch(k_dense<1, true>, grid, block, sh, s, p, l, w)
+                  : launch(k_dense<1, false>, grid, block, sh, s, p, l, w);
+    return al ? launch(k_dense<0, true>, grid, block, sh, s, p, l, w)
+              : launch(k_dense<0, false>, grid, block, sh, s, p, l, w);
+}
+
+}  // namespace smp

@@ -1,0 +1,218 @@
+"""Thin ctypes binding of the C ABI in ``include/sampler.h``.
+
+Same entry points, same names; this module only marshals arguments (torch
+tensors -> device pointers, the current HIP stream) and turns return codes
+into exceptions.  Every step of the sampling runs in the HIP kernels of
+``libsampler.so``; there is no other implementation behind these calls, and a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsampler.so")
+
+SAMPLER_OK, SAMPLER_EINVAL, SAMPLER_ENOMEM, SAMPLER_EHIP = 0, -1, -2, -3
+SAMPLER_F32, SAMPLER_BF16 = 0, 1
+SAMPLER_ROW_TOPK, SAMPLER_ROW_TOPP, SAMPLER_ROW_SAMPLE, SAMPLER_ROW_ALL = 1, 2, 4, 7
+SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_PROFILE = 1, 2, 256
+SAMPLER_TOPK_MAX = 1024
+SAMPLER_VOCAB_MAX = 1 << 21
+
+EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_last_profile",
+           "sampler_destroy", "sampler_strerror")
+
+
+class SamplerError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {sampler_strerror(code)} ({code})")
+        self.code = code
+
+
+class sampler_opts(ctypes.Structure):
+    _fields_ = [("topk_guess", ctypes.c_int32), ("chunks_per_row", ctypes.c_int32)]
+
+
+class sampler_args(ctypes.Structure):
+    _fields_ = [
+        ("logits", ctypes.c_void_p),
+        ("ld", ctypes.c_int64),
+        ("top_k", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("temperature", ctypes.c_float),
+        ("repetition_penalty", ctypes.c_float),
+        ("penalty_ids", ctypes.c_void_p),
+        ("penalty_offsets", ctypes.c_void_p),
+        ("row_flags", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
+        ("out_idx", ctypes.c_void_p),
+        ("out_logits", ctypes.c_void_p),
+        ("out_probs", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsampler.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP sampler library not found at {path}; build it with "
+            "`python -m decode_token_sampling_row_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.sampler_create.argtypes = [ctypes.POINTER(P), ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.POINTER(sampler_opts)]
+    lib.sampler_create.restype = ctypes.c_int
+    lib.sampler_check.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sampler_args)]
+    lib.sampler_check.restype = ctypes.c_int
+    lib.sampler_run.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sampler_args), P]
+    lib.sampler_run.restype = ctypes.c_int
+    lib.sampler_last_profile.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]
+    lib.sampler_last_profile.restype = ctypes.c_int
+    lib.sampler_destroy.argtypes = [P]
+    lib.sampler_destroy.restype = ctypes.c_int
+    lib.sampler_strerror.argtypes = [ctypes.c_int]
+    lib.sampler_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def sampler_strerror(code: int) -> str:
+    return load_library().sampler_strerror(int(code)).decode()
+
+
+def sampler_create(max_batch: int, vocab: int, dtype: int, topk_guess: int = 0,
+                   chunks_per_row: int = 0) -> ctypes.c_void_p:
+    """sampler_create on the current HIP device; returns the handle."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    opts = sampler_opts(int(topk_guess), int(chunks_per_row))
+    rc = lib.sampler_create(ctypes.byref(h), int(max_batch), int(vocab), int(dtype),
+                            ctypes.byref(opts))
+    if rc != SAMPLER_OK:
+        raise SamplerError(rc, "sampler_create")
+    return h
+
+
+def sampler_destroy(h) -> None:
+    rc = load_library().sampler_destroy(h)
+    if rc != SAMPLER_OK:
+        raise SamplerError(rc, "sampler_destroy")
+
+
+def _ptr(t, dtype=None, what=""):
+    if t is None:
+        return None
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
+              temperature=1.0, repetition_penalty=1.0, penalty_ids=None,
+              penalty_offsets=None, row_flags=None, out_logits=None, out_probs=None,
+              profile=False) -> sampler_args:
+    """Marshal torch tensors into a sampler_args struct."""
+    import torch
+
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B, ld] with unit column stride")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be float32 or bfloat16")
+    for name, t in (("q", q), ("out_logits", out_logits), ("out_probs", out_probs)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, V]")
+    flags = 0
+    if out_logits is not None:
+        flags |= SAMPLER_NEED_LOGITS
+    if out_probs is not None:
+        flags |= SAMPLER_NEED_PROBS
+    if profile:
+        flags |= SAMPLER_PROFILE
+    a = sampler_args()
+    a.logits = _ptr(logits, None, "logits")
+    a.ld = logits.stride(0)
+    a.top_k = _ptr(top_k, torch.int32, "top_k")
+    a.top_p = _ptr(top_p, torch.float32, "top_p")
+    a.q = _ptr(q, torch.float32, "q")
+    a.eps = float(eps)
+    a.temperature = float(temperature)
+    a.repetition_penalty = float(repetition_penalty)
+    a.penalty_ids = _ptr(penalty_ids, torch.int32, "penalty_ids")
+    a.penalty_offsets = _ptr(penalty_offsets, torch.int64, "penalty_offsets")
+    a.row_flags = _ptr(row_flags, torch.uint8, "row_flags")
+    a.flags = flags
+    a.out_idx = _ptr(out_idx, torch.int64, "out_idx")
+    a.out_logits = _ptr(out_logits, torch.float32, "out_logits")
+    a.out_probs = _ptr(out_probs, torch.float32, "out_probs")
+    return a
+
+
+def sampler_check(h, batch: int, args: sampler_args) -> int:
+    return load_library().sampler_check(h, int(batch), ctypes.byref(args))
+
+
+def sampler_run(h, batch: int, args: sampler_args, stream: Optional[int] = None) -> None:
+    """sampler_run on `stream` (raw hipStream_t; default torch's current stream)."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = load_library().sampler_run(h, int(batch), ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != SAMPLER_OK:
+        raise SamplerError(rc, "sampler_run")
+
+
+def sampler_last_profile(h, n: int = 4):
+    buf = (ctypes.c_float * n)()
+    rc = load_library().sampler_last_profile(h, buf, int(n))
+    if rc < 0:
+        raise SamplerError(rc, "sampler_last_profile")
+    return [float(buf[i]) for i in range(rc)]
+
+
+class Sampler:
+    """Owns one handle; ``run`` marshals tensors and calls sampler_run."""
+
+    def __init__(self, max_batch: int, vocab: int, dtype, topk_guess: int = 0,
+                 chunks_per_row: int = 0):
+        import torch
+
+        dt = SAMPLER_BF16 if dtype in (torch.bfloat16, SAMPLER_BF16, "bf16") else SAMPLER_F32
+        self.vocab = int(vocab)
+        self.dtype = dt
+        self.handle = sampler_create(max_batch, vocab, dt, topk_guess, chunks_per_row)
+
+    def run(self, logits, out_idx, stream=None, **kw) -> None:
+        args = make_args(logits, out_idx, **kw)
+        sampler_run(self.handle, logits.shape[0], args, stream)
+
+    def last_profile(self):
+        return sampler_last_profile(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            sampler_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -5,7 +5,9 @@ holds none of the sampler's arithmetic, so the HIP path and the CPU oracle can
 both be fed from it without sharing any of the method.
 
 Every array comes from ``numpy.random.default_rng(SeedSequence([cfg, stream,
-seed]))`` with fixed streams:
+seed]))`` -- [B, V] arrays from one generator per block of 16 rows,
+``SeedSequence([cfg, stream, seed, block])``, filled on several host threads
+(the values do not depend on the thread count) -- with fixed streams:
 
     0 logits   1 q   2 top_k   3 top_p   4 history ids   5 spike positions
     6 spike sizes   7 row choice (rows whose k is zeroed)
@@ -37,8 +39,33 @@ F32, BF16 = "f32", "bf16"
 S_LOGITS, S_Q, S_TOPK, S_TOPP, S_IDS, S_POS, S_SIZE, S_ROWS = range(8)
 
 
-def _rng(cfg: int, stream: int, seed: int) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([cfg, stream, seed]))
+ROW_BLOCK = 16
+
+
+def _rng(cfg: int, stream: int, seed: int, *extra: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([cfg, stream, seed, *extra]))
+
+
+def _rows(cfg: int, stream: int, seed: int, B: int, V: int, draw) -> np.ndarray:
+    """[B, V] float32 filled block by block: draw(generator, rows, V)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+
+    out = np.empty((B, V), np.float32)
+
+    def fill(blk):
+        r0, r1 = blk * ROW_BLOCK, min(B, (blk + 1) * ROW_BLOCK)
+        out[r0:r1] = draw(_rng(cfg, stream, seed, blk), r1 - r0, V)
+
+    nblk = (B + ROW_BLOCK - 1) // ROW_BLOCK
+    workers = max(1, min(16, os.cpu_count() or 1, nblk))
+    if workers == 1:
+        for i in range(nblk):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -89,13 +116,19 @@ def _store(x32: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _q(cfg: int, B: int, V: int, seed: int) -> np.ndarray:
-    return _rng(cfg, S_Q, seed).standard_exponential((B, V), dtype=np.float32)
+    return _rows(cfg, S_Q, seed, B, V,
+                 lambda g, n, v: g.standard_exponential((n, v), dtype=np.float32))
+
+
+def _normal(cfg: int, B: int, V: int, seed: int, scale: float) -> np.ndarray:
+    return _rows(cfg, S_LOGITS, seed, B, V,
+                 lambda g, n, v: g.standard_normal((n, v), dtype=np.float32) * np.float32(scale))
 
 
 def config1(B: int = 4, V: int = 32000, seed: int = 0) -> Workload:
     """B=4, V=32000, fp32 N(0, 2^2); T=0.85, k=50, p=0.85 on every row; all
     three stages on; dense filtered logits requested."""
-    x = _rng(1, S_LOGITS, seed).standard_normal((B, V), dtype=np.float32) * np.float32(2.0)
+    x = _normal(1, B, V, seed, 2.0)
     return Workload("cfg1_topk_topp_sample_dense", B, V, F32, _store(x, F32), _q(1, B, V, seed),
                     np.full(B, 50, np.int32), np.full(B, 0.85, np.float32),
                     np.full(B, ALL_STAGES, np.uint8), eps=1e-20, temperature=0.85,
@@ -106,7 +139,7 @@ def config2(B: int = 64, V: int = 151936, seed: int = 0) -> Workload:
     """B=64, V=151936, bf16 of N(0,1) plus 8 spikes of +U[6,10] per row;
     k ~ U{1..1024} with round(10%) of rows set to 0 (stage skipped);
     p ~ U[0.5, 1); sampling on; no dense output."""
-    x = _rng(2, S_LOGITS, seed).standard_normal((B, V), dtype=np.float32)
+    x = _normal(2, B, V, seed, 1.0)
     pos_rng, size_rng = _rng(2, S_POS, seed), _rng(2, S_SIZE, seed)
     n_spk = min(8, V)
     for b in range(B):
@@ -126,17 +159,12 @@ def config3(B: int = 128, V: int = 128256, seed: int = 0) -> Workload:
     """Top-p only (k = 0 on every row): B=128, V=128256, fp32.  Even rows are
     peaked (N(0,1) with 20 entries +12), odd rows flat (N(0, 0.05)).
     p = 0.9 when (row // 2) is even, else 0.99.  Sampling on."""
-    g = _rng(3, S_LOGITS, seed)
-    x = np.empty((B, V), np.float32)
+    x = _normal(3, B, V, seed, 1.0)
+    x[1::2] *= np.float32(0.05)  # flat rows
     pos_rng = _rng(3, S_POS, seed)
     n_spk = min(20, V)
-    for b in range(B):
-        if b % 2 == 0:
-            row = g.standard_normal(V, dtype=np.float32)
-            row[pos_rng.choice(V, size=n_spk, replace=False)] += np.float32(12.0)
-        else:
-            row = g.standard_normal(V, dtype=np.float32) * np.float32(0.05)
-        x[b] = row
+    for b in range(0, B, 2):     # peaked rows
+        x[b, pos_rng.choice(V, size=n_spk, replace=False)] += np.float32(12.0)
     p = np.where((np.arange(B) // 2) % 2 == 0, 0.9, 0.99).astype(np.float32)
     return Workload("cfg3_topp_only_peaked_flat", B, V, F32, _store(x, F32), _q(3, B, V, seed),
                     np.zeros(B, np.int32), p, np.full(B, ALL_STAGES, np.uint8), eps=1e-20)
@@ -146,7 +174,7 @@ def config4(B: int = 256, V: int = 6400, seed: int = 0, hist: int = 512) -> Work
     """Penalty + temperature: B=256, V=6400, fp32 N(0, 3^2); each row has a
     history of 512 ids uniform in [0, V) (duplicates allowed); rho=1.1,
     T=0.85, k=50 (k=1 on rows r % 32 == 0), p=0.85; all stages on."""
-    x = _rng(4, S_LOGITS, seed).standard_normal((B, V), dtype=np.float32) * np.float32(3.0)
+    x = _normal(4, B, V, seed, 3.0)
     ids = _rng(4, S_IDS, seed).integers(0, V, size=B * hist).astype(np.int32)
     offsets = (np.arange(B + 1, dtype=np.int64) * hist)
     k = np.full(B, 50, np.int32)
@@ -160,12 +188,8 @@ def config5(B: int = 1024, V: int = 262144, seed: int = 0) -> Workload:
     """Large batch: B=1024, V=262144, bf16 of 4 * Gumbel(0,1); row r runs
     stage combination r % 8 (bit0 top-k with k=1024, bit1 top-p with
     p=0.95, bit2 sample); dense filtered logits on every row."""
-    g = _rng(5, S_LOGITS, seed)
-    x = np.empty((B, V), np.float32)
-    step = max(1, (1 << 24) // max(V, 1))
-    for b0 in range(0, B, step):
-        b1 = min(B, b0 + step)
-        x[b0:b1] = (4.0 * g.gumbel(0.0, 1.0, size=(b1 - b0, V))).astype(np.float32)
+    x = _rows(5, S_LOGITS, seed, B, V,
+              lambda g, n, v: (4.0 * g.gumbel(0.0, 1.0, size=(n, v))).astype(np.float32))
     flags = (np.arange(B) % 8).astype(np.uint8)
     return Workload("cfg5_large_batch_8_combos", B, V, BF16, _store(x, BF16), _q(5, B, V, seed),
                     np.full(B, 1024, np.int32), np.full(B, 0.95, np.float32), flags,

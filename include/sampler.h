@@ -1,0 +1,160 @@
+/*
+ * sampler.h -- C ABI of the MI355X (gfx950) batched logits sampler.
+ *
+ * One call post-processes a [batch, vocab] logits matrix, row by row:
+ *
+ *   1. repetition penalty over the row's history ids: a logit x of a token
+ *      that appears in the history becomes x / rho when x > 0, else x * rho;
+ *      each distinct id counts once, ids outside [0, vocab) are ignored
+ *      (MiniMind generation chapter, sec. 10.7 "repetition penalty"; the C++
+ *      post-processing blog, repetition_penalty);
+ *   2. temperature: x / T (MiniMind sec. 10.4);  -0 is then written as +0;
+ *   3. top-k: when the row's top-k bit is set and 1 <= k <= min(vocab, 1024),
+ *      keep exactly the k largest logits, ties broken by the smaller vocab id;
+ *      any other k skips the stage (Ascend torch_npu npu_top_k_top_p_sample
+ *      page, topK section: valid range and Card(top_k_value) = top_k);
+ *   4. softmax over the survivors (same page, topK/topP sections);
+ *   5. top-p: when the row's top-p bit is set and p < 1, keep the shortest
+ *      prefix of the survivors (in the order of step 3) whose probability
+ *      mass reaches p; the first survivor is always kept; p >= 1 or NaN skips
+ *      the stage (Ascend page topP section; MiniMind sec. 10.6);
+ *   6. exponential sampling: with the sample bit set, the output token is the
+ *      kept id i maximising softmax_K(x)_i / (q[row, i] + eps), lowest id on
+ *      exact ties -- q is paired with candidates by vocabulary id; without it
+ *      the output is the first kept token, i.e. the greedy argmax (Ascend
+ *      page, Sample section; MiniMind sec. 10.8);
+ *   7. optional dense outputs: the filtered logits (x at kept ids, -inf
+ *      elsewhere; the Ascend page's logits_top_kp_select) and the
+ *      probabilities renormalised over the kept set (0 elsewhere).
+ *
+ * Every step runs in hand-written HIP kernels on the caller's stream; the
+ * library never copies data to the host and never synchronises in
+ * sampler_run.
+ */
+#ifndef MI355X_SAMPLER_H
+#define MI355X_SAMPLER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define SAMPLER_OK 0
+#define SAMPLER_EINVAL (-1)   /* null / inconsistent argument               */
+#define SAMPLER_ENOMEM (-2)   /* device workspace allocation failed         */
+#define SAMPLER_EHIP (-3)     /* HIP runtime or kernel launch error         */
+
+/* ---- logits storage types ---------------------------------------------- */
+#define SAMPLER_F32 0
+#define SAMPLER_BF16 1
+
+/* ---- per-row stage bits (row_flags[b]) ----------------------------------- */
+#define SAMPLER_ROW_TOPK 1u
+#define SAMPLER_ROW_TOPP 2u
+#define SAMPLER_ROW_SAMPLE 4u
+#define SAMPLER_ROW_ALL 7u
+
+/* ---- call flags (sampler_args.flags) ------------------------------------- */
+#define SAMPLER_NEED_LOGITS 1u  /* write out_logits                          */
+#define SAMPLER_NEED_PROBS 2u   /* write out_probs (debug; re-reads logits)  */
+#define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
+                                   figures with sampler_last_profile         */
+
+/* Largest k of the top-k stage and largest top-k guess. */
+#define SAMPLER_TOPK_MAX 1024
+/* Largest vocabulary the library accepts. */
+#define SAMPLER_VOCAB_MAX (1 << 21)
+
+typedef struct sampler_s sampler_t;
+
+/* Tuning knobs.  None of them changes any result. */
+typedef struct sampler_opts {
+    /* Size G of the top-k guess used for top-p rows whose top-k stage is off
+     * (Ascend page, topP section: the guess succeeds when the G most likely
+     * tokens already hold mass >= p; otherwise a full-row cutoff search
+     * runs).  0 = default (256); otherwise 1..1024. */
+    int32_t topk_guess;
+    /* Chunks each row is split into for the streaming pass.  0 = default
+     * (8); otherwise 1..8. */
+    int32_t chunks_per_row;
+} sampler_opts;
+
+/*
+ * Arguments of one call.  All array pointers are DEVICE pointers on the
+ * handle's device; the caller owns every buffer.  Shapes use B = batch of
+ * the call and V = the handle's vocab.
+ */
+typedef struct sampler_args {
+    const void *logits;        /* [B, ld] row-major, SAMPLER_F32 or _BF16 */
+    int64_t ld;                /* row stride of logits in elements, >= V   */
+    const int32_t *top_k;      /* [B] or NULL (top-k off for every row)    */
+    const float *top_p;        /* [B] or NULL (top-p off for every row)    */
+    const float *q;            /* [B, V] fp32 sampling weights, row stride V;
+                                  NULL = sampling off for every row         */
+    float eps;                 /* >= 0, added to q                         */
+    float temperature;         /* > 0; 1 = stage off                        */
+    float repetition_penalty;  /* > 0; 1 = stage off                        */
+    const int32_t *penalty_ids;     /* [nnz] history ids, or NULL          */
+    const int64_t *penalty_offsets; /* [B+1] CSR offsets into penalty_ids */
+    const uint8_t *row_flags;  /* [B] SAMPLER_ROW_* bits, NULL = all on     */
+    uint32_t flags;            /* SAMPLER_NEED_LOGITS | _NEED_PROBS | _PROFILE */
+    int64_t *out_idx;          /* [B] sampled (or greedy) vocab id          */
+    float *out_logits;         /* [B, V] row stride V; iff NEED_LOGITS      */
+    float *out_probs;          /* [B, V] row stride V; iff NEED_PROBS       */
+} sampler_args;
+
+/*
+ * Create a handle for batches of at most max_batch rows of vocab V logits of
+ * the given storage type on the current HIP device.  Allocates the device
+ * workspace (about 72 KiB per row).  opts may be NULL.
+ * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
+ * (max_batch < 1, V < 1 or > SAMPLER_VOCAB_MAX, unknown dtype, bad opts),
+ * SAMPLER_ENOMEM or SAMPLER_EHIP.
+ */
+int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtype,
+                   const sampler_opts *opts);
+
+/*
+ * Check the arguments of a call without touching the GPU.  Returns SAMPLER_OK
+ * or SAMPLER_EINVAL: batch outside [0, max_batch], logits / out_idx NULL,
+ * ld < V, temperature or penalty not finite and > 0, eps negative or not
+ * finite, a requested dense output with a NULL buffer, exactly one of the
+ * penalty arrays NULL, unknown flag bits, or row_flags == NULL (every row
+ * samples) with q == NULL.
+ * Per-row values are never errors: k outside [1, min(V, 1024)] skips top-k,
+ * p >= 1 or NaN skips top-p, history ids outside [0, V) are ignored.
+ */
+int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a);
+
+/*
+ * Run one call on `stream` (a hipStream_t; NULL = the null stream).
+ * Asynchronous: outputs are valid once the stream has completed.  Runs
+ * sampler_check first.  The handle's workspace is reused by every call, so
+ * calls with one handle must be ordered on one stream (not thread-safe).
+ * Rows whose logits are NaN, or entirely -inf, are outside the contract.
+ * Returns SAMPLER_OK, SAMPLER_EINVAL or SAMPLER_EHIP (launch failure).
+ */
+int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream);
+
+/*
+ * Kernel times of the last sampler_run made with SAMPLER_PROFILE, in
+ * milliseconds, in launch order: [0] chunk pass, [1] row merge/cutoff/sample,
+ * [2] full-row top-p cutoff (rows whose guess failed), [3] dense writer.
+ * Waits for that call to finish.  Kernels that were not launched read 0.
+ * Returns the number of entries written (<= n), or a negative error code.
+ */
+int sampler_last_profile(sampler_t *h, float *ms, int32_t n);
+
+/* Free the workspace and the handle.  NULL is accepted. */
+int sampler_destroy(sampler_t *h);
+
+/* Static description of a return code. */
+const char *sampler_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355X_SAMPLER_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C-ABI library that need no GPU: it builds, loads,
+exports every entry point the header declares, the Python argument structs
+match the C layout, and argument validation that runs before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from decode_token_sampling_row_amd import sampler as smp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sampler.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(smp.LIB_PATH):
+        from decode_token_sampling_row_amd import build
+
+        build.build()
+    return smp.load_library()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sampler_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(smp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", smp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for name in _declared():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_args_struct_layout_matches_header():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "sampler.h"
+    #define O(f) printf("%zu ", offsetof(sampler_args, f))
+    int main(void) {
+      printf("%zu %zu ", sizeof(sampler_args), sizeof(sampler_opts));
+      O(logits); O(ld); O(top_k); O(top_p); O(q); O(eps); O(temperature);
+      O(repetition_penalty); O(penalty_ids); O(penalty_offsets); O(row_flags);
+      O(flags); O(out_idx); O(out_logits); O(out_probs);
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    A = smp.sampler_args
+    want = [ctypes.sizeof(A), ctypes.sizeof(smp.sampler_opts)] + [getattr(A, f).offset
+                                                                   for f, _ in A._fields_]
+    assert got == want
+
+
+def test_constants_match_header():
+    txt = open(HEADER).read()
+
+    def val(name):
+        m = re.search(rf"#define {name} \(?(-?[0-9u]+)", txt)
+        return int(m.group(1).rstrip("u"))
+
+    for name in ["SAMPLER_OK", "SAMPLER_EINVAL", "SAMPLER_ENOMEM", "SAMPLER_EHIP",
+                 "SAMPLER_F32", "SAMPLER_BF16", "SAMPLER_ROW_TOPK", "SAMPLER_ROW_TOPP",
+                 "SAMPLER_ROW_SAMPLE", "SAMPLER_ROW_ALL", "SAMPLER_NEED_LOGITS",
+                 "SAMPLER_NEED_PROBS", "SAMPLER_PROFILE", "SAMPLER_TOPK_MAX"]:
+        assert getattr(smp, name) == val(name), name
+
+
+def test_create_rejects_bad_arguments_before_touching_the_gpu(lib):
+    h = ctypes.c_void_p()
+    bad = [(0, 10, 0), (-1, 10, 0), (4, 0, 0), (4, (1 << 21) + 1, 0), (4, 10, 2), (4, 10, -1)]
+    for mb, v, dt in bad:
+        assert lib.sampler_create(ctypes.byref(h), mb, v, dt, None) == smp.SAMPLER_EINVAL
+    for g, c in [(-1, 0), (1025, 0), (0, 9), (0, -2)]:
+        o = smp.sampler_opts(g, c)
+        assert lib.sampler_create(ctypes.byref(h), 4, 100, 0, ctypes.byref(o)) == smp.SAMPLER_EINVAL
+    assert lib.sampler_create(None, 4, 100, 0, None) == smp.SAMPLER_EINVAL
+
+
+def test_null_handle_paths(lib):
+    a = smp.sampler_args()
+    assert lib.sampler_check(None, 1, ctypes.byref(a)) == smp.SAMPLER_EINVAL
+    assert lib.sampler_run(None, 1, ctypes.byref(a), None) == smp.SAMPLER_EINVAL
+    assert lib.sampler_destroy(None) == smp.SAMPLER_OK
+    buf = (ctypes.c_float * 4)()
+    assert lib.sampler_last_profile(None, buf, 4) == smp.SAMPLER_EINVAL
+
+
+def test_strerror(lib):
+    assert smp.sampler_strerror(0) == "ok"
+    assert "invalid" in smp.sampler_strerror(-1)
+    assert smp.sampler_strerror(12345) == "unknown error"
+
+
+def test_create_without_gpu_reports_hip_error(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    assert lib.sampler_create(ctypes.byref(h), 4, 100, 0, None) == smp.SAMPLER_EHIP

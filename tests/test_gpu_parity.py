@@ -1,0 +1,273 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Seeded inputs from ``workloads``; reduced sizes compare every row, the full
+sizes compare sampled rows in the launch configuration the benchmark uses.
+Edge cases: tiny and ragged vocabularies, segment boundaries, k = V, exact
+ties everywhere, signed zeros and -inf, padded row strides, every stage
+combination, top-p boundary cases that need the full-row search, and the
+tuning knobs (guess size, chunks per row), which must not change anything.
+"""
+import numpy as np
+import pytest
+
+from decode_token_sampling_row_amd import workloads as wl
+
+from gpu_util import compare, device_inputs, run_hip, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    from decode_token_sampling_row_amd import sampler
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sampler.load_library()  # fails loudly when the HIP library is missing
+    yield
+
+
+def _log(label, stats):
+    print(f"[parity] {label}: {stats}", flush=True)
+
+
+SMALL = [
+    ("cfg1_full", 1, None, None),
+    ("cfg4_full", 4, None, None),
+    ("cfg2_B24_V20008", 2, 24, 20008),
+    ("cfg2_B12_V20011_unaligned", 2, 12, 20011),
+    ("cfg3_B16_V30000", 3, 16, 30000),
+    ("cfg5_B32_V40000", 5, 32, 40000),
+    ("cfg4_B64_V6403_unaligned", 4, 64, 6403),
+    ("cfg1_B8_V70000", 1, 8, 70000),
+]
+
+
+@pytest.mark.parametrize("label,cfg,B,V", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_every_row(label, cfg, B, V):
+    W = wl.make(cfg, B=B, V=V, seed=1)
+    print(f"[case] {label} B={W.B} V={W.V} dtype={W.dtype}", flush=True)
+    hip = run_hip(W, need_logits=True, need_probs=True)
+    ref = run_oracle(W, need_logits=True, need_probs=True)
+    _log(label, compare(W, hip, ref, label=label))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_parity_full_size_sampled_rows(cfg):
+    import torch
+
+    W = wl.make(cfg, seed=0)
+    print(f"[case] full cfg{cfg} B={W.B} V={W.V}", flush=True)
+    hip = run_hip(W, need_logits=W.need_logits)
+    rng = np.random.default_rng(cfg)
+    rows = np.unique(np.concatenate([np.arange(min(W.B, 16)),
+                                     rng.choice(W.B, size=min(W.B, 16), replace=False)]))
+    ref = run_oracle(W, need_logits=W.need_logits, rows=rows)
+    _log(f"full cfg{cfg}", compare(W, hip, ref, rows=rows, label=f"full cfg{cfg}"))
+    torch.cuda.empty_cache()
+
+
+def _custom(x, top_k=None, top_p=None, flags=7, q=None, dtype=wl.F32, seed=0, **kw):
+    x = np.asarray(x, np.float32)
+    B, V = x.shape
+    rng = np.random.default_rng(seed)
+    if q is None:
+        q = rng.standard_exponential((B, V)).astype(np.float32)
+    logits = wl.to_bf16_bits(x) if dtype == wl.BF16 else x
+    bc = lambda v, dt: None if v is None else np.broadcast_to(np.asarray(v, dt), (B,)).copy()
+    return wl.Workload("custom", B, V, dtype, logits, q, bc(top_k, np.int32),
+                       bc(top_p, np.float32), bc(flags, np.uint8), **kw)
+
+
+def _check(W, label, need_probs=True, **kw):
+    print(f"[case] {label} B={W.B} V={W.V}", flush=True)
+    hip = run_hip(W, need_logits=True, need_probs=need_probs, **kw)
+    ref = run_oracle(W, need_logits=True, need_probs=need_probs)
+    _log(label, compare(W, hip, ref, label=label))
+    return hip, ref
+
+
+def _all_combos(B):
+    return (np.arange(B) % 8).astype(np.uint8)
+
+
+@pytest.mark.parametrize("V", [1, 2, 5, 63, 64, 65, 1000, 2047, 2048, 2049])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_tiny_and_ragged_vocab(V, dtype):
+    rng = np.random.default_rng(V)
+    B = 16
+    x = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+    k = rng.integers(0, min(V, 1024) + 2, size=B)
+    p = rng.uniform(0.0, 1.0, size=B)
+    W = _custom(x, top_k=k, top_p=p, flags=_all_combos(B), dtype=dtype)
+    _check(W, f"tiny V={V} {dtype}")
+
+
+@pytest.mark.parametrize("V", [8191, 8192, 8193, 32768, 32769])
+def test_segment_boundaries(V):
+    rng = np.random.default_rng(V)
+    B = 16
+    x = (rng.standard_normal((B, V)) * 3).astype(np.float32)
+    k = np.array([1, 2, 50, 1023, 1024, 1024, 0, 7] * 2)
+    W = _custom(x, top_k=k, top_p=0.9, flags=_all_combos(B))
+    _check(W, f"segments V={V}")
+
+
+def test_k_equals_vocab_and_cap():
+    rng = np.random.default_rng(3)
+    for V, ks in [(700, [700, 699, 1, 701]), (1024, [1024, 1023]), (5000, [1024, 1025])]:
+        x = (rng.standard_normal((len(ks), V))).astype(np.float32)
+        W = _custom(x, top_k=ks, top_p=0.97, flags=[1, 3, 5, 7][: len(ks)])
+        _check(W, f"k~V V={V}")
+
+
+def test_exact_ties_everywhere():
+    B, V = 16, 30000
+    x = np.zeros((B, V), np.float32)
+    x[1::2] = np.round(np.random.default_rng(5).standard_normal((B // 2, V)) * 2) / 2
+    for dt in (wl.F32, wl.BF16):
+        W = _custom(x, top_k=np.array([10, 1024, 1, 0] * 4), top_p=0.5, flags=_all_combos(B),
+                    dtype=dt)
+        _check(W, f"ties {dt}")
+
+
+def test_signed_zero_and_neg_inf():
+    rng = np.random.default_rng(9)
+    B, V = 16, 5000
+    x = (rng.standard_normal((B, V))).astype(np.float32)
+    x[:, ::7] = -0.0
+    x[:, 3::11] = 0.0
+    x[:, 5::13] = -np.inf
+    W = _custom(x, top_k=np.array([100, 0] * 8), top_p=0.95, flags=_all_combos(B))
+    hip, _ = _check(W, "zeros/-inf")
+    assert not np.signbit(hip["logits"][np.isfinite(hip["logits"]) & (hip["logits"] == 0)]).any()
+
+
+@pytest.mark.parametrize("pad", [8, 3])
+def test_padded_row_stride(pad):
+    W = wl.make(5, B=16, V=20000, seed=2)
+    _check(W, f"ld=V+{pad}", ld_pad=pad)
+
+
+@pytest.mark.parametrize("guess,chunks", [(1, 8), (16, 1), (1024, 3), (256, 8), (64, 5)])
+def test_knobs_do_not_change_results(guess, chunks):
+    W = wl.make(3, B=8, V=30000, seed=4)
+    W.row_flags = np.array([2, 6, 3, 7, 2, 6, 1, 0], np.uint8)
+    W.top_k = np.array([0, 0, 40, 1024, 0, 0, 77, 0], np.int32)
+    base = run_hip(W, need_logits=True, need_probs=True)
+    other = run_hip(W, need_logits=True, need_probs=True, guess=guess, chunks=chunks)
+    np.testing.assert_array_equal(base["idx"], other["idx"])
+    np.testing.assert_array_equal(base["logits"].view(np.uint32), other["logits"].view(np.uint32))
+    np.testing.assert_array_equal(base["probs"], other["probs"])
+
+
+def test_repeated_runs_bit_identical():
+    import torch
+
+    from decode_token_sampling_row_amd.sampler import Sampler
+
+    W = wl.make(5, B=64, V=50000, seed=6)
+    d = device_inputs(W)
+    s = Sampler(W.B, W.V, torch.bfloat16)
+    first = run_hip(W, need_logits=True, sampler=s, inputs=d)
+    for _ in range(4):
+        again = run_hip(W, need_logits=True, sampler=s, inputs=d)
+        np.testing.assert_array_equal(first["idx"], again["idx"])
+        np.testing.assert_array_equal(first["logits"].view(np.uint32),
+                                      again["logits"].view(np.uint32))
+
+
+def test_fallback_with_huge_tie_block():
+    """The top-p cutoff falls inside a block of >4096 equal logits: the kept
+    members of the block are the ones with the smallest vocab ids."""
+    B, V = 4, 30000
+    x = np.full((B, V), -2.0, np.float32)
+    x[:, :10] = 3.0
+    x[:, 5000:25000] = 0.0
+    W = _custom(x, top_k=0, top_p=np.array([0.5, 0.9, 0.3, 0.7]), flags=[2, 6, 2, 6])
+    _check(W, "tie block")
+
+
+def test_flat_rows_force_full_row_search():
+    rng = np.random.default_rng(11)
+    B, V = 8, 128256
+    x = (rng.standard_normal((B, V)) * 0.05).astype(np.float32)
+    W = _custom(x, top_k=0, top_p=np.array([0.9, 0.99, 0.5, 0.999, 0.1, 0.95, 0.75, 0.6]),
+                flags=[2, 6] * 4)
+    _check(W, "flat full-row search")
+
+
+def test_top_p_nonpositive_keeps_one():
+    rng = np.random.default_rng(12)
+    B, V = 8, 9000
+    x = (rng.standard_normal((B, V))).astype(np.float32)
+    W = _custom(x, top_k=np.array([0, 0, 30, 30, 0, 0, 5, 5]), top_p=np.array(
+        [0.0, -1.0, 0.0, -0.5, 1e-30, 0.0, 1.0, 2.0]), flags=[2, 6, 3, 7, 6, 2, 7, 3])
+    hip, ref = _check(W, "p<=0")
+    assert (np.isfinite(hip["logits"]).sum(axis=1)[:6] == 1).all()
+
+
+def test_penalty_ids_out_of_range_and_duplicates():
+    rng = np.random.default_rng(13)
+    B, V = 8, 4000
+    x = (rng.standard_normal((B, V)) * 3).astype(np.float32)
+    ids = np.concatenate([rng.integers(-50, V + 50, size=300) for _ in range(B)]).astype(np.int32)
+    offs = (np.arange(B + 1) * 300).astype(np.int64)
+    for rho in (1.3, 0.7):
+        W = _custom(x, top_k=np.array([50, 0] * 4), top_p=0.8, flags=_all_combos(B),
+                    penalty=rho, temperature=0.7, ids=ids, offsets=offs)
+        _check(W, f"penalty rho={rho}")
+
+
+def test_empty_batch_and_argument_checks():
+    import ctypes
+
+    import torch
+
+    from decode_token_sampling_row_amd import sampler as smp
+
+    s = smp.Sampler(4, 100, torch.float32)
+    lib = smp.load_library()
+    x = torch.zeros((4, 100), device="cuda")
+    idx = torch.zeros(4, dtype=torch.int64, device="cuda")
+    q = torch.ones((4, 100), device="cuda")
+    good = smp.make_args(x, idx, q=q)
+    assert smp.sampler_check(s.handle, 4, good) == 0
+    assert smp.sampler_check(s.handle, 0, smp.sampler_args()) == 0
+    smp.sampler_run(s.handle, 0, smp.sampler_args())  # empty batch: no-op
+    assert smp.sampler_check(s.handle, 5, good) == smp.SAMPLER_EINVAL
+    for field, val in [("temperature", 0.0), ("temperature", float("inf")),
+                       ("repetition_penalty", -1.0), ("eps", -1e-3), ("flags", 8),
+                       ("ld", 99), ("out_idx", None), ("logits", None)]:
+        a = smp.make_args(x, idx, q=q)
+        setattr(a, field, val)
+        assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL, field
+    a = smp.make_args(x, idx, q=q)
+    a.flags = smp.SAMPLER_NEED_LOGITS
+    assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL
+    a = smp.make_args(x, idx)  # every row samples (row_flags NULL) but no q
+    assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL
+    a = smp.make_args(x, idx, q=q)
+    a.penalty_ids = a.q
+    assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL
+    with pytest.raises(smp.SamplerError):
+        smp.sampler_run(s.handle, 4, a)
+    s.close()
+    del lib, ctypes
+
+
+def test_profile_reports_kernel_times():
+    import torch
+
+    from decode_token_sampling_row_amd.sampler import Sampler
+
+    W = wl.make(5, B=16, V=40000, seed=3)
+    d = device_inputs(W)
+    s = Sampler(W.B, W.V, torch.bfloat16)
+    out_idx = torch.zeros(W.B, dtype=torch.int64, device="cuda")
+    out_l = torch.empty((W.B, W.V), device="cuda")
+    s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"],
+          row_flags=d["row_flags"], out_logits=out_l, profile=True)
+    ms = s.last_profile()
+    assert len(ms) == 4 and all(t >= 0 for t in ms) and ms[0] > 0 and ms[3] > 0
