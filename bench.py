@@ -1,0 +1,197 @@
+"""Benchmark of the batched logits sampler on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
+
+A step is one sampler_run over one batch: the whole hot path (penalty,
+temperature, top-k, softmax, top-p, exponential race, dense filtered
+logits) on synthetic logits already resident in HBM.  The default workload
+is batch 1024 x vocab 262144 bf16 logits (4 x Gumbel), rows cycling through
+the eight top-k / top-p / sample combinations, dense output on every row.
+
+Prints one JSON line: rows/s (value), ms per step, achieved HBM GB/s of the
+path's algorithmic bytes, a roofline entry for the dominant kernel (timed with
+HIP events on the stream it runs on), and the CPU oracle timed on a bounded
+sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at batch x vocab"
+KERNELS = ["k_stream", "k_select", "k_rows", "k_fallback", "k_dense"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    return ap.parse_args()
+
+
+def model_bytes(W, kept):
+    """Algorithmic bytes per call, per kernel, from the per-row model:
+    logits once (V * elem), dense fp32 output (4V) when requested, q read
+    where the method reads it (4 |K| for sampling rows), history ids (4 each),
+    the output id (8) and the per-row k, p, flags (9)."""
+    B, V = W.B, W.V
+    flags = W.row_flags if W.row_flags is not None else np.full(B, 7, np.uint8)
+    kmax = min(V, 1024)
+    tk = ((flags & 1) != 0) & (W.top_k is not None)
+    if W.top_k is not None:
+        tk &= (W.top_k >= 1) & (W.top_k <= kmax)
+    tp = ((flags & 2) != 0) & (W.top_p is not None)
+    if W.top_p is not None:
+        tp &= W.top_p < 1.0
+    sm = ((flags & 4) != 0) & (W.q is not None)
+    filtered = tk | tp
+    nids = np.zeros(B, np.int64)
+    if W.ids is not None and W.penalty != 1.0:
+        nids = np.diff(W.offsets)
+    unf = ~filtered
+    stream = int(unf.sum()) * V * W.elem_bytes            # logits of unfiltered rows
+    stream += int((sm & unf).sum()) * 4 * V                # the race streams q
+    if W.need_logits:
+        stream += int(unf.sum()) * 4 * V                   # dense copy of unfiltered rows
+    select = int(filtered.sum()) * V * W.elem_bytes        # logits of filtered rows
+    pen = int(nids.sum()) * 4
+    rows = int((kept[sm & filtered]).sum()) * 4 + B * (8 + 9)
+    dense = int(filtered.sum()) * 4 * V if W.need_logits else 0
+    return {"k_stream": stream + pen, "k_select": select, "k_rows": rows, "k_fallback": 0,
+            "k_dense": dense}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sampler is "
+              "row-parallel and shards by rows with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_token_sampling_row_amd import workloads as wl
+    from decode_token_sampling_row_amd.sampler import Sampler
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    t0 = time.time()
+    W = wl.make(args.config, seed=args.seed)
+    print(f"[bench] workload {W.name} B={W.B} V={W.V} {W.dtype} generated in "
+          f"{time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    if W.dtype == wl.BF16:
+        logits = torch.from_numpy(W.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        logits = torch.from_numpy(W.logits).to(dev)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, top_k, top_p, flags = t(W.q), t(W.top_k), t(W.top_p), t(W.row_flags)
+    ids, offs = t(W.ids), t(W.offsets)
+    out_idx = torch.empty(W.B, dtype=torch.int64, device=dev)
+    out_l = torch.empty((W.B, W.V), dtype=torch.float32, device=dev) if W.need_logits else None
+    s = Sampler(W.B, W.V, torch.bfloat16 if W.dtype == wl.BF16 else torch.float32)
+    kw = dict(top_k=top_k, top_p=top_p, q=q, eps=W.eps, temperature=W.temperature,
+              repetition_penalty=W.penalty, penalty_ids=ids, penalty_offsets=offs,
+              row_flags=flags, out_logits=out_l)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        s.run(logits, out_idx, **kw)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        s.run(logits, out_idx, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    # per-kernel times: HIP events the library records between its launches
+    per = np.zeros(len(KERNELS))
+    nprof = max(5, min(args.steps, 20))
+    for _ in range(nprof):
+        s.run(logits, out_idx, profile=True, **kw)
+        per += np.array(s.last_profile())
+    per /= nprof
+
+    # kept-set sizes for the byte model (outside the timed region)
+    if out_l is not None:
+        kept = torch.isfinite(out_l).sum(dim=1).cpu().numpy()
+    else:
+        kept = np.full(W.B, 1, np.int64)
+    mb = model_bytes(W, kept)
+    total_bytes = sum(mb.values())
+    dom = int(np.argmax(per))
+    dom_name = KERNELS[dom]
+    dom_gbps = mb[dom_name] / (per[dom] * 1e-3) / 1e9 if per[dom] > 0 else 0.0
+    path_gbps = total_bytes / (ms * 1e-3) / 1e9
+    rows_per_s = W.B / (ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+
+        threads = max(1, min(16, os.cpu_count() or 1))
+        n = min(W.B, args.cpu_rows)
+        rows = np.arange(n)
+        c0 = time.perf_counter()
+        orc.run(W.logits, orc.BF16 if W.dtype == wl.BF16 else orc.F32, vocab=W.V,
+                top_k=W.top_k, top_p=W.top_p, q=W.q, eps=W.eps, temperature=W.temperature,
+                penalty=W.penalty, ids=W.ids, offsets=W.offsets, row_flags=W.row_flags,
+                need_logits=W.need_logits, rows=rows, threads=threads)
+        dt = time.perf_counter() - c0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"rows 0..{n - 1} of the same workload (all stage combinations), "
+                         f"{dt:.2f} s wall on {threads} threads"}
+
+    out = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": W.name, "batch": W.B, "vocab": W.V, "logits_dtype": W.dtype,
+                   "dense_logits": bool(W.need_logits)},
+        "hbm_gbps": path_gbps,
+        "hbm_frac": path_gbps / HBM_PEAK_GBPS,
+        "model_bytes_per_step": total_bytes,
+        "kernel_ms": {k: float(v) for k, v in zip(KERNELS, per)},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes": mb[dom_name],
+                     "kernel_ms": float(per[dom])},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    s.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -21,10 +21,10 @@ struct sampler_s {
     int device;
     KWork ws;
     void *ws_base;
-    hipEvent_t ev[5];
+    hipEvent_t ev[6];
     bool events_ok;
     bool prof_pending;
-    bool launched[4];
+    bool launched[5];
 };
 
 namespace {
@@ -92,7 +92,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     const size_t B = (size_t)max_batch;
     size_t off = 0;
     const size_t o_cand = off;
-    off = align_up(off + B * NCH_MAX * KMAX * sizeof(uint64_t), 256);
+    off = align_up(off + B * NCH_MAX * SLOT * sizeof(uint64_t), 256);
     const size_t o_ccnt = off;
     off = align_up(off + B * NCH_MAX * sizeof(int32_t), 256);
     const size_t o_cstat = off;
@@ -101,6 +101,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * sizeof(RowInfo), 256);
     const size_t o_klist = off;
     off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
+    const size_t o_rowkey = off;
+    off = align_up(off + B * sizeof(uint32_t), 256);
     void *base = nullptr;
     hipError_t e = hipMalloc(&base, off);
     if (e != hipSuccess) {
@@ -115,8 +117,9 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.cstat = (ChunkStat *)(c + o_cstat);
     s->ws.info = (RowInfo *)(c + o_info);
     s->ws.klist = (uint64_t *)(c + o_klist);
+    s->ws.rowkey = (uint32_t *)(c + o_rowkey);
     s->events_ok = true;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 6; ++i)
         if (hipEventCreate(&s->ev[i]) != hipSuccess) s->events_ok = false;
     s->prof_pending = false;
     *h = s;
@@ -178,33 +181,39 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
                     (p.out_probs == nullptr || aligned16(p.out_probs));
 
     const bool prof = (a->flags & SAMPLER_PROFILE) && h->events_ok;
-    for (int i = 0; i < 4; ++i) h->launched[i] = false;
+    for (int i = 0; i < 5; ++i) h->launched[i] = false;
     auto mark = [&](int i) {
         if (prof) (void)hipEventRecord(h->ev[i], st);
     };
 
     hipError_t e;
     mark(0);
-    e = launch_chunk(p, l, h->ws, h->dtype, al, st);
+    e = launch_stream(p, l, h->ws, h->dtype, al, st);
     if (e != hipSuccess) return SAMPLER_EHIP;
     h->launched[0] = true;
     mark(1);
+    if (a->top_k != nullptr || a->top_p != nullptr) {
+        e = launch_select(p, l, h->ws, h->dtype, al, st);
+        if (e != hipSuccess) return SAMPLER_EHIP;
+        h->launched[1] = true;
+    }
+    mark(2);
     e = launch_rows(p, l, h->ws, st);
     if (e != hipSuccess) return SAMPLER_EHIP;
-    h->launched[1] = true;
-    mark(2);
+    h->launched[2] = true;
+    mark(3);
     if (a->top_p != nullptr) {
         e = launch_fallback(p, l, h->ws, h->dtype, al, st);
-        if (e != hipSuccess) return SAMPLER_EHIP;
-        h->launched[2] = true;
-    }
-    mark(3);
-    if (p.out_logits || p.out_probs) {
-        e = launch_dense(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
         h->launched[3] = true;
     }
     mark(4);
+    if (p.out_logits || p.out_probs) {
+        e = launch_dense(p, l, h->ws, h->dtype, al, st);
+        if (e != hipSuccess) return SAMPLER_EHIP;
+        h->launched[4] = true;
+    }
+    mark(5);
     h->prof_pending = prof;
     return SAMPLER_OK;
 }
@@ -212,8 +221,8 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
 int sampler_last_profile(sampler_t *h, float *ms, int32_t n) {
     if (h == nullptr || ms == nullptr || n < 0) return SAMPLER_EINVAL;
     if (!h->prof_pending) return SAMPLER_EINVAL;
-    if (hipEventSynchronize(h->ev[4]) != hipSuccess) return SAMPLER_EHIP;
-    int w = n < 4 ? n : 4;
+    if (hipEventSynchronize(h->ev[5]) != hipSuccess) return SAMPLER_EHIP;
+    int w = n < 5 ? n : 5;
     for (int i = 0; i < w; ++i) {
         float t = 0.0f;
         if (h->launched[i] && hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]) != hipSuccess)
@@ -227,7 +236,7 @@ int sampler_destroy(sampler_t *h) {
     if (h == nullptr) return SAMPLER_OK;
     int rc = SAMPLER_OK;
     if (h->ws_base && hipFree(h->ws_base) != hipSuccess) rc = SAMPLER_EHIP;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 6; ++i)
         if (h->events_ok) (void)hipEventDestroy(h->ev[i]);
     delete h;
     return rc;

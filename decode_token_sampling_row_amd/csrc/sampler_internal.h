@@ -6,22 +6,24 @@
 
 namespace smp {
 
-// Streaming-pass geometry (chunk kernel): 256 threads x 8 elements per tile.
+// Streaming-pass geometry (chunk kernels): 256 threads x 8 elements per tile.
 constexpr int K1_THREADS = 256;
 constexpr int VEC = 8;
 constexpr int TILE = K1_THREADS * VEC;  // 2048 elements
 constexpr int NCH_MAX = 8;              // chunks per row
 constexpr int KMAX = 1024;              // largest k / guess
-constexpr int CAP = 4096;               // LDS candidate buffer entries
+constexpr int SLOT = 2048;              // candidates a chunk may hand over
+constexpr int SEL_CAP = 4096;           // LDS candidate buffer entries
+constexpr int SEL_SOFT = 3072;          // cut the buffer back above this fill
 // Row kernels.
 constexpr int K2_THREADS = 1024;
 constexpr int K3_THREADS = 1024;
 constexpr int K3_BINS = 2048;           // value-space histogram bins
 constexpr int K3_COLLECT = 4096;        // bucket members sorted in LDS
 constexpr int K3_SEG = 65536;           // penalty-bitmap segment
-// Dense writer: 256 threads x 32 elements.
+// Dense writer: 256 threads x 128 elements.
 constexpr int K4_THREADS = 256;
-constexpr int TILE4 = 8192;
+constexpr int TILE4 = 32768;
 
 // Row kinds written by the merge kernel.
 enum RowKind : int32_t {
@@ -81,16 +83,19 @@ struct KPlan {
 };
 
 struct KWork {
-    uint64_t *cand;   // [maxB][NCH_MAX][KMAX]
+    uint64_t *cand;   // [maxB][NCH_MAX][SLOT]
     int32_t *ccnt;    // [maxB][NCH_MAX]
     ChunkStat *cstat; // [maxB][NCH_MAX]
     RowInfo *info;    // [maxB]
     uint64_t *klist;  // [maxB][KMAX]
+    uint32_t *rowkey; // [maxB] admission key shared by a row's chunks
 };
 
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
-hipError_t launch_chunk(const KParams &p, const KPlan &l, const KWork &w, int dtype,
-                        bool aligned, hipStream_t s);
+hipError_t launch_stream(const KParams &p, const KPlan &l, const KWork &w, int dtype,
+                         bool aligned, hipStream_t s);
+hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int dtype,
+                         bool aligned, hipStream_t s);
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                            bool aligned, hipStream_t s);

@@ -49,8 +49,9 @@ constexpr uint32_t NEED_LOGITS = 1u;
 constexpr uint32_t NEED_PROBS = 2u;
 // top-p decisions taken from a guess must clear the cutoff by this much
 // (relative to the row's total mass); the row's total is accumulated from
-// fp32 exponentials, good to a few 1e-7.
-constexpr double GUESS_MARGIN = 2e-6;
+// fp32 exponentials, good to about 1e-6.  Rows inside the margin take the
+// exact full-row search.
+constexpr double GUESS_MARGIN = 1e-5;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -58,8 +59,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- keys
 
 __device__ __forceinline__ uint32_t f2key(float x) {
-    uint32_t b = __float_as_uint(x);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    const uint32_t b = __float_as_uint(x);
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key2f(uint32_t k) {
     uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -105,11 +106,24 @@ __device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
     return md;
 }
 
-// Penalty, temperature, -0 -> +0.  Division is IEEE correctly rounded.
-__device__ __forceinline__ float xform(float x, bool hit, const KParams &P) {
-    if (hit) x = (x > 0.0f) ? x / P.rho : x * P.rho;
-    if (P.temperature != 1.0f) x = x / P.temperature;
-    return (x == 0.0f) ? 0.0f : x;
+// Penalty, temperature, -0 -> +0 (adding +0 maps -0 to +0 and leaves every
+// other value unchanged).  Division is IEEE correctly rounded.  XF = false
+// compiles the call without penalty or temperature down to the +0.
+template <bool XF>
+__device__ __forceinline__ float xform(float x, uint32_t hit, const KParams &P) {
+    if (XF) {
+        if (hit) x = (x > 0.0f) ? x / P.rho : x * P.rho;
+        if (P.temperature != 1.0f) x = x / P.temperature;
+    }
+    return x + 0.0f;
+}
+
+// Penalty bits of the 8 elements starting at row-relative offset r (a
+// multiple of 8) of a bitmap that starts at offset 0.
+template <bool XF>
+__device__ __forceinline__ uint32_t pen_bits(const uint32_t *bm, int r, const KParams &P) {
+    if (!XF || !P.pen) return 0u;
+    return (bm[r >> 5] >> (r & 31)) & 0xffu;
 }
 
 // Row index of workgroup i in a grid of n row-workgroups: consecutive
@@ -161,13 +175,16 @@ __device__ __forceinline__ void load8(const void *p, int64_t j, int nv, float (&
     }
 }
 
+// Plain write-back stores: each lane writes 32 contiguous bytes as two 16-byte
+// stores, and L2 merges the two half lines of a wave before they reach HBM
+// (streaming stores of half lines write at a fraction of the bandwidth).
 template <bool AL>
 __device__ __forceinline__ void store8(float *p, int64_t j, int nv, const float (&x)[8]) {
     if (AL && nv == 8) {
         f32x4 a = {x[0], x[1], x[2], x[3]};
         f32x4 c = {x[4], x[5], x[6], x[7]};
-        __builtin_nontemporal_store(a, (f32x4 *)(p + j));
-        __builtin_nontemporal_store(c, (f32x4 *)(p + j) + 1);
+        *(f32x4 *)(p + j) = a;
+        *((f32x4 *)(p + j) + 1) = c;
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -306,17 +323,19 @@ struct Race {
     float x, qe;
     uint32_t idx;
 };
+// The exponentials use the hardware exp2 (relative error ~1e-6 where the
+// two logits are far apart, where the comparison is never close).
 __device__ __forceinline__ bool race_ahead(const Race &a, const Race &b) {
     if (a.idx == NONE) return false;
     if (b.idx == NONE) return true;
-    float f = expf(a.x - b.x) * b.qe;
+    float f = __expf(a.x - b.x) * b.qe;
     if (f > a.qe) return true;
     if (f < a.qe) return false;
     return a.idx < b.idx;
 }
 __device__ __forceinline__ void race_offer(Race &best, float x, float qe, uint32_t j) {
     if (!(x > -INFINITY)) return;  // probability 0: never drawn
-    if (best.idx == NONE || expf(x - best.x) * best.qe > qe) {
+    if (best.idx == NONE || __expf(x - best.x) * best.qe > qe) {
         best.x = x;
         best.qe = qe;
         best.idx = j;
@@ -355,60 +374,89 @@ __device__ __forceinline__ Race wg_race(Race r, float *scx, float *scq, uint32_t
     return t;
 }
 
+// Wave 0 finds, in a 256-bin count histogram read from the top bin down,
+// the bin where the running count first reaches `need`; writes sel[0] = bin,
+// sel[1] = count above it, sel[2] = its count.  Needs 1 <= need <= total.
+__device__ __forceinline__ void wave0_find_bin(const uint32_t *hist, uint32_t need,
+                                               uint32_t *sel) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        uint32_t s = h0 + h1 + h2 + h3;
+        uint32_t S = s;  // suffix sum over lanes >= lane
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            uint32_t t = (uint32_t)__shfl_down((int)S, d, 64);
+            if (lane + d < 64) S += t;
+        }
+        uint32_t above = S - s;
+        if (above < need && S >= need) {
+            uint32_t acc = above, d, c;
+            if (acc + h3 >= need) {
+                d = 4 * lane + 3; c = h3;
+            } else if (acc + h3 + h2 >= need) {
+                acc += h3; d = 4 * lane + 2; c = h2;
+            } else if (acc + h3 + h2 + h1 >= need) {
+                acc += h3 + h2; d = 4 * lane + 1; c = h1;
+            } else {
+                acc += h3 + h2 + h1; d = 4 * lane; c = h0;
+            }
+            sel[0] = d;
+            sel[1] = acc;
+            sel[2] = c;
+        }
+    }
+}
+
 // Radix select over distinct 64-bit composites held in registers.  Finds
 // (prefix, pmask) such that exactly kk of the valid entries satisfy
-// (v & pmask) >= prefix, i.e. the kk largest.  8-bit digits from the top,
-// stopping as soon as the boundary bucket is taken whole.  Needs
-// 1 <= kk <= number of valid entries.
+// (v & pmask) >= prefix, i.e. the kk largest.  The bits all entries share
+// are skipped first (min/max reduction), then digits of up to 8 bits are
+// taken from the highest differing bit down, stopping as soon as the
+// boundary bucket is taken whole.  Needs 1 <= kk < number of valid entries.
 template <int NT, int R>
 __device__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t kk,
-                                uint32_t *hist, uint32_t *sel, uint64_t &prefix_out,
-                                uint64_t &pmask_out) {
-    uint64_t prefix = 0, pmask = 0;
+                                uint32_t *hist, uint32_t *sel, uint64_t *sc64,
+                                uint64_t &prefix_out, uint64_t &pmask_out) {
+    uint64_t mn = ~0ull, mx = 0ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if ((vmask >> r) & 1u) {
+            mn = v[r] < mn ? v[r] : mn;
+            mx = v[r] > mx ? v[r] : mx;
+        }
+    mn = wg_min_u64<NT>(mn, sc64);
+    mx = wg_max_u64<NT>(mx, sc64);
+    const uint64_t diff = mn ^ mx;
+    if (diff == 0) {
+        prefix_out = mx;
+        pmask_out = ~0ull;
+        return;
+    }
+    int hi = 63 - __clzll(diff);
+    uint64_t pmask = (hi == 63) ? 0ull : (~0ull << (hi + 1));
+    uint64_t prefix = mx & pmask;
     uint32_t need = kk;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (;;) {
+        const int width = hi + 1 < 8 ? hi + 1 : 8;
+        const int shift = hi + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
         for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (((vmask >> r) & 1u) && (v[r] & pmask) == prefix)
-                atomicAdd(&hist[(uint32_t)(v[r] >> shift) & 255u], 1u);
+                atomicAdd(&hist[(uint32_t)(v[r] >> shift) & dmask], 1u);
         __syncthreads();
-        if (threadIdx.x < 64) {
-            const int lane = threadIdx.x;
-            uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-            uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-            uint32_t s = h0 + h1 + h2 + h3;
-            uint32_t S = s;  // suffix sum over lanes >= lane
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                uint32_t t = (uint32_t)__shfl_down((int)S, d, 64);
-                if (lane + d < 64) S += t;
-            }
-            uint32_t above = S - s;
-            if (above < need && S >= need) {
-                uint32_t acc = above;
-                uint32_t d = 4 * lane, c = h0;
-                if (acc + h3 >= need) {
-                    d = 4 * lane + 3; c = h3;
-                } else if (acc + h3 + h2 >= need) {
-                    acc += h3; d = 4 * lane + 2; c = h2;
-                } else if (acc + h3 + h2 + h1 >= need) {
-                    acc += h3 + h2; d = 4 * lane + 1; c = h1;
-                } else {
-                    acc += h3 + h2 + h1; d = 4 * lane; c = h0;
-                }
-                sel[0] = d;
-                sel[1] = acc;
-                sel[2] = c;
-            }
-        }
+        wave0_find_bin(hist, need, sel);
         __syncthreads();
-        uint32_t d = sel[0], above = sel[1], cntd = sel[2];
+        const uint32_t d = sel[0], above = sel[1], cntd = sel[2];
         need -= above;
         prefix |= (uint64_t)d << shift;
-        pmask |= (uint64_t)0xff << shift;
-        if (cntd == need) break;
+        pmask |= (uint64_t)dmask << shift;
+        if (cntd == need || shift == 0) break;
+        hi = shift - 1;
     }
     prefix_out = prefix;
     pmask_out = pmask;
@@ -434,6 +482,35 @@ __device__ void bitonic_desc(uint64_t *s, int n) {
             __syncthreads();
         }
     }
+}
+
+// Descending bitonic sort of s[0..n), n a power of two <= NT: one element per
+// thread, partners closer than 64 exchanged with lane shuffles, farther ones
+// through LDS.  Callers barrier before; ends with a barrier.
+template <int NT>
+__device__ void bitonic_desc_reg(uint64_t *s, int n) {
+    const int i = threadIdx.x;
+    uint64_t v = (i < n) ? s[i] : 0ull;
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t o;
+            if (j >= 64) {
+                __syncthreads();
+                if (i < n) s[i] = v;
+                __syncthreads();
+                o = (i < n) ? s[i ^ j] : 0ull;
+            } else {
+                o = shx64(v, j);
+            }
+            const bool desc = (i & k) == 0;
+            const bool lower = (i & j) == 0;
+            const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
+            v = (desc == lower) ? mx : mn;
+        }
+    }
+    __syncthreads();
+    if (i < n) s[i] = v;
+    __syncthreads();
 }
 
 __device__ __forceinline__ int pow2_ceil(int n) {
@@ -462,266 +539,759 @@ __device__ __forceinline__ const void *row_ptr(const KParams &P, int dt, int b) 
     return (const char *)P.logits + (int64_t)b * P.ld * (dt == 1 ? 2 : 4);
 }
 
-// ================================================================== k_chunk
+// ================================================================== chunk passes
 
-constexpr int U = 4;  // tiles per batch
+constexpr int U = 4;           // k_stream: tiles per batch (256 threads)
+constexpr int SEL_THREADS = 512;
+constexpr int SEL_U = 1;       // k_select: tiles per batch (512 threads)
+constexpr int SEL_DEPTH = 4;   // k_select: batches in flight
 
-struct ChunkShared {
-    uint64_t buf[CAP];
-    uint32_t hist[256];
-    uint32_t sel[4];
-    uint32_t sc[16];
+__device__ __forceinline__ int group_nv(int j, int end) {
+    const int rem = end - j;
+    return rem <= 0 ? 0 : (rem >= 8 ? 8 : rem);
+}
+
+// Raw (not yet widened) registers of one group of 8 logits, so that the
+// loads of the next batch can be in flight while the current one is used.
+template <int DT>
+struct Raw;
+template <>
+struct Raw<1> {
+    u32x4 v;  // 8 bf16
+};
+template <>
+struct Raw<0> {
+    f32x4 a, b;  // 8 fp32
+};
+
+template <int DT, bool AL>
+__device__ __forceinline__ void load_raw(const void *p, int64_t j, int nv, Raw<DT> &r) {
+    if (DT == 1) {
+        u32x4 &v = reinterpret_cast<Raw<1> &>(r).v;
+        if (AL && nv == 8) {
+            v = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)p + j));
+        } else {
+            const uint16_t *h = (const uint16_t *)p + j;
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t lo = (2 * i < nv) ? h[2 * i] : 0u;
+                uint32_t hi = (2 * i + 1 < nv) ? h[2 * i + 1] : 0u;
+                w[i] = lo | (hi << 16);
+            }
+            v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+        }
+    } else {
+        Raw<0> &f = reinterpret_cast<Raw<0> &>(r);
+        if (AL && nv == 8) {
+            const f32x4 *q = (const f32x4 *)((const float *)p + j);
+            f.a = __builtin_nontemporal_load(q);
+            f.b = __builtin_nontemporal_load(q + 1);
+        } else {
+            const float *q = (const float *)p + j;
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = (i < nv) ? q[i] : 0.0f;
+            f.a.x = t[0]; f.a.y = t[1]; f.a.z = t[2]; f.a.w = t[3];
+            f.b.x = t[4]; f.b.y = t[5]; f.b.z = t[6]; f.b.w = t[7];
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_raw(const Raw<DT> &r, float (&x)[8]) {
+    if (DT == 1) {
+        const u32x4 &u = reinterpret_cast<const Raw<1> &>(r).v;
+        x[0] = __uint_as_float(u.x << 16);
+        x[1] = __uint_as_float(u.x & 0xffff0000u);
+        x[2] = __uint_as_float(u.y << 16);
+        x[3] = __uint_as_float(u.y & 0xffff0000u);
+        x[4] = __uint_as_float(u.z << 16);
+        x[5] = __uint_as_float(u.z & 0xffff0000u);
+        x[6] = __uint_as_float(u.w << 16);
+        x[7] = __uint_as_float(u.w & 0xffff0000u);
+    } else {
+        const Raw<0> &f = reinterpret_cast<const Raw<0> &>(r);
+        x[0] = f.a.x; x[1] = f.a.y; x[2] = f.a.z; x[3] = f.a.w;
+        x[4] = f.b.x; x[5] = f.b.y; x[6] = f.b.z; x[7] = f.b.w;
+    }
+}
+
+// Issue the loads of one batch (UU groups per thread; row-relative offsets).
+template <int DT, bool AL, int NT, int UU>
+__device__ __forceinline__ void issue_batch(const void *rowp, int base, int c1,
+                                            Raw<DT> (&raw)[UU]) {
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const int j = base + (u * NT + (int)threadIdx.x) * VEC;
+        load_raw<DT, AL>(rowp, j, group_nv(j, c1), raw[u]);
+    }
+}
+
+// Widen and transform a loaded batch.  FULL: the whole batch lies inside the
+// chunk (no per-element bounds).
+template <int DT, int NT, int UU, bool XF, bool FULL, bool CANON = true>
+__device__ __forceinline__ void finish_batch(const Raw<DT> (&raw)[UU], int base, int c0, int c1,
+                                             const uint32_t *bm, const KParams &P,
+                                             float (&x)[UU][8], int (&jb)[UU], int (&nv)[UU]) {
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        jb[u] = base + (u * NT + (int)threadIdx.x) * VEC;
+        nv[u] = FULL ? 8 : group_nv(jb[u], c1);
+        unpack_raw<DT>(raw[u], x[u]);
+        const uint32_t bits = (FULL || nv[u] > 0) ? pen_bits<XF>(bm, jb[u] - c0, P) : 0u;
+        if (XF || CANON) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[u][i] = xform<XF>(x[u][i], (bits >> i) & 1u, P);
+        }
+    }
+}
+
+// Running (max, sum exp(x - max), finite min) of one thread.  Terms are
+// hardware fp32 exponentials (exp2 of a scaled argument: relative error grows
+// like |x - max| * 2^-24, so the mass-weighted error of the total stays near
+// 1e-6 even for long flat tails) summed in double; when the running max rises
+// the sum is rescaled by an fp32 exponential of the (non-positive)
+// difference, a few times per chunk at most.
+struct Stats {
+    float m, xmin;
+    double z;
+};
+template <int UU>
+__device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][8], const int (&nv)[UU]) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nv[u]) {
+                tm = fmaxf(tm, x[u][i]);
+                if (x[u][i] > -INFINITY) st.xmin = fminf(st.xmin, x[u][i]);
+            }
+    if (tm > st.m) {
+        if (st.z != 0.0) st.z *= (double)expf(st.m - tm);
+        st.m = tm;
+    }
+    if (st.m > -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < UU; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < nv[u]) st.z += (double)__expf(x[u][i] - st.m);
+    }
+}
+
+// Workgroup merge of per-thread Stats into one ChunkStat's m / z / xmin.
+template <int NT>
+__device__ void stats_reduce(const Stats &st, float *scf, double *scd, ChunkStat &cs) {
+    float m = st.m;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, shxf(m, s));
+    if ((threadIdx.x & 63) == 0) scf[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float M = scf[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, scf[i]);
+    __syncthreads();
+    double z = (st.z != 0.0) ? st.z * exp((double)st.m - (double)M) : 0.0;
+    z = wg_sum_f64<NT>(z, scd);
+    float mn = st.xmin;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) mn = fminf(mn, shxf(mn, s));
+    if ((threadIdx.x & 63) == 0) scf[threadIdx.x >> 6] = mn;
+    __syncthreads();
+    float MN = scf[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) MN = fminf(MN, scf[i]);
+    __syncthreads();
+    cs.m = M;
+    cs.z = z;
+    cs.xmin = MN;
+}
+
+__device__ __forceinline__ ChunkStat empty_stat() {
+    ChunkStat cs;
+    cs.m = -INFINITY;
+    cs.xmin = INFINITY;
+    cs.z = 0.0;
+    cs.rx = -INFINITY;
+    cs.rqe = 1.0f;
+    cs.ridx = NONE;
+    cs.pad = 0;
+    return cs;
+}
+
+// ---------------------------------------------------------------- k_stream
+// Rows with neither top-k nor top-p: K is the whole row.  Writes the dense
+// output (x itself), runs the exponential race over the whole chunk (q is
+// streamed in the same pass) or the greedy argmax, and (for the optional
+// probabilities) the chunk's max / sum-exp.  No barrier in the loop.
+
+struct StreamShared {
     uint64_t sc64[16];
     double scd[16];
     float scx[16], scq[16];
     uint32_t sci[16];
 };
 
-// Cut buf[0..cnt) back to its kk largest (cnt > kk); returns the smallest
-// kept composite, the new admission threshold.
-__device__ uint64_t chunk_reduce(ChunkShared &S, uint32_t cnt, uint32_t kk) {
-    constexpr int R = CAP / K1_THREADS;
-    uint64_t v[R];
-    uint32_t vm = 0;
+struct StreamState {
+    Stats st;
+    Race rc;
+    uint64_t am;
+};
+
+template <int DT, bool AL, bool XF, bool FULL>
+__device__ __forceinline__ void stream_batch(const Raw<DT> (&cur)[U], int base, int c0, int c1,
+                                             const uint32_t *bm, const KParams &P, float *rowo,
+                                             const float *rowq, bool do_stats, bool do_race,
+                                             StreamState &ss) {
+    float x[U][8];
+    int jb[U], nv[U];
+    finish_batch<DT, K1_THREADS, U, XF, FULL>(cur, base, c0, c1, bm, P, x, jb, nv);
+    if (rowo) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        uint32_t i = threadIdx.x + r * K1_THREADS;
-        v[r] = (i < cnt) ? S.buf[i] : 0ull;
-        if (i < cnt) vm |= 1u << r;
+        for (int u = 0; u < U; ++u)
+            if (FULL || nv[u] > 0) store8<AL>(rowo, jb[u], nv[u], x[u]);
     }
-    uint64_t prefix, pmask;
-    wg_radix_select<K1_THREADS, R>(v, vm, kk, S.hist, S.sel, prefix, pmask);
-    uint32_t km = 0;
+    if (do_stats) stats_batch(ss.st, x, nv);
+    if (do_race) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
-    uint32_t tot;
-    uint32_t off = wg_excl_scan_u32<K1_THREADS>(__popc(km), S.sc, tot);
-    uint64_t mn = ~0ull;
+        for (int u = 0; u < U; ++u) {
+            float qv[8];
+            load8<0, AL>(rowq, jb[u], nv[u], qv);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        if ((km >> r) & 1u) {
-            S.buf[off++] = v[r];
-            mn = v[r] < mn ? v[r] : mn;
+            for (int i = 0; i < 8; ++i)
+                if (FULL || i < nv[u]) race_offer(ss.rc, x[u][i], qv[i] + P.eps, (uint32_t)(jb[u] + i));
         }
-    return wg_min_u64<K1_THREADS>(mn, S.sc64);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (FULL || i < nv[u]) {
+                    const uint64_t cv = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
+                    ss.am = cv > ss.am ? cv : ss.am;
+                }
+    }
 }
 
-template <int DT, bool AL>
-__global__ __launch_bounds__(K1_THREADS) void k_chunk(KParams P, KPlan L, KWork W) {
-    __shared__ ChunkShared S;
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(K1_THREADS) void k_stream(KParams P, KPlan L, KWork W) {
+    __shared__ StreamShared S;
     extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
-
     const int tid = threadIdx.x;
     const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
-    const int64_t V = P.V;
-    const int64_t c0 = (int64_t)c * L.chunk_len;
-    const int64_t c1 = min(c0 + L.chunk_len, V);
-    const int slot = b * NCH_MAX + c;
+    if (c == 0 && tid == 0) W.rowkey[b] = 0u;  // the row's shared admission key
     const Mode md = row_mode(P, b);
-
-    const bool filtered = md.tk || md.tp;
-    const bool do_sel = filtered;
-    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-    const bool do_stats = (md.tp && !md.tk) || (!filtered && (P.flags & NEED_PROBS));
-    const bool do_race = !filtered && md.sm;
-    const bool do_argmax = !filtered && !md.sm;
-    const bool do_dense = !filtered && (P.flags & NEED_LOGITS);
-
-    if (c0 >= c1) {  // empty chunk (only when V < nch * chunk_len)
+    if (md.tk || md.tp) return;
+    const int c0 = c * (int)L.chunk_len;
+    const int c1 = min(c0 + (int)L.chunk_len, P.V);
+    const int slot = b * NCH_MAX + c;
+    if (c0 >= c1) {
         if (tid == 0) {
             W.ccnt[slot] = 0;
-            ChunkStat cs;
-            cs.m = -INFINITY; cs.xmin = INFINITY; cs.z = 0.0;
-            cs.rx = -INFINITY; cs.rqe = 1.0f; cs.ridx = NONE; cs.pad = 0;
-            W.cstat[slot] = cs;
+            W.cstat[slot] = empty_stat();
         }
         return;
     }
-    if (P.pen) build_bitmap<K1_THREADS>(bm, c0, c1 - c0, P, b);
-
+    if (XF && P.pen) build_bitmap<K1_THREADS>(bm, c0, c1 - c0, P, b);
+    const bool do_race = md.sm;
+    const bool do_stats = (P.flags & NEED_PROBS) != 0;
     const void *rowp = row_ptr(P, DT, b);
-    const float *rowq = P.q ? P.q + (int64_t)b * V : nullptr;
-    float *rowo = P.out_logits ? P.out_logits + (int64_t)b * V : nullptr;
+    const float *rowq = P.q ? P.q + (int64_t)b * P.V : nullptr;
+    float *rowo = P.out_logits ? P.out_logits + (int64_t)b * P.V : nullptr;
 
-    uint64_t T = 0;    // admission threshold (uniform)
-    uint32_t cnt = 0;  // buffer fill (uniform)
-    float st_m = -INFINITY, st_min = INFINITY;
-    double st_z = 0.0;
-    Race rc;
-    rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
-    uint64_t am = 0;
-
-    for (int64_t base = c0; base < c1; base += (int64_t)TILE * U) {
-        float x[U][8];
-        int nv[U];
-        int64_t jb[U];
+    StreamState ss;
+    ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
+    ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE;
+    ss.am = 0;
+    constexpr int BATCH = K1_THREADS * VEC * U;
+    Raw<DT> cur[U], nxt[U];
+    issue_batch<DT, AL, K1_THREADS, U>(rowp, c0, c1, cur);
+    for (int base = c0; base < c1; base += BATCH) {
+        if (base + BATCH < c1) issue_batch<DT, AL, K1_THREADS, U>(rowp, base + BATCH, c1, nxt);
+        if (base + BATCH <= c1)
+            stream_batch<DT, AL, XF, true>(cur, base, c0, c1, bm, P, rowo, rowq, do_stats, do_race, ss);
+        else
+            stream_batch<DT, AL, XF, false>(cur, base, c0, c1, bm, P, rowo, rowq, do_stats, do_race, ss);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            jb[u] = base + (int64_t)u * TILE + (int64_t)tid * VEC;
-            int64_t rem = c1 - jb[u];
-            nv[u] = rem <= 0 ? 0 : (rem >= 8 ? 8 : (int)rem);
-            load8<DT, AL>(rowp, jb[u], nv[u], x[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint32_t bits = 0;
-            if (P.pen && nv[u] > 0) {
-                int64_t r = jb[u] - c0;
-                bits = (bm[r >> 5] >> (r & 31)) & 0xffu;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[u][i] = xform(x[u][i], (bits >> i) & 1u, P);
-        }
-        if (do_dense) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (nv[u] > 0) store8<AL>(rowo, jb[u], nv[u], x[u]);
-        }
-        if (do_stats) {
-            float tm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i < nv[u]) {
-                        tm = fmaxf(tm, x[u][i]);
-                        if (x[u][i] > -INFINITY) st_min = fminf(st_min, x[u][i]);
-                    }
-            if (tm > st_m) {
-                if (st_z != 0.0) st_z *= exp((double)st_m - (double)tm);
-                st_m = tm;
-            }
-            if (st_m > -INFINITY) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (i < nv[u]) st_z += (double)expf(x[u][i] - st_m);
-            }
-        }
-        if (do_race) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float qv[8];
-                load8<0, AL>(rowq, jb[u], nv[u], qv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i < nv[u]) race_offer(rc, x[u][i], qv[i] + P.eps, (uint32_t)(jb[u] + i));
-            }
-        }
-        if (do_argmax) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i < nv[u]) {
-                        uint64_t cv = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
-                        am = cv > am ? cv : am;
-                    }
-        }
-        if (do_sel) {
-            uint32_t pm = 0;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T)
-                        pm |= 1u << (u * 8 + i);
-            uint32_t tot;
-            uint32_t off = wg_excl_scan_u32<K1_THREADS>(__popc(pm), S.sc, tot);
-            if (cnt + tot <= (uint32_t)CAP) {
-                uint32_t pos = cnt + off;
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if ((pm >> (u * 8 + i)) & 1u)
-                            S.buf[pos++] = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
-                cnt += tot;
-            } else {
-                // Tile by tile; cut the buffer back when a tile would overflow.
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    uint32_t m8 = 0;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T) m8 |= 1u << i;
-                    uint32_t t8;
-                    uint32_t o8 = wg_excl_scan_u32<K1_THREADS>(__popc(m8), S.sc, t8);
-                    if (cnt + t8 > (uint32_t)CAP) {
-                        T = chunk_reduce(S, cnt, kk);
-                        cnt = kk;
-                        m8 = 0;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (i < nv[u] && mkcomp(x[u][i], (uint32_t)(jb[u] + i)) > T)
-                                m8 |= 1u << i;
-                        o8 = wg_excl_scan_u32<K1_THREADS>(__popc(m8), S.sc, t8);
-                    }
-                    uint32_t pos = cnt + o8;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if ((m8 >> i) & 1u) S.buf[pos++] = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
-                    cnt += t8;
-                }
-            }
-        }
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
-
-    if (do_sel) {
-        __syncthreads();
-        if (cnt > kk) {
-            T = chunk_reduce(S, cnt, kk);
-            cnt = kk;
-        }
-        uint64_t *dst = W.cand + (int64_t)slot * KMAX;
-        for (uint32_t i = tid; i < cnt; i += K1_THREADS) dst[i] = S.buf[i];
-        if (tid == 0) W.ccnt[slot] = (int32_t)cnt;
-    }
-    if (do_argmax) {
-        am = wg_max_u64<K1_THREADS>(am, S.sc64);
-        if (tid == 0) {
-            W.cand[(int64_t)slot * KMAX] = am;
-            W.ccnt[slot] = 1;
-        }
-    }
-    ChunkStat cs;
-    cs.m = -INFINITY; cs.xmin = INFINITY; cs.z = 0.0;
-    cs.rx = -INFINITY; cs.rqe = 1.0f; cs.ridx = NONE; cs.pad = 0;
-    if (do_stats) {
-        // merge (m, z) pairs: max first, then rescaled sums
-        float m = st_m;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, shxf(m, s));
-        if ((tid & 63) == 0) S.scx[tid >> 6] = m;
-        __syncthreads();
-        float M = S.scx[0];
-#pragma unroll
-        for (int i = 1; i < K1_THREADS / 64; ++i) M = fmaxf(M, S.scx[i]);
-        __syncthreads();
-        double z = (st_z != 0.0) ? st_z * exp((double)st_m - (double)M) : 0.0;
-        z = wg_sum_f64<K1_THREADS>(z, S.scd);
-        float mn = st_min;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) mn = fminf(mn, shxf(mn, s));
-        if ((tid & 63) == 0) S.scq[tid >> 6] = mn;
-        __syncthreads();
-        float MN = S.scq[0];
-#pragma unroll
-        for (int i = 1; i < K1_THREADS / 64; ++i) MN = fminf(MN, S.scq[i]);
-        __syncthreads();
-        cs.m = M;
-        cs.z = z;
-        cs.xmin = MN;
-    }
+    ChunkStat cs = empty_stat();
+    if (do_stats) stats_reduce<K1_THREADS>(ss.st, S.scx, S.scd, cs);
     if (do_race) {
-        Race r = wg_race<K1_THREADS>(rc, S.scx, S.scq, S.sci);
+        Race r = wg_race<K1_THREADS>(ss.rc, S.scx, S.scq, S.sci);
         cs.rx = r.x;
         cs.rqe = r.qe;
         cs.ridx = r.idx;
+    } else {
+        const uint64_t am = wg_max_u64<K1_THREADS>(ss.am, S.sc64);
+        if (tid == 0) {
+            W.cand[(int64_t)slot * SLOT] = am;
+            W.ccnt[slot] = 1;
+        }
     }
     if (tid == 0) W.cstat[slot] = cs;
+}
+
+// ---------------------------------------------------------------- k_select
+// Rows with top-k and/or top-p.  Keeps a superset of the chunk's kk largest
+// (kk = k, or the top-k guess G for top-p rows without top-k) in an LDS
+// buffer: an element enters when its value key is >= the admission key; when
+// the buffer fills it is cut back to a superset of its kk largest -- with a
+// 256-bin value histogram (the kept part is every entry at or above the bin
+// where the count from the top reaches kk), or an exact radix select when
+// one bin holds too many equal or near-equal values -- and the admission key
+// becomes the smallest kept value.  This is the rolling, prefiltered top-k of
+// the Ascend npu_top_k_top_p_sample page (topK section) with the exact cut
+// deferred to the row merge.  Top-p rows without top-k also accumulate the
+// chunk's max / sum-exp for the softmax over the whole row.
+
+struct SelShared {
+    uint64_t buf[2][SEL_CAP];  // candidate buffer, two halves used in turn
+    uint32_t hist[256];
+    uint32_t sel[4];
+    uint32_t sc[16];
+    uint64_t sc64[16];
+    double scd[16];
+    float scf[16];
+    uint32_t cnt;    // reserved entries of the active half
+    uint32_t ffail;  // first reservation that did not fit
+    uint32_t kcnt;   // entries written by a compaction
+    uint32_t rkey;   // admission key published by the row's other chunks
+    float shi[SEL_THREADS / 64];  // per-wave largest appended value
+};
+
+__device__ __forceinline__ uint32_t bin256(float x, float lo, float scale) {
+    float t = (x - lo) * scale;
+    if (!(t >= 0.0f)) return 0u;
+    if (t >= 255.0f) return 255u;
+    return (uint32_t)t;
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t bal) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// Workgroup reduction of (count, finite min, max) over SEL_THREADS threads.
+__device__ __forceinline__ void sel_span(SelShared &S, uint32_t &cnt, float &lo, float &hi) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        cnt += shx(cnt, s);
+        lo = fminf(lo, shxf(lo, s));
+        hi = fmaxf(hi, shxf(hi, s));
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        S.sc[w] = cnt;
+        S.scf[w] = lo;
+        S.scf[8 + w] = hi;
+    }
+    __syncthreads();
+    cnt = S.sc[0];
+    lo = S.scf[0];
+    hi = S.scf[8];
+#pragma unroll
+    for (int i = 1; i < SEL_THREADS / 64; ++i) {
+        cnt += S.sc[i];
+        lo = fminf(lo, S.scf[i]);
+        hi = fmaxf(hi, S.scf[8 + i]);
+    }
+    __syncthreads();
+}
+
+// Exact radix select over the entries of src[0..n) whose value key is >=
+// tkey (distinct composites, 1 <= kk < their count), read from LDS in every
+// pass: (v & pmask) >= prefix holds for exactly the kk largest of them.
+// Common high bits are skipped first.
+template <int NT>
+__device__ void radix_select_lds(const uint64_t *src, uint32_t n, uint32_t tkey, uint32_t kk,
+                                 SelShared &S, uint64_t &prefix_out, uint64_t &pmask_out) {
+    uint64_t mn = ~0ull, mx = 0ull;
+    for (uint32_t i = threadIdx.x; i < n; i += NT) {
+        const uint64_t v = src[i];
+        if ((uint32_t)(v >> 32) >= tkey) {
+            mn = v < mn ? v : mn;
+            mx = v > mx ? v : mx;
+        }
+    }
+    mn = wg_min_u64<NT>(mn, S.sc64);
+    mx = wg_max_u64<NT>(mx, S.sc64);
+    const uint64_t diff = mn ^ mx;
+    if (diff == 0) {
+        prefix_out = mx;
+        pmask_out = ~0ull;
+        return;
+    }
+    int hi = 63 - __clzll(diff);
+    uint64_t pmask = (hi == 63) ? 0ull : (~0ull << (hi + 1));
+    uint64_t prefix = mx & pmask;
+    uint32_t need = kk;
+    for (;;) {
+        const int width = hi + 1 < 8 ? hi + 1 : 8;
+        const int shift = hi + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n; i += NT) {
+            const uint64_t v = src[i];
+            if ((uint32_t)(v >> 32) >= tkey && (v & pmask) == prefix)
+                atomicAdd(&S.hist[(uint32_t)(v >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        wave0_find_bin(S.hist, need, S.sel);
+        __syncthreads();
+        const uint32_t d = S.sel[0], above = S.sel[1], cntd = S.sel[2];
+        need -= above;
+        prefix |= (uint64_t)d << shift;
+        pmask |= (uint64_t)dmask << shift;
+        if (cntd == need || shift == 0) break;
+        hi = shift - 1;
+    }
+    prefix_out = prefix;
+    pmask_out = pmask;
+}
+
+// Cut S.buf[half][0..n) (n > kk) back to a superset of the kk largest of its
+// entries whose value key is >= tkey, holding at most `limit` entries (limit
+// >= kk): every such entry at or above the 256-bin value-histogram bin where
+// the count from the top reaches kk -- bins span [value(tkey), hi], hi an
+// upper bound of the buffer -- or exactly the kk largest when that bin is too
+// full.  The survivors go to the other half.  Returns their count; when at
+// least kk survive, tkey rises to the smallest surviving key.
+__device__ uint32_t sel_reduce(SelShared &S, int half, uint32_t n, uint32_t kk, uint32_t limit,
+                               uint32_t &tkey, float hi) {
+    constexpr int NT = SEL_THREADS;
+    const uint64_t *src = S.buf[half];
+    uint64_t *dst = S.buf[half ^ 1];
+    float lo = key2f(tkey);
+    if (tkey == 0u) {
+        // no floor yet: take the smallest finite value in the buffer
+        lo = INFINITY;
+        for (uint32_t i = threadIdx.x; i < n; i += NT) {
+            const float xv = cval(src[i]);
+            if (xv > -INFINITY) lo = fminf(lo, xv);
+        }
+        uint32_t dummy = 0;
+        float dh = -INFINITY;
+        sel_span(S, dummy, lo, dh);
+    }
+    if (threadIdx.x == 0) S.kcnt = 0;
+    bool exact = true;
+    uint32_t bstar = 0;
+    float scale = 0.0f;
+    if (hi > lo && lo > -INFINITY) {
+        scale = 256.0f / (hi - lo);
+        for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n; i += NT) {
+            const uint64_t v = src[i];
+            if ((uint32_t)(v >> 32) >= tkey) atomicAdd(&S.hist[bin256(cval(v), lo, scale)], 1u);
+        }
+        __syncthreads();
+        // fewer than kk entries at or above the floor: keep them all
+        uint32_t tot = 0;
+        if (threadIdx.x < 64) {
+            const uint32_t t4 = S.hist[4 * threadIdx.x] + S.hist[4 * threadIdx.x + 1] +
+                                S.hist[4 * threadIdx.x + 2] + S.hist[4 * threadIdx.x + 3];
+            tot = t4;
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) tot += shx(tot, sft);
+            if (threadIdx.x == 0) S.sel[3] = tot;
+        }
+        __syncthreads();
+        tot = S.sel[3];
+        if (tot <= kk) {
+            bstar = 0;
+            exact = false;
+        } else {
+            wave0_find_bin(S.hist, kk, S.sel);
+            __syncthreads();
+            bstar = S.sel[0];
+            exact = S.sel[1] + S.sel[2] > limit;
+        }
+    }
+    uint64_t prefix = 0, pmask = 0;
+    if (exact) {
+        uint32_t cnt = 0;
+        for (uint32_t i = threadIdx.x; i < n; i += NT) cnt += (uint32_t)(src[i] >> 32) >= tkey;
+        float l2 = 0.0f, h2 = 0.0f;
+        sel_span(S, cnt, l2, h2);
+        if (cnt > kk) {
+            radix_select_lds<NT>(src, n, tkey, kk, S, prefix, pmask);
+        } else {
+            exact = false;  // keep every entry at or above the floor
+            bstar = 0;
+            scale = 0.0f;
+            lo = 0.0f;
+        }
+    }
+    const int lane = threadIdx.x & 63;
+    uint32_t mk = NONE;
+    const uint32_t rounds = (n + NT - 1) / NT;
+    for (uint32_t rd = 0; rd < rounds; ++rd) {
+        const uint32_t i = rd * NT + threadIdx.x;
+        const uint64_t v = (i < n) ? src[i] : 0ull;
+        bool keep = i < n && (uint32_t)(v >> 32) >= tkey;
+        if (keep) keep = exact ? ((v & pmask) >= prefix) : (bin256(cval(v), lo, scale) >= bstar);
+        const uint64_t bal = __ballot(keep);
+        if (bal == 0) continue;
+        uint32_t wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&S.kcnt, (uint32_t)__popcll(bal));
+        wbase = (uint32_t)__shfl((int)wbase, 0, 64);
+        if (keep) {
+            dst[wbase + lane_rank(bal)] = v;
+            const uint32_t k = (uint32_t)(v >> 32);
+            mk = k < mk ? k : mk;
+        }
+    }
+    mk = wg_min_u32<NT>(mk, S.sc);
+    const uint32_t kept = S.kcnt;
+    if (kept >= kk && mk != NONE && mk > tkey) tkey = mk;
+    return kept;
+}
+
+// Append the elements of one group of 8 (values x[], first id j, nv valid)
+// with x >= tval to the active half: one LDS reservation per wave, slots
+// placed with ballots; hi tracks the largest value appended.  Returns true
+// when the wave's reservation did not fit (nothing written; the group stays
+// pending).
+template <bool FULL>
+__device__ __forceinline__ bool sel_append(SelShared &S, int half, const float (&x)[8], uint32_t j,
+                                           int nv, float tval, float &hi) {
+    const int lane = threadIdx.x & 63;
+    uint64_t bal[8];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        bal[i] = __ballot((FULL || i < nv) && x[i] >= tval);
+        tot += (uint32_t)__popcll(bal[i]);
+    }
+    if (tot == 0) return false;
+    uint32_t wbase = 0;
+    if (lane == 0) wbase = atomicAdd(&S.cnt, tot);
+    wbase = (uint32_t)__shfl((int)wbase, 0, 64);
+    if (wbase + tot > (uint32_t)SEL_CAP) {
+        if (lane == 0) atomicMin(&S.ffail, wbase);
+        return true;
+    }
+    uint64_t *dst = S.buf[half];
+    uint32_t off = wbase;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (bal[i] == 0) continue;
+        if ((bal[i] >> lane) & 1ull) {
+            const float xc = x[i] + 0.0f;  // -0 -> +0 before the key
+            dst[off + lane_rank(bal[i])] = mkcomp(xc, j + i);
+            hi = fmaxf(hi, xc);
+        }
+        off += (uint32_t)__popcll(bal[i]);
+    }
+    return false;
+}
+
+__device__ __forceinline__ float key_floor(uint32_t tkey) {
+    return tkey ? key2f(tkey) : -INFINITY;
+}
+
+// Admission key from one group of 8 per thread held in registers (the first
+// batch of a chunk): a value key k such that at least kk of the batch's
+// elements have key >= k, taken at the 256-bin histogram bin where the
+// count from the top reaches kk.  0 (admit everything) when the batch has
+// fewer than kk elements.
+__device__ uint32_t batch_key(SelShared &S, const float (&x)[8], int nv, uint32_t kk) {
+    uint32_t cnt = 0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nv) {
+            ++cnt;
+            if (x[i] > -INFINITY) {
+                lo = fminf(lo, x[i]);
+                hi = fmaxf(hi, x[i]);
+            }
+        }
+    sel_span(S, cnt, lo, hi);
+    if (cnt < kk || !(hi > lo)) return 0u;
+    const float scale = 256.0f / (hi - lo);
+    for (int i = threadIdx.x; i < 256; i += SEL_THREADS) S.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nv) atomicAdd(&S.hist[bin256(x[i], lo, scale)], 1u);
+    __syncthreads();
+    wave0_find_bin(S.hist, kk, S.sel);
+    __syncthreads();
+    const uint32_t bstar = S.sel[0];
+    uint32_t mk = NONE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nv && bin256(x[i], lo, scale) >= bstar) mk = min(mk, f2key(x[i] + 0.0f));
+    mk = wg_min_u32<SEL_THREADS>(mk, S.sc);
+    return mk == NONE ? 0u : mk;
+}
+
+// One batch before the workgroup barrier: widen/transform, top-p statistics,
+// the first batch's admission key, and the append.  Returns true when this
+// wave's append did not fit.
+template <int DT, bool XF, bool FULL>
+__device__ __forceinline__ bool select_front(SelShared &S, const Raw<DT> &cur, int base, int c0,
+                                             int c1, const uint32_t *bm, const KParams &P,
+                                             bool do_stats, Stats &st, bool &first, uint32_t kk,
+                                             uint32_t &tkey, uint32_t &rk_seen, uint32_t *rowkey,
+                                             int half, float &hi, float (&xo)[8], int &j0,
+                                             int &nv0) {
+    float x[1][8];
+    int jb[1], nv[1];
+    finish_batch<DT, SEL_THREADS, 1, XF, FULL, false>(*(const Raw<DT>(*)[1]) & cur, base, c0, c1,
+                                                      bm, P, x, jb, nv);
+    if (do_stats) stats_batch(st, x, nv);
+    if (first) {
+        // the first batch sets the admission key from its own values
+        first = false;
+        tkey = batch_key(S, x[0], nv[0], kk);
+        if (threadIdx.x == 0 && tkey) rk_seen = atomicMax(rowkey, tkey);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xo[i] = x[0][i];
+    j0 = jb[0];
+    nv0 = nv[0];
+    return sel_append<FULL>(S, half, x[0], (uint32_t)j0, nv0, key_floor(tkey), hi);
+}
+
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, KWork W) {
+    __shared__ SelShared S;
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
+    const Mode md = row_mode(P, b);
+    if (!(md.tk || md.tp)) return;
+    const int c0 = c * (int)L.chunk_len;
+    const int c1 = min(c0 + (int)L.chunk_len, P.V);
+    const int slot = b * NCH_MAX + c;
+    if (c0 >= c1) {
+        if (tid == 0) {
+            W.ccnt[slot] = 0;
+            W.cstat[slot] = empty_stat();
+        }
+        return;
+    }
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    const bool do_stats = !md.tk;
+    if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, c0, c1 - c0, P, b);
+    if (tid == 0) {
+        S.cnt = 0;
+        S.ffail = NONE;
+    }
+    const void *rowp = row_ptr(P, DT, b);
+    uint32_t *rowkey = W.rowkey + b;
+    uint32_t rk_seen = 0;  // thread 0: row key returned by the last publication
+
+    uint32_t tkey = 0;  // admission key: 0 admits everything
+    uint32_t valid = 0;
+    int half = 0;       // active half of the buffer
+    bool first = true;
+    float hi = -INFINITY;  // largest value this thread appended
+    Stats st;
+    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
+    constexpr int BATCH = SEL_THREADS * VEC;
+    Raw<DT> ring[SEL_DEPTH];
+#pragma unroll
+    for (int d = 0; d < SEL_DEPTH; ++d)
+        if (c0 + d * BATCH < c1)
+            issue_batch<DT, AL, SEL_THREADS, 1>(rowp, c0 + d * BATCH, c1, *(Raw<DT>(*)[1]) & ring[d]);
+    for (int base = c0; base < c1; base += BATCH) {
+        const Raw<DT> cur = ring[0];
+#pragma unroll
+        for (int d = 0; d + 1 < SEL_DEPTH; ++d) ring[d] = ring[d + 1];
+        if (base + SEL_DEPTH * BATCH < c1)
+            issue_batch<DT, AL, SEL_THREADS, 1>(rowp, base + SEL_DEPTH * BATCH, c1,
+                                               *(Raw<DT>(*)[1]) & ring[SEL_DEPTH - 1]);
+        float x[8];
+        int j0, nv0;
+        bool pending =
+            (base + BATCH <= c1)
+                ? select_front<DT, XF, true>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
+                                             tkey, rk_seen, rowkey, half, hi, x, j0, nv0)
+                : select_front<DT, XF, false>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
+                                              tkey, rk_seen, rowkey, half, hi, x, j0, nv0);
+        __syncthreads();
+        uint32_t ff = S.ffail;
+        valid = min(S.cnt, ff);
+        bool ovf = ff != NONE;
+        while (ovf || valid > (uint32_t)SEL_SOFT) {
+            // adopt the key the row's other chunks have published, cut back
+            float h = hi;
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) h = fmaxf(h, shxf(h, sft));
+            if ((tid & 63) == 0) S.shi[tid >> 6] = h;
+            if (tid == 0) S.rkey = rk_seen;
+            __syncthreads();
+            tkey = max(tkey, S.rkey);
+            h = S.shi[0];
+#pragma unroll
+            for (int i = 1; i < SEL_THREADS / 64; ++i) h = fmaxf(h, S.shi[i]);
+            const uint32_t kept = sel_reduce(S, half, valid, kk, SLOT, tkey, h);
+            half ^= 1;
+            if (tid == 0) {
+                S.cnt = kept;
+                S.ffail = NONE;
+                rk_seen = atomicMax(rowkey, tkey);
+            }
+            __syncthreads();
+            valid = kept;
+            if (!ovf) break;
+            if (pending) pending = sel_append<false>(S, half, x, (uint32_t)j0, nv0, key_floor(tkey), hi);
+            __syncthreads();
+            ff = S.ffail;
+            valid = min(S.cnt, ff);
+            ovf = ff != NONE;
+        }
+    }
+    // hand over the survivors above the latest row key
+    float h = hi;
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) h = fmaxf(h, shxf(h, sft));
+    if ((tid & 63) == 0) S.shi[tid >> 6] = h;
+    if (tid == 0)
+        S.rkey = max(rk_seen,
+                     (uint32_t)__hip_atomic_load(rowkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    tkey = max(tkey, S.rkey);
+    h = S.shi[0];
+#pragma unroll
+    for (int i = 1; i < SEL_THREADS / 64; ++i) h = fmaxf(h, S.shi[i]);
+    if (valid > (uint32_t)SLOT) {
+        valid = sel_reduce(S, half, valid, kk, SLOT, tkey, h);
+        half ^= 1;
+        __syncthreads();
+    }
+    // copy out the entries at or above the floor
+    if (tid == 0) S.kcnt = 0;
+    __syncthreads();
+    uint64_t *dst = W.cand + (int64_t)slot * SLOT;
+    const int lane = tid & 63;
+    const uint32_t rounds = (valid + SEL_THREADS - 1) / SEL_THREADS;
+    for (uint32_t rd = 0; rd < rounds; ++rd) {
+        const uint32_t i = rd * SEL_THREADS + tid;
+        const uint64_t v = (i < valid) ? S.buf[half][i] : 0ull;
+        const bool keep = i < valid && (uint32_t)(v >> 32) >= tkey;
+        const uint64_t bal = __ballot(keep);
+        if (bal == 0) continue;
+        uint32_t wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&S.kcnt, (uint32_t)__popcll(bal));
+        wbase = (uint32_t)__shfl((int)wbase, 0, 64);
+        if (keep) dst[wbase + lane_rank(bal)] = v;
+    }
+    ChunkStat cs = empty_stat();
+    if (do_stats) stats_reduce<SEL_THREADS>(st, S.scf, S.scd, cs);
+    __syncthreads();
+    if (tid == 0) {
+        W.ccnt[slot] = (int32_t)S.kcnt;
+        W.cstat[slot] = cs;
+    }
 }
 
 // ================================================================== k_rows
@@ -805,7 +1375,7 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
             uint64_t am = 0;
             for (int c = 0; c < nch; ++c)
                 if (W.ccnt[slot0 + c] > 0) {
-                    uint64_t v = W.cand[(int64_t)(slot0 + c) * KMAX];
+                    uint64_t v = W.cand[(int64_t)(slot0 + c) * SLOT];
                     am = v > am ? v : am;
                 }
             idx = cidx(am);
@@ -837,22 +1407,22 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
     const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
     uint32_t N = 0;
     for (int c = 0; c < nch; ++c) N += (uint32_t)W.ccnt[slot0 + c];
-    constexpr int R2 = NCH_MAX * KMAX / K2_THREADS;  // 8
+    constexpr int R2 = NCH_MAX * SLOT / K2_THREADS;  // 16
     uint64_t v[R2];
     uint32_t vm = 0;
 #pragma unroll
     for (int r = 0; r < R2; ++r) {
-        uint32_t s = tid + r * K2_THREADS;
-        uint32_t c = s / kk, i = s - c * kk;
-        bool ok = c < (uint32_t)nch && i < (uint32_t)W.ccnt[slot0 + min(c, (uint32_t)nch - 1)];
-        v[r] = ok ? W.cand[(int64_t)(slot0 + c) * KMAX + i] : 0ull;
+        const uint32_t s = tid + r * K2_THREADS;
+        const uint32_t c = s / SLOT, i = s % SLOT;
+        const bool ok = c < (uint32_t)nch && i < (uint32_t)W.ccnt[slot0 + min(c, (uint32_t)nch - 1)];
+        v[r] = ok ? W.cand[(int64_t)(slot0 + c) * SLOT + i] : 0ull;
         if (ok) vm |= 1u << r;
     }
     const uint32_t nsel = min(kk, N);
     uint32_t km = vm;
     if (N > kk) {
         uint64_t prefix, pmask;
-        wg_radix_select<K2_THREADS, R2>(v, vm, kk, S.hist, S.sel, prefix, pmask);
+        wg_radix_select<K2_THREADS, R2>(v, vm, kk, S.hist, S.sel, S.sc64, prefix, pmask);
         km = 0;
 #pragma unroll
         for (int r = 0; r < R2; ++r)
@@ -868,7 +1438,7 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
     const int npad = pow2_ceil((int)nsel);
     for (int i = nsel + tid; i < npad; i += K2_THREADS) S.srt[i] = 0ull;
     __syncthreads();
-    bitonic_desc<K2_THREADS>(S.srt, npad);
+    bitonic_desc_reg<K2_THREADS>(S.srt, npad);
 
     // ---- softmax over the sorted candidates, in double
     const float x0 = cval(S.srt[0]);
@@ -1036,7 +1606,7 @@ __device__ __forceinline__ bool in_play(const FallbackShared &S, float x, uint32
 }
 
 // Visit every element (x transformed, id j) of row b; f(x, j).
-template <int DT, bool AL, class F>
+template <int DT, bool AL, bool XF, class F>
 __device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
     const void *rowp = row_ptr(P, DT, b);
     const int64_t V = P.V;
@@ -1055,13 +1625,13 @@ __device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (i < nv) f(xform(x[i], (bits >> i) & 1u, P), (uint32_t)(j + i));
+                if (i < nv) f(xform<XF>(x[i], (bits >> i) & 1u, P), (uint32_t)(j + i));
         }
     }
     __syncthreads();
 }
 
-template <int DT, bool AL>
+template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
@@ -1101,7 +1671,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             }
             __syncthreads();
             double zt = 0.0;
-            row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+            row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
                 if (!(x > -INFINITY)) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
@@ -1154,7 +1724,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         if (path == 1) {
             if (tid == 0) S.counter = 0;
             __syncthreads();
-            row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+            row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
                 if (!(x > -INFINITY)) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
@@ -1225,7 +1795,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                     uint32_t mm = 0;
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        if (i < nv && xform(x[i], (bits >> i) & 1u, P) == xt) mm |= 1u << i;
+                        if (i < nv && xform<XF>(x[i], (bits >> i) & 1u, P) == xt) mm |= 1u << i;
                     uint32_t tot;
                     uint32_t off = wg_excl_scan_u32<K3_THREADS>(__popc(mm), S.sc, tot);
                     if (seen + off < cneed && cneed <= seen + off + __popc(mm)) {
@@ -1255,7 +1825,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         Race rc;
         rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
         const float *rowq = P.q + (int64_t)b * P.V;
-        row_pass<DT, AL>(P, b, S.bm, [&](float x, uint32_t j) {
+        row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
             if (mkcomp(x, j) >= Tstar) race_offer(rc, x, rowq[j] + P.eps, j);
         });
         Race r = wg_race<K3_THREADS>(rc, S.scx, S.scq, S.sci);
@@ -1272,10 +1842,22 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 
 // ================================================================== k_dense
 
-template <int DT, bool AL>
+// Dense filtered logits (and optional probabilities) of one 32768-element
+// tile of one row.  Rows with a kept list: the tile is written from a bitmap
+// of the kept positions and the kept values placed by their rank among the
+// set bits (no read of the logits, full-line stores).  Rows whose kept set is
+// a threshold (after the full-row search) re-read and re-transform the tile.
+
+struct DenseShared {
+    uint32_t tb[TILE4 / 32];    // kept positions in the tile
+    uint32_t wpre[TILE4 / 32];  // set bits before each word
+    float lval[KMAX];           // kept values by rank
+    uint32_t sc[16];
+};
+
+template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K4_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
-    __shared__ float tv[TILE4];
-    __shared__ uint32_t tb[TILE4 / 32];
+    __shared__ DenseShared S;
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
     const int tid = threadIdx.x;
     const int b = blockIdx.x / L.nt4, t = blockIdx.x % L.nt4;
@@ -1288,60 +1870,88 @@ __global__ __launch_bounds__(K4_THREADS) void k_dense(KParams P, KPlan L, KWork 
     float *ol = want_l ? P.out_logits + (int64_t)b * V : nullptr;
     float *op = want_p ? P.out_probs + (int64_t)b * V : nullptr;
     const double m = (double)info.m, ZK = info.ZK;
+    constexpr int G = TILE4 / (K4_THREADS * VEC);  // groups of 8 per thread
+    constexpr int WPT = TILE4 / 32 / K4_THREADS;   // bitmap words per thread
 
     if (info.kind == KIND_LIST) {
-        for (int w = tid; w < TILE4 / 32; w += K4_THREADS) tb[w] = 0u;
+#pragma unroll
+        for (int w = 0; w < WPT; ++w) S.tb[tid * WPT + w] = 0u;
         __syncthreads();
         const uint64_t *kl = W.klist + (int64_t)b * KMAX;
-        for (int i = tid; i < info.nK; i += K4_THREADS) {
-            uint64_t cv = kl[i];
-            int64_t j = cidx(cv);
+        const int nK = info.nK;
+        for (int i = tid; i < nK; i += K4_THREADS) {
+            const int64_t j = cidx(kl[i]);
             if (j >= t0 && j < t1) {
-                int r = (int)(j - t0);
-                tv[r] = cval(cv);
-                atomicOr(&tb[r >> 5], 1u << (r & 31));
+                const int r = (int)(j - t0);
+                atomicOr(&S.tb[r >> 5], 1u << (r & 31));
             }
         }
         __syncthreads();
-        for (int g = 0; g < TILE4 / (K4_THREADS * VEC); ++g) {
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int w = 0; w < WPT; ++w) cnt += __popc(S.tb[tid * WPT + w]);
+        uint32_t tot;
+        uint32_t run = wg_excl_scan_u32<K4_THREADS>(cnt, S.sc, tot);
+#pragma unroll
+        for (int w = 0; w < WPT; ++w) {
+            S.wpre[tid * WPT + w] = run;
+            run += __popc(S.tb[tid * WPT + w]);
+        }
+        __syncthreads();
+        for (int i = tid; i < nK; i += K4_THREADS) {
+            const uint64_t cv = kl[i];
+            const int64_t j = cidx(cv);
+            if (j >= t0 && j < t1) {
+                const int r = (int)(j - t0);
+                const uint32_t below = S.tb[r >> 5] & ((1u << (r & 31)) - 1u);
+                S.lval[S.wpre[r >> 5] + __popc(below)] = cval(cv);
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int g = 0; g < G; ++g) {
             const int r0 = (g * K4_THREADS + tid) * VEC;
             const int64_t j = t0 + r0;
-            int64_t rem = t1 - j;
-            if (rem <= 0) continue;
-            const int nv = rem >= 8 ? 8 : (int)rem;
-            const uint32_t bits = (tb[r0 >> 5] >> (r0 & 31)) & 0xffu;
-            if (want_l) {
-                float o[8];
+            const int nv = group_nv(j, t1);
+            if (nv == 0) continue;
+            const uint32_t word = S.tb[r0 >> 5];
+            const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
+            float xv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[i] = ((bits >> i) & 1u) ? tv[r0 + i] : -INFINITY;
-                store8<AL>(ol, j, nv, o);
+            for (int i = 0; i < 8; ++i) xv[i] = -INFINITY;
+            if (bits) {
+                const uint32_t base = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
+                uint32_t k = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if ((bits >> i) & 1u) xv[i] = S.lval[base + k++];
             }
+            if (want_l) store8<AL>(ol, j, nv, xv);
             if (want_p) {
                 float o[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    o[i] = ((bits >> i) & 1u) ? (float)(exp((double)tv[r0 + i] - m) / ZK) : 0.0f;
+                    o[i] = ((bits >> i) & 1u) ? (float)(exp((double)xv[i] - m) / ZK) : 0.0f;
                 store8<AL>(op, j, nv, o);
             }
         }
         return;
     }
     if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
-    // K = { comp >= T }: re-read the tile
-    if (P.pen) build_bitmap<K4_THREADS>(bm, t0, t1 - t0, P, b);
+    // K = { comp >= T } (T = 0 keeps the whole row): re-read the tile
+    if (XF && P.pen) build_bitmap<K4_THREADS>(bm, t0, t1 - t0, P, b);
     const void *rowp = row_ptr(P, DT, b);
     const uint64_t T = info.T;
-    for (int g = 0; g < TILE4 / (K4_THREADS * VEC); ++g) {
+    for (int g = 0; g < G; ++g) {
         const int r0 = (g * K4_THREADS + tid) * VEC;
         const int64_t j = t0 + r0;
-        int64_t rem = t1 - j;
-        if (rem <= 0) continue;
-        const int nv = rem >= 8 ? 8 : (int)rem;
+        const int nv = group_nv(j, t1);
+        if (nv == 0) continue;
         float x[8];
         load8<DT, AL>(rowp, j, nv, x);
-        uint32_t bits = P.pen ? ((bm[r0 >> 5] >> (r0 & 31)) & 0xffu) : 0u;
+        const uint32_t bits = pen_bits<XF>(bm, r0, P);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = xform(x[i], (bits >> i) & 1u, P);
+        for (int i = 0; i < 8; ++i) x[i] = xform<XF>(x[i], (bits >> i) & 1u, P);
         if (want_l && info.kind == KIND_THRESH) {
             float o[8];
 #pragma unroll
@@ -1371,15 +1981,34 @@ hipError_t launch(K kern, dim3 grid, dim3 block, size_t shmem, hipStream_t s, co
 
 }  // namespace
 
-hipError_t launch_chunk(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
-                        hipStream_t s) {
+// Instantiation table: storage type x 16-byte-aligned rows x transform stage
+// (penalty or temperature present).
+#define SMP_PICK(KERN, grid, block, shmem)                                                 \
+    (xf ? (dtype == 1 ? (al ? launch(KERN<1, true, true>, grid, block, shmem, s, p, l, w)   \
+                            : launch(KERN<1, false, true>, grid, block, shmem, s, p, l, w)) \
+                      : (al ? launch(KERN<0, true, true>, grid, block, shmem, s, p, l, w)   \
+                            : launch(KERN<0, false, true>, grid, block, shmem, s, p, l, w)))\
+        : (dtype == 1 ? (al ? launch(KERN<1, true, false>, grid, block, shmem, s, p, l, w)  \
+                            : launch(KERN<1, false, false>, grid, block, shmem, s, p, l, w))\
+                      : (al ? launch(KERN<0, true, false>, grid, block, shmem, s, p, l, w)  \
+                            : launch(KERN<0, false, false>, grid, block, shmem, s, p, l, w))))
+
+static bool any_transform(const KParams &p) { return p.pen || p.temperature != 1.0f; }
+
+hipError_t launch_stream(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                         hipStream_t s) {
+    const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(K1_THREADS);
     size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
-    if (dtype == 1)
-        return al ? launch(k_chunk<1, true>, grid, block, sh, s, p, l, w)
-                  : launch(k_chunk<1, false>, grid, block, sh, s, p, l, w);
-    return al ? launch(k_chunk<0, true>, grid, block, sh, s, p, l, w)
-              : launch(k_chunk<0, false>, grid, block, sh, s, p, l, w);
+    return SMP_PICK(k_stream, grid, block, sh);
+}
+
+hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                         hipStream_t s) {
+    const bool xf = any_transform(p);
+    dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(SEL_THREADS);
+    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
+    return SMP_PICK(k_select, grid, block, sh);
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {
@@ -1388,23 +2017,19 @@ hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStre
 
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                            hipStream_t s) {
+    const bool xf = any_transform(p);
     dim3 grid((unsigned)p.B), block(K3_THREADS);
-    if (dtype == 1)
-        return al ? launch(k_fallback<1, true>, grid, block, 0, s, p, l, w)
-                  : launch(k_fallback<1, false>, grid, block, 0, s, p, l, w);
-    return al ? launch(k_fallback<0, true>, grid, block, 0, s, p, l, w)
-              : launch(k_fallback<0, false>, grid, block, 0, s, p, l, w);
+    return SMP_PICK(k_fallback, grid, block, 0);
 }
 
 hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                         hipStream_t s) {
+    const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nt4)), block(K4_THREADS);
     size_t sh = p.pen ? (size_t)(TILE4 / 32) * 4 : 0;
-    if (dtype == 1)
-        return al ? launch(k_dense<1, true>, grid, block, sh, s, p, l, w)
-                  : launch(k_dense<1, false>, grid, block, sh, s, p, l, w);
-    return al ? launch(k_dense<0, true>, grid, block, sh, s, p, l, w)
-              : launch(k_dense<0, false>, grid, block, sh, s, p, l, w);
+    return SMP_PICK(k_dense, grid, block, sh);
 }
+
+#undef SMP_PICK
 
 }  // namespace smp

@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(
             f"HIP sampler library not found at {path}; build it with "
             "`python -m decode_token_sampling_row_amd.build` (hipcc, gfx950)")
+    # torch's HIP runtime must be the one in the process: the library then
+    # binds to it (same soname) and accepts torch's streams and allocations.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.sampler_create.argtypes = [ctypes.POINTER(P), ctypes.c_int32, ctypes.c_int32,
@@ -179,7 +182,7 @@ def sampler_run(h, batch: int, args: sampler_args, stream: Optional[int] = None)
         raise SamplerError(rc, "sampler_run")
 
 
-def sampler_last_profile(h, n: int = 4):
+def sampler_last_profile(h, n: int = 5):
     buf = (ctypes.c_float * n)()
     rc = load_library().sampler_last_profile(h, buf, int(n))
     if rc < 0:

@@ -61,6 +61,7 @@ extern "C" {
 #define SAMPLER_NEED_PROBS 2u   /* write out_probs (debug; re-reads logits)  */
 #define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
                                    figures with sampler_last_profile         */
+#define SAMPLER_PROFILE_SLOTS 5
 
 /* Largest k of the top-k stage and largest top-k guess. */
 #define SAMPLER_TOPK_MAX 1024
@@ -140,10 +141,12 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
 
 /*
  * Kernel times of the last sampler_run made with SAMPLER_PROFILE, in
- * milliseconds, in launch order: [0] chunk pass, [1] row merge/cutoff/sample,
- * [2] full-row top-p cutoff (rows whose guess failed), [3] dense writer.
- * Waits for that call to finish.  Kernels that were not launched read 0.
- * Returns the number of entries written (<= n), or a negative error code.
+ * milliseconds, in launch order: [0] streaming pass of unfiltered rows,
+ * [1] streaming candidate pass of top-k / top-p rows, [2] row merge /
+ * cutoff / sample, [3] full-row top-p cutoff (rows whose guess failed),
+ * [4] dense writer.  Waits for that call to finish.  Kernels that were not
+ * launched read 0.  Returns the number of entries written (<= n), or a
+ * negative error code.
  */
 int sampler_last_profile(sampler_t *h, float *ms, int32_t n);
 
