@@ -12,6 +12,9 @@
 
 using namespace smp;
 
+constexpr int PROF_KERNELS = SAMPLER_PROFILE_SLOTS;
+constexpr int PROF_RING = 64;
+
 struct sampler_s {
     int32_t max_batch;
     int32_t vocab;
@@ -21,10 +24,12 @@ struct sampler_s {
     int device;
     KWork ws;
     void *ws_base;
-    hipEvent_t ev[6];
+    // profiling: a ring of PROF_RING calls, PROF_KERNELS + 1 events each
+    hipEvent_t ev[PROF_RING][PROF_KERNELS + 1];
+    bool events_made;
     bool events_ok;
-    bool prof_pending;
-    bool launched[5];
+    int nprof;   // profiled calls since the last read
+    bool launched[PROF_RING][PROF_KERNELS];
 };
 
 namespace {
@@ -103,6 +108,14 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
     const size_t o_rowkey = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
+    const size_t o_rowthr = off;
+    off = align_up(off + B * sizeof(float), 256);
+    const size_t o_rcand = off;
+    off = align_up(off + B * SLOT * sizeof(uint64_t), 256);
+    const size_t o_rcnt = off;
+    off = align_up(off + B * sizeof(int32_t), 256);
+    const size_t o_rmask = off;
+    off = align_up(off + B * sizeof(uint32_t), 256);
     void *base = nullptr;
     hipError_t e = hipMalloc(&base, off);
     if (e != hipSuccess) {
@@ -118,10 +131,13 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.info = (RowInfo *)(c + o_info);
     s->ws.klist = (uint64_t *)(c + o_klist);
     s->ws.rowkey = (uint32_t *)(c + o_rowkey);
-    s->events_ok = true;
-    for (int i = 0; i < 6; ++i)
-        if (hipEventCreate(&s->ev[i]) != hipSuccess) s->events_ok = false;
-    s->prof_pending = false;
+    s->ws.rowthr = (float *)(c + o_rowthr);
+    s->ws.rcand = (uint64_t *)(c + o_rcand);
+    s->ws.rcnt = (int32_t *)(c + o_rcnt);
+    s->ws.rmask = (uint32_t *)(c + o_rmask);
+    s->events_made = false;
+    s->events_ok = false;
+    s->nprof = 0;
     *h = s;
     return SAMPLER_OK;
 }
@@ -180,55 +196,80 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
                     (p.out_logits == nullptr || aligned16(p.out_logits)) &&
                     (p.out_probs == nullptr || aligned16(p.out_probs));
 
-    const bool prof = (a->flags & SAMPLER_PROFILE) && h->events_ok;
-    for (int i = 0; i < 5; ++i) h->launched[i] = false;
+    bool prof = (a->flags & SAMPLER_PROFILE) != 0;
+    if (prof && !h->events_made) {
+        h->events_made = true;
+        h->events_ok = true;
+        for (int r = 0; r < PROF_RING; ++r)
+            for (int i = 0; i <= PROF_KERNELS; ++i)
+                if (hipEventCreate(&h->ev[r][i]) != hipSuccess) h->events_ok = false;
+    }
+    prof = prof && h->events_ok;
+    const int slot = h->nprof % PROF_RING;
+    bool *launched = h->launched[slot];
+    for (int i = 0; i < PROF_KERNELS; ++i) launched[i] = false;
     auto mark = [&](int i) {
-        if (prof) (void)hipEventRecord(h->ev[i], st);
+        if (prof) (void)hipEventRecord(h->ev[slot][i], st);
     };
+    const bool filtering = a->top_k != nullptr || a->top_p != nullptr;
 
     hipError_t e;
     mark(0);
     e = launch_stream(p, l, h->ws, h->dtype, al, st);
     if (e != hipSuccess) return SAMPLER_EHIP;
-    h->launched[0] = true;
+    launched[0] = true;
     mark(1);
-    if (a->top_k != nullptr || a->top_p != nullptr) {
+    if (filtering) {
         e = launch_select(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
-        h->launched[1] = true;
+        launched[1] = true;
     }
     mark(2);
+    if (filtering) {
+        e = launch_fix(p, l, h->ws, h->dtype, al, st);
+        if (e != hipSuccess) return SAMPLER_EHIP;
+        launched[2] = true;
+    }
+    mark(3);
     e = launch_rows(p, l, h->ws, st);
     if (e != hipSuccess) return SAMPLER_EHIP;
-    h->launched[2] = true;
-    mark(3);
+    launched[3] = true;
+    mark(4);
     if (a->top_p != nullptr) {
         e = launch_fallback(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
-        h->launched[3] = true;
+        launched[4] = true;
     }
-    mark(4);
+    mark(5);
     if (p.out_logits || p.out_probs) {
         e = launch_dense(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
-        h->launched[4] = true;
+        launched[5] = true;
     }
-    mark(5);
-    h->prof_pending = prof;
+    mark(6);
+    if (prof) ++h->nprof;
     return SAMPLER_OK;
 }
 
-int sampler_last_profile(sampler_t *h, float *ms, int32_t n) {
+int sampler_profile(sampler_t *h, float *ms, int32_t n) {
     if (h == nullptr || ms == nullptr || n < 0) return SAMPLER_EINVAL;
-    if (!h->prof_pending) return SAMPLER_EINVAL;
-    if (hipEventSynchronize(h->ev[5]) != hipSuccess) return SAMPLER_EHIP;
-    int w = n < 5 ? n : 5;
+    if (h->nprof == 0) return SAMPLER_EINVAL;
+    const int calls = h->nprof < PROF_RING ? h->nprof : PROF_RING;
+    const int last = (h->nprof - 1) % PROF_RING;
+    if (hipEventSynchronize(h->ev[last][PROF_KERNELS]) != hipSuccess) return SAMPLER_EHIP;
+    const int w = n < PROF_KERNELS ? n : PROF_KERNELS;
     for (int i = 0; i < w; ++i) {
-        float t = 0.0f;
-        if (h->launched[i] && hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]) != hipSuccess)
-            return SAMPLER_EHIP;
-        ms[i] = h->launched[i] ? t : 0.0f;
+        double sum = 0.0;
+        for (int r = 0; r < calls; ++r) {
+            float t = 0.0f;
+            if (h->launched[r][i] &&
+                hipEventElapsedTime(&t, h->ev[r][i], h->ev[r][i + 1]) != hipSuccess)
+                return SAMPLER_EHIP;
+            sum += h->launched[r][i] ? t : 0.0f;
+        }
+        ms[i] = (float)(sum / calls);
     }
+    h->nprof = 0;
     return w;
 }
 
@@ -236,8 +277,10 @@ int sampler_destroy(sampler_t *h) {
     if (h == nullptr) return SAMPLER_OK;
     int rc = SAMPLER_OK;
     if (h->ws_base && hipFree(h->ws_base) != hipSuccess) rc = SAMPLER_EHIP;
-    for (int i = 0; i < 6; ++i)
-        if (h->events_ok) (void)hipEventDestroy(h->ev[i]);
+    if (h->events_made)
+        for (int r = 0; r < PROF_RING; ++r)
+            for (int i = 0; i <= PROF_KERNELS; ++i)
+                if (h->ev[r][i]) (void)hipEventDestroy(h->ev[r][i]);
     delete h;
     return rc;
 }

@@ -13,8 +13,13 @@ constexpr int TILE = K1_THREADS * VEC;  // 2048 elements
 constexpr int NCH_MAX = 8;              // chunks per row
 constexpr int KMAX = 1024;              // largest k / guess
 constexpr int SLOT = 2048;              // candidates a chunk may hand over
-constexpr int SEL_CAP = 4096;           // LDS candidate buffer entries
-constexpr int SEL_SOFT = 3072;          // cut the buffer back above this fill
+constexpr int SEL_CAP = 2048;           // entries per half of the LDS candidate buffer
+constexpr int SEL_SOFT = 1536;          // exact pass: cut a half back above this fill
+constexpr int SEL_LIMIT = 1536;         // exact pass: most entries a cut-back keeps
+// Row admission estimate: EST_SEGS evenly spaced runs of EST_SEG logits.
+constexpr int EST_SEGS = 16;
+constexpr int EST_SEG = 1024;
+constexpr int EST_N = EST_SEGS * EST_SEG;
 // Row kernels.
 constexpr int K2_THREADS = 1024;
 constexpr int K3_THREADS = 1024;
@@ -40,7 +45,7 @@ struct ChunkStat {
     float rx;      // race winner: logit
     float rqe;     // race winner: q + eps
     uint32_t ridx; // race winner: vocab id (0xffffffff = none)
-    uint32_t pad;
+    uint32_t nstr; // select pass: handed-over entries above the row estimate
 };
 
 struct RowInfo {
@@ -84,11 +89,15 @@ struct KPlan {
 
 struct KWork {
     uint64_t *cand;   // [maxB][NCH_MAX][SLOT]
-    int32_t *ccnt;    // [maxB][NCH_MAX]
+    int32_t *ccnt;    // [maxB][NCH_MAX] (-1: the chunk overflowed the fast pass)
     ChunkStat *cstat; // [maxB][NCH_MAX]
     RowInfo *info;    // [maxB]
     uint64_t *klist;  // [maxB][KMAX]
-    uint32_t *rowkey; // [maxB] admission key shared by a row's chunks
+    uint32_t *rowkey; // [maxB] exact admission key shared by a row's chunks
+    float *rowthr;    // [maxB] estimated admission value of the row
+    uint64_t *rcand;  // [maxB][SLOT] candidates of a row's redone chunks
+    int32_t *rcnt;    // [maxB] entries in rcand
+    uint32_t *rmask;  // [maxB] chunks replaced by rcand (0 = none)
 };
 
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
@@ -96,6 +105,8 @@ hipError_t launch_stream(const KParams &p, const KPlan &l, const KWork &w, int d
                          bool aligned, hipStream_t s);
 hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                          bool aligned, hipStream_t s);
+hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
+                      hipStream_t s);
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                            bool aligned, hipStream_t s);

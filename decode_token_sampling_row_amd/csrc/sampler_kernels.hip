@@ -522,7 +522,7 @@ __device__ __forceinline__ int pow2_ceil(int n) {
 // Chunk/segment-local bitmap of a row's history ids (duplicates collapse,
 // ids outside [seg0, seg0 + len) ignored).  Begins and ends with barriers.
 template <int NT>
-__device__ void build_bitmap(uint32_t *bm, int64_t seg0, int64_t len, const KParams &P, int b) {
+__device__ __forceinline__ void build_bitmap(uint32_t *bm, int64_t seg0, int64_t len, const KParams &P, int b) {
     const int nw = (int)((len + 31) >> 5);
     __syncthreads();
     for (int w = threadIdx.x; w < nw; w += NT) bm[w] = 0u;
@@ -543,7 +543,6 @@ __device__ __forceinline__ const void *row_ptr(const KParams &P, int dt, int b) 
 
 constexpr int U = 4;           // k_stream: tiles per batch (256 threads)
 constexpr int SEL_THREADS = 512;
-constexpr int SEL_U = 1;       // k_select: tiles per batch (512 threads)
 constexpr int SEL_DEPTH = 4;   // k_select: batches in flight
 
 __device__ __forceinline__ int group_nv(int j, int end) {
@@ -650,7 +649,9 @@ __device__ __forceinline__ void finish_batch(const Raw<DT> (&raw)[UU], int base,
 // Running (max, sum exp(x - max), finite min) of one thread.  Terms are
 // hardware fp32 exponentials (exp2 of a scaled argument: relative error grows
 // like |x - max| * 2^-24, so the mass-weighted error of the total stays near
-// 1e-6 even for long flat tails) summed in double; when the running max rises
+// 1e-6 even for long flat tails), summed in fp32 per group of 8 (each term
+// <= 1, so a group sum carries a few 1e-7 relative) and the group sums in
+// double; when the running max rises
 // the sum is rescaled by an fp32 exponential of the (non-positive)
 // difference, a few times per chunk at most.
 struct Stats {
@@ -674,16 +675,19 @@ __device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][8], 
     }
     if (st.m > -INFINITY) {
 #pragma unroll
-        for (int u = 0; u < UU; ++u)
+        for (int u = 0; u < UU; ++u) {
+            float zs = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (i < nv[u]) st.z += (double)__expf(x[u][i] - st.m);
+                if (i < nv[u]) zs += __expf(x[u][i] - st.m);
+            st.z += (double)zs;
+        }
     }
 }
 
 // Workgroup merge of per-thread Stats into one ChunkStat's m / z / xmin.
 template <int NT>
-__device__ void stats_reduce(const Stats &st, float *scf, double *scd, ChunkStat &cs) {
+__device__ __forceinline__ void stats_reduce(const Stats &st, float *scf, double *scd, ChunkStat &cs) {
     float m = st.m;
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, shxf(m, s));
@@ -717,7 +721,7 @@ __device__ __forceinline__ ChunkStat empty_stat() {
     cs.rx = -INFINITY;
     cs.rqe = 1.0f;
     cs.ridx = NONE;
-    cs.pad = 0;
+    cs.nstr = 0;
     return cs;
 }
 
@@ -726,13 +730,129 @@ __device__ __forceinline__ ChunkStat empty_stat() {
 // output (x itself), runs the exponential race over the whole chunk (q is
 // streamed in the same pass) or the greedy argmax, and (for the optional
 // probabilities) the chunk's max / sum-exp.  No barrier in the loop.
+// For rows with top-k or top-p the first workgroup of the row estimates the
+// admission value the select pass filters with.
 
 struct StreamShared {
     uint64_t sc64[16];
     double scd[16];
     float scx[16], scq[16];
     uint32_t sci[16];
+    uint32_t hist[256];
+    uint32_t sel[4];
 };
+
+// Admission value t of a top-k / top-p row, chosen so that the row holds at
+// least kk elements >= t with high probability, and not many more: close
+// below the r-th largest raw logit of a sample -- EST_SEGS runs of EST_SEG
+// elements, one in each of EST_SEGS equal segments of the row, or the whole
+// row when it is shorter than EST_N -- r
+// being the sample rank expected for the row's kk-th largest plus four
+// standard deviations of it plus 8.  The sample's order keys are binned by
+// their distance below the sample maximum, first in steps of 2^16 (one bf16
+// ulp), and in steps of 2^24 when the 255 top bins hold fewer than r; only
+// the top 255 bins are counted, so the bins stay sparse and the LDS atomics
+// rarely collide.  -inf (admit everything) when r would exceed the sample.
+// Only the speed of the select pass depends on t: that pass checks that what
+// it admitted holds the row's kk largest and redoes the row exactly when it
+// does not.
+// First element of sample run s of row b (V > EST_N): inside the s-th of
+// EST_SEGS equal segments, at one of 16 offsets that depend on s and b, a
+// multiple of 8.  Staggered so that the runs of all rows do not start at
+// the same offsets modulo a large power of two, where they would all fall
+// on the same few memory channels.
+__device__ __forceinline__ int est_run_start(int s, int b, int V) {
+    const int64_t seg0 = ((int64_t)s * V / EST_SEGS) & ~(int64_t)(VEC - 1);
+    const int64_t seg1 = ((int64_t)(s + 1) * V / EST_SEGS) & ~(int64_t)(VEC - 1);
+    const int64_t room = seg1 - seg0 - EST_SEG;  // >= 0 when V > EST_N
+    const int64_t step = (room / 16) & ~(int64_t)(VEC - 1);
+    return (int)(seg0 + (int64_t)((s * 5 + b * 3) & 15) * step);
+}
+
+template <int DT, bool AL>
+__device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t kk, StreamShared &S) {
+    constexpr int NT = K1_THREADS;
+    constexpr int PER = EST_N / (NT * VEC);  // groups of 8 per thread
+    constexpr int GPS = EST_SEG / VEC;       // groups per run
+    const int V = P.V;
+    const bool whole = V <= EST_N;
+    const int n = whole ? V : EST_N;
+    const double r0 = (double)kk * (double)n / (double)V;
+    const double rr = ceil(r0 + 4.0 * sqrt(r0) + 8.0);
+    if (rr >= (double)n) return -INFINITY;
+    const uint32_t r = (uint32_t)rr;
+    const void *rowp = row_ptr(P, DT, b);
+    // the whole sample in registers, every load in flight at once
+    Raw<DT> raw[PER];
+    int nv[PER];
+#pragma unroll
+    for (int g = 0; g < PER; ++g) {
+        const int gi = (int)threadIdx.x + g * NT;
+        int j;
+        if (whole) {
+            j = gi * VEC;
+        } else {
+            const int seg = gi / GPS;
+            j = est_run_start(seg, b, V) + (gi % GPS) * VEC;
+        }
+        nv[g] = group_nv(j, V);
+        load_raw<DT, AL>(rowp, j, nv[g], raw[g]);
+    }
+    // the sample maximum
+    uint32_t mx = 0;
+#pragma unroll
+    for (int g = 0; g < PER; ++g) {
+        float x[8];
+        unpack_raw<DT>(raw[g], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nv[g]) mx = max(mx, f2key(x[i]));
+    }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) mx = max(mx, shx(mx, sft));
+    if ((threadIdx.x & 63) == 0) S.sci[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = S.sci[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) mx = max(mx, S.sci[i]);
+    for (int shift = 16; shift <= 24; shift += 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < PER; ++g) {
+            float x[8];
+            unpack_raw<DT>(raw[g], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t d = (mx - f2key(x[i])) >> shift;
+                if (i < nv[g] && d < 255u) atomicAdd(&S.hist[255 - d], 1u);
+            }
+        }
+        __syncthreads();
+        uint32_t tot = 0;
+        if (threadIdx.x < 64) {
+            tot = S.hist[4 * threadIdx.x] + S.hist[4 * threadIdx.x + 1] +
+                  S.hist[4 * threadIdx.x + 2] + S.hist[4 * threadIdx.x + 3];
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) tot += shx(tot, sft);
+            if (threadIdx.x == 0) S.sel[3] = tot;
+        }
+        __syncthreads();
+        tot = S.sel[3];
+        if (tot >= r || shift == 24) {
+            if (tot < r) return -INFINITY;  // unreachable: 255 * 2^24 spans every key
+            wave0_find_bin(S.hist, r, S.sel);
+            __syncthreads();
+            const uint32_t d = 255u - S.sel[0];
+            // every key of bins 0..d, i.e. key > mx - (d + 1) * 2^shift
+            const uint64_t lo = (uint64_t)mx - (((uint64_t)d + 1) << shift) + 1;
+            const uint32_t fk = lo > (uint64_t)mx ? 0u : (uint32_t)lo;
+            return fk <= f2key(-INFINITY) ? -INFINITY : key2f(fk);
+        }
+        __syncthreads();
+    }
+    return -INFINITY;
+}
 
 struct StreamState {
     Stats st;
@@ -781,9 +901,21 @@ __global__ __launch_bounds__(K1_THREADS) void k_stream(KParams P, KPlan L, KWork
     extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
     const int tid = threadIdx.x;
     const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
-    if (c == 0 && tid == 0) W.rowkey[b] = 0u;  // the row's shared admission key
+    if (c == 0 && tid == 0) {
+        W.rowkey[b] = 0u;  // the row's exact admission key
+        W.rmask[b] = 0u;   // no chunk redone
+    }
     const Mode md = row_mode(P, b);
-    if (md.tk || md.tp) return;
+    if (md.tk || md.tp) {
+        // one workgroup per row estimates; which one rotates with the row so
+        // the estimates spread over the XCDs (workgroup i runs on XCD i % 8)
+        if (c == b % L.nch) {
+            const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+            const float t = row_estimate<DT, AL>(P, b, kk, S);
+            if (tid == 0) W.rowthr[b] = t;
+        }
+        return;
+    }
     const int c0 = c * (int)L.chunk_len;
     const int c1 = min(c0 + (int)L.chunk_len, P.V);
     const int slot = b * NCH_MAX + c;
@@ -1160,42 +1292,26 @@ __device__ __forceinline__ bool select_front(SelShared &S, const Raw<DT> &cur, i
     return sel_append<FULL>(S, half, x[0], (uint32_t)j0, nv0, key_floor(tkey), hi);
 }
 
+// Exact selection over the chunk [c0, c1) of row b, appended to the `valid`
+// entries already in S.buf[half] (hi: an upper bound of their values, or
+// -inf): on return S.buf[half] holds `valid` entries, and every element of
+// the chunk and of the earlier entries that is among their kk largest, or
+// whose value key is >= the returned tkey (tkey only rises), is among them.
+// tkey on entry is a valid admission key for the row (0 = none).  The
+// penalty bitmap bm must describe [c0, c1).
 template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, KWork W) {
-    __shared__ SelShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
+__device__ void select_exact(SelShared &S, const KParams &P, const uint32_t *bm,
+                             const void *rowp, int c0, int c1, uint32_t kk, bool do_stats,
+                             Stats &st, uint32_t *rowkey, uint32_t &tkey, int &half,
+                             uint32_t &valid, float &hi) {
     const int tid = threadIdx.x;
-    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
-    const Mode md = row_mode(P, b);
-    if (!(md.tk || md.tp)) return;
-    const int c0 = c * (int)L.chunk_len;
-    const int c1 = min(c0 + (int)L.chunk_len, P.V);
-    const int slot = b * NCH_MAX + c;
-    if (c0 >= c1) {
-        if (tid == 0) {
-            W.ccnt[slot] = 0;
-            W.cstat[slot] = empty_stat();
-        }
-        return;
-    }
-    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-    const bool do_stats = !md.tk;
-    if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, c0, c1 - c0, P, b);
     if (tid == 0) {
-        S.cnt = 0;
+        S.cnt = valid;
         S.ffail = NONE;
     }
-    const void *rowp = row_ptr(P, DT, b);
-    uint32_t *rowkey = W.rowkey + b;
+    __syncthreads();
     uint32_t rk_seen = 0;  // thread 0: row key returned by the last publication
-
-    uint32_t tkey = 0;  // admission key: 0 admits everything
-    uint32_t valid = 0;
-    int half = 0;       // active half of the buffer
     bool first = true;
-    float hi = -INFINITY;  // largest value this thread appended
-    Stats st;
-    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
     constexpr int BATCH = SEL_THREADS * VEC;
     Raw<DT> ring[SEL_DEPTH];
 #pragma unroll
@@ -1211,12 +1327,14 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, K
                                                *(Raw<DT>(*)[1]) & ring[SEL_DEPTH - 1]);
         float x[8];
         int j0, nv0;
+        const uint32_t tk_in = tkey;
         bool pending =
             (base + BATCH <= c1)
                 ? select_front<DT, XF, true>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
                                              tkey, rk_seen, rowkey, half, hi, x, j0, nv0)
                 : select_front<DT, XF, false>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
                                               tkey, rk_seen, rowkey, half, hi, x, j0, nv0);
+        tkey = max(tkey, tk_in);
         __syncthreads();
         uint32_t ff = S.ffail;
         valid = min(S.cnt, ff);
@@ -1233,7 +1351,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, K
             h = S.shi[0];
 #pragma unroll
             for (int i = 1; i < SEL_THREADS / 64; ++i) h = fmaxf(h, S.shi[i]);
-            const uint32_t kept = sel_reduce(S, half, valid, kk, SLOT, tkey, h);
+            const uint32_t kept = sel_reduce(S, half, valid, kk, SEL_LIMIT, tkey, h);
             half ^= 1;
             if (tid == 0) {
                 S.cnt = kept;
@@ -1250,34 +1368,191 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, K
             ovf = ff != NONE;
         }
     }
-    // hand over the survivors above the latest row key
-    float h = hi;
-#pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) h = fmaxf(h, shxf(h, sft));
-    if ((tid & 63) == 0) S.shi[tid >> 6] = h;
+    // the latest row key bounds every chunk's output
     if (tid == 0)
         S.rkey = max(rk_seen,
                      (uint32_t)__hip_atomic_load(rowkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     __syncthreads();
     tkey = max(tkey, S.rkey);
-    h = S.shi[0];
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------- k_select
+// Fast pass over one chunk of a top-k / top-p row: one streaming pass, no
+// barrier, admitting against the row's estimated value (see row_estimate).
+// A chunk whose admissions do not fit the buffer hands over nothing and is
+// marked (count -1) for the exact pass; so is, in effect, a row whose fast
+// chunks turn out not to hold its kk largest (k_fix decides).
+
+struct FastShared {
+    uint64_t buf[SLOT];  // admitted entries
+    uint32_t cnt;        // reserved entries
+    uint32_t ffail;      // set when a reservation did not fit
+    uint32_t nstr;       // admitted entries with y > yt
+    float scf[16];
+    double scd[16];
+};
+
+// Admit the elements of one group of 8 (first id j): non-penalised elements
+// with raw x >= traw, penalised ones (and, for rows that accumulate
+// statistics, all of them) with transformed y >= yt, where yt is the
+// transform of traw; every element left out therefore has y <= yt.  One LDS
+// reservation per wave; a reservation that does not fit sets S.ffail and
+// writes nothing.
+template <int DT, bool XF, bool FULL>
+__device__ __forceinline__ void fast_group(FastShared &S, const Raw<DT> &cur, int j, int c0,
+                                           int c1, const uint32_t *bm, const KParams &P,
+                                           bool do_stats, Stats &st, float traw, float yt) {
+    const int lane = threadIdx.x & 63;
+    const int nv = FULL ? 8 : group_nv(j, c1);
+    float x[8];
+    unpack_raw<DT>(cur, x);
+    const uint32_t bits = (FULL || nv > 0) ? pen_bits<XF>(bm, j - c0, P) : 0u;
+    bool pass[8];
+    if (do_stats) {
+        float y[1][8];
+        int nvv[1] = {nv};
 #pragma unroll
-    for (int i = 1; i < SEL_THREADS / 64; ++i) h = fmaxf(h, S.shi[i]);
-    if (valid > (uint32_t)SLOT) {
-        valid = sel_reduce(S, half, valid, kk, SLOT, tkey, h);
-        half ^= 1;
-        __syncthreads();
+        for (int i = 0; i < 8; ++i) y[0][i] = xform<XF>(x[i], (bits >> i) & 1u, P);
+        stats_batch(st, y, nvv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pass[i] = (FULL || i < nv) && y[0][i] >= yt;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pass[i] = (FULL || i < nv) && x[i] >= traw;
+        if (XF && bits) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((bits >> i) & 1u) pass[i] = (FULL || i < nv) && xform<XF>(x[i], 1u, P) >= yt;
+        }
     }
-    // copy out the entries at or above the floor
+    uint64_t bal[8];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        bal[i] = __ballot(pass[i]);
+        tot += (uint32_t)__popcll(bal[i]);
+    }
+    if (tot == 0) return;
+    uint32_t wbase = 0;
+    if (lane == 0) wbase = atomicAdd(&S.cnt, tot);
+    wbase = (uint32_t)__shfl((int)wbase, 0, 64);
+    if (wbase + tot > (uint32_t)SLOT) {
+        if (lane == 0) S.ffail = 1u;
+        return;
+    }
+    uint32_t off = wbase;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (bal[i] == 0) continue;
+        if (pass[i]) {
+            const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
+            S.buf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
+        }
+        off += (uint32_t)__popcll(bal[i]);
+    }
+}
+
+// Batches in flight per thread: 8 groups of bf16 or 4 of fp32 (128 bytes).
+template <int DT>
+struct FastDepth {
+    static constexpr int value = DT == 1 ? 8 : 4;
+};
+
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(SEL_THREADS, 8) void k_select(KParams P, KPlan L, KWork W) {
+    __shared__ FastShared S;
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
+    const Mode md = row_mode(P, b);
+    if (!(md.tk || md.tp)) return;
+    // every one of the L.nch chunks of a row is non-empty
+    const int c0 = c * (int)L.chunk_len;
+    const int c1 = min(c0 + (int)L.chunk_len, P.V);
+    const int slot = b * NCH_MAX + c;
+    const bool do_stats = !md.tk;
+    const void *rowp = row_ptr(P, DT, b);
+    const float traw = W.rowthr[b];
+    const float yt = xform<XF>(traw, 0u, P);
+    if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, c0, c1 - c0, P, b);
+    if (tid == 0) {
+        S.cnt = 0;
+        S.ffail = 0;
+        S.nstr = 0;
+    }
+    __syncthreads();
+
+    Stats st;
+    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
+    constexpr int D = FastDepth<DT>::value;
+    constexpr int BATCH = SEL_THREADS * VEC;
+    const int jt = tid * VEC;
+    Raw<DT> ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int j = c0 + d * BATCH + jt;
+        if (c0 + d * BATCH < c1) load_raw<DT, AL>(rowp, j, group_nv(j, c1), ring[d]);
+    }
+    for (int base = c0; base < c1; base += D * BATCH) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int bb = base + d * BATCH;
+            if (bb < c1) {
+                if (bb + BATCH <= c1)
+                    fast_group<DT, XF, true>(S, ring[d], bb + jt, c0, c1, bm, P, do_stats, st, traw, yt);
+                else
+                    fast_group<DT, XF, false>(S, ring[d], bb + jt, c0, c1, bm, P, do_stats, st, traw, yt);
+                const int nb = bb + D * BATCH;
+                if (nb < c1) load_raw<DT, AL>(rowp, nb + jt, group_nv(nb + jt, c1), ring[d]);
+            }
+        }
+    }
+    __syncthreads();
+    const bool ovf = S.ffail != 0u;
+    const uint32_t n = S.cnt;
+    if (!ovf) {
+        // hand the admitted entries over as they are, counting those above yt
+        uint64_t *dst = W.cand + (int64_t)slot * SLOT;
+        uint32_t strict = 0;
+        for (uint32_t i = tid; i < n; i += SEL_THREADS) {
+            const uint64_t v = S.buf[i];
+            dst[i] = v;
+            strict += cval(v) > yt;
+        }
+#pragma unroll
+        for (int sft = 32; sft >= 1; sft >>= 1) strict += shx(strict, sft);
+        if ((tid & 63) == 0 && strict) atomicAdd(&S.nstr, strict);
+    }
+    ChunkStat cs = empty_stat();
+    if (do_stats) stats_reduce<SEL_THREADS>(st, S.scf, S.scd, cs);
+    __syncthreads();
+    if (tid == 0) {
+        cs.nstr = S.nstr;
+        W.ccnt[slot] = ovf ? -1 : (int32_t)n;
+        W.cstat[slot] = cs;
+    }
+}
+
+// ---------------------------------------------------------------- k_fix
+// Exact selection, one workgroup per top-k / top-p row, for what the fast
+// pass could not settle: chunks that overflowed, and -- when fewer than kk
+// of the entries handed over lie above the row's estimated value yt, so the
+// row's kk-th largest may be an element a fast chunk left out (those all
+// have y <= yt) -- the fast chunks too.  Everything it selects goes to the
+// row's redo slot, which replaces the chunks in rmask.
+
+// Copy the entries of S.buf[half][0..n) whose value key is >= tkey to dst;
+// their number ends in S.kcnt.
+__device__ void copy_out(SelShared &S, int half, uint32_t n, uint32_t tkey, uint64_t *dst) {
+    const int tid = threadIdx.x, lane = tid & 63;
     if (tid == 0) S.kcnt = 0;
     __syncthreads();
-    uint64_t *dst = W.cand + (int64_t)slot * SLOT;
-    const int lane = tid & 63;
-    const uint32_t rounds = (valid + SEL_THREADS - 1) / SEL_THREADS;
+    const uint32_t rounds = (n + SEL_THREADS - 1) / SEL_THREADS;
     for (uint32_t rd = 0; rd < rounds; ++rd) {
         const uint32_t i = rd * SEL_THREADS + tid;
-        const uint64_t v = (i < valid) ? S.buf[half][i] : 0ull;
-        const bool keep = i < valid && (uint32_t)(v >> 32) >= tkey;
+        const uint64_t v = (i < n) ? S.buf[half][i] : 0ull;
+        const bool keep = i < n && (uint32_t)(v >> 32) >= tkey;
         const uint64_t bal = __ballot(keep);
         if (bal == 0) continue;
         uint32_t wbase = 0;
@@ -1285,12 +1560,78 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void k_select(KParams P, KPlan L, K
         wbase = (uint32_t)__shfl((int)wbase, 0, 64);
         if (keep) dst[wbase + lane_rank(bal)] = v;
     }
-    ChunkStat cs = empty_stat();
-    if (do_stats) stats_reduce<SEL_THREADS>(st, S.scf, S.scd, cs);
     __syncthreads();
+}
+
+// Entries of S.buf[half][0..n) with value key >= tkey and value > yt.
+__device__ uint32_t count_above(SelShared &S, int half, uint32_t n, uint32_t tkey, float yt) {
+    if (threadIdx.x == 0) S.kcnt = 0;
+    __syncthreads();
+    uint32_t cnt = 0;
+    for (uint32_t i = threadIdx.x; i < n; i += SEL_THREADS) {
+        const uint64_t v = S.buf[half][i];
+        cnt += (uint32_t)(v >> 32) >= tkey && cval(v) > yt;
+    }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) cnt += shx(cnt, sft);
+    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(&S.kcnt, cnt);
+    __syncthreads();
+    const uint32_t tot = S.kcnt;
+    __syncthreads();
+    return tot;
+}
+
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(SEL_THREADS, 4) void k_fix(KParams P, KPlan L, KWork W) {
+    __shared__ SelShared S;
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk being selected
+    const int tid = threadIdx.x;
+    const int b = xcd_row(blockIdx.x, gridDim.x);
+    const Mode md = row_mode(P, b);
+    if (!(md.tk || md.tp)) return;
+    const int nch = L.nch;
+    const int slot0 = b * NCH_MAX;
+    uint32_t ovf = 0, fastm = 0, strict = 0;
+    for (int c = 0; c < nch; ++c) {
+        if (W.ccnt[slot0 + c] < 0) {
+            ovf |= 1u << c;
+        } else {
+            fastm |= 1u << c;
+            strict += W.cstat[slot0 + c].nstr;
+        }
+    }
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    const float traw = W.rowthr[b];
+    const float yt = xform<XF>(traw, 0u, P);
+    // fast chunks that admitted everything (traw = -inf) are complete
+    const bool check = fastm != 0u && traw > -INFINITY;
+    if (ovf == 0u && !(check && strict < kk)) return;
+
+    const void *rowp = row_ptr(P, DT, b);
+    Stats st;  // unused: the chunk statistics come from the fast pass
+    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
+    uint32_t tkey = 0, valid = 0;
+    int half = 0;
+    float hi = -INFINITY;
+    uint32_t jobs = ovf, done = 0;
+    for (int phase = 0; phase < 2; ++phase) {
+        for (uint32_t m = jobs; m; m &= m - 1) {
+            const int cc = __ffs(m) - 1;
+            const int d0 = cc * (int)L.chunk_len;
+            const int d1 = min(d0 + (int)L.chunk_len, P.V);
+            if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, d0, d1 - d0, P, b);
+            select_exact<DT, AL, XF>(S, P, bm, rowp, d0, d1, kk, false, st, W.rowkey + b, tkey,
+                                     half, valid, hi);
+        }
+        done |= jobs;
+        if (phase > 0 || !check) break;
+        if (strict + count_above(S, half, valid, tkey, yt) >= kk) break;
+        jobs = fastm;
+    }
+    copy_out(S, half, valid, tkey, W.rcand + (int64_t)b * SLOT);
     if (tid == 0) {
-        W.ccnt[slot] = (int32_t)S.kcnt;
-        W.cstat[slot] = cs;
+        W.rcnt[b] = (int32_t)S.kcnt;
+        W.rmask[b] = done;
     }
 }
 
@@ -1403,19 +1744,33 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
         return;
     }
 
-    // ---- candidates: exact top-kk over the row
+    // ---- candidates: exact top-kk over the row.  Sources 0..nch-1 are the
+    // chunks' hand-overs, source NCH_MAX the row's redo slot, which replaces
+    // the chunks in rmask.
     const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    const uint32_t rmask = W.rmask[b];
+    uint32_t scnt[NCH_MAX + 1];
     uint32_t N = 0;
-    for (int c = 0; c < nch; ++c) N += (uint32_t)W.ccnt[slot0 + c];
-    constexpr int R2 = NCH_MAX * SLOT / K2_THREADS;  // 16
+#pragma unroll
+    for (int c = 0; c <= NCH_MAX; ++c) {
+        uint32_t n = 0;
+        if (c == NCH_MAX) n = rmask ? (uint32_t)W.rcnt[b] : 0u;
+        else if (c < nch && !((rmask >> c) & 1u)) n = (uint32_t)max(W.ccnt[slot0 + c], 0);
+        scnt[c] = n;
+        N += n;
+    }
+    constexpr int R2 = (NCH_MAX + 1) * SLOT / K2_THREADS;  // 18
     uint64_t v[R2];
     uint32_t vm = 0;
 #pragma unroll
     for (int r = 0; r < R2; ++r) {
-        const uint32_t s = tid + r * K2_THREADS;
-        const uint32_t c = s / SLOT, i = s % SLOT;
-        const bool ok = c < (uint32_t)nch && i < (uint32_t)W.ccnt[slot0 + min(c, (uint32_t)nch - 1)];
-        v[r] = ok ? W.cand[(int64_t)(slot0 + c) * SLOT + i] : 0ull;
+        constexpr int CPS = SLOT / K2_THREADS;  // rounds per source
+        const int c = r / CPS;
+        const uint32_t i = (uint32_t)((r % CPS) * K2_THREADS + tid);
+        const bool ok = i < scnt[c];
+        const uint64_t *src = (c == NCH_MAX) ? W.rcand + (int64_t)b * SLOT
+                                             : W.cand + (int64_t)(slot0 + c) * SLOT;
+        v[r] = ok ? src[i] : 0ull;
         if (ok) vm |= 1u << r;
     }
     const uint32_t nsel = min(kk, N);
@@ -2009,6 +2364,14 @@ hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int d
     dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(SEL_THREADS);
     size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
     return SMP_PICK(k_select, grid, block, sh);
+}
+
+hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                      hipStream_t s) {
+    const bool xf = any_transform(p);
+    dim3 grid((unsigned)p.B), block(SEL_THREADS);
+    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
+    return SMP_PICK(k_fix, grid, block, sh);
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {

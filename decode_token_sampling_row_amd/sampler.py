@@ -22,8 +22,9 @@ SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_PROFILE = 1, 2, 256
 SAMPLER_TOPK_MAX = 1024
 SAMPLER_VOCAB_MAX = 1 << 21
 
-EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_last_profile",
+EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_profile",
            "sampler_destroy", "sampler_strerror")
+SAMPLER_PROFILE_SLOTS = 6
 
 
 class SamplerError(RuntimeError):
@@ -80,8 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.sampler_check.restype = ctypes.c_int
     lib.sampler_run.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sampler_args), P]
     lib.sampler_run.restype = ctypes.c_int
-    lib.sampler_last_profile.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]
-    lib.sampler_last_profile.restype = ctypes.c_int
+    lib.sampler_profile.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]
+    lib.sampler_profile.restype = ctypes.c_int
     lib.sampler_destroy.argtypes = [P]
     lib.sampler_destroy.restype = ctypes.c_int
     lib.sampler_strerror.argtypes = [ctypes.c_int]
@@ -182,11 +183,12 @@ def sampler_run(h, batch: int, args: sampler_args, stream: Optional[int] = None)
         raise SamplerError(rc, "sampler_run")
 
 
-def sampler_last_profile(h, n: int = 5):
+def sampler_profile(h, n: int = SAMPLER_PROFILE_SLOTS):
+    """Per-kernel milliseconds averaged over the profiled calls since the last read."""
     buf = (ctypes.c_float * n)()
-    rc = load_library().sampler_last_profile(h, buf, int(n))
+    rc = load_library().sampler_profile(h, buf, int(n))
     if rc < 0:
-        raise SamplerError(rc, "sampler_last_profile")
+        raise SamplerError(rc, "sampler_profile")
     return [float(buf[i]) for i in range(rc)]
 
 
@@ -206,8 +208,8 @@ class Sampler:
         args = make_args(logits, out_idx, **kw)
         sampler_run(self.handle, logits.shape[0], args, stream)
 
-    def last_profile(self):
-        return sampler_last_profile(self.handle)
+    def profile(self):
+        return sampler_profile(self.handle)
 
     def close(self):
         if self.handle is not None:

@@ -60,8 +60,8 @@ extern "C" {
 #define SAMPLER_NEED_LOGITS 1u  /* write out_logits                          */
 #define SAMPLER_NEED_PROBS 2u   /* write out_probs (debug; re-reads logits)  */
 #define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
-                                   figures with sampler_last_profile         */
-#define SAMPLER_PROFILE_SLOTS 5
+                                   averages with sampler_profile             */
+#define SAMPLER_PROFILE_SLOTS 6
 
 /* Largest k of the top-k stage and largest top-k guess. */
 #define SAMPLER_TOPK_MAX 1024
@@ -109,7 +109,7 @@ typedef struct sampler_args {
 /*
  * Create a handle for batches of at most max_batch rows of vocab V logits of
  * the given storage type on the current HIP device.  Allocates the device
- * workspace (about 72 KiB per row).  opts may be NULL.
+ * workspace (about 152 KiB per row).  opts may be NULL.
  * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
  * (max_batch < 1, V < 1 or > SAMPLER_VOCAB_MAX, unknown dtype, bad opts),
  * SAMPLER_ENOMEM or SAMPLER_EHIP.
@@ -140,15 +140,20 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a);
 int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream);
 
 /*
- * Kernel times of the last sampler_run made with SAMPLER_PROFILE, in
- * milliseconds, in launch order: [0] streaming pass of unfiltered rows,
- * [1] streaming candidate pass of top-k / top-p rows, [2] row merge /
- * cutoff / sample, [3] full-row top-p cutoff (rows whose guess failed),
- * [4] dense writer.  Waits for that call to finish.  Kernels that were not
- * launched read 0.  Returns the number of entries written (<= n), or a
- * negative error code.
+ * Kernel times, in milliseconds, averaged over the sampler_run calls made
+ * with SAMPLER_PROFILE since the previous sampler_profile call (the last 64
+ * of them if there were more), in launch order: [0] streaming pass of
+ * unfiltered rows (and the admission estimate of the others), [1] fast
+ * select pass of top-k / top-p rows, [2] exact selection of what the fast
+ * pass left open, [3] row merge / cutoff / sample, [4] full-row top-p
+ * cutoff (rows whose guess failed), [5] dense writer.  Each time runs from
+ * an event recorded on the call's stream just before the kernel to one
+ * recorded just after it.  Kernels that were not launched count 0.  Waits
+ * for the last profiled call to finish, then forgets the calls it averaged.
+ * Returns the number of entries written (<= n), or a negative error code
+ * (SAMPLER_EINVAL when no profiled call is pending).
  */
-int sampler_last_profile(sampler_t *h, float *ms, int32_t n);
+int sampler_profile(sampler_t *h, float *ms, int32_t n);
 
 /* Free the workspace and the handle.  NULL is accepted. */
 int sampler_destroy(sampler_t *h);

@@ -79,7 +79,8 @@ def test_constants_match_header():
     for name in ["SAMPLER_OK", "SAMPLER_EINVAL", "SAMPLER_ENOMEM", "SAMPLER_EHIP",
                  "SAMPLER_F32", "SAMPLER_BF16", "SAMPLER_ROW_TOPK", "SAMPLER_ROW_TOPP",
                  "SAMPLER_ROW_SAMPLE", "SAMPLER_ROW_ALL", "SAMPLER_NEED_LOGITS",
-                 "SAMPLER_NEED_PROBS", "SAMPLER_PROFILE", "SAMPLER_TOPK_MAX"]:
+                 "SAMPLER_NEED_PROBS", "SAMPLER_PROFILE", "SAMPLER_PROFILE_SLOTS",
+                 "SAMPLER_TOPK_MAX"]:
         assert getattr(smp, name) == val(name), name
 
 
@@ -100,7 +101,7 @@ def test_null_handle_paths(lib):
     assert lib.sampler_run(None, 1, ctypes.byref(a), None) == smp.SAMPLER_EINVAL
     assert lib.sampler_destroy(None) == smp.SAMPLER_OK
     buf = (ctypes.c_float * 4)()
-    assert lib.sampler_last_profile(None, buf, 4) == smp.SAMPLER_EINVAL
+    assert lib.sampler_profile(None, buf, 4) == smp.SAMPLER_EINVAL
 
 
 def test_strerror(lib):

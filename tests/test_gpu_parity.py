@@ -191,6 +191,49 @@ def test_fallback_with_huge_tie_block():
     _check(W, "tie block")
 
 
+def _sample_runs(V, b):
+    """Positions of the 16 runs of 1024 logits of row b that the select pass
+    estimates its admission value from: run s lies in the s-th sixteenth of
+    the row (bounds rounded down to multiples of 8), at one of 16 staggered
+    offsets."""
+    pos = []
+    for s in range(16):
+        seg0 = (s * V // 16) & ~7
+        seg1 = ((s + 1) * V // 16) & ~7
+        step = ((seg1 - seg0 - 1024) // 16) & ~7
+        a = seg0 + ((s * 5 + b * 3) & 15) * step
+        pos.append(np.arange(a, a + 1024))
+    return np.concatenate(pos)
+
+
+@pytest.mark.parametrize("case", ["high", "low", "chunk0_heavy"])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_unrepresentative_sample(case, dtype):
+    """Rows on which the admission estimate is wrong.  high: the row's
+    largest values all sit in the sampled runs, so too few elements are
+    admitted and the row is redone exactly; low: the sampled runs hold the
+    smallest values, so every chunk overflows its buffer and takes the exact
+    pass; chunk0_heavy: the first chunk is full of large values outside the
+    sample, so that chunk overflows while the others stay on the fast path."""
+    rng = np.random.default_rng(21)
+    B, V = 16, 262144
+    x = rng.standard_normal((B, V)).astype(np.float32)
+    for b in range(B):
+        pos = _sample_runs(V, b)
+        if case == "high":
+            x[b, pos] += 6.0
+        elif case == "low":
+            x[b, pos] -= 6.0
+        else:
+            heavy = np.zeros(V, bool)
+            heavy[: V // 8] = True
+            heavy[pos] = False
+            x[b, heavy] += 6.0
+    k = np.array([1024, 50, 1, 0, 1024, 300, 0, 1000] * 2)
+    W = _custom(x, top_k=k, top_p=0.9, flags=_all_combos(B), dtype=dtype)
+    _check(W, f"sample {case} {dtype}")
+
+
 def test_flat_rows_force_full_row_search():
     rng = np.random.default_rng(11)
     B, V = 8, 128256
@@ -262,14 +305,21 @@ def test_empty_batch_and_argument_checks():
 def test_profile_reports_kernel_times():
     import torch
 
-    from decode_token_sampling_row_amd.sampler import Sampler
+    from decode_token_sampling_row_amd.sampler import SamplerError, Sampler
 
     W = wl.make(5, B=16, V=40000, seed=3)
     d = device_inputs(W)
     s = Sampler(W.B, W.V, torch.bfloat16)
     out_idx = torch.zeros(W.B, dtype=torch.int64, device="cuda")
     out_l = torch.empty((W.B, W.V), device="cuda")
-    s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"],
-          row_flags=d["row_flags"], out_logits=out_l, profile=True)
-    ms = s.last_profile()
-    assert len(ms) == 5 and all(t >= 0 for t in ms) and ms[1] > 0 and ms[4] > 0
+    with pytest.raises(SamplerError):
+        s.profile()  # nothing profiled yet
+    for _ in range(3):
+        s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"],
+              row_flags=d["row_flags"], out_logits=out_l, profile=True)
+    ms = s.profile()
+    assert len(ms) == 6 and all(t >= 0 for t in ms)
+    assert ms[0] > 0 and ms[1] > 0 and ms[3] > 0 and ms[5] > 0
+    with pytest.raises(SamplerError):
+        s.profile()  # the averaged calls are forgotten
+    s.close()
