@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at batch x vocab"
-KERNELS = ["k_stream", "k_select", "k_rows", "k_fallback", "k_dense"]
+KERNELS = ["k_stream", "k_select", "k_fix", "k_rows", "k_fallback", "k_dense"]
 
 
 def parse():
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     return ap.parse_args()
 
 
@@ -72,8 +72,8 @@ def model_bytes(W, kept):
     pen = int(nids.sum()) * 4
     rows = int((kept[sm & filtered]).sum()) * 4 + B * (8 + 9)
     dense = int(filtered.sum()) * 4 * V if W.need_logits else 0
-    return {"k_stream": stream + pen, "k_select": select, "k_rows": rows, "k_fallback": 0,
-            "k_dense": dense}
+    return {"k_stream": stream + pen, "k_select": select, "k_fix": 0, "k_rows": rows,
+            "k_fallback": 0, "k_dense": dense}
 
 
 def main():
@@ -126,13 +126,12 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
-    # per-kernel times: HIP events the library records between its launches
-    per = np.zeros(len(KERNELS))
-    nprof = max(5, min(args.steps, 20))
-    for _ in range(nprof):
+    # per-kernel times: a second timed region of the same K steps, with the
+    # library recording HIP events on the launch stream around each kernel
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
         s.run(logits, out_idx, profile=True, **kw)
-        per += np.array(s.last_profile())
-    per /= nprof
+    per = np.array(s.profile())
 
     # kept-set sizes for the byte model (outside the timed region)
     if out_l is not None:
