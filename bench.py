@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at batch x vocab"
-KERNELS = ["k_stream", "k_select", "k_fix", "k_rows", "k_fallback", "k_dense"]
+KERNELS = ["k_plan", "k_pass", "k_fix", "k_rows", "k_fallback", "k_dense"]
 
 
 def parse():
@@ -46,9 +46,11 @@ def parse():
 
 def model_bytes(W, kept):
     """Algorithmic bytes per call, per kernel, from the per-row model:
-    logits once (V * elem), dense fp32 output (4V) when requested, q read
-    where the method reads it (4 |K| for sampling rows), history ids (4 each),
-    the output id (8) and the per-row k, p, flags (9)."""
+    logits once (V * elem), the dense fp32 output (4V) when requested, q
+    where the method reads it (all V for rows that sample without a filter,
+    4 |K| gathered for filtered sampling rows), history ids (4 each), the
+    output id (8) and the per-row k, p, flags (9).  The pass moves the
+    streamed part; the merge gathers q at K and writes the kept values."""
     B, V = W.B, W.V
     flags = W.row_flags if W.row_flags is not None else np.full(B, 7, np.uint8)
     kmax = min(V, 1024)
@@ -64,16 +66,14 @@ def model_bytes(W, kept):
     if W.ids is not None and W.penalty != 1.0:
         nids = np.diff(W.offsets)
     unf = ~filtered
-    stream = int(unf.sum()) * V * W.elem_bytes            # logits of unfiltered rows
-    stream += int((sm & unf).sum()) * 4 * V                # the race streams q
+    npass = B * V * W.elem_bytes                      # logits of every row
+    npass += int((sm & unf).sum()) * 4 * V            # the race streams q
     if W.need_logits:
-        stream += int(unf.sum()) * 4 * V                   # dense copy of unfiltered rows
-    select = int(filtered.sum()) * V * W.elem_bytes        # logits of filtered rows
-    pen = int(nids.sum()) * 4
+        npass += B * 4 * V                            # dense output (-inf on filtered rows)
+    npass += int(nids.sum()) * 4
     rows = int((kept[sm & filtered]).sum()) * 4 + B * (8 + 9)
-    dense = int(filtered.sum()) * 4 * V if W.need_logits else 0
-    return {"k_stream": stream + pen, "k_select": select, "k_fix": 0, "k_rows": rows,
-            "k_fallback": 0, "k_dense": dense}
+    return {"k_plan": 0, "k_pass": npass, "k_fix": 0, "k_rows": rows, "k_fallback": 0,
+            "k_dense": 0}
 
 
 def main():

@@ -20,7 +20,7 @@ struct sampler_s {
     int32_t vocab;
     int32_t dtype;
     int32_t guess;
-    int32_t chunks;
+    int32_t seg;
     int device;
     KWork ws;
     void *ws_base;
@@ -35,23 +35,18 @@ struct sampler_s {
 namespace {
 
 constexpr int32_t DEFAULT_GUESS = 256;
-constexpr int32_t DEFAULT_CHUNKS = 8;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-KPlan make_plan(const sampler_s *h) {
+KPlan make_plan(int32_t vocab, int32_t seg) {
     KPlan l;
-    const int64_t V = h->vocab;
-    int64_t tiles = (V + TILE - 1) / TILE;
-    int64_t nch = h->chunks;
-    if (nch > tiles) nch = tiles;
-    if (nch < 1) nch = 1;
-    int64_t per = (V + nch - 1) / nch;
-    l.chunk_len = (per + TILE - 1) / TILE * TILE;
-    l.nch = (int32_t)((V + l.chunk_len - 1) / l.chunk_len);
-    l.nt4 = (int32_t)((V + TILE4 - 1) / TILE4);
+    const int64_t V = vocab;
+    l.seg = seg;
+    l.nt = (int32_t)((V + seg - 1) / seg);
+    const int64_t tc = ROWCAP / l.nt;
+    l.wcap = (int32_t)((tc < TCAP_MAX ? tc : TCAP_MAX) / 4);
     return l;
 }
 
@@ -75,13 +70,17 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     *h = nullptr;
     if (max_batch < 1 || vocab < 1 || vocab > SAMPLER_VOCAB_MAX) return SAMPLER_EINVAL;
     if (dtype != SAMPLER_F32 && dtype != SAMPLER_BF16) return SAMPLER_EINVAL;
-    int32_t guess = DEFAULT_GUESS, chunks = DEFAULT_CHUNKS;
+    int32_t guess = DEFAULT_GUESS, seg = SEG_DEFAULT;
     if (opts) {
         if (opts->topk_guess < 0 || opts->topk_guess > SAMPLER_TOPK_MAX) return SAMPLER_EINVAL;
-        if (opts->chunks_per_row < 0 || opts->chunks_per_row > NCH_MAX) return SAMPLER_EINVAL;
+        if (opts->segment_len != 0 &&
+            (opts->segment_len < SEG_MIN || opts->segment_len > SEG_MAX ||
+             opts->segment_len % SEG_MIN != 0))
+            return SAMPLER_EINVAL;
         if (opts->topk_guess) guess = opts->topk_guess;
-        if (opts->chunks_per_row) chunks = opts->chunks_per_row;
+        if (opts->segment_len) seg = opts->segment_len;
     }
+    const KPlan plan = make_plan(vocab, seg);
 
     sampler_s *s = new (std::nothrow) sampler_s();
     if (!s) return SAMPLER_ENOMEM;
@@ -89,19 +88,20 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->vocab = vocab;
     s->dtype = dtype;
     s->guess = guess;
-    s->chunks = chunks;
+    s->seg = seg;
     if (hipGetDevice(&s->device) != hipSuccess) {
         delete s;
         return SAMPLER_EHIP;
     }
     const size_t B = (size_t)max_batch;
     size_t off = 0;
+    const size_t NTL = (size_t)plan.nt * 4;  // wave sub-slots per row
     const size_t o_cand = off;
-    off = align_up(off + B * NCH_MAX * SLOT * sizeof(uint64_t), 256);
-    const size_t o_ccnt = off;
-    off = align_up(off + B * NCH_MAX * sizeof(int32_t), 256);
+    off = align_up(off + B * ROWCAP * sizeof(uint64_t), 256);
+    const size_t o_wcnt = off;
+    off = align_up(off + B * NTL * sizeof(uint32_t), 256);
     const size_t o_cstat = off;
-    off = align_up(off + B * NCH_MAX * sizeof(ChunkStat), 256);
+    off = align_up(off + B * NTL * sizeof(ChunkStat), 256);
     const size_t o_info = off;
     off = align_up(off + B * sizeof(RowInfo), 256);
     const size_t o_klist = off;
@@ -109,6 +109,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     const size_t o_rowkey = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
     const size_t o_rowthr = off;
+    off = align_up(off + B * sizeof(float), 256);
+    const size_t o_rowref = off;
     off = align_up(off + B * sizeof(float), 256);
     const size_t o_rcand = off;
     off = align_up(off + B * SLOT * sizeof(uint64_t), 256);
@@ -126,12 +128,13 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     char *c = (char *)base;
     s->ws_base = base;
     s->ws.cand = (uint64_t *)(c + o_cand);
-    s->ws.ccnt = (int32_t *)(c + o_ccnt);
+    s->ws.wcnt = (uint32_t *)(c + o_wcnt);
     s->ws.cstat = (ChunkStat *)(c + o_cstat);
     s->ws.info = (RowInfo *)(c + o_info);
     s->ws.klist = (uint64_t *)(c + o_klist);
     s->ws.rowkey = (uint32_t *)(c + o_rowkey);
     s->ws.rowthr = (float *)(c + o_rowthr);
+    s->ws.rowref = (float *)(c + o_rowref);
     s->ws.rcand = (uint64_t *)(c + o_rcand);
     s->ws.rcnt = (int32_t *)(c + o_rcnt);
     s->ws.rmask = (uint32_t *)(c + o_rmask);
@@ -189,7 +192,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.guess = h->guess;
     p.pen = (a->repetition_penalty != 1.0f && a->penalty_ids != nullptr) ? 1 : 0;
 
-    const KPlan l = make_plan(h);
+    const KPlan l = make_plan(h->vocab, h->seg);
     const int esize = h->dtype == SAMPLER_BF16 ? 2 : 4;
     const bool al = aligned16(a->logits) && ((a->ld * esize) % 16) == 0 &&
                     (h->vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
@@ -215,15 +218,15 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
 
     hipError_t e;
     mark(0);
-    e = launch_stream(p, l, h->ws, h->dtype, al, st);
-    if (e != hipSuccess) return SAMPLER_EHIP;
-    launched[0] = true;
-    mark(1);
     if (filtering) {
-        e = launch_select(p, l, h->ws, h->dtype, al, st);
+        e = launch_plan(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
-        launched[1] = true;
+        launched[0] = true;
     }
+    mark(1);
+    e = launch_pass(p, l, h->ws, h->dtype, al, st);
+    if (e != hipSuccess) return SAMPLER_EHIP;
+    launched[1] = true;
     mark(2);
     if (filtering) {
         e = launch_fix(p, l, h->ws, h->dtype, al, st);
@@ -241,7 +244,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         launched[4] = true;
     }
     mark(5);
-    if (p.out_logits || p.out_probs) {
+    if (p.out_probs || (p.out_logits && filtering)) {
         e = launch_dense(p, l, h->ws, h->dtype, al, st);
         if (e != hipSuccess) return SAMPLER_EHIP;
         launched[5] = true;

@@ -6,29 +6,29 @@
 
 namespace smp {
 
-// Streaming-pass geometry (chunk kernels): 256 threads x 8 elements per tile.
-constexpr int K1_THREADS = 256;
-constexpr int VEC = 8;
-constexpr int TILE = K1_THREADS * VEC;  // 2048 elements
-constexpr int NCH_MAX = 8;              // chunks per row
-constexpr int KMAX = 1024;              // largest k / guess
-constexpr int SLOT = 2048;              // candidates a chunk may hand over
-constexpr int SEL_CAP = 2048;           // entries per half of the LDS candidate buffer
-constexpr int SEL_SOFT = 1536;          // exact pass: cut a half back above this fill
-constexpr int SEL_LIMIT = 1536;         // exact pass: most entries a cut-back keeps
-// Row admission estimate: EST_SEGS evenly spaced runs of EST_SEG logits.
+// Streaming pass: one workgroup per tile of `seg` elements of a row.
+constexpr int SEG_DEFAULT = 8192;  // the segment length v of the pages' rolling top-k
+constexpr int SEG_MIN = 1024;
+constexpr int SEG_MAX = 32768;
+constexpr int ROWCAP = 8192;       // candidate entries per row, over all its tiles
+constexpr int TCAP_MAX = 2048;     // candidate entries per tile (its four waves)
+constexpr int WCAP_MAX = TCAP_MAX / 4;  // candidate entries per wave
+constexpr int KMAX = 1024;         // largest k / guess
+constexpr int SLOT = 2048;         // entries of a row's exact re-selection
+constexpr int SEL_CAP = 2048;      // entries per half of the exact pass's LDS buffer
+constexpr int SEL_SOFT = 1536;     // exact pass: cut a half back above this fill
+constexpr int SEL_LIMIT = 1536;    // exact pass: most entries a cut-back keeps
+constexpr int VEC = 8;             // elements per group in the exact pass
+// Row admission estimate: EST_SEGS runs of EST_SEG logits.
 constexpr int EST_SEGS = 16;
 constexpr int EST_SEG = 1024;
 constexpr int EST_N = EST_SEGS * EST_SEG;
+constexpr int K1_THREADS = 256;    // estimate workgroup
 // Row kernels.
-constexpr int K2_THREADS = 1024;
 constexpr int K3_THREADS = 1024;
-constexpr int K3_BINS = 2048;           // value-space histogram bins
-constexpr int K3_COLLECT = 4096;        // bucket members sorted in LDS
-constexpr int K3_SEG = 65536;           // penalty-bitmap segment
-// Dense writer: 256 threads x 128 elements.
-constexpr int K4_THREADS = 256;
-constexpr int TILE4 = 32768;
+constexpr int K3_BINS = 2048;      // value-space histogram bins
+constexpr int K3_COLLECT = 4096;   // bucket members sorted in LDS
+constexpr int K3_SEG = 65536;      // penalty-bitmap segment
 
 // Row kinds written by the merge kernel.
 enum RowKind : int32_t {
@@ -45,7 +45,7 @@ struct ChunkStat {
     float rx;      // race winner: logit
     float rqe;     // race winner: q + eps
     uint32_t ridx; // race winner: vocab id (0xffffffff = none)
-    uint32_t nstr; // select pass: handed-over entries above the row estimate
+    uint32_t nstr; // select tiles: handed-over entries above the row estimate
 };
 
 struct RowInfo {
@@ -82,29 +82,30 @@ struct KParams {
 };
 
 struct KPlan {
-    int32_t nch;        // chunks per row
-    int64_t chunk_len;  // elements per chunk (multiple of TILE)
-    int32_t nt4;        // dense-writer tiles per row
+    int32_t seg;   // elements per pass tile (a multiple of 1024)
+    int32_t nt;    // tiles per row
+    int32_t wcap;  // candidate entries per wave sub-slot (4 nt wcap <= ROWCAP)
 };
 
 struct KWork {
-    uint64_t *cand;   // [maxB][NCH_MAX][SLOT]
-    int32_t *ccnt;    // [maxB][NCH_MAX] (-1: the chunk overflowed the fast pass)
-    ChunkStat *cstat; // [maxB][NCH_MAX]
+    uint64_t *cand;   // [maxB][ROWCAP]; sub-slot s (tile t, wave w: 4t + w) at s * wcap
+    uint32_t *wcnt;   // [maxB][nt][4] entries | strict count << 16 (all ones: overflow)
+    ChunkStat *cstat; // [maxB][nt][4] per-wave statistics / winners
     RowInfo *info;    // [maxB]
-    uint64_t *klist;  // [maxB][KMAX]
-    uint32_t *rowkey; // [maxB] exact admission key shared by a row's chunks
+    uint64_t *klist;  // [maxB][KMAX] kept list of rows with a list
+    uint32_t *rowkey; // [maxB] exact admission key of the row's re-selection
     float *rowthr;    // [maxB] estimated admission value of the row
-    uint64_t *rcand;  // [maxB][SLOT] candidates of a row's redone chunks
+    float *rowref;    // [maxB] transformed sample maximum (reference for exponentials)
+    uint64_t *rcand;  // [maxB][SLOT] exact re-selection of a row
     int32_t *rcnt;    // [maxB] entries in rcand
-    uint32_t *rmask;  // [maxB] chunks replaced by rcand (0 = none)
+    uint32_t *rmask;  // [maxB] nonzero: the row's candidates are rcand
 };
 
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
-hipError_t launch_stream(const KParams &p, const KPlan &l, const KWork &w, int dtype,
-                         bool aligned, hipStream_t s);
-hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int dtype,
-                         bool aligned, hipStream_t s);
+hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
+                       hipStream_t s);
+hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
+                       hipStream_t s);
 hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
                       hipStream_t s);
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);

@@ -45,7 +45,6 @@ namespace smp {
 namespace {
 
 constexpr uint32_t NONE = 0xffffffffu;
-constexpr uint32_t NEED_LOGITS = 1u;
 constexpr uint32_t NEED_PROBS = 2u;
 // top-p decisions taken from a guess must clear the cutoff by this much
 // (relative to the row's total mass); the row's total is accumulated from
@@ -54,6 +53,7 @@ constexpr uint32_t NEED_PROBS = 2u;
 constexpr double GUESS_MARGIN = 1e-5;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- keys
@@ -81,27 +81,16 @@ struct Mode {
 };
 
 __device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
+    // the three loads are independent of one another (one round trip)
+    const uint32_t rf = P.row_flags ? (uint32_t)P.row_flags[b] : 7u;
+    const int k = P.top_k ? P.top_k[b] : 0;
+    const float p = P.top_p ? P.top_p[b] : 1.0f;
+    const int kmax = P.V < KMAX ? P.V : KMAX;
     Mode md;
-    uint32_t rf = P.row_flags ? (uint32_t)P.row_flags[b] : 7u;
-    int kmax = P.V < KMAX ? P.V : KMAX;
-    md.k = 0;
-    md.p = 1.0f;
-    md.tk = false;
-    if ((rf & 1u) && P.top_k) {
-        int k = P.top_k[b];
-        if (k >= 1 && k <= kmax) {
-            md.tk = true;
-            md.k = k;
-        }
-    }
-    md.tp = false;
-    if ((rf & 2u) && P.top_p) {
-        float p = P.top_p[b];
-        if (p < 1.0f) {  // NaN compares false: stage off
-            md.tp = true;
-            md.p = p;
-        }
-    }
+    md.tk = (rf & 1u) && P.top_k && k >= 1 && k <= kmax;
+    md.k = md.tk ? k : 0;
+    md.tp = (rf & 2u) && P.top_p && p < 1.0f;  // NaN compares false: stage off
+    md.p = md.tp ? p : 1.0f;
     md.sm = (rf & 4u) && P.q;
     return md;
 }
@@ -541,9 +530,8 @@ __device__ __forceinline__ const void *row_ptr(const KParams &P, int dt, int b) 
 
 // ================================================================== chunk passes
 
-constexpr int U = 4;           // k_stream: tiles per batch (256 threads)
-constexpr int SEL_THREADS = 512;
-constexpr int SEL_DEPTH = 4;   // k_select: batches in flight
+constexpr int SEL_THREADS = 512;  // exact selection workgroup
+constexpr int SEL_DEPTH = 4;      // exact selection: batches in flight
 
 __device__ __forceinline__ int group_nv(int j, int end) {
     const int rem = end - j;
@@ -658,13 +646,13 @@ struct Stats {
     float m, xmin;
     double z;
 };
-template <int UU>
-__device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][8], const int (&nv)[UU]) {
+template <int UU, int N = 8>
+__device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][N], const int (&nv)[UU]) {
     float tm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UU; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < N; ++i)
             if (i < nv[u]) {
                 tm = fmaxf(tm, x[u][i]);
                 if (x[u][i] > -INFINITY) st.xmin = fminf(st.xmin, x[u][i]);
@@ -678,7 +666,7 @@ __device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][8], 
         for (int u = 0; u < UU; ++u) {
             float zs = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < N; ++i)
                 if (i < nv[u]) zs += __expf(x[u][i] - st.m);
             st.z += (double)zs;
         }
@@ -725,13 +713,11 @@ __device__ __forceinline__ ChunkStat empty_stat() {
     return cs;
 }
 
-// ---------------------------------------------------------------- k_stream
-// Rows with neither top-k nor top-p: K is the whole row.  Writes the dense
-// output (x itself), runs the exponential race over the whole chunk (q is
-// streamed in the same pass) or the greedy argmax, and (for the optional
-// probabilities) the chunk's max / sum-exp.  No barrier in the loop.
-// For rows with top-k or top-p the first workgroup of the row estimates the
-// admission value the select pass filters with.
+// ---------------------------------------------------------------- k_plan
+// Per row, before the streaming pass: the admission estimate of rows with
+// top-k or top-p (the value the pass filters their tiles with), and the
+// transformed sample maximum, the reference the pass sums exponentials
+// against.
 
 struct StreamShared {
     uint64_t sc64[16];
@@ -753,6 +739,7 @@ struct StreamShared {
 // ulp), and in steps of 2^24 when the 255 top bins hold fewer than r; only
 // the top 255 bins are counted, so the bins stay sparse and the LDS atomics
 // rarely collide.  -inf (admit everything) when r would exceed the sample.
+// smax receives the sample maximum (raw).
 // Only the speed of the select pass depends on t: that pass checks that what
 // it admitted holds the row's kk largest and redoes the row exactly when it
 // does not.
@@ -770,7 +757,8 @@ __device__ __forceinline__ int est_run_start(int s, int b, int V) {
 }
 
 template <int DT, bool AL>
-__device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t kk, StreamShared &S) {
+__device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t kk, StreamShared &S,
+                                              float &smax) {
     constexpr int NT = K1_THREADS;
     constexpr int PER = EST_N / (NT * VEC);  // groups of 8 per thread
     constexpr int GPS = EST_SEG / VEC;       // groups per run
@@ -779,8 +767,7 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t 
     const int n = whole ? V : EST_N;
     const double r0 = (double)kk * (double)n / (double)V;
     const double rr = ceil(r0 + 4.0 * sqrt(r0) + 8.0);
-    if (rr >= (double)n) return -INFINITY;
-    const uint32_t r = (uint32_t)rr;
+    const uint32_t r = rr < (double)n ? (uint32_t)rr : 0u;  // 0: admit everything
     const void *rowp = row_ptr(P, DT, b);
     // the whole sample in registers, every load in flight at once
     Raw<DT> raw[PER];
@@ -815,6 +802,8 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t 
     mx = S.sci[0];
 #pragma unroll
     for (int i = 1; i < NT / 64; ++i) mx = max(mx, S.sci[i]);
+    smax = key2f(mx);
+    if (r == 0) return -INFINITY;
     for (int shift = 16; shift <= 24; shift += 8) {
         for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
         __syncthreads();
@@ -854,130 +843,39 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t 
     return -INFINITY;
 }
 
-struct StreamState {
-    Stats st;
-    Race rc;
-    uint64_t am;
-};
-
-template <int DT, bool AL, bool XF, bool FULL>
-__device__ __forceinline__ void stream_batch(const Raw<DT> (&cur)[U], int base, int c0, int c1,
-                                             const uint32_t *bm, const KParams &P, float *rowo,
-                                             const float *rowq, bool do_stats, bool do_race,
-                                             StreamState &ss) {
-    float x[U][8];
-    int jb[U], nv[U];
-    finish_batch<DT, K1_THREADS, U, XF, FULL>(cur, base, c0, c1, bm, P, x, jb, nv);
-    if (rowo) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (FULL || nv[u] > 0) store8<AL>(rowo, jb[u], nv[u], x[u]);
-    }
-    if (do_stats) stats_batch(ss.st, x, nv);
-    if (do_race) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float qv[8];
-            load8<0, AL>(rowq, jb[u], nv[u], qv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (FULL || i < nv[u]) race_offer(ss.rc, x[u][i], qv[i] + P.eps, (uint32_t)(jb[u] + i));
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (FULL || i < nv[u]) {
-                    const uint64_t cv = mkcomp(x[u][i], (uint32_t)(jb[u] + i));
-                    ss.am = cv > ss.am ? cv : ss.am;
-                }
-    }
-}
-
+// One workgroup per row, before the pass: clears the row's exact-pass key
+// and redo mask, and for rows with top-k or top-p writes the admission
+// estimate.
 template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(K1_THREADS) void k_stream(KParams P, KPlan L, KWork W) {
+__global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W) {
     __shared__ StreamShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
-    if (c == 0 && tid == 0) {
-        W.rowkey[b] = 0u;  // the row's exact admission key
-        W.rmask[b] = 0u;   // no chunk redone
+    const int b = blockIdx.x;
+    if (threadIdx.x == 0) {
+        W.rowkey[b] = 0u;
+        W.rmask[b] = 0u;
     }
     const Mode md = row_mode(P, b);
-    if (md.tk || md.tp) {
-        // one workgroup per row estimates; which one rotates with the row so
-        // the estimates spread over the XCDs (workgroup i runs on XCD i % 8)
-        if (c == b % L.nch) {
-            const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-            const float t = row_estimate<DT, AL>(P, b, kk, S);
-            if (tid == 0) W.rowthr[b] = t;
-        }
-        return;
+    if (!(md.tk || md.tp)) return;
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    float smax;
+    const float t = row_estimate<DT, AL>(P, b, kk, S, smax);
+    if (threadIdx.x == 0) {
+        W.rowthr[b] = t;
+        W.rowref[b] = xform<XF>(smax, 0u, P);
     }
-    const int c0 = c * (int)L.chunk_len;
-    const int c1 = min(c0 + (int)L.chunk_len, P.V);
-    const int slot = b * NCH_MAX + c;
-    if (c0 >= c1) {
-        if (tid == 0) {
-            W.ccnt[slot] = 0;
-            W.cstat[slot] = empty_stat();
-        }
-        return;
-    }
-    if (XF && P.pen) build_bitmap<K1_THREADS>(bm, c0, c1 - c0, P, b);
-    const bool do_race = md.sm;
-    const bool do_stats = (P.flags & NEED_PROBS) != 0;
-    const void *rowp = row_ptr(P, DT, b);
-    const float *rowq = P.q ? P.q + (int64_t)b * P.V : nullptr;
-    float *rowo = P.out_logits ? P.out_logits + (int64_t)b * P.V : nullptr;
-
-    StreamState ss;
-    ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
-    ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE;
-    ss.am = 0;
-    constexpr int BATCH = K1_THREADS * VEC * U;
-    Raw<DT> cur[U], nxt[U];
-    issue_batch<DT, AL, K1_THREADS, U>(rowp, c0, c1, cur);
-    for (int base = c0; base < c1; base += BATCH) {
-        if (base + BATCH < c1) issue_batch<DT, AL, K1_THREADS, U>(rowp, base + BATCH, c1, nxt);
-        if (base + BATCH <= c1)
-            stream_batch<DT, AL, XF, true>(cur, base, c0, c1, bm, P, rowo, rowq, do_stats, do_race, ss);
-        else
-            stream_batch<DT, AL, XF, false>(cur, base, c0, c1, bm, P, rowo, rowq, do_stats, do_race, ss);
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
-    ChunkStat cs = empty_stat();
-    if (do_stats) stats_reduce<K1_THREADS>(ss.st, S.scx, S.scd, cs);
-    if (do_race) {
-        Race r = wg_race<K1_THREADS>(ss.rc, S.scx, S.scq, S.sci);
-        cs.rx = r.x;
-        cs.rqe = r.qe;
-        cs.ridx = r.idx;
-    } else {
-        const uint64_t am = wg_max_u64<K1_THREADS>(ss.am, S.sc64);
-        if (tid == 0) {
-            W.cand[(int64_t)slot * SLOT] = am;
-            W.ccnt[slot] = 1;
-        }
-    }
-    if (tid == 0) W.cstat[slot] = cs;
 }
 
-// ---------------------------------------------------------------- k_select
-// Rows with top-k and/or top-p.  Keeps a superset of the chunk's kk largest
-// (kk = k, or the top-k guess G for top-p rows without top-k) in an LDS
-// buffer: an element enters when its value key is >= the admission key; when
-// the buffer fills it is cut back to a superset of its kk largest -- with a
-// 256-bin value histogram (the kept part is every entry at or above the bin
-// where the count from the top reaches kk), or an exact radix select when
-// one bin holds too many equal or near-equal values -- and the admission key
-// becomes the smallest kept value.  This is the rolling, prefiltered top-k of
-// the Ascend npu_top_k_top_p_sample page (topK section) with the exact cut
-// deferred to the row merge.  Top-p rows without top-k also accumulate the
-// chunk's max / sum-exp for the softmax over the whole row.
+// ---------------------------------------------------------------- exact selection
+// Used by k_fix for what the fast pass leaves open.  Keeps a superset of a
+// chunk's kk largest (kk = k, or the top-k guess G for top-p rows without
+// top-k) in an LDS buffer: an element enters when its value key is >= the
+// admission key; when the buffer fills it is cut back to a superset of its kk
+// largest -- with a 256-bin value histogram (the kept part is every entry at
+// or above the bin where the count from the top reaches kk), or an exact
+// radix select when one bin holds too many equal or near-equal values -- and
+// the admission key becomes the smallest kept value.  This is the rolling,
+// prefiltered top-k of the Ascend npu_top_k_top_p_sample page (topK section)
+// with the exact cut deferred to the row merge.
 
 struct SelShared {
     uint64_t buf[2][SEL_CAP];  // candidate buffer, two halves used in turn
@@ -1377,170 +1275,426 @@ __device__ void select_exact(SelShared &S, const KParams &P, const uint32_t *bm,
     __syncthreads();
 }
 
-// ---------------------------------------------------------------- k_select
-// Fast pass over one chunk of a top-k / top-p row: one streaming pass, no
-// barrier, admitting against the row's estimated value (see row_estimate).
-// A chunk whose admissions do not fit the buffer hands over nothing and is
-// marked (count -1) for the exact pass; so is, in effect, a row whose fast
-// chunks turn out not to hold its kk largest (k_fix decides).
+// ---------------------------------------------------------------- k_pass
+// The one streaming pass over the logits: one workgroup per tile of
+// L.seg elements (the segment length v of the Ascend page's rolling top-k by
+// default), every tile of every row in one grid, so the hardware dispatcher
+// spreads rows of every kind over all CUs.  Each thread keeps its whole share
+// of the tile in flight: groups of 4 consecutive elements, one 16-byte store
+// per group, consecutive lanes on consecutive groups.
+//  * rows without top-k / top-p: the dense output gets the transformed
+//    logits; the exponential race over the tile runs with q read in the same
+//    pass, or the greedy argmax; optional statistics for the probabilities;
+//  * rows with top-k or top-p: admission against the row's estimate (see
+//    row_estimate), each wave appending to its own sub-slot, and statistics
+//    for rows without top-k; their dense output is written once the kept
+//    set is known (k_dense), in whole lines.  A wave whose admissions exceed
+//    its sub-slot (L.wcap) marks it overflowed; k_fix then redoes the row.
 
-struct FastShared {
-    uint64_t buf[SLOT];  // admitted entries
-    uint32_t cnt;        // reserved entries
-    uint32_t ffail;      // set when a reservation did not fit
-    uint32_t nstr;       // admitted entries with y > yt
-    float scf[16];
-    double scd[16];
+constexpr int PASS_THREADS = 256;
+constexpr int PASS_WAVES = PASS_THREADS / 64;
+constexpr int PASS_D = 8;                      // groups of 4 in flight per thread
+constexpr int PGROUP = PASS_THREADS * 4;       // elements per group row
+
+template <int DT>
+struct Raw4;
+template <>
+struct Raw4<1> {
+    u32x2 v;  // 4 bf16
+};
+template <>
+struct Raw4<0> {
+    f32x4 v;  // 4 fp32
 };
 
-// Admit the elements of one group of 8 (first id j): non-penalised elements
-// with raw x >= traw, penalised ones (and, for rows that accumulate
-// statistics, all of them) with transformed y >= yt, where yt is the
-// transform of traw; every element left out therefore has y <= yt.  One LDS
-// reservation per wave; a reservation that does not fit sets S.ffail and
-// writes nothing.
-template <int DT, bool XF, bool FULL>
-__device__ __forceinline__ void fast_group(FastShared &S, const Raw<DT> &cur, int j, int c0,
-                                           int c1, const uint32_t *bm, const KParams &P,
-                                           bool do_stats, Stats &st, float traw, float yt) {
-    const int lane = threadIdx.x & 63;
-    const int nv = FULL ? 8 : group_nv(j, c1);
-    float x[8];
-    unpack_raw<DT>(cur, x);
-    const uint32_t bits = (FULL || nv > 0) ? pen_bits<XF>(bm, j - c0, P) : 0u;
-    bool pass[8];
-    if (do_stats) {
-        float y[1][8];
-        int nvv[1] = {nv};
+__device__ __forceinline__ int nv4(int j, int end) {
+    const int rem = end - j;
+    return rem <= 0 ? 0 : (rem >= 4 ? 4 : rem);
+}
+
+template <int DT, bool AL>
+__device__ __forceinline__ void load4(const void *p, int j, int nv, Raw4<DT> &r) {
+    if (DT == 1) {
+        u32x2 &v = reinterpret_cast<Raw4<1> &>(r).v;
+        if (AL && nv == 4) {
+            v = __builtin_nontemporal_load((const u32x2 *)((const uint16_t *)p + j));
+        } else {
+            const uint16_t *h = (const uint16_t *)p + j;
+            uint32_t w[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[0][i] = xform<XF>(x[i], (bits >> i) & 1u, P);
-        stats_batch(st, y, nvv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pass[i] = (FULL || i < nv) && y[0][i] >= yt;
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t lo = (2 * i < nv) ? h[2 * i] : 0u;
+                const uint32_t hi = (2 * i + 1 < nv) ? h[2 * i + 1] : 0u;
+                w[i] = lo | (hi << 16);
+            }
+            v.x = w[0];
+            v.y = w[1];
+        }
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pass[i] = (FULL || i < nv) && x[i] >= traw;
-        if (XF && bits) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if ((bits >> i) & 1u) pass[i] = (FULL || i < nv) && xform<XF>(x[i], 1u, P) >= yt;
+        f32x4 &v = reinterpret_cast<Raw4<0> &>(r).v;
+        if (AL && nv == 4) {
+            v = __builtin_nontemporal_load((const f32x4 *)((const float *)p + j));
+        } else {
+            const float *q = (const float *)p + j;
+            v.x = nv > 0 ? q[0] : 0.0f;
+            v.y = nv > 1 ? q[1] : 0.0f;
+            v.z = nv > 2 ? q[2] : 0.0f;
+            v.w = nv > 3 ? q[3] : 0.0f;
         }
-    }
-    uint64_t bal[8];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        bal[i] = __ballot(pass[i]);
-        tot += (uint32_t)__popcll(bal[i]);
-    }
-    if (tot == 0) return;
-    uint32_t wbase = 0;
-    if (lane == 0) wbase = atomicAdd(&S.cnt, tot);
-    wbase = (uint32_t)__shfl((int)wbase, 0, 64);
-    if (wbase + tot > (uint32_t)SLOT) {
-        if (lane == 0) S.ffail = 1u;
-        return;
-    }
-    uint32_t off = wbase;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (bal[i] == 0) continue;
-        if (pass[i]) {
-            const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
-            S.buf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
-        }
-        off += (uint32_t)__popcll(bal[i]);
     }
 }
 
-// Batches in flight per thread: 8 groups of bf16 or 4 of fp32 (128 bytes).
 template <int DT>
-struct FastDepth {
-    static constexpr int value = DT == 1 ? 8 : 4;
+__device__ __forceinline__ void unpack4(const Raw4<DT> &r, float (&x)[4]) {
+    if (DT == 1) {
+        const u32x2 &u = reinterpret_cast<const Raw4<1> &>(r).v;
+        x[0] = __uint_as_float(u.x << 16);
+        x[1] = __uint_as_float(u.x & 0xffff0000u);
+        x[2] = __uint_as_float(u.y << 16);
+        x[3] = __uint_as_float(u.y & 0xffff0000u);
+    } else {
+        const f32x4 &v = reinterpret_cast<const Raw4<0> &>(r).v;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+}
+
+template <bool AL>
+__device__ __forceinline__ void store4(float *p, int j, int nv, const float (&x)[4]) {
+    if (AL && nv == 4) {
+        *(f32x4 *)(p + j) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < nv) p[j + i] = x[i];
+    }
+}
+
+// Penalty bits of the 4 elements starting at tile-relative offset r (a
+// multiple of 4).
+template <bool XF>
+__device__ __forceinline__ uint32_t pen_bits4(const uint32_t *bm, int r, const KParams &P) {
+    if (!XF || !P.pen) return 0u;
+    return (bm[r >> 5] >> (r & 31)) & 0xfu;
+}
+
+// ---- wave-level reductions (every lane gets the result)
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = shx64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shxf(v, m));
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shxd(v, m);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shx(v, m);
+    return v;
+}
+__device__ __forceinline__ Race wave_race(Race r) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        Race o;
+        o.x = shxf(r.x, m);
+        o.qe = shxf(r.qe, m);
+        o.idx = shx(r.idx, m);
+        if (race_ahead(o, r)) r = o;
+    }
+    return r;
+}
+
+struct StreamState {
+    Stats st;
+    Race rc;
+    uint64_t am;
 };
 
-template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(SEL_THREADS, 8) void k_select(KParams P, KPlan L, KWork W) {
-    __shared__ FastShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x / L.nch, c = blockIdx.x % L.nch;
-    const Mode md = row_mode(P, b);
-    if (!(md.tk || md.tp)) return;
-    // every one of the L.nch chunks of a row is non-empty
-    const int c0 = c * (int)L.chunk_len;
-    const int c1 = min(c0 + (int)L.chunk_len, P.V);
-    const int slot = b * NCH_MAX + c;
-    const bool do_stats = !md.tk;
-    const void *rowp = row_ptr(P, DT, b);
-    const float traw = W.rowthr[b];
-    const float yt = xform<XF>(traw, 0u, P);
-    if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, c0, c1 - c0, P, b);
-    if (tid == 0) {
-        S.cnt = 0;
-        S.ffail = 0;
-        S.nstr = 0;
-    }
-    __syncthreads();
+// Sum of exp(y - ref) for a select tile of a row without top-k: fp32 terms
+// (the hardware exp2 of an exactly computed difference) against the row's
+// reference (the transformed sample maximum), summed in fp32 over a lane's
+// share and in double over the wave.  A wave that meets a value more than 64
+// above the reference sums its share again against its own maximum.
+struct RefSum {
+    float z;     // sum of exp(y - ref)
+    float ymax;  // largest y seen
+};
 
-    Stats st;
-    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
-    constexpr int D = FastDepth<DT>::value;
-    constexpr int BATCH = SEL_THREADS * VEC;
-    const int jt = tid * VEC;
-    Raw<DT> ring[D];
+// What a wave of a select tile has handed over so far.
+struct WaveSel {
+    uint32_t cnt;     // entries written (uniform over the wave)
+    uint32_t strict;  // this lane's entries with y > yt
+    bool ovf;         // an append did not fit
+};
+
+// One group of 4 (first id j, nv valid) of a tile.
+//   KIND 0: greedy row, 1: racing row, 2: select row.
+template <int DT, bool AL, bool XF, int KIND>
+__device__ __forceinline__ void pass_group(const Raw4<DT> &raw, const Raw4<0> &qraw, int j, int nv,
+                                           int c0, const uint32_t *bm, const KParams &P,
+                                           float *rowo, bool do_stats, StreamState &ss,
+                                           RefSum &rs, WaveSel &ws, uint64_t *wbuf, uint32_t wcap,
+                                           float ref, float traw, float yt) {
+    float x[4];
+    unpack4<DT>(raw, x);
+    const uint32_t bits = nv > 0 ? pen_bits4<XF>(bm, j - c0, P) : 0u;
+    if (KIND == 2) {
+        bool pass[4];
+        if (do_stats) {
+            float y[4];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        const int j = c0 + d * BATCH + jt;
-        if (c0 + d * BATCH < c1) load_raw<DT, AL>(rowp, j, group_nv(j, c1), ring[d]);
+            for (int i = 0; i < 4; ++i) y[i] = xform<XF>(x[i], (bits >> i) & 1u, P);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nv) {
+                    rs.ymax = fmaxf(rs.ymax, y[i]);
+                    rs.z += __builtin_amdgcn_exp2f((y[i] - ref) * 1.4426950408889634f);
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pass[i] = i < nv && y[i] >= yt;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pass[i] = i < nv && x[i] >= traw;
+            if (XF && bits) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((bits >> i) & 1u) pass[i] = i < nv && xform<XF>(x[i], 1u, P) >= yt;
+            }
+        }
+        uint64_t bal[4];
+        uint32_t tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bal[i] = __ballot(pass[i]);
+            tot += (uint32_t)__popcll(bal[i]);
+        }
+        if (tot == 0) return;
+        if (ws.ovf || ws.cnt + tot > wcap) {
+            ws.ovf = true;
+            return;
+        }
+        uint32_t off = ws.cnt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (bal[i] == 0) continue;
+            if (pass[i]) {
+                const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
+                wbuf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
+                ws.strict += y > yt;
+            }
+            off += (uint32_t)__popcll(bal[i]);
+        }
+        ws.cnt = off;
+    } else {
+        float y[1][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[0][i] = xform<XF>(x[i], (bits >> i) & 1u, P);
+        if (rowo && nv > 0) store4<AL>(rowo, j, nv, y[0]);
+        if (do_stats) {
+            int nvv[1] = {nv};
+            stats_batch<1, 4>(ss.st, y, nvv);
+        }
+        if (KIND == 1) {
+            float qv[4];
+            unpack4<0>(qraw, qv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nv) race_offer(ss.rc, y[0][i], qv[i] + P.eps, (uint32_t)(j + i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nv) {
+                    const uint64_t cv = mkcomp(y[0][i], (uint32_t)(j + i));
+                    ss.am = cv > ss.am ? cv : ss.am;
+                }
+        }
     }
-    for (int base = c0; base < c1; base += D * BATCH) {
+}
+
+// Sum of exp(y - m) over this lane's groups of the tile [c0, c1), read
+// again (rare path: a value far above the row's reference).
+template <int DT, bool AL, bool XF>
+__device__ double lane_sum_again(const KParams &P, const uint32_t *bm, int b, int c0, int c1,
+                                 float m) {
+    const void *rowp = row_ptr(P, DT, b);
+    double z = 0.0;
+    for (int j = c0 + (int)threadIdx.x * 4; j < c1; j += PGROUP) {
+        const int nv = nv4(j, c1);
+        Raw4<DT> raw;
+        load4<DT, AL>(rowp, j, nv, raw);
+        float x[4];
+        unpack4<DT>(raw, x);
+        const uint32_t bits = pen_bits4<XF>(bm, j - c0, P);
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int bb = base + d * BATCH;
-            if (bb < c1) {
-                if (bb + BATCH <= c1)
-                    fast_group<DT, XF, true>(S, ring[d], bb + jt, c0, c1, bm, P, do_stats, st, traw, yt);
-                else
-                    fast_group<DT, XF, false>(S, ring[d], bb + jt, c0, c1, bm, P, do_stats, st, traw, yt);
-                const int nb = bb + D * BATCH;
-                if (nb < c1) load_raw<DT, AL>(rowp, nb + jt, group_nv(nb + jt, c1), ring[d]);
+        for (int i = 0; i < 4; ++i)
+            if (i < nv) z += (double)__expf(xform<XF>(x[i], (bits >> i) & 1u, P) - m);
+    }
+    return z;
+}
+
+// One tile, each wave on its own: no barrier (the penalty bitmap aside).
+// Wave w of tile t of row b collects its candidates in its own LDS buffer
+// (appends to global memory in the middle of the load stream would make the
+// wave wait for its stores), hands them over in sub-slot t * PASS_WAVES + w
+// of the row at the end, and writes its statistics / winner to the same
+// entry of the row's wave records.
+template <int DT, bool AL, bool XF, int KIND>
+__device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, const KPlan &L,
+                                          const KWork &W, const Mode &md, int b, int t,
+                                          float traw, float ref, Raw4<DT> (&ring)[PASS_D],
+                                          uint64_t (&wbufs)[PASS_WAVES][WCAP_MAX]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c0 = t * L.seg;
+    const int c1 = min(c0 + L.seg, P.V);
+    const int ng = (c1 - c0 + PGROUP - 1) / PGROUP;  // group rows in the tile
+    const void *rowp = row_ptr(P, DT, b);
+    const float *rowq = KIND == 1 ? P.q + (int64_t)b * P.V : nullptr;
+    float *rowo = (KIND != 2 && P.out_logits) ? P.out_logits + (int64_t)b * P.V : nullptr;
+    const bool do_stats = KIND == 2 ? !md.tk : (P.flags & NEED_PROBS) != 0;
+    const int j0 = c0 + tid * 4;
+    const int wslot = (b * L.nt + t) * PASS_WAVES + (tid >> 6);
+    const uint32_t wcap = (uint32_t)L.wcap;
+    uint64_t *wbuf = wbufs[tid >> 6];
+    const float yt = KIND == 2 ? xform<XF>(traw, 0u, P) : 0.0f;
+    StreamState ss;
+    ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
+    ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE;
+    ss.am = 0;
+    RefSum rs;
+    rs.z = 0.0f;
+    rs.ymax = -INFINITY;
+    WaveSel ws;
+    ws.cnt = 0;
+    ws.strict = 0;
+    ws.ovf = false;
+    // q runs QD groups ahead (fewer registers than the logits ring)
+    constexpr int QD = KIND == 1 ? PASS_D / 2 : 1;
+    Raw4<0> qring[QD];
+    if (KIND == 1) {
+#pragma unroll
+        for (int d = 0; d < QD; ++d)
+            if (d < ng) {
+                const int j = j0 + d * PGROUP;
+                const int nv = nv4(j, c1);
+                if (nv > 0) load4<0, AL>(rowq, j, nv, qring[d]);
+            }
+    }
+    for (int g0 = 0; g0 < ng; g0 += PASS_D) {
+#pragma unroll
+        for (int d = 0; d < PASS_D; ++d) {
+            const int g = g0 + d;
+            if (g < ng) {
+                const int j = j0 + g * PGROUP;
+                const int nv = nv4(j, c1);
+                pass_group<DT, AL, XF, KIND>(ring[d], qring[d % QD], j, nv, c0, bm, P, rowo,
+                                             do_stats, ss, rs, ws, wbuf, wcap, ref, traw, yt);
+                const int gn = g + PASS_D;
+                if (gn < ng) {
+                    const int jn = j0 + gn * PGROUP;
+                    const int nvn = nv4(jn, c1);
+                    if (nvn > 0) load4<DT, AL>(rowp, jn, nvn, ring[d]);
+                }
+                if (KIND == 1 && g + QD < ng) {
+                    const int jq = j0 + (g + QD) * PGROUP;
+                    const int nvq = nv4(jq, c1);
+                    if (nvq > 0) load4<0, AL>(rowq, jq, nvq, qring[d % QD]);
+                }
             }
         }
     }
-    __syncthreads();
-    const bool ovf = S.ffail != 0u;
-    const uint32_t n = S.cnt;
-    if (!ovf) {
-        // hand the admitted entries over as they are, counting those above yt
-        uint64_t *dst = W.cand + (int64_t)slot * SLOT;
-        uint32_t strict = 0;
-        for (uint32_t i = tid; i < n; i += SEL_THREADS) {
-            const uint64_t v = S.buf[i];
-            dst[i] = v;
-            strict += cval(v) > yt;
-        }
-#pragma unroll
-        for (int sft = 32; sft >= 1; sft >>= 1) strict += shx(strict, sft);
-        if ((tid & 63) == 0 && strict) atomicAdd(&S.nstr, strict);
-    }
     ChunkStat cs = empty_stat();
-    if (do_stats) stats_reduce<SEL_THREADS>(st, S.scf, S.scd, cs);
-    __syncthreads();
-    if (tid == 0) {
-        cs.nstr = S.nstr;
-        W.ccnt[slot] = ovf ? -1 : (int32_t)n;
-        W.cstat[slot] = cs;
+    if (KIND == 2) {
+        if (do_stats) {
+            const float ym = wave_max_f32(rs.ymax);
+            if (ym > ref + 64.0f) {
+                cs.m = ym;
+                cs.z = wave_sum_f64(lane_sum_again<DT, AL, XF>(P, bm, b, c0, c1, ym));
+            } else {
+                cs.m = ref;
+                cs.z = wave_sum_f64((double)rs.z);
+            }
+        }
+        if (!ws.ovf) {
+            uint64_t *dst =
+                W.cand + (int64_t)b * ROWCAP + (int64_t)(t * PASS_WAVES + (tid >> 6)) * wcap;
+            for (uint32_t i = lane; i < ws.cnt; i += 64) dst[i] = wbuf[i];
+        }
+        const uint32_t strict = wave_sum_u32(ws.strict);
+        if (lane == 0) {
+            W.wcnt[wslot] = ws.ovf ? 0xffffffffu : (ws.cnt | (strict << 16));
+            W.cstat[wslot] = cs;
+        }
+    } else {
+        if (do_stats) {
+            const float M = wave_max_f32(ss.st.m);
+            const double z = (ss.st.z != 0.0) ? ss.st.z * exp((double)ss.st.m - (double)M) : 0.0;
+            cs.m = M;
+            cs.z = wave_sum_f64(z);
+        }
+        if (KIND == 1) {
+            const Race r = wave_race(ss.rc);
+            cs.rx = r.x;
+            cs.rqe = r.qe;
+            cs.ridx = r.idx;
+        } else {
+            // the greedy winner, as (value, id): the largest value, lowest id
+            const uint64_t am = wave_max_u64(ss.am);
+            cs.rx = am ? cval(am) : -INFINITY;
+            cs.rqe = 1.0f;
+            cs.ridx = am ? cidx(am) : NONE;
+        }
+        if (lane == 0) W.cstat[wslot] = cs;
     }
 }
 
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
+    __shared__ uint64_t wbufs[PASS_WAVES][WCAP_MAX];  // each wave's candidates
+    extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
+    const int b = blockIdx.x / L.nt, t = blockIdx.x % L.nt;
+    const int c0 = t * L.seg;
+    const int c1 = min(c0 + L.seg, P.V);
+    const int ng = (c1 - c0 + PGROUP - 1) / PGROUP;
+    // the tile's logits are requested before anything about the row
+    const void *rowp = row_ptr(P, DT, b);
+    const int j0 = c0 + (int)threadIdx.x * 4;
+    Raw4<DT> ring[PASS_D];
+#pragma unroll
+    for (int d = 0; d < PASS_D; ++d)
+        if (d < ng) {
+            const int j = j0 + d * PGROUP;
+            const int nv = nv4(j, c1);
+            if (nv > 0) load4<DT, AL>(rowp, j, nv, ring[d]);
+        }
+    const Mode md = row_mode(P, b);
+    const bool filtering = P.top_k || P.top_p;  // the planning kernel ran
+    const float traw = filtering ? W.rowthr[b] : 0.0f;
+    const float ref = filtering ? W.rowref[b] : 0.0f;
+    if (XF && P.pen) build_bitmap<PASS_THREADS>(bm, c0, c1 - c0, P, b);
+    if (md.tk || md.tp)
+        pass_tile<DT, AL, XF, 2>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+    else if (md.sm)
+        pass_tile<DT, AL, XF, 1>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+    else
+        pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+}
+
 // ---------------------------------------------------------------- k_fix
-// Exact selection, one workgroup per top-k / top-p row, for what the fast
-// pass could not settle: chunks that overflowed, and -- when fewer than kk
-// of the entries handed over lie above the row's estimated value yt, so the
-// row's kk-th largest may be an element a fast chunk left out (those all
-// have y <= yt) -- the fast chunks too.  Everything it selects goes to the
-// row's redo slot, which replaces the chunks in rmask.
+// Exact selection, one workgroup per top-k / top-p row, for what the pass
+// could not settle: a row with a wave that overflowed its sub-slot, or a row
+// where fewer than kk of the handed-over entries lie above the estimate's
+// transform yt (so its kk-th largest may be an element left out; those all
+// have y <= yt).  The whole row is selected again, segment by segment, into
+// the row's redo slot, which then replaces its tiles.
 
 // Copy the entries of S.buf[half][0..n) whose value key is >= tkey to dst;
 // their number ends in S.kcnt.
@@ -1563,90 +1717,89 @@ __device__ void copy_out(SelShared &S, int half, uint32_t n, uint32_t tkey, uint
     __syncthreads();
 }
 
-// Entries of S.buf[half][0..n) with value key >= tkey and value > yt.
-__device__ uint32_t count_above(SelShared &S, int half, uint32_t n, uint32_t tkey, float yt) {
-    if (threadIdx.x == 0) S.kcnt = 0;
-    __syncthreads();
-    uint32_t cnt = 0;
-    for (uint32_t i = threadIdx.x; i < n; i += SEL_THREADS) {
-        const uint64_t v = S.buf[half][i];
-        cnt += (uint32_t)(v >> 32) >= tkey && cval(v) > yt;
-    }
-#pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) cnt += shx(cnt, sft);
-    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(&S.kcnt, cnt);
-    __syncthreads();
-    const uint32_t tot = S.kcnt;
-    __syncthreads();
-    return tot;
-}
-
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(SEL_THREADS, 4) void k_fix(KParams P, KPlan L, KWork W) {
     __shared__ SelShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of the chunk being selected
+    extern __shared__ uint32_t bm[];  // penalty bitmap of one segment
     const int tid = threadIdx.x;
     const int b = xcd_row(blockIdx.x, gridDim.x);
     const Mode md = row_mode(P, b);
     if (!(md.tk || md.tp)) return;
-    const int nch = L.nch;
-    const int slot0 = b * NCH_MAX;
-    uint32_t ovf = 0, fastm = 0, strict = 0;
-    for (int c = 0; c < nch; ++c) {
-        if (W.ccnt[slot0 + c] < 0) {
-            ovf |= 1u << c;
-        } else {
-            fastm |= 1u << c;
-            strict += W.cstat[slot0 + c].nstr;
-        }
+    const int ns = L.nt * PASS_WAVES;  // wave sub-slots of the row
+    // sub-slots read in parallel: overflow flag and strict count
+    uint32_t o = 0, st_cnt = 0;
+    for (int i = tid; i < ns; i += SEL_THREADS) {
+        const uint32_t v = W.wcnt[b * ns + i];
+        if (v == 0xffffffffu) o = 1;
+        else st_cnt += v >> 16;
     }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+        o |= shx(o, sft);
+        st_cnt += shx(st_cnt, sft);
+    }
+    if ((tid & 63) == 0) {
+        S.sc[tid >> 6] = o;
+        S.sc[8 + (tid >> 6)] = st_cnt;
+    }
+    __syncthreads();
+    bool ovf = false;
+    uint32_t strict = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_THREADS / 64; ++i) {
+        ovf |= S.sc[i] != 0u;
+        strict += S.sc[8 + i];
+    }
+    __syncthreads();
     const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
     const float traw = W.rowthr[b];
-    const float yt = xform<XF>(traw, 0u, P);
-    // fast chunks that admitted everything (traw = -inf) are complete
-    const bool check = fastm != 0u && traw > -INFINITY;
-    if (ovf == 0u && !(check && strict < kk)) return;
+    // with traw = -inf every element was admitted, so no check is needed
+    if (!ovf && !(traw > -INFINITY && strict < kk)) return;
 
     const void *rowp = row_ptr(P, DT, b);
-    Stats st;  // unused: the chunk statistics come from the fast pass
+    Stats st;  // unused: the tile statistics come from the pass
     st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
     uint32_t tkey = 0, valid = 0;
     int half = 0;
     float hi = -INFINITY;
-    uint32_t jobs = ovf, done = 0;
-    for (int phase = 0; phase < 2; ++phase) {
-        for (uint32_t m = jobs; m; m &= m - 1) {
-            const int cc = __ffs(m) - 1;
-            const int d0 = cc * (int)L.chunk_len;
-            const int d1 = min(d0 + (int)L.chunk_len, P.V);
-            if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, d0, d1 - d0, P, b);
-            select_exact<DT, AL, XF>(S, P, bm, rowp, d0, d1, kk, false, st, W.rowkey + b, tkey,
-                                     half, valid, hi);
-        }
-        done |= jobs;
-        if (phase > 0 || !check) break;
-        if (strict + count_above(S, half, valid, tkey, yt) >= kk) break;
-        jobs = fastm;
+    for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, P.V);
+        if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, s0, s1 - s0, P, b);
+        select_exact<DT, AL, XF>(S, P, bm, rowp, s0, s1, kk, false, st, W.rowkey + b, tkey, half,
+                                 valid, hi);
     }
     copy_out(S, half, valid, tkey, W.rcand + (int64_t)b * SLOT);
     if (tid == 0) {
         W.rcnt[b] = (int32_t)S.kcnt;
-        W.rmask[b] = done;
+        W.rmask[b] = 1u;
     }
 }
 
 // ================================================================== k_rows
+// Per row, one workgroup of ROWS_THREADS: the exact kk largest of the row's
+// candidates (held in registers, radix select), ordered only as far as top-p
+// needs; fp64 softmax and prefix masses; the top-p cutoff (the top-k guess of
+// the Ascend page's topP section is accepted only with a safe margin); the
+// exponential race over K with q gathered by id, or the greedy pick; the
+// kept list for the dense writer.  Rows without top-k / top-p merge their
+// tiles' race or argmax winners.
+
+constexpr int ROWS_THREADS = 256;
+
+constexpr int RCAP = 4096;       // candidates held in registers by the merge
+constexpr int NUC_STEPS = 16;    // top-p prefixes found without a sort, at most
 
 struct RowsShared {
-    uint64_t srt[KMAX];
-    double ev[KMAX];
-    double cs[KMAX];
+    uint64_t srt[KMAX];       // the kk selected
+    uint64_t nuc[NUC_STEPS];  // a short top-p prefix, in order
     uint32_t hist[256];
     uint32_t sel[4];
     uint32_t sc[16];
     uint64_t sc64[16];
     double scd[16];
     uint32_t sci[16];
+    uint32_t cnt;
+    double fd[2];
 };
 
 template <int NT>
@@ -1679,26 +1832,95 @@ __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double
     return bi;
 }
 
-__global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W) {
+// Radix select over n distinct composites read by get(i), i < n (1 <= kk <
+// n): (prefix, pmask) such that exactly kk of them satisfy (v & pmask) >=
+// prefix.  Common high bits are skipped, then digits of up to 8 bits.
+template <int NT, class G>
+__device__ void radix_select_any(uint32_t n, uint32_t kk, G &&get, uint32_t *hist, uint32_t *sel,
+                                 uint64_t *sc64, uint64_t &prefix_out, uint64_t &pmask_out) {
+    uint64_t mn = ~0ull, mx = 0ull;
+    for (uint32_t i = threadIdx.x; i < n; i += NT) {
+        const uint64_t v = get(i);
+        mn = v < mn ? v : mn;
+        mx = v > mx ? v : mx;
+    }
+    mn = wg_min_u64<NT>(mn, sc64);
+    mx = wg_max_u64<NT>(mx, sc64);
+    const uint64_t diff = mn ^ mx;
+    if (diff == 0) {
+        prefix_out = mx;
+        pmask_out = ~0ull;
+        return;
+    }
+    int hib = 63 - __clzll(diff);
+    uint64_t pmask = (hib == 63) ? 0ull : (~0ull << (hib + 1));
+    uint64_t prefix = mx & pmask;
+    uint32_t need = kk;
+    for (;;) {
+        const int width = hib + 1 < 8 ? hib + 1 : 8;
+        const int shift = hib + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n; i += NT) {
+            const uint64_t v = get(i);
+            if ((v & pmask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        wave0_find_bin(hist, need, sel);
+        __syncthreads();
+        const uint32_t d = sel[0], above = sel[1], cntd = sel[2];
+        __syncthreads();
+        need -= above;
+        prefix |= (uint64_t)d << shift;
+        pmask |= (uint64_t)dmask << shift;
+        if (cntd == need || shift == 0) break;
+        hib = shift - 1;
+    }
+    prefix_out = prefix;
+    pmask_out = pmask;
+}
+
+__global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork W) {
     __shared__ RowsShared S;
+    extern __shared__ uint32_t toff[];  // per-tile candidate offsets, L.nt + 1
+    constexpr int NT = ROWS_THREADS;
     const int tid = threadIdx.x;
     const int b = xcd_row(blockIdx.x, gridDim.x);
     const Mode md = row_mode(P, b);
     const bool filtered = md.tk || md.tp;
-    const int nch = L.nch;
-    const int slot0 = b * NCH_MAX;
+    const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
+    const ChunkStat *cst = W.cstat + (int64_t)b * nt;
 
-    // merged chunk statistics (identical in every thread)
+    // merged tile statistics, the tiles read in parallel
+    float m_loc = -INFINITY, mn_loc = INFINITY;
+    for (int t = tid; t < nt; t += NT) {
+        m_loc = fmaxf(m_loc, cst[t].m);
+        mn_loc = fminf(mn_loc, cst[t].xmin);
+    }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+        m_loc = fmaxf(m_loc, shxf(m_loc, sft));
+        mn_loc = fminf(mn_loc, shxf(mn_loc, sft));
+    }
+    if ((tid & 63) == 0) {
+        S.scd[tid >> 6] = m_loc;
+        S.scd[8 + (tid >> 6)] = mn_loc;
+    }
+    __syncthreads();
     float M = -INFINITY, XMIN = INFINITY;
-    for (int c = 0; c < nch; ++c) {
-        M = fmaxf(M, W.cstat[slot0 + c].m);
-        XMIN = fminf(XMIN, W.cstat[slot0 + c].xmin);
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        M = fmaxf(M, (float)S.scd[i]);
+        XMIN = fminf(XMIN, (float)S.scd[8 + i]);
     }
-    double Z = 0.0;
-    for (int c = 0; c < nch; ++c) {
-        ChunkStat cs = W.cstat[slot0 + c];
-        if (cs.z != 0.0) Z += cs.z * exp((double)cs.m - (double)M);
+    __syncthreads();
+    double z_loc = 0.0;
+    for (int t = tid; t < nt; t += NT) {
+        const ChunkStat cs = cst[t];
+        if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
     }
+    const double Z = wg_sum_f64<NT>(z_loc, S.scd);
 
     RowInfo info;
     info.kind = KIND_UNFILTERED;
@@ -1711,30 +1933,42 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
     info.pad = 0;
 
     if (!filtered) {
+        // merge the tiles' winners: the race by ratio (lowest id on a tie),
+        // the argmax by (value, lowest id)
         uint32_t idx;
-        if (!md.sm) {
-            uint64_t am = 0;
-            for (int c = 0; c < nch; ++c)
-                if (W.ccnt[slot0 + c] > 0) {
-                    uint64_t v = W.cand[(int64_t)(slot0 + c) * SLOT];
-                    am = v > am ? v : am;
-                }
-            idx = cidx(am);
-        } else {
+        if (md.sm) {
+            float xr_loc = -INFINITY;
+            for (int t = tid; t < nt; t += NT)
+                if (cst[t].ridx != NONE) xr_loc = fmaxf(xr_loc, cst[t].rx);
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) xr_loc = fmaxf(xr_loc, shxf(xr_loc, sft));
+            if ((tid & 63) == 0) S.scd[tid >> 6] = xr_loc;
+            __syncthreads();
             float xr = -INFINITY;
-            for (int c = 0; c < nch; ++c)
-                if (W.cstat[slot0 + c].ridx != NONE) xr = fmaxf(xr, W.cstat[slot0 + c].rx);
+#pragma unroll
+            for (int i = 0; i < NT / 64; ++i) xr = fmaxf(xr, (float)S.scd[i]);
+            __syncthreads();
             double br = -1.0;
-            idx = NONE;
-            for (int c = 0; c < nch; ++c) {
-                ChunkStat cs = W.cstat[slot0 + c];
+            uint32_t bi = NONE;
+            for (int t = tid; t < nt; t += NT) {
+                const ChunkStat cs = cst[t];
                 if (cs.ridx == NONE) continue;
-                double r = exp((double)cs.rx - (double)xr) / (double)cs.rqe;
-                if (r > br || (r == br && cs.ridx < idx)) {
+                const double r = exp((double)cs.rx - (double)xr) / (double)cs.rqe;
+                if (r > br || (r == br && cs.ridx < bi)) {
                     br = r;
-                    idx = cs.ridx;
+                    bi = cs.ridx;
                 }
             }
+            idx = wg_best_ratio<NT>(br, bi, S.scd, S.sci);
+        } else {
+            uint64_t am = 0;
+            for (int t = tid; t < nt; t += NT)
+                if (cst[t].ridx != NONE) {
+                    const uint64_t v = mkcomp(cst[t].rx, cst[t].ridx);
+                    am = v > am ? v : am;
+                }
+            am = wg_max_u64<NT>(am, S.sc64);
+            idx = am ? cidx(am) : NONE;
         }
         info.idx0 = idx;
         if (tid == 0) {
@@ -1744,120 +1978,249 @@ __global__ __launch_bounds__(K2_THREADS) void k_rows(KParams P, KPlan L, KWork W
         return;
     }
 
-    // ---- candidates: exact top-kk over the row.  Sources 0..nch-1 are the
-    // chunks' hand-overs, source NCH_MAX the row's redo slot, which replaces
-    // the chunks in rmask.
+    // ---- candidates of the row: the waves' sub-slots, or the redo slot
     const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-    const uint32_t rmask = W.rmask[b];
-    uint32_t scnt[NCH_MAX + 1];
-    uint32_t N = 0;
-#pragma unroll
-    for (int c = 0; c <= NCH_MAX; ++c) {
-        uint32_t n = 0;
-        if (c == NCH_MAX) n = rmask ? (uint32_t)W.rcnt[b] : 0u;
-        else if (c < nch && !((rmask >> c) & 1u)) n = (uint32_t)max(W.ccnt[slot0 + c], 0);
-        scnt[c] = n;
-        N += n;
+    const bool redone = W.rmask[b] != 0u;
+    const uint64_t *rowc = W.cand + (int64_t)b * ROWCAP;
+    const uint64_t *redc = W.rcand + (int64_t)b * SLOT;
+    uint32_t N;
+    if (redone) {
+        N = (uint32_t)W.rcnt[b];
+    } else {
+        // exclusive prefix of the sub-slot counts (none overflowed here)
+        const int per = (nt + NT - 1) / NT;
+        uint32_t loc = 0;
+        for (int i = 0; i < per; ++i) {
+            const int t = tid * per + i;
+            if (t < nt) loc += W.wcnt[b * nt + t] & 0xffffu;
+        }
+        uint32_t run = wg_excl_scan_u32<NT>(loc, S.sc, N);
+        for (int i = 0; i < per; ++i) {
+            const int t = tid * per + i;
+            if (t < nt) {
+                toff[t] = run;
+                run += W.wcnt[b * nt + t] & 0xffffu;
+            }
+        }
+        if (tid == 0) toff[nt] = N;
+        __syncthreads();
     }
-    constexpr int R2 = (NCH_MAX + 1) * SLOT / K2_THREADS;  // 18
-    uint64_t v[R2];
-    uint32_t vm = 0;
-#pragma unroll
-    for (int r = 0; r < R2; ++r) {
-        constexpr int CPS = SLOT / K2_THREADS;  // rounds per source
-        const int c = r / CPS;
-        const uint32_t i = (uint32_t)((r % CPS) * K2_THREADS + tid);
-        const bool ok = i < scnt[c];
-        const uint64_t *src = (c == NCH_MAX) ? W.rcand + (int64_t)b * SLOT
-                                             : W.cand + (int64_t)(slot0 + c) * SLOT;
-        v[r] = ok ? src[i] : 0ull;
-        if (ok) vm |= 1u << r;
-    }
-    const uint32_t nsel = min(kk, N);
-    uint32_t km = vm;
-    if (N > kk) {
-        uint64_t prefix, pmask;
-        wg_radix_select<K2_THREADS, R2>(v, vm, kk, S.hist, S.sel, S.sc64, prefix, pmask);
-        km = 0;
-#pragma unroll
-        for (int r = 0; r < R2; ++r)
-            if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
-    }
-    {
-        uint32_t tot;
-        uint32_t off = wg_excl_scan_u32<K2_THREADS>(__popc(km), S.sc, tot);
-#pragma unroll
-        for (int r = 0; r < R2; ++r)
-            if ((km >> r) & 1u) S.srt[off++] = v[r];
-    }
-    const int npad = pow2_ceil((int)nsel);
-    for (int i = nsel + tid; i < npad; i += K2_THREADS) S.srt[i] = 0ull;
-    __syncthreads();
-    bitonic_desc_reg<K2_THREADS>(S.srt, npad);
+    const uint32_t tcap = (uint32_t)L.wcap;
+    // entry e of the row's candidates, wherever it lives
+    auto gget = [&](uint32_t e) -> uint64_t {
+        if (redone) return redc[e];
+        int lo = 0, hi = nt;  // toff[lo] <= e < toff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (toff[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        return rowc[(int64_t)lo * tcap + (e - toff[lo])];
+    };
 
-    // ---- softmax over the sorted candidates, in double
-    const float x0 = cval(S.srt[0]);
-    double e = 0.0;
-    if ((uint32_t)tid < nsel) e = exp((double)cval(S.srt[tid]) - (double)x0);
-    double tot_e;
-    double incl = wg_excl_scan_f64<K2_THREADS>(e, S.scd, tot_e) + e;
-    if ((uint32_t)tid < nsel) {
-        S.ev[tid] = e;
-        S.cs[tid] = incl;
+    // ---- the kk largest (exactly, under the composite order) into srt.  Up
+    // to RCAP candidates are held in registers, RCAP / NT per thread; more
+    // (rare) are selected by passes over the slots themselves.
+    const uint32_t nsel = min(kk, N);
+    if (N <= (uint32_t)RCAP) {
+        constexpr int R = RCAP / NT;
+        uint64_t v[R];
+        uint32_t vm = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t e = (uint32_t)(r * NT + tid);
+            v[r] = e < N ? gget(e) : 0ull;
+            if (e < N) vm |= 1u << r;
+        }
+        uint32_t km = vm;
+        if (N > kk) {
+            uint64_t prefix, pmask;
+            wg_radix_select<NT, R>(v, vm, kk, S.hist, S.sel, S.sc64, prefix, pmask);
+            km = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
+        }
+        uint32_t tot;
+        uint32_t off = wg_excl_scan_u32<NT>(__popc(km), S.sc, tot);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if ((km >> r) & 1u) S.srt[off++] = v[r];
+    } else {
+        uint64_t prefix, pmask;
+        radix_select_any<NT>(N, kk, gget, S.hist, S.sel, S.sc64, prefix, pmask);
+        if (tid == 0) S.cnt = 0;
+        __syncthreads();
+        for (uint32_t e = tid; e < N; e += NT) {
+            const uint64_t v = gget(e);
+            if ((v & pmask) >= prefix) S.srt[atomicAdd(&S.cnt, 1u)] = v;
+        }
     }
     __syncthreads();
+
+    // ---- the maximum and the softmax total, in double.  Thread tid owns
+    // positions 4 tid .. 4 tid + 3 of srt.
+    uint64_t v4[4];
+    uint64_t mxv = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = 4 * tid + i;
+        v4[i] = p < nsel ? S.srt[p] : 0ull;
+        mxv = v4[i] > mxv ? v4[i] : mxv;
+    }
+    const uint64_t top = wg_max_u64<NT>(mxv, S.sc64);
+    const float x0 = cval(top);
+    double loc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * tid + i < nsel) loc += exp((double)cval(v4[i]) - (double)x0);
+    const double tot_e = wg_sum_f64<NT>(loc, S.scd);
     double Zc;
-    if (md.tk) Zc = S.cs[nsel - 1];
+    if (md.tk) Zc = tot_e;
     else Zc = (Z != 0.0) ? Z * exp((double)M - (double)x0) : tot_e;
 
+    // ---- top-p.  The kept set is the shortest prefix, in the order, whose
+    // mass reaches p Zc.  Short prefixes (the usual case) are found by taking
+    // the maxima one at a time; longer ones by sorting every candidate.
     uint32_t nK = nsel;
     bool settled = true;
+    bool use_nuc = false;  // K is S.nuc[0..nK), else S.srt[0..nK)
     if (md.tp) {
         const double pZ = (double)md.p * Zc;
-        uint32_t first = NONE;
-        if ((uint32_t)tid < nsel && S.cs[tid] >= pZ) first = (uint32_t)tid;
-        first = wg_min_u32<K2_THREADS>(first, S.sc);
-        if (md.tk) {
-            nK = (first == NONE) ? nsel : first + 1;
-        } else {
-            // top-k guess (Ascend page, topP section): settled only when the
-            // cutoff lies inside the guess with a safe margin on both sides.
-            if (first == NONE) {
-                settled = false;
-            } else {
-                double hi = S.cs[first] - pZ;
-                double lo = (first == 0) ? INFINITY : pZ - S.cs[first - 1];
-                settled = hi > GUESS_MARGIN * Zc && lo > GUESS_MARGIN * Zc;
-                if (md.p <= 0.0f) settled = true;
-                nK = first + 1;
+        double at = 0.0, below = 0.0;
+        bool found = false;
+        {
+            uint32_t rem = 0;  // positions of this thread already taken
+            double cum = 0.0;
+            for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
+                uint64_t mx = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
+                mx = wg_max_u64<NT>(mx, S.sc64);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
+                const double em = exp((double)cval(mx) - (double)x0);
+                below = cum;
+                cum += em;
+                if (tid == 0) S.nuc[it] = mx;
+                if (cum >= pZ) {
+                    found = true;
+                    at = cum;
+                    nK = it + 1;
+                    break;
+                }
             }
+        }
+        if (found) {
+            use_nuc = true;
+        } else {
+            // the whole order: sort, then prefix masses by position
+            const int npad = pow2_ceil((int)nsel);
+            for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
+            __syncthreads();
+            bitonic_desc<NT>(S.srt, npad);
+            double e[4];
+            double l2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                l2 += e[i];
+            }
+            double t2;
+            const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
+            uint32_t first = NONE;
+            double run = before, a_ = 0.0, b_ = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                run += e[i];
+                if (p < nsel && first == NONE && run >= pZ) {
+                    first = p;
+                    a_ = run;
+                    b_ = run - e[i];
+                }
+            }
+            const uint32_t mine = first;
+            first = wg_min_u32<NT>(first, S.sc);
+            if (first != NONE && mine == first) {
+                S.fd[0] = a_;
+                S.fd[1] = b_;
+            }
+            __syncthreads();
+            if (first != NONE) {
+                found = true;
+                nK = first + 1;
+                at = S.fd[0];
+                below = S.fd[1];
+            }
+            __syncthreads();
+        }
+        if (md.tk) {
+            if (!found) nK = nsel;  // rounding: the whole top-k set
+        } else if (!found) {
+            // top-k guess (Ascend page, topP section): the guess does not
+            // reach p; the full-row search decides
+            settled = false;
+        } else {
+            // settled only when the cutoff lies inside the guess with a safe
+            // margin on both sides
+            const double hi_m = at - pZ;
+            const double lo_m = (nK == 1) ? INFINITY : pZ - below;
+            settled = (hi_m > GUESS_MARGIN * Zc && lo_m > GUESS_MARGIN * Zc) || md.p <= 0.0f;
         }
     }
     info.m = x0;
-    info.idx0 = cidx(S.srt[0]);
+    info.idx0 = cidx(top);
     if (!settled) {
         info.kind = KIND_FALLBACK;
         if (tid == 0) W.info[b] = info;
         return;
     }
+    __syncthreads();
 
-    // ---- exponential race over K (or greedy)
-    uint32_t idx = cidx(S.srt[0]);
+    // ---- exponential race over K (or greedy), and the kept list
+    const uint64_t *kp = use_nuc ? S.nuc : S.srt;
+    uint32_t idx = cidx(top);
+    double zk = 0.0;
+    double rbest = -1.0;
+    uint32_t ibest = NONE;
+    uint64_t *kl = W.klist + (int64_t)b * KMAX;
+    constexpr int KR = KMAX / NT;
+    float qv[KR];
     if (md.sm) {
-        double r = -1.0;
-        uint32_t id = NONE;
-        if ((uint32_t)tid < nK) {
-            id = cidx(S.srt[tid]);
-            double den = (double)P.q[(int64_t)b * P.V + id] + (double)P.eps;
-            double ei = S.ev[tid];
-            r = (ei == 0.0) ? 0.0 : ei / den;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const uint32_t p = (uint32_t)(r * NT + tid);
+            qv[r] = p < nK ? P.q[(int64_t)b * P.V + cidx(kp[p])] : 1.0f;
         }
-        idx = wg_best_ratio<K2_THREADS>(r, id, S.scd, S.sci);
     }
-    for (uint32_t i = tid; i < nK; i += K2_THREADS) W.klist[(int64_t)b * KMAX + i] = S.srt[i];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const uint32_t p = (uint32_t)(r * NT + tid);
+        if (p < nK) {
+            const uint64_t v = kp[p];
+            const uint32_t id = cidx(v);
+            const double ei = exp((double)cval(v) - (double)x0);
+            zk += ei;
+            if (md.sm) {
+                const double den = (double)qv[r] + (double)P.eps;
+                const double rr = (ei == 0.0) ? 0.0 : ei / den;
+                if (rr > rbest || (rr == rbest && id < ibest)) {
+                    rbest = rr;
+                    ibest = id;
+                }
+            }
+            kl[p] = v;
+        }
+    }
+    if (md.sm) idx = wg_best_ratio<NT>(rbest, ibest, S.scd, S.sci);
+    zk = wg_sum_f64<NT>(zk, S.scd);
     info.kind = KIND_LIST;
     info.nK = (int32_t)nK;
-    info.ZK = S.cs[nK - 1];
+    info.ZK = zk;
     if (tid == 0) {
         P.out_idx[b] = (int64_t)idx;
         W.info[b] = info;
@@ -2012,8 +2375,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             uint32_t klo = 0;
             uint64_t span = 1;
             if (level == 0) {
-                lo = info.xmin;
-                scale = (info.m > info.xmin) ? (float)K3_BINS / (info.m - info.xmin) : 0.0f;
+                // bins over the 128 below the row maximum; smaller values (whose
+                // mass is below 1e-55 of the maximum's) fall in bin 0
+                lo = info.m - 128.0f;
+                scale = (float)K3_BINS / 128.0f;
             } else {
                 klo = S.lv_klo[level];
                 span = S.lv_span[level];
@@ -2197,132 +2562,130 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 
 // ================================================================== k_dense
 
-// Dense filtered logits (and optional probabilities) of one 32768-element
-// tile of one row.  Rows with a kept list: the tile is written from a bitmap
-// of the kept positions and the kept values placed by their rank among the
-// set bits (no read of the logits, full-line stores).  Rows whose kept set is
-// a threshold (after the full-row search) re-read and re-transform the tile.
+// Dense outputs of one tile (the pass's tiles) of one row, in whole lines:
+// the filtered logits of rows with top-k / top-p (x at the kept ids, -inf
+// elsewhere; rows without a filter got theirs from the pass) and, when asked
+// for, the probabilities (pi at the kept ids, 0 elsewhere).  Rows with a
+// kept list place its values through a bitmap of the kept positions and
+// their ranks among the set bits, without reading the logits; threshold
+// rows (after the full-row search) and unfiltered rows re-read the tile.
+
+constexpr int DENSE_THREADS = 256;
 
 struct DenseShared {
-    uint32_t tb[TILE4 / 32];    // kept positions in the tile
-    uint32_t wpre[TILE4 / 32];  // set bits before each word
-    float lval[KMAX];           // kept values by rank
+    uint32_t tb[SEG_MAX / 32];    // kept positions in the tile
+    uint32_t wpre[SEG_MAX / 32];  // set bits before each word
+    float lval[KMAX];             // kept values by rank
     uint32_t sc[16];
 };
 
 template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(K4_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
+__global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
     __shared__ DenseShared S;
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
+    constexpr int NT = DENSE_THREADS;
     const int tid = threadIdx.x;
-    const int b = blockIdx.x / L.nt4, t = blockIdx.x % L.nt4;
-    const int64_t V = P.V;
-    const int64_t t0 = (int64_t)t * TILE4, t1 = min(t0 + (int64_t)TILE4, V);
+    const int b = blockIdx.x / L.nt, t = blockIdx.x % L.nt;
+    const int t0 = t * L.seg, t1 = min(t0 + L.seg, P.V);
     const RowInfo info = W.info[b];
-    const bool want_l = (P.flags & NEED_LOGITS) && P.out_logits;
-    const bool want_p = (P.flags & NEED_PROBS) && P.out_probs;
-    if (info.kind == KIND_UNFILTERED && !want_p) return;
-    float *ol = want_l ? P.out_logits + (int64_t)b * V : nullptr;
-    float *op = want_p ? P.out_probs + (int64_t)b * V : nullptr;
+    float *ol = (P.out_logits && info.kind != KIND_UNFILTERED)
+                    ? P.out_logits + (int64_t)b * P.V : nullptr;
+    float *op = P.out_probs ? P.out_probs + (int64_t)b * P.V : nullptr;
+    if (!ol && !op) return;
     const double m = (double)info.m, ZK = info.ZK;
-    constexpr int G = TILE4 / (K4_THREADS * VEC);  // groups of 8 per thread
-    constexpr int WPT = TILE4 / 32 / K4_THREADS;   // bitmap words per thread
+    const int ng = (t1 - t0 + PGROUP - 1) / PGROUP;
+    const int nw = (t1 - t0 + 31) / 32;  // bitmap words
 
     if (info.kind == KIND_LIST) {
-#pragma unroll
-        for (int w = 0; w < WPT; ++w) S.tb[tid * WPT + w] = 0u;
+        for (int w = tid; w < nw; w += NT) S.tb[w] = 0u;
         __syncthreads();
         const uint64_t *kl = W.klist + (int64_t)b * KMAX;
         const int nK = info.nK;
-        for (int i = tid; i < nK; i += K4_THREADS) {
-            const int64_t j = cidx(kl[i]);
+        for (int i = tid; i < nK; i += NT) {
+            const int j = (int)cidx(kl[i]);
             if (j >= t0 && j < t1) {
-                const int r = (int)(j - t0);
+                const int r = j - t0;
                 atomicOr(&S.tb[r >> 5], 1u << (r & 31));
             }
         }
         __syncthreads();
+        // ranks: set bits before each word (words split evenly over threads)
+        const int per = (nw + NT - 1) / NT;
         uint32_t cnt = 0;
-#pragma unroll
-        for (int w = 0; w < WPT; ++w) cnt += __popc(S.tb[tid * WPT + w]);
+        for (int i = 0; i < per; ++i) {
+            const int w = tid * per + i;
+            if (w < nw) cnt += __popc(S.tb[w]);
+        }
         uint32_t tot;
-        uint32_t run = wg_excl_scan_u32<K4_THREADS>(cnt, S.sc, tot);
-#pragma unroll
-        for (int w = 0; w < WPT; ++w) {
-            S.wpre[tid * WPT + w] = run;
-            run += __popc(S.tb[tid * WPT + w]);
+        uint32_t run = wg_excl_scan_u32<NT>(cnt, S.sc, tot);
+        for (int i = 0; i < per; ++i) {
+            const int w = tid * per + i;
+            if (w < nw) {
+                S.wpre[w] = run;
+                run += __popc(S.tb[w]);
+            }
         }
         __syncthreads();
-        for (int i = tid; i < nK; i += K4_THREADS) {
+        for (int i = tid; i < nK; i += NT) {
             const uint64_t cv = kl[i];
-            const int64_t j = cidx(cv);
+            const int j = (int)cidx(cv);
             if (j >= t0 && j < t1) {
-                const int r = (int)(j - t0);
+                const int r = j - t0;
                 const uint32_t below = S.tb[r >> 5] & ((1u << (r & 31)) - 1u);
                 S.lval[S.wpre[r >> 5] + __popc(below)] = cval(cv);
             }
         }
         __syncthreads();
-#pragma unroll 4
-        for (int g = 0; g < G; ++g) {
-            const int r0 = (g * K4_THREADS + tid) * VEC;
-            const int64_t j = t0 + r0;
-            const int nv = group_nv(j, t1);
+        for (int g = 0; g < ng; ++g) {
+            const int r0 = g * PGROUP + tid * 4;
+            const int j = t0 + r0;
+            const int nv = nv4(j, t1);
             if (nv == 0) continue;
             const uint32_t word = S.tb[r0 >> 5];
-            const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
-            float xv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = -INFINITY;
+            const uint32_t bits = (word >> (r0 & 31)) & 0xfu;
+            float xv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             if (bits) {
-                const uint32_t base = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
-                uint32_t k = 0;
+                uint32_t k = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if ((bits >> i) & 1u) xv[i] = S.lval[base + k++];
+                for (int i = 0; i < 4; ++i)
+                    if ((bits >> i) & 1u) xv[i] = S.lval[k++];
             }
-            if (want_l) store8<AL>(ol, j, nv, xv);
-            if (want_p) {
-                float o[8];
+            if (ol) store4<AL>(ol, j, nv, xv);
+            if (op) {
+                float o[4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < 4; ++i)
                     o[i] = ((bits >> i) & 1u) ? (float)(exp((double)xv[i] - m) / ZK) : 0.0f;
-                store8<AL>(op, j, nv, o);
+                store4<AL>(op, j, nv, o);
             }
         }
         return;
     }
     if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
     // K = { comp >= T } (T = 0 keeps the whole row): re-read the tile
-    if (XF && P.pen) build_bitmap<K4_THREADS>(bm, t0, t1 - t0, P, b);
+    if (XF && P.pen) build_bitmap<NT>(bm, t0, t1 - t0, P, b);
     const void *rowp = row_ptr(P, DT, b);
     const uint64_t T = info.T;
-    for (int g = 0; g < G; ++g) {
-        const int r0 = (g * K4_THREADS + tid) * VEC;
-        const int64_t j = t0 + r0;
-        const int nv = group_nv(j, t1);
+    for (int g = 0; g < ng; ++g) {
+        const int r0 = g * PGROUP + tid * 4;
+        const int j = t0 + r0;
+        const int nv = nv4(j, t1);
         if (nv == 0) continue;
-        float x[8];
-        load8<DT, AL>(rowp, j, nv, x);
-        const uint32_t bits = pen_bits<XF>(bm, r0, P);
+        Raw4<DT> raw;
+        load4<DT, AL>(rowp, j, nv, raw);
+        float x[4];
+        unpack4<DT>(raw, x);
+        const uint32_t bits = pen_bits4<XF>(bm, r0, P);
+        float lo[4], po[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = xform<XF>(x[i], (bits >> i) & 1u, P);
-        if (want_l && info.kind == KIND_THRESH) {
-            float o[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                o[i] = (mkcomp(x[i], (uint32_t)(j + i)) >= T) ? x[i] : -INFINITY;
-            store8<AL>(ol, j, nv, o);
+        for (int i = 0; i < 4; ++i) {
+            const float xi = xform<XF>(x[i], (bits >> i) & 1u, P);
+            const bool in = mkcomp(xi, (uint32_t)(j + i)) >= T;
+            lo[i] = in ? xi : -INFINITY;
+            po[i] = in ? (float)(exp((double)xi - m) / ZK) : 0.0f;
         }
-        if (want_p) {
-            float o[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                o[i] = (mkcomp(x[i], (uint32_t)(j + i)) >= T)
-                           ? (float)(exp((double)x[i] - m) / ZK)
-                           : 0.0f;
-            store8<AL>(op, j, nv, o);
-        }
+        if (ol) store4<AL>(ol, j, nv, lo);
+        if (op) store4<AL>(op, j, nv, po);
     }
 }
 
@@ -2350,32 +2713,32 @@ hipError_t launch(K kern, dim3 grid, dim3 block, size_t shmem, hipStream_t s, co
 
 static bool any_transform(const KParams &p) { return p.pen || p.temperature != 1.0f; }
 
-hipError_t launch_stream(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
-                         hipStream_t s) {
+hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                       hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(K1_THREADS);
-    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
-    return SMP_PICK(k_stream, grid, block, sh);
+    dim3 grid((unsigned)p.B), block(K1_THREADS);
+    return SMP_PICK(k_plan, grid, block, 0);
 }
 
-hipError_t launch_select(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
-                         hipStream_t s) {
+hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
+                       hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)((int64_t)p.B * l.nch)), block(SEL_THREADS);
-    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
-    return SMP_PICK(k_select, grid, block, sh);
+    dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(PASS_THREADS);
+    size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
+    return SMP_PICK(k_pass, grid, block, sh);
 }
 
 hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                       hipStream_t s) {
     const bool xf = any_transform(p);
     dim3 grid((unsigned)p.B), block(SEL_THREADS);
-    size_t sh = p.pen ? (size_t)((l.chunk_len + 31) / 32) * 4 : 0;
+    size_t sh = p.pen ? (size_t)(K3_SEG / 32) * 4 : 0;
     return SMP_PICK(k_fix, grid, block, sh);
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {
-    return launch(k_rows, dim3((unsigned)p.B), dim3(K2_THREADS), 0, s, p, l, w);
+    const size_t sh = (size_t)(l.nt * PASS_WAVES + 1) * 4;  // per-sub-slot candidate offsets
+    return launch(k_rows, dim3((unsigned)p.B), dim3(ROWS_THREADS), sh, s, p, l, w);
 }
 
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
@@ -2388,8 +2751,8 @@ hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int
 hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                         hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)((int64_t)p.B * l.nt4)), block(K4_THREADS);
-    size_t sh = p.pen ? (size_t)(TILE4 / 32) * 4 : 0;
+    dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(DENSE_THREADS);
+    size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
     return SMP_PICK(k_dense, grid, block, sh);
 }
 

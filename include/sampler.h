@@ -77,9 +77,10 @@ typedef struct sampler_opts {
      * tokens already hold mass >= p; otherwise a full-row cutoff search
      * runs).  0 = default (256); otherwise 1..1024. */
     int32_t topk_guess;
-    /* Chunks each row is split into for the streaming pass.  0 = default
-     * (8); otherwise 1..8. */
-    int32_t chunks_per_row;
+    /* Elements per tile of the streaming pass (one workgroup per tile; the
+     * Ascend page's rolling top-k uses segments of 8192).  0 = default
+     * (8192); otherwise a multiple of 1024 in [1024, 32768]. */
+    int32_t segment_len;
 } sampler_opts;
 
 /*
@@ -109,7 +110,8 @@ typedef struct sampler_args {
 /*
  * Create a handle for batches of at most max_batch rows of vocab V logits of
  * the given storage type on the current HIP device.  Allocates the device
- * workspace (about 152 KiB per row).  opts may be NULL.
+ * workspace (about 100 KiB per row at the default segment length).  opts
+ * may be NULL.
  * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
  * (max_batch < 1, V < 1 or > SAMPLER_VOCAB_MAX, unknown dtype, bad opts),
  * SAMPLER_ENOMEM or SAMPLER_EHIP.
@@ -142,14 +144,14 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
 /*
  * Kernel times, in milliseconds, averaged over the sampler_run calls made
  * with SAMPLER_PROFILE since the previous sampler_profile call (the last 64
- * of them if there were more), in launch order: [0] streaming pass of
- * unfiltered rows (and the admission estimate of the others), [1] fast
- * select pass of top-k / top-p rows, [2] exact selection of what the fast
- * pass left open, [3] row merge / cutoff / sample, [4] full-row top-p
- * cutoff (rows whose guess failed), [5] dense writer.  Each time runs from
- * an event recorded on the call's stream just before the kernel to one
- * recorded just after it.  Kernels that were not launched count 0.  Waits
- * for the last profiled call to finish, then forgets the calls it averaged.
+ * of them if there were more), in launch order: [0] per-row planning (the
+ * admission estimate of top-k / top-p rows), [1] the streaming pass over the
+ * logits (every row), [2] exact selection of what the pass left open, [3]
+ * row merge / cutoff / sample, [4] full-row top-p cutoff (rows whose guess
+ * failed), [5] dense probabilities.  Each time runs from an event recorded
+ * on the call's stream just before the kernel to one recorded just after
+ * it.  Kernels that were not launched count 0.  Waits for the last profiled
+ * call to finish, then forgets the calls it averaged.
  * Returns the number of entries written (<= n), or a negative error code
  * (SAMPLER_EINVAL when no profiled call is pending).
  */

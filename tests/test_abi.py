@@ -89,7 +89,7 @@ def test_create_rejects_bad_arguments_before_touching_the_gpu(lib):
     bad = [(0, 10, 0), (-1, 10, 0), (4, 0, 0), (4, (1 << 21) + 1, 0), (4, 10, 2), (4, 10, -1)]
     for mb, v, dt in bad:
         assert lib.sampler_create(ctypes.byref(h), mb, v, dt, None) == smp.SAMPLER_EINVAL
-    for g, c in [(-1, 0), (1025, 0), (0, 9), (0, -2)]:
+    for g, c in [(-1, 0), (1025, 0), (0, 512), (0, -1024), (0, 1500), (0, 33792)]:
         o = smp.sampler_opts(g, c)
         assert lib.sampler_create(ctypes.byref(h), 4, 100, 0, ctypes.byref(o)) == smp.SAMPLER_EINVAL
     assert lib.sampler_create(None, 4, 100, 0, None) == smp.SAMPLER_EINVAL

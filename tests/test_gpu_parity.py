@@ -5,7 +5,7 @@ sizes compare sampled rows in the launch configuration the benchmark uses.
 Edge cases: tiny and ragged vocabularies, segment boundaries, k = V, exact
 ties everywhere, signed zeros and -inf, padded row strides, every stage
 combination, top-p boundary cases that need the full-row search, and the
-tuning knobs (guess size, chunks per row), which must not change anything.
+tuning knobs (guess size, segment length), which must not change anything.
 """
 import numpy as np
 import pytest
@@ -150,17 +150,17 @@ def test_padded_row_stride(pad):
     _check(W, f"ld=V+{pad}", ld_pad=pad)
 
 
-@pytest.mark.parametrize("guess,chunks", [(1, 8), (16, 1), (1024, 3), (256, 8), (64, 5)])
-def test_knobs_do_not_change_results(guess, chunks):
+@pytest.mark.parametrize("guess,seg", [(1, 8192), (16, 1024), (1024, 3072), (256, 32768), (64, 5120)])
+def test_knobs_do_not_change_results(guess, seg):
     W = wl.make(3, B=8, V=30000, seed=4)
     W.row_flags = np.array([2, 6, 3, 7, 2, 6, 1, 0], np.uint8)
     W.top_k = np.array([0, 0, 40, 1024, 0, 0, 77, 0], np.int32)
     base = run_hip(W, need_logits=True, need_probs=True)
-    other = run_hip(W, need_logits=True, need_probs=True, guess=guess, chunks=chunks)
+    other = run_hip(W, need_logits=True, need_probs=True, guess=guess, seg=seg)
     np.testing.assert_array_equal(base["idx"], other["idx"])
     np.testing.assert_array_equal(base["logits"].view(np.uint32), other["logits"].view(np.uint32))
     # probabilities are a floating-point output: the row normaliser is summed
-    # in a chunk-dependent order
+    # in a tile-dependent order
     np.testing.assert_allclose(base["probs"], other["probs"], rtol=1e-6, atol=1e-12)
 
 
@@ -318,8 +318,12 @@ def test_profile_reports_kernel_times():
         s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"],
               row_flags=d["row_flags"], out_logits=out_l, profile=True)
     ms = s.profile()
-    assert len(ms) == 6 and all(t >= 0 for t in ms)
-    assert ms[0] > 0 and ms[1] > 0 and ms[3] > 0 and ms[5] > 0
+    assert len(ms) == 6 and all(t >= 0 for t in ms) and all(t > 0 for t in ms)
+    # without top-k / top-p and dense outputs, neither the planning, the
+    # exact selection, the full-row search nor the dense writer is launched
+    s.run(d["logits"], out_idx, q=d["q"], row_flags=d["row_flags"], profile=True)
+    ms = s.profile()
+    assert ms[1] > 0 and ms[3] > 0 and ms[0] == ms[2] == ms[4] == ms[5] == 0
     with pytest.raises(SamplerError):
         s.profile()  # the averaged calls are forgotten
     s.close()
