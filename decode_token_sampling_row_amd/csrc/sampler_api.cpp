@@ -106,6 +106,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * sizeof(RowInfo), 256);
     const size_t o_klist = off;
     off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
+    const size_t o_ktoff = off;
+    off = align_up(off + B * ((size_t)plan.nt + 1) * sizeof(uint32_t), 256);
     const size_t o_rowkey = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
     const size_t o_rowthr = off;
@@ -132,6 +134,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.cstat = (ChunkStat *)(c + o_cstat);
     s->ws.info = (RowInfo *)(c + o_info);
     s->ws.klist = (uint64_t *)(c + o_klist);
+    s->ws.ktoff = (uint32_t *)(c + o_ktoff);
     s->ws.rowkey = (uint32_t *)(c + o_rowkey);
     s->ws.rowthr = (float *)(c + o_rowthr);
     s->ws.rowref = (float *)(c + o_rowref);

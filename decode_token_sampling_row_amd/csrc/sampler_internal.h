@@ -75,7 +75,8 @@ struct KParams {
     float temperature;
     float rho;
     uint32_t flags;
-    int32_t B;
+    int32_t b0;  // first row of the launch (rows b0 .. b0 + B - 1)
+    int32_t B;   // rows of the launch
     int32_t V;
     int32_t guess;
     int32_t pen;  // penalty stage active for the call
@@ -92,7 +93,8 @@ struct KWork {
     uint32_t *wcnt;   // [maxB][nt][4] entries | strict count << 16 (all ones: overflow)
     ChunkStat *cstat; // [maxB][nt][4] per-wave statistics / winners
     RowInfo *info;    // [maxB]
-    uint64_t *klist;  // [maxB][KMAX] kept list of rows with a list
+    uint64_t *klist;  // [maxB][KMAX] kept list of rows with a list, grouped by tile
+    uint32_t *ktoff;  // [maxB][nt + 1] start of each tile's group in klist
     uint32_t *rowkey; // [maxB] exact admission key of the row's re-selection
     float *rowthr;    // [maxB] estimated admission value of the row
     float *rowref;    // [maxB] transformed sample maximum (reference for exponentials)

@@ -849,7 +849,7 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t 
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W) {
     __shared__ StreamShared S;
-    const int b = blockIdx.x;
+    const int b = P.b0 + (int)blockIdx.x;
     if (threadIdx.x == 0) {
         W.rowkey[b] = 0u;
         W.rmask[b] = 0u;
@@ -1660,7 +1660,7 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
     __shared__ uint64_t wbufs[PASS_WAVES][WCAP_MAX];  // each wave's candidates
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
-    const int b = blockIdx.x / L.nt, t = blockIdx.x % L.nt;
+    const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
     const int c0 = t * L.seg;
     const int c1 = min(c0 + L.seg, P.V);
     const int ng = (c1 - c0 + PGROUP - 1) / PGROUP;
@@ -1722,7 +1722,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void k_fix(KParams P, KPlan L, KWor
     __shared__ SelShared S;
     extern __shared__ uint32_t bm[];  // penalty bitmap of one segment
     const int tid = threadIdx.x;
-    const int b = xcd_row(blockIdx.x, gridDim.x);
+    const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
     const Mode md = row_mode(P, b);
     if (!(md.tk || md.tp)) return;
     const int ns = L.nt * PASS_WAVES;  // wave sub-slots of the row
@@ -1886,7 +1886,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     extern __shared__ uint32_t toff[];  // per-tile candidate offsets, L.nt + 1
     constexpr int NT = ROWS_THREADS;
     const int tid = threadIdx.x;
-    const int b = xcd_row(blockIdx.x, gridDim.x);
+    const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
     const Mode md = row_mode(P, b);
     const bool filtered = md.tk || md.tp;
     const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
@@ -2197,6 +2197,39 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             qv[r] = p < nK ? P.q[(int64_t)b * P.V + cidx(kp[p])] : 1.0f;
         }
     }
+    // the kept list goes out grouped by tile (any order within a tile), so
+    // that each dense-writer workgroup reads only its own entries; toff (no
+    // longer needed for the candidates) counts them per tile
+    const int ntile = L.nt;
+    for (int i = tid; i <= ntile; i += NT) toff[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const uint32_t p = (uint32_t)(r * NT + tid);
+        if (p < nK) atomicAdd(&toff[cidx(kp[p]) / (uint32_t)L.seg], 1u);
+    }
+    __syncthreads();
+    {
+        const int per = (ntile + NT - 1) / NT;
+        uint32_t lc = 0;
+        for (int i = 0; i < per; ++i) {
+            const int t = tid * per + i;
+            if (t < ntile) lc += toff[t];
+        }
+        uint32_t tot2;
+        uint32_t run = wg_excl_scan_u32<NT>(lc, S.sc, tot2);
+        for (int i = 0; i < per; ++i) {
+            const int t = tid * per + i;
+            if (t < ntile) {
+                const uint32_t c = toff[t];
+                toff[t] = run;
+                W.ktoff[(int64_t)b * (ntile + 1) + t] = run;
+                run += c;
+            }
+        }
+        if (tid == 0) W.ktoff[(int64_t)b * (ntile + 1) + ntile] = nK;
+        __syncthreads();
+    }
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const uint32_t p = (uint32_t)(r * NT + tid);
@@ -2213,7 +2246,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                     ibest = id;
                 }
             }
-            kl[p] = v;
+            kl[atomicAdd(&toff[id / (uint32_t)L.seg], 1u)] = v;
         }
     }
     if (md.sm) idx = wg_best_ratio<NT>(rbest, ibest, S.scd, S.sci);
@@ -2353,7 +2386,7 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
-    const int b = xcd_row(blockIdx.x, gridDim.x);
+    const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
     RowInfo info = W.info[b];
     if (info.kind != KIND_FALLBACK) return;
     const Mode md = row_mode(P, b);
@@ -2566,8 +2599,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 // the filtered logits of rows with top-k / top-p (x at the kept ids, -inf
 // elsewhere; rows without a filter got theirs from the pass) and, when asked
 // for, the probabilities (pi at the kept ids, 0 elsewhere).  Rows with a
-// kept list place its values through a bitmap of the kept positions and
-// their ranks among the set bits, without reading the logits; threshold
+// kept list place the tile's kept values through a bitmap of their positions
+// and their ranks among the set bits, without reading the logits; threshold
 // rows (after the full-row search) and unfiltered rows re-read the tile.
 
 constexpr int DENSE_THREADS = 256;
@@ -2576,6 +2609,7 @@ struct DenseShared {
     uint32_t tb[SEG_MAX / 32];    // kept positions in the tile
     uint32_t wpre[SEG_MAX / 32];  // set bits before each word
     float lval[KMAX];             // kept values by rank
+    uint64_t kv[KMAX];            // the tile's kept entries
     uint32_t sc[16];
 };
 
@@ -2585,7 +2619,7 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
     constexpr int NT = DENSE_THREADS;
     const int tid = threadIdx.x;
-    const int b = blockIdx.x / L.nt, t = blockIdx.x % L.nt;
+    const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
     const int t0 = t * L.seg, t1 = min(t0 + L.seg, P.V);
     const RowInfo info = W.info[b];
     float *ol = (P.out_logits && info.kind != KIND_UNFILTERED)
@@ -2594,19 +2628,20 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
     if (!ol && !op) return;
     const double m = (double)info.m, ZK = info.ZK;
     const int ng = (t1 - t0 + PGROUP - 1) / PGROUP;
-    const int nw = (t1 - t0 + 31) / 32;  // bitmap words
 
     if (info.kind == KIND_LIST) {
-        for (int w = tid; w < nw; w += NT) S.tb[w] = 0u;
-        __syncthreads();
+        const int nw = (t1 - t0 + 31) / 32;  // bitmap words
+        // the tile's kept entries (the merge grouped them by tile), staged
+        const uint32_t *kto = W.ktoff + (int64_t)b * (L.nt + 1);
+        const int k0 = (int)kto[t], k1 = (int)kto[t + 1];
         const uint64_t *kl = W.klist + (int64_t)b * KMAX;
-        const int nK = info.nK;
-        for (int i = tid; i < nK; i += NT) {
-            const int j = (int)cidx(kl[i]);
-            if (j >= t0 && j < t1) {
-                const int r = j - t0;
-                atomicOr(&S.tb[r >> 5], 1u << (r & 31));
-            }
+        for (int w = tid; w < nw; w += NT) S.tb[w] = 0u;
+        for (int i = k0 + tid; i < k1; i += NT) S.kv[i - k0] = kl[i];
+        __syncthreads();
+        const int nk = k1 - k0;
+        for (int i = tid; i < nk; i += NT) {
+            const int r = (int)cidx(S.kv[i]) - t0;
+            atomicOr(&S.tb[r >> 5], 1u << (r & 31));
         }
         __syncthreads();
         // ranks: set bits before each word (words split evenly over threads)
@@ -2626,37 +2661,40 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
             }
         }
         __syncthreads();
-        for (int i = tid; i < nK; i += NT) {
-            const uint64_t cv = kl[i];
-            const int j = (int)cidx(cv);
-            if (j >= t0 && j < t1) {
-                const int r = j - t0;
-                const uint32_t below = S.tb[r >> 5] & ((1u << (r & 31)) - 1u);
-                S.lval[S.wpre[r >> 5] + __popc(below)] = cval(cv);
-            }
+        for (int i = tid; i < nk; i += NT) {
+            const uint64_t cv = S.kv[i];
+            const int r = (int)cidx(cv) - t0;
+            const uint32_t below = S.tb[r >> 5] & ((1u << (r & 31)) - 1u);
+            S.lval[S.wpre[r >> 5] + __popc(below)] = cval(cv);
         }
         __syncthreads();
-        for (int g = 0; g < ng; ++g) {
-            const int r0 = g * PGROUP + tid * 4;
+        // whole lines: each lane writes 8 consecutive floats (two 16-byte
+        // stores), the pattern that sustains the highest write rate
+        constexpr int DGROUP = NT * VEC;
+        const int ng8 = (t1 - t0 + DGROUP - 1) / DGROUP;
+        for (int g = 0; g < ng8; ++g) {
+            const int r0 = g * DGROUP + tid * VEC;
             const int j = t0 + r0;
-            const int nv = nv4(j, t1);
+            const int nv = group_nv(j, t1);
             if (nv == 0) continue;
             const uint32_t word = S.tb[r0 >> 5];
-            const uint32_t bits = (word >> (r0 & 31)) & 0xfu;
-            float xv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
+            float xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = -INFINITY;
             if (bits) {
                 uint32_t k = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 8; ++i)
                     if ((bits >> i) & 1u) xv[i] = S.lval[k++];
             }
-            if (ol) store4<AL>(ol, j, nv, xv);
+            if (ol) store8<AL>(ol, j, nv, xv);
             if (op) {
-                float o[4];
+                float o[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 8; ++i)
                     o[i] = ((bits >> i) & 1u) ? (float)(exp((double)xv[i] - m) / ZK) : 0.0f;
-                store4<AL>(op, j, nv, o);
+                store8<AL>(op, j, nv, o);
             }
         }
         return;
