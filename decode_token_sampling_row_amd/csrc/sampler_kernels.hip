@@ -1378,14 +1378,6 @@ __device__ __forceinline__ uint32_t pen_bits4(const uint32_t *bm, int r, const K
 }
 
 // ---- wave-level reductions (every lane gets the result)
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shx64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
-}
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shxf(v, m));
@@ -1416,7 +1408,8 @@ __device__ __forceinline__ Race wave_race(Race r) {
 struct StreamState {
     Stats st;
     Race rc;
-    uint64_t am;
+    float bx;     // greedy: this lane's largest value
+    uint32_t bj;  // greedy: its lowest id (this lane's ids increase)
 };
 
 // Sum of exp(y - ref) for a select tile of a row without top-k: fp32 terms
@@ -1429,101 +1422,117 @@ struct RefSum {
     float ymax;  // largest y seen
 };
 
-// What a wave of a select tile has handed over so far.
+// What a wave of a select tile has collected so far.
 struct WaveSel {
-    uint32_t cnt;     // entries written (uniform over the wave)
-    uint32_t strict;  // this lane's entries with y > yt
-    bool ovf;         // an append did not fit
+    uint32_t cnt;  // entries in the wave's buffer (uniform over the wave)
+    bool ovf;      // an append did not fit
 };
 
-// One group of 4 (first id j, nv valid) of a tile.
-//   KIND 0: greedy row, 1: racing row, 2: select row.
-template <int DT, bool AL, bool XF, int KIND>
-__device__ __forceinline__ void pass_group(const Raw4<DT> &raw, const Raw4<0> &qraw, int j, int nv,
-                                           int c0, const uint32_t *bm, const KParams &P,
-                                           float *rowo, bool do_stats, StreamState &ss,
-                                           RefSum &rs, WaveSel &ws, uint64_t *wbuf, uint32_t wcap,
-                                           float ref, float traw, float yt) {
+// Append the admitted elements of one group of 4 (c[i]: this lane's element
+// i is admitted; bal[i]: the wave's ballot of it) to the wave's buffer, in
+// ballot order.
+template <bool XF>
+__device__ __forceinline__ void sel_append4(const float (&x)[4], uint32_t bits, const bool (&c)[4],
+                                            const uint64_t (&bal)[4], int j, const KParams &P,
+                                            WaveSel &ws, uint64_t *wbuf, uint32_t wcap) {
+    const uint32_t n0 = (uint32_t)__popcll(bal[0]), n1 = (uint32_t)__popcll(bal[1]);
+    const uint32_t n2 = (uint32_t)__popcll(bal[2]), n3 = (uint32_t)__popcll(bal[3]);
+    const uint32_t tot = n0 + n1 + n2 + n3;
+    if (tot == 0) return;
+    if (ws.ovf || ws.cnt + tot > wcap) {
+        ws.ovf = true;
+        return;
+    }
+    const uint32_t nn[4] = {n0, n1, n2, n3};
+    uint32_t off = ws.cnt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (bal[i] == 0) continue;
+        if (c[i]) {
+            const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
+            wbuf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
+        }
+        off += nn[i];
+    }
+    ws.cnt = off;
+}
+
+// One group of 4 (first id j, nv valid) of a select tile: admit
+// non-penalised elements with raw x >= traw and penalised ones (and, for
+// rows that accumulate statistics, all of them) with transformed y >= yt,
+// where yt is the transform of traw; every element left out therefore has
+// y <= yt.
+template <int DT, bool XF, bool FULL, bool STATS>
+__device__ __forceinline__ void sel_group(const Raw4<DT> &raw, int j, int nv, int c0,
+                                          const uint32_t *bm, const KParams &P, RefSum &rs,
+                                          WaveSel &ws, uint64_t *wbuf, uint32_t wcap, float ref,
+                                          float traw, float yt) {
     float x[4];
     unpack4<DT>(raw, x);
-    const uint32_t bits = nv > 0 ? pen_bits4<XF>(bm, j - c0, P) : 0u;
-    if (KIND == 2) {
-        bool pass[4];
-        if (do_stats) {
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = xform<XF>(x[i], (bits >> i) & 1u, P);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < nv) {
-                    rs.ymax = fmaxf(rs.ymax, y[i]);
-                    rs.z += __builtin_amdgcn_exp2f((y[i] - ref) * 1.4426950408889634f);
-                }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pass[i] = i < nv && y[i] >= yt;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pass[i] = i < nv && x[i] >= traw;
-            if (XF && bits) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if ((bits >> i) & 1u) pass[i] = i < nv && xform<XF>(x[i], 1u, P) >= yt;
-            }
-        }
-        uint64_t bal[4];
-        uint32_t tot = 0;
+    const uint32_t bits = (FULL || nv > 0) ? pen_bits4<XF>(bm, j - c0, P) : 0u;
+    bool c[4];
+    if (STATS) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            bal[i] = __ballot(pass[i]);
-            tot += (uint32_t)__popcll(bal[i]);
-        }
-        if (tot == 0) return;
-        if (ws.ovf || ws.cnt + tot > wcap) {
-            ws.ovf = true;
-            return;
-        }
-        uint32_t off = ws.cnt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (bal[i] == 0) continue;
-            if (pass[i]) {
-                const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
-                wbuf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
-                ws.strict += y > yt;
+            const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
+            if (FULL || i < nv) {
+                rs.ymax = fmaxf(rs.ymax, y);
+                rs.z += __builtin_amdgcn_exp2f((y - ref) * 1.4426950408889634f);
             }
-            off += (uint32_t)__popcll(bal[i]);
+            c[i] = (FULL || i < nv) && y >= yt;
         }
-        ws.cnt = off;
     } else {
-        float y[1][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[0][i] = xform<XF>(x[i], (bits >> i) & 1u, P);
-        if (rowo && nv > 0) store4<AL>(rowo, j, nv, y[0]);
-        if (do_stats) {
-            int nvv[1] = {nv};
-            stats_batch<1, 4>(ss.st, y, nvv);
-        }
-        if (KIND == 1) {
-            float qv[4];
-            unpack4<0>(qraw, qv);
+        for (int i = 0; i < 4; ++i) c[i] = (FULL || i < nv) && x[i] >= traw;
+        if (XF && bits) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < nv) race_offer(ss.rc, y[0][i], qv[i] + P.eps, (uint32_t)(j + i));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < nv) {
-                    const uint64_t cv = mkcomp(y[0][i], (uint32_t)(j + i));
-                    ss.am = cv > ss.am ? cv : ss.am;
-                }
+                if ((bits >> i) & 1u) c[i] = (FULL || i < nv) && xform<XF>(x[i], 1u, P) >= yt;
         }
+    }
+    uint64_t bal[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bal[i] = __ballot(c[i]);
+    if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;
+    sel_append4<XF>(x, bits, c, bal, j, P, ws, wbuf, wcap);
+}
+
+// One group of 4 of a row without top-k / top-p: transform, dense store,
+// statistics, and the race (q given) or the greedy argmax.
+template <int DT, bool AL, bool XF, bool FULL, bool STATS, bool RACE>
+__device__ __forceinline__ void stream_group(const Raw4<DT> &raw, const Raw4<0> &qraw, int j, int nv,
+                                             int c0, const uint32_t *bm, const KParams &P,
+                                             float *rowo, StreamState &ss) {
+    float y[1][4];
+    unpack4<DT>(raw, y[0]);
+    const uint32_t bits = (FULL || nv > 0) ? pen_bits4<XF>(bm, j - c0, P) : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[0][i] = xform<XF>(y[0][i], (bits >> i) & 1u, P);
+    if (rowo && (FULL || nv > 0)) store4<AL>(rowo, j, FULL ? 4 : nv, y[0]);
+    if (STATS) {
+        int nvv[1] = {FULL ? 4 : nv};
+        stats_batch<1, 4>(ss.st, y, nvv);
+    }
+    if (RACE) {
+        float qv[4];
+        unpack4<0>(qraw, qv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (FULL || i < nv) race_offer(ss.rc, y[0][i], qv[i] + P.eps, (uint32_t)(j + i));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((FULL || i < nv) && y[0][i] > ss.bx) {
+                ss.bx = y[0][i];
+                ss.bj = (uint32_t)(j + i);
+            }
     }
 }
 
 // Sum of exp(y - m) over this lane's groups of the tile [c0, c1), read
 // again (rare path: a value far above the row's reference).
 template <int DT, bool AL, bool XF>
-__device__ double lane_sum_again(const KParams &P, const uint32_t *bm, int b, int c0, int c1,
+__device__ __forceinline__ double lane_sum_again(const KParams &P, const uint32_t *bm, int b, int c0, int c1,
                                  float m) {
     const void *rowp = row_ptr(P, DT, b);
     double z = 0.0;
@@ -1541,6 +1550,54 @@ __device__ double lane_sum_again(const KParams &P, const uint32_t *bm, int b, in
     return z;
 }
 
+// The group loop of a tile: PASS_D groups in flight per thread (q for racing
+// rows QD groups ahead), each group processed as soon as it arrives.
+template <int DT, bool AL, bool XF, int KIND, bool FULL, bool STATS>
+__device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, int c0, int c1,
+                                          int ng, int j0, const void *rowp, const float *rowq,
+                                          float *rowo, Raw4<DT> (&ring)[PASS_D], StreamState &ss,
+                                          RefSum &rs, WaveSel &ws, uint64_t *wbuf, uint32_t wcap,
+                                          float ref, float traw, float yt) {
+    constexpr int QD = KIND == 1 ? PASS_D / 2 : 1;
+    Raw4<0> qring[QD];
+    if (KIND == 1) {
+#pragma unroll
+        for (int d = 0; d < QD; ++d)
+            if (d < ng) {
+                const int j = j0 + d * PGROUP;
+                const int nv = FULL ? 4 : nv4(j, c1);
+                if (nv > 0) load4<0, AL>(rowq, j, nv, qring[d]);
+            }
+    }
+    for (int g0 = 0; g0 < ng; g0 += PASS_D) {
+#pragma unroll
+        for (int d = 0; d < PASS_D; ++d) {
+            const int g = g0 + d;
+            if (g < ng) {
+                const int j = j0 + g * PGROUP;
+                const int nv = FULL ? 4 : nv4(j, c1);
+                if (KIND == 2)
+                    sel_group<DT, XF, FULL, STATS>(ring[d], j, nv, c0, bm, P, rs, ws, wbuf, wcap,
+                                                   ref, traw, yt);
+                else
+                    stream_group<DT, AL, XF, FULL, STATS, KIND == 1>(ring[d], qring[d % QD], j, nv,
+                                                                     c0, bm, P, rowo, ss);
+                const int gn = g + PASS_D;
+                if (gn < ng) {
+                    const int jn = j0 + gn * PGROUP;
+                    const int nvn = FULL ? 4 : nv4(jn, c1);
+                    if (nvn > 0) load4<DT, AL>(rowp, jn, nvn, ring[d]);
+                }
+                if (KIND == 1 && g + QD < ng) {
+                    const int jq = j0 + (g + QD) * PGROUP;
+                    const int nvq = FULL ? 4 : nv4(jq, c1);
+                    if (nvq > 0) load4<0, AL>(rowq, jq, nvq, qring[d % QD]);
+                }
+            }
+        }
+    }
+}
+
 // One tile, each wave on its own: no barrier (the penalty bitmap aside).
 // Wave w of tile t of row b collects its candidates in its own LDS buffer
 // (appends to global memory in the middle of the load stream would make the
@@ -1556,6 +1613,7 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     const int c0 = t * L.seg;
     const int c1 = min(c0 + L.seg, P.V);
     const int ng = (c1 - c0 + PGROUP - 1) / PGROUP;  // group rows in the tile
+    const bool full = c0 + ng * PGROUP <= c1;        // every group whole
     const void *rowp = row_ptr(P, DT, b);
     const float *rowq = KIND == 1 ? P.q + (int64_t)b * P.V : nullptr;
     float *rowo = (KIND != 2 && P.out_logits) ? P.out_logits + (int64_t)b * P.V : nullptr;
@@ -1568,49 +1626,25 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     StreamState ss;
     ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
     ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE;
-    ss.am = 0;
+    ss.bx = -INFINITY;
+    ss.bj = j0 < c1 ? (uint32_t)j0 : NONE;  // kept if every value is -inf
     RefSum rs;
     rs.z = 0.0f;
     rs.ymax = -INFINITY;
     WaveSel ws;
     ws.cnt = 0;
-    ws.strict = 0;
     ws.ovf = false;
-    // q runs QD groups ahead (fewer registers than the logits ring)
-    constexpr int QD = KIND == 1 ? PASS_D / 2 : 1;
-    Raw4<0> qring[QD];
-    if (KIND == 1) {
-#pragma unroll
-        for (int d = 0; d < QD; ++d)
-            if (d < ng) {
-                const int j = j0 + d * PGROUP;
-                const int nv = nv4(j, c1);
-                if (nv > 0) load4<0, AL>(rowq, j, nv, qring[d]);
-            }
+#define SMP_TILE_LOOP(F, ST)                                                                    \
+    tile_loop<DT, AL, XF, KIND, F, ST>(bm, P, c0, c1, ng, j0, rowp, rowq, rowo, ring, ss, rs, ws, \
+                                       wbuf, wcap, ref, traw, yt)
+    if (full) {
+        if (do_stats) SMP_TILE_LOOP(true, true);
+        else SMP_TILE_LOOP(true, false);
+    } else {
+        if (do_stats) SMP_TILE_LOOP(false, true);
+        else SMP_TILE_LOOP(false, false);
     }
-    for (int g0 = 0; g0 < ng; g0 += PASS_D) {
-#pragma unroll
-        for (int d = 0; d < PASS_D; ++d) {
-            const int g = g0 + d;
-            if (g < ng) {
-                const int j = j0 + g * PGROUP;
-                const int nv = nv4(j, c1);
-                pass_group<DT, AL, XF, KIND>(ring[d], qring[d % QD], j, nv, c0, bm, P, rowo,
-                                             do_stats, ss, rs, ws, wbuf, wcap, ref, traw, yt);
-                const int gn = g + PASS_D;
-                if (gn < ng) {
-                    const int jn = j0 + gn * PGROUP;
-                    const int nvn = nv4(jn, c1);
-                    if (nvn > 0) load4<DT, AL>(rowp, jn, nvn, ring[d]);
-                }
-                if (KIND == 1 && g + QD < ng) {
-                    const int jq = j0 + (g + QD) * PGROUP;
-                    const int nvq = nv4(jq, c1);
-                    if (nvq > 0) load4<0, AL>(rowq, jq, nvq, qring[d % QD]);
-                }
-            }
-        }
-    }
+#undef SMP_TILE_LOOP
     ChunkStat cs = empty_stat();
     if (KIND == 2) {
         if (do_stats) {
@@ -1623,12 +1657,18 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
                 cs.z = wave_sum_f64((double)rs.z);
             }
         }
+        // hand the entries over, counting those above yt
+        uint32_t strict = 0;
         if (!ws.ovf) {
             uint64_t *dst =
                 W.cand + (int64_t)b * ROWCAP + (int64_t)(t * PASS_WAVES + (tid >> 6)) * wcap;
-            for (uint32_t i = lane; i < ws.cnt; i += 64) dst[i] = wbuf[i];
+            for (uint32_t i = lane; i < ws.cnt; i += 64) {
+                const uint64_t v = wbuf[i];
+                dst[i] = v;
+                strict += cval(v) > yt;
+            }
         }
-        const uint32_t strict = wave_sum_u32(ws.strict);
+        strict = wave_sum_u32(strict);
         if (lane == 0) {
             W.wcnt[wslot] = ws.ovf ? 0xffffffffu : (ws.cnt | (strict << 16));
             W.cstat[wslot] = cs;
@@ -1646,11 +1686,14 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
             cs.rqe = r.qe;
             cs.ridx = r.idx;
         } else {
-            // the greedy winner, as (value, id): the largest value, lowest id
-            const uint64_t am = wave_max_u64(ss.am);
-            cs.rx = am ? cval(am) : -INFINITY;
+            // the greedy winner: the largest value, lowest id among equals
+            const float m = wave_max_f32(ss.bx);
+            uint32_t id = (ss.bx == m) ? ss.bj : NONE;
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) id = min(id, shx(id, sft));
+            cs.rx = m;
             cs.rqe = 1.0f;
-            cs.ridx = am ? cidx(am) : NONE;
+            cs.ridx = id;
         }
         if (lane == 0) W.cstat[wslot] = cs;
     }
