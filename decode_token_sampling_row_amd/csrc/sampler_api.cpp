@@ -120,6 +120,10 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * sizeof(int32_t), 256);
     const size_t o_rmask = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
+    const size_t o_fbcnt = off;
+    off = align_up(off + sizeof(uint32_t), 256);
+    const size_t o_fblist = off;
+    off = align_up(off + B * sizeof(uint32_t), 256);
     void *base = nullptr;
     hipError_t e = hipMalloc(&base, off);
     if (e != hipSuccess) {
@@ -141,6 +145,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.rcand = (uint64_t *)(c + o_rcand);
     s->ws.rcnt = (int32_t *)(c + o_rcnt);
     s->ws.rmask = (uint32_t *)(c + o_rmask);
+    s->ws.fbcnt = (uint32_t *)(c + o_fbcnt);
+    s->ws.fblist = (uint32_t *)(c + o_fblist);
     s->events_made = false;
     s->events_ok = false;
     s->nprof = 0;

@@ -101,6 +101,8 @@ struct KWork {
     uint64_t *rcand;  // [maxB][SLOT] exact re-selection of a row
     int32_t *rcnt;    // [maxB] entries in rcand
     uint32_t *rmask;  // [maxB] nonzero: the row's candidates are rcand
+    uint32_t *fbcnt;  // [1] rows queued for the full-row top-p search
+    uint32_t *fblist; // [maxB] those rows
 };
 
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.

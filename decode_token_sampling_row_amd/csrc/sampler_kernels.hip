@@ -2,27 +2,38 @@
 //
 // Pipeline of one call (all on the caller's stream):
 //
-//   k_chunk     grid = B x nch.  One workgroup streams one chunk of one row
-//               once from HBM: widen bf16 -> fp32, repetition penalty (LDS
-//               bitmap of the chunk's history ids), temperature.  Depending on
-//               the row's stages it then
-//                 - keeps the chunk's top-kk candidates in an LDS buffer
-//                   filtered by a rising threshold (the rolling top-k of the
-//                   Ascend npu_top_k_top_p_sample page, topK section: each
-//                   batch of elements is prefiltered by the k-th value of
-//                   what came before, the buffer is cut back to exactly kk by
-//                   a radix select when it fills);
-//                 - accumulates the chunk's max / sum-exp for top-p rows
-//                   without top-k (the softmax of that page's topP section);
-//                 - runs the exponential race over the whole chunk for rows
-//                   that only sample (streams q in the same pass);
-//                 - writes the dense output of unfiltered rows.
-//   k_rows      grid = B.  Merges the <= 8 chunk results of a row: exact
-//               top-kk by radix select, bitonic sort, softmax in double,
-//               inclusive scan, shortest prefix reaching p, exponential race
-//               over the kept set (gather of q at the kept ids), output id.
-//               Rows whose guess does not settle top-p are flagged.
-//   k_fallback  grid = B (flagged rows only).  Full-row top-p cutoff: a
+//   k_plan      grid = B.  Rows with top-k / top-p: an admission value from a
+//               sample of the row (16 staggered runs of 1024 logits), below
+//               which no element can be among the row's kk largest with high
+//               probability; the sample maximum as the reference for sums of
+//               exponentials.
+//   k_pass      grid = B x tiles of seg (8192 by default, the segment length
+//               of the rolling top-k of the Ascend npu_top_k_top_p_sample
+//               page, topK section).  Each workgroup reads one tile of one
+//               row once from HBM: widen bf16 -> fp32, repetition penalty
+//               (LDS bitmap of the tile's history ids), temperature.  Then,
+//               each wave on its own:
+//                 - rows with top-k / top-p: admit what reaches the row's
+//                   admission value into the wave's LDS buffer and hand it
+//                   over to the wave's sub-slot of the row; rows without
+//                   top-k also sum exp(y - ref) (the softmax of that page's
+//                   topP section);
+//                 - rows that only sample: the exponential race over the
+//                   tile, q streamed alongside;
+//                 - greedy rows: the argmax;
+//                 - the dense output of rows without a filter.
+//   k_fix       grid = B / 8, one row checked per wave.  A row whose wave
+//               overflowed its sub-slot, or whose handed-over entries above
+//               the admission value number fewer than kk, is selected again
+//               exactly (the page's rolling top-k, LDS buffer cut back by
+//               radix select).
+//   k_rows      grid = B.  Per row: exact top-kk of the candidates by radix
+//               select, softmax in double, the shortest prefix reaching p
+//               (top-k guess accepted with a margin), exponential race over
+//               the kept set (gather of q at the kept ids), output id, the
+//               kept list grouped by tile.  Rows whose guess does not settle
+//               top-p are queued.
+//   k_fallback  grid = min(B, 256) over the queue.  Full-row top-p cutoff: a
 //               value-space mass histogram, then key-space refinement, then
 //               an exact sort of the boundary bucket in LDS (or a rank among
 //               ties by vocab id), then the race over the kept set.  This is
@@ -37,6 +48,7 @@
 // distinct, so every selection below is exact and deterministic.
 
 #include <math.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "sampler_internal.h"
@@ -398,36 +410,106 @@ __device__ __forceinline__ void wave0_find_bin(const uint32_t *hist, uint32_t ne
     }
 }
 
+// Workgroup reduction of four 64-bit values at once: minimum, maximum, OR
+// and AND (sc: 4 * NT / 64 entries).  Two barriers.
+template <int NT>
+__device__ __forceinline__ void wg_min_max_or_and(uint64_t &mn, uint64_t &mx, uint64_t &o,
+                                                  uint64_t &a, uint64_t *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t x0 = shx64(mn, m), x1 = shx64(mx, m), x2 = shx64(o, m), x3 = shx64(a, m);
+        mn = x0 < mn ? x0 : mn;
+        mx = x1 > mx ? x1 : mx;
+        o |= x2;
+        a &= x3;
+    }
+    constexpr int NW = NT / 64;
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        sc[w] = mn;
+        sc[NW + w] = mx;
+        sc[2 * NW + w] = o;
+        sc[3 * NW + w] = a;
+    }
+    __syncthreads();
+    mn = ~0ull;
+    mx = 0ull;
+    o = 0ull;
+    a = ~0ull;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        mn = sc[i] < mn ? sc[i] : mn;
+        mx = sc[NW + i] > mx ? sc[NW + i] : mx;
+        o |= sc[2 * NW + i];
+        a &= sc[3 * NW + i];
+    }
+    __syncthreads();
+}
+
 // Radix select over distinct 64-bit composites held in registers.  Finds
 // (prefix, pmask) such that exactly kk of the valid entries satisfy
-// (v & pmask) >= prefix, i.e. the kk largest.  The bits all entries share
-// are skipped first (min/max reduction), then digits of up to 8 bits are
-// taken from the highest differing bit down, stopping as soon as the
-// boundary bucket is taken whole.  Needs 1 <= kk < number of valid entries.
+// (v & pmask) >= prefix, i.e. the kk largest.  Digits of up to 8 bits are
+// taken from the highest bit that differs among the entries down, skipping
+// bits every entry shares (the low half of a bf16 value's key, the high bits
+// of ids below V), and stopping as soon as the boundary bucket is taken
+// whole.  Once only id bits remain, the bucket is a run of equal values: if
+// it fits in tie[] (tcap entries of LDS), its members are ranked by direct
+// comparison and the need-th largest becomes the exact boundary.  Needs
+// 1 <= kk < number of valid entries.
 template <int NT, int R>
 __device__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t kk,
-                                uint32_t *hist, uint32_t *sel, uint64_t *sc64,
-                                uint64_t &prefix_out, uint64_t &pmask_out) {
-    uint64_t mn = ~0ull, mx = 0ull;
+                                uint32_t *hist, uint32_t *sel, uint64_t *sc64, uint64_t *tie,
+                                uint32_t tcap, uint32_t *tcnt, uint64_t &prefix_out,
+                                uint64_t &pmask_out) {
+    uint64_t mn = ~0ull, mx = 0ull, o = 0ull, an = ~0ull;
 #pragma unroll
     for (int r = 0; r < R; ++r)
         if ((vmask >> r) & 1u) {
             mn = v[r] < mn ? v[r] : mn;
             mx = v[r] > mx ? v[r] : mx;
+            o |= v[r];
+            an &= v[r];
         }
-    mn = wg_min_u64<NT>(mn, sc64);
-    mx = wg_max_u64<NT>(mx, sc64);
-    const uint64_t diff = mn ^ mx;
-    if (diff == 0) {
+    wg_min_max_or_and<NT>(mn, mx, o, an, sc64);
+    const uint64_t vary = o ^ an;  // bits that differ somewhere
+    if (vary == 0) {               // a single entry
         prefix_out = mx;
         pmask_out = ~0ull;
         return;
     }
-    int hi = 63 - __clzll(diff);
+    int hi = 63 - __clzll(vary);
     uint64_t pmask = (hi == 63) ? 0ull : (~0ull << (hi + 1));
     uint64_t prefix = mx & pmask;
     uint32_t need = kk;
     for (;;) {
+        if (hi < 32) {
+            // equal values from here on: rank the bucket's members directly
+            uint32_t cnt = 0;
+            if (threadIdx.x == 0) *tcnt = 0;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (((vmask >> r) & 1u) && (v[r] & pmask) == prefix) {
+                    const uint32_t pos = atomicAdd(tcnt, 1u);
+                    if (pos < tcap) tie[pos] = v[r];
+                }
+            __syncthreads();
+            cnt = *tcnt;
+            if (cnt <= tcap) {
+                for (uint32_t i = threadIdx.x; i < cnt; i += NT) {
+                    const uint64_t me = tie[i];
+                    uint32_t above = 0;
+                    for (uint32_t j2 = 0; j2 < cnt; ++j2) above += tie[j2] > me;
+                    if (above == need - 1) sc64[0] = me;
+                }
+                __syncthreads();
+                prefix = sc64[0];
+                pmask = ~0ull;
+                __syncthreads();
+                break;
+            }
+            // a run of equal values larger than tie[]: id digits as below
+        }
         const int width = hi + 1 < 8 ? hi + 1 : 8;
         const int shift = hi + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
@@ -445,7 +527,14 @@ __device__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t
         prefix |= (uint64_t)d << shift;
         pmask |= (uint64_t)dmask << shift;
         if (cntd == need || shift == 0) break;
-        hi = shift - 1;
+        // next digit: from the highest bit below this one that differs
+        // somewhere; the bits skipped are the same in every entry
+        const uint64_t rest = vary & ((1ull << shift) - 1ull);
+        if (rest == 0) break;  // cannot happen for distinct entries
+        hi = 63 - __clzll(rest);
+        const uint64_t skip = ((1ull << shift) - 1ull) & ~((1ull << (hi + 1)) - 1ull);
+        pmask |= skip;
+        prefix |= mx & skip;
     }
     prefix_out = prefix;
     pmask_out = pmask;
@@ -739,7 +828,9 @@ struct StreamShared {
 // ulp), and in steps of 2^24 when the 255 top bins hold fewer than r; only
 // the top 255 bins are counted, so the bins stay sparse and the LDS atomics
 // rarely collide.  -inf (admit everything) when r would exceed the sample.
-// smax receives the sample maximum (raw).
+// smax receives the sample maximum (raw); active whether the row has top-k
+// or top-p at all (the sample is requested before the row's stages are
+// known, so that the two latencies overlap).
 // Only the speed of the select pass depends on t: that pass checks that what
 // it admitted holds the row's kk largest and redoes the row exactly when it
 // does not.
@@ -757,17 +848,14 @@ __device__ __forceinline__ int est_run_start(int s, int b, int V) {
 }
 
 template <int DT, bool AL>
-__device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t kk, StreamShared &S,
-                                              float &smax) {
+__device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamShared &S,
+                                              float &smax, bool &active) {
     constexpr int NT = K1_THREADS;
     constexpr int PER = EST_N / (NT * VEC);  // groups of 8 per thread
     constexpr int GPS = EST_SEG / VEC;       // groups per run
     const int V = P.V;
     const bool whole = V <= EST_N;
     const int n = whole ? V : EST_N;
-    const double r0 = (double)kk * (double)n / (double)V;
-    const double rr = ceil(r0 + 4.0 * sqrt(r0) + 8.0);
-    const uint32_t r = rr < (double)n ? (uint32_t)rr : 0u;  // 0: admit everything
     const void *rowp = row_ptr(P, DT, b);
     // the whole sample in registers, every load in flight at once
     Raw<DT> raw[PER];
@@ -785,6 +873,15 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, uint32_t 
         nv[g] = group_nv(j, V);
         load_raw<DT, AL>(rowp, j, nv[g], raw[g]);
     }
+    // the row's stages, read while the sample is on its way (rows without
+    // top-k / top-p leave here, their sample unused)
+    const Mode md = row_mode(P, b);
+    active = md.tk || md.tp;
+    if (!active) return 0.0f;
+    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+    const double r0 = (double)kk * (double)n / (double)V;
+    const double rr = ceil(r0 + 4.0 * sqrt(r0) + 8.0);
+    const uint32_t r = rr < (double)n ? (uint32_t)rr : 0u;  // 0: admit everything
     // the sample maximum
     uint32_t mx = 0;
 #pragma unroll
@@ -853,12 +950,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
     if (threadIdx.x == 0) {
         W.rowkey[b] = 0u;
         W.rmask[b] = 0u;
+        if (blockIdx.x == 0) *W.fbcnt = 0u;  // the full-row search queue
     }
-    const Mode md = row_mode(P, b);
-    if (!(md.tk || md.tp)) return;
-    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
     float smax;
-    const float t = row_estimate<DT, AL>(P, b, kk, S, smax);
+    bool active;
+    const float t = row_estimate<DT, AL>(P, b, S, smax, active);
+    if (!active) return;
     if (threadIdx.x == 0) {
         W.rowthr[b] = t;
         W.rowref[b] = xform<XF>(smax, 0u, P);
@@ -1764,57 +1861,66 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(SEL_THREADS, 4) void k_fix(KParams P, KPlan L, KWork W) {
     __shared__ SelShared S;
     extern __shared__ uint32_t bm[];  // penalty bitmap of one segment
-    const int tid = threadIdx.x;
-    const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
-    const Mode md = row_mode(P, b);
-    if (!(md.tk || md.tp)) return;
-    const int ns = L.nt * PASS_WAVES;  // wave sub-slots of the row
-    // sub-slots read in parallel: overflow flag and strict count
-    uint32_t o = 0, st_cnt = 0;
-    for (int i = tid; i < ns; i += SEL_THREADS) {
-        const uint32_t v = W.wcnt[b * ns + i];
-        if (v == 0xffffffffu) o = 1;
-        else st_cnt += v >> 16;
-    }
+    constexpr int RPW = SEL_THREADS / 64;  // rows per workgroup, one checked per wave
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ns = L.nt * PASS_WAVES;  // wave sub-slots of a row
+    {
+        // wave w checks row RPW * blockIdx + w: its sub-slots read in
+        // parallel for the overflow flag and the strict count
+        const int rb = (int)blockIdx.x * RPW + (tid >> 6);
+        uint32_t redo = 0;
+        if (rb < P.B) {
+            const int b = P.b0 + rb;
+            const Mode md = row_mode(P, b);
+            if (md.tk || md.tp) {
+                uint32_t o = 0, st_cnt = 0;
+                for (int i = lane; i < ns; i += 64) {
+                    const uint32_t v = W.wcnt[(int64_t)b * ns + i];
+                    if (v == 0xffffffffu) o = 1;
+                    else st_cnt += v >> 16;
+                }
 #pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) {
-        o |= shx(o, sft);
-        st_cnt += shx(st_cnt, sft);
-    }
-    if ((tid & 63) == 0) {
-        S.sc[tid >> 6] = o;
-        S.sc[8 + (tid >> 6)] = st_cnt;
+                for (int sft = 32; sft >= 1; sft >>= 1) {
+                    o |= shx(o, sft);
+                    st_cnt += shx(st_cnt, sft);
+                }
+                const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+                const float traw = W.rowthr[b];
+                // with traw = -inf every element was admitted, so no check
+                redo = (o != 0u || (traw > -INFINITY && st_cnt < kk)) ? 1u : 0u;
+            }
+        }
+        if (lane == 0) S.sc[tid >> 6] = redo;
     }
     __syncthreads();
-    bool ovf = false;
-    uint32_t strict = 0;
+    uint32_t flags = 0;
 #pragma unroll
-    for (int i = 0; i < SEL_THREADS / 64; ++i) {
-        ovf |= S.sc[i] != 0u;
-        strict += S.sc[8 + i];
-    }
+    for (int i = 0; i < RPW; ++i) flags |= (S.sc[i] != 0u ? 1u : 0u) << i;
     __syncthreads();
-    const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-    const float traw = W.rowthr[b];
-    // with traw = -inf every element was admitted, so no check is needed
-    if (!ovf && !(traw > -INFINITY && strict < kk)) return;
-
-    const void *rowp = row_ptr(P, DT, b);
-    Stats st;  // unused: the tile statistics come from the pass
-    st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
-    uint32_t tkey = 0, valid = 0;
-    int half = 0;
-    float hi = -INFINITY;
-    for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
-        const int s1 = min(s0 + K3_SEG, P.V);
-        if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, s0, s1 - s0, P, b);
-        select_exact<DT, AL, XF>(S, P, bm, rowp, s0, s1, kk, false, st, W.rowkey + b, tkey, half,
-                                 valid, hi);
-    }
-    copy_out(S, half, valid, tkey, W.rcand + (int64_t)b * SLOT);
-    if (tid == 0) {
-        W.rcnt[b] = (int32_t)S.kcnt;
-        W.rmask[b] = 1u;
+    // the rows to redo, one after another with the whole workgroup
+    for (int i = 0; i < RPW; ++i) {
+        if (!((flags >> i) & 1u)) continue;
+        const int b = P.b0 + (int)blockIdx.x * RPW + i;
+        const Mode md = row_mode(P, b);
+        const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
+        const void *rowp = row_ptr(P, DT, b);
+        Stats st;  // unused: the tile statistics come from the pass
+        st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
+        uint32_t tkey = 0, valid = 0;
+        int half = 0;
+        float hi = -INFINITY;
+        for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
+            const int s1 = min(s0 + K3_SEG, P.V);
+            if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, s0, s1 - s0, P, b);
+            select_exact<DT, AL, XF>(S, P, bm, rowp, s0, s1, kk, false, st, W.rowkey + b, tkey,
+                                     half, valid, hi);
+        }
+        copy_out(S, half, valid, tkey, W.rcand + (int64_t)b * SLOT);
+        if (tid == 0) {
+            W.rcnt[b] = (int32_t)S.kcnt;
+            W.rmask[b] = 1u;
+        }
+        __syncthreads();  // the next row reuses the shared buffers
     }
 }
 
@@ -1833,6 +1939,7 @@ constexpr int RCAP = 4096;       // candidates held in registers by the merge
 constexpr int NUC_STEPS = 16;    // top-p prefixes found without a sort, at most
 
 struct RowsShared {
+    uint32_t addr[RCAP];      // slot address of each candidate (in-register path)
     uint64_t srt[KMAX];       // the kk selected
     uint64_t nuc[NUC_STEPS];  // a short top-p prefix, in order
     uint32_t hist[256];
@@ -1935,49 +2042,59 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
     const ChunkStat *cst = W.cstat + (int64_t)b * nt;
 
-    // merged tile statistics, the tiles read in parallel
-    float m_loc = -INFINITY, mn_loc = INFINITY;
-    for (int t = tid; t < nt; t += NT) {
-        m_loc = fmaxf(m_loc, cst[t].m);
-        mn_loc = fminf(mn_loc, cst[t].xmin);
-    }
+    // merged wave statistics (max, min, sum of exp), the records read in
+    // parallel; rows with top-k need none of them
+    auto merge_stats = [&](float &M, float &XMIN, double &Z) {
+        float m_loc = -INFINITY, mn_loc = INFINITY;
+        for (int t = tid; t < nt; t += NT) {
+            m_loc = fmaxf(m_loc, cst[t].m);
+            mn_loc = fminf(mn_loc, cst[t].xmin);
+        }
 #pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) {
-        m_loc = fmaxf(m_loc, shxf(m_loc, sft));
-        mn_loc = fminf(mn_loc, shxf(mn_loc, sft));
-    }
-    if ((tid & 63) == 0) {
-        S.scd[tid >> 6] = m_loc;
-        S.scd[8 + (tid >> 6)] = mn_loc;
-    }
-    __syncthreads();
-    float M = -INFINITY, XMIN = INFINITY;
+        for (int sft = 32; sft >= 1; sft >>= 1) {
+            m_loc = fmaxf(m_loc, shxf(m_loc, sft));
+            mn_loc = fminf(mn_loc, shxf(mn_loc, sft));
+        }
+        if ((tid & 63) == 0) {
+            S.scd[tid >> 6] = m_loc;
+            S.scd[8 + (tid >> 6)] = mn_loc;
+        }
+        __syncthreads();
+        M = -INFINITY;
+        XMIN = INFINITY;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-        M = fmaxf(M, (float)S.scd[i]);
-        XMIN = fminf(XMIN, (float)S.scd[8 + i]);
-    }
-    __syncthreads();
-    double z_loc = 0.0;
-    for (int t = tid; t < nt; t += NT) {
-        const ChunkStat cs = cst[t];
-        if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
-    }
-    const double Z = wg_sum_f64<NT>(z_loc, S.scd);
+        for (int i = 0; i < NT / 64; ++i) {
+            M = fmaxf(M, (float)S.scd[i]);
+            XMIN = fminf(XMIN, (float)S.scd[8 + i]);
+        }
+        __syncthreads();
+        double z_loc = 0.0;
+        for (int t = tid; t < nt; t += NT) {
+            const ChunkStat cs = cst[t];
+            if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
+        }
+        Z = wg_sum_f64<NT>(z_loc, S.scd);
+    };
 
     RowInfo info;
     info.kind = KIND_UNFILTERED;
     info.nK = P.V;
     info.T = 0;
-    info.ZK = Z;
-    info.m = M;
-    info.xmin = XMIN;
+    info.ZK = 0.0;
+    info.m = -INFINITY;
+    info.xmin = INFINITY;
     info.idx0 = NONE;
     info.pad = 0;
 
     if (!filtered) {
         // merge the tiles' winners: the race by ratio (lowest id on a tie),
         // the argmax by (value, lowest id)
+        float M, XMIN;
+        double Z;
+        merge_stats(M, XMIN, Z);
+        info.ZK = Z;
+        info.m = M;
+        info.xmin = XMIN;
         uint32_t idx;
         if (md.sm) {
             float xr_loc = -INFINITY;
@@ -2062,23 +2179,47 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     };
 
     // ---- the kk largest (exactly, under the composite order) into srt.  Up
-    // to RCAP candidates are held in registers, RCAP / NT per thread; more
-    // (rare) are selected by passes over the slots themselves.
+    // to RCAP candidates are held in registers, RCAP / NT per thread, loaded
+    // before the statistics are merged so that their latency overlaps it;
+    // more (rare) are selected by passes over the slots themselves.
     const uint32_t nsel = min(kk, N);
-    if (N <= (uint32_t)RCAP) {
-        constexpr int R = RCAP / NT;
-        uint64_t v[R];
-        uint32_t vm = 0;
+    const bool inreg = N <= (uint32_t)RCAP;
+    constexpr int R = RCAP / NT;
+    uint64_t v[R];
+    uint32_t vm = 0;
+    if (inreg) {
+        if (!redone) {
+            // where candidate e lives, written slot by slot (a lookup per
+            // candidate instead of a search over the slot offsets)
+            for (int t = tid; t < nt; t += NT) {
+                const uint32_t e0 = toff[t], e1 = toff[t + 1];
+                for (uint32_t e = e0; e < e1; ++e) S.addr[e] = (uint32_t)t * tcap + (e - e0);
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t e = (uint32_t)(r * NT + tid);
-            v[r] = e < N ? gget(e) : 0ull;
-            if (e < N) vm |= 1u << r;
+            if (e < N) {
+                v[r] = redone ? redc[e] : rowc[S.addr[e]];
+                vm |= 1u << r;
+            } else {
+                v[r] = 0ull;
+            }
         }
+    }
+    float M = -INFINITY, XMIN = INFINITY;
+    double Z = 0.0;
+    if (!md.tk) merge_stats(M, XMIN, Z);
+    info.ZK = Z;
+    info.m = M;
+    info.xmin = XMIN;
+    if (inreg) {
         uint32_t km = vm;
         if (N > kk) {
             uint64_t prefix, pmask;
-            wg_radix_select<NT, R>(v, vm, kk, S.hist, S.sel, S.sc64, prefix, pmask);
+            wg_radix_select<NT, R>(v, vm, kk, S.hist, S.sel, S.sc64, S.srt, KMAX, &S.sel[3],
+                                   prefix, pmask);
             km = 0;
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -2095,8 +2236,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         if (tid == 0) S.cnt = 0;
         __syncthreads();
         for (uint32_t e = tid; e < N; e += NT) {
-            const uint64_t v = gget(e);
-            if ((v & pmask) >= prefix) S.srt[atomicAdd(&S.cnt, 1u)] = v;
+            const uint64_t c = gget(e);
+            if ((c & pmask) >= prefix) S.srt[atomicAdd(&S.cnt, 1u)] = c;
         }
     }
     __syncthreads();
@@ -2219,7 +2360,10 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.idx0 = cidx(top);
     if (!settled) {
         info.kind = KIND_FALLBACK;
-        if (tid == 0) W.info[b] = info;
+        if (tid == 0) {
+            W.info[b] = info;
+            W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
+        }
         return;
     }
     __syncthreads();
@@ -2429,9 +2573,11 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
-    const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
+    // the rows the merge queued, spread over the workgroups
+    const uint32_t nq = *W.fbcnt;
+    for (uint32_t qi = blockIdx.x; qi < nq; qi += gridDim.x) {
+    const int b = (int)W.fblist[qi];
     RowInfo info = W.info[b];
-    if (info.kind != KIND_FALLBACK) return;
     const Mode md = row_mode(P, b);
     const double m = (double)info.m;
 
@@ -2634,6 +2780,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         info.ZK = ZK;
         W.info[b] = info;
     }
+    __syncthreads();  // the next row reuses the shared buffers
+    }
 }
 
 // ================================================================== k_dense
@@ -2649,21 +2797,24 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 constexpr int DENSE_THREADS = 256;
 
 struct DenseShared {
-    uint32_t tb[SEG_MAX / 32];    // kept positions in the tile
-    uint32_t wpre[SEG_MAX / 32];  // set bits before each word
-    float lval[KMAX];             // kept values by rank
-    uint64_t kv[KMAX];            // the tile's kept entries
+    float lval[KMAX];  // the tile's kept values by rank
     uint32_t sc[16];
 };
 
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
     __shared__ DenseShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
+    // tile bitmap and per-word ranks of listed rows (2 x seg / 32 words), or
+    // the penalty bitmap of threshold rows
+    extern __shared__ uint32_t dyn[];
     constexpr int NT = DENSE_THREADS;
     const int tid = threadIdx.x;
     const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
     const int t0 = t * L.seg, t1 = min(t0 + L.seg, P.V);
+    // the tile's range of the kept list, requested with the row's kind (a
+    // row without a list ignores it)
+    const uint32_t *kto = W.ktoff + (int64_t)b * (L.nt + 1);
+    const uint32_t k0r = kto[t], k1r = kto[t + 1];
     const RowInfo info = W.info[b];
     float *ol = (P.out_logits && info.kind != KIND_UNFILTERED)
                     ? P.out_logits + (int64_t)b * P.V : nullptr;
@@ -2674,42 +2825,53 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
 
     if (info.kind == KIND_LIST) {
         const int nw = (t1 - t0 + 31) / 32;  // bitmap words
-        // the tile's kept entries (the merge grouped them by tile), staged
-        const uint32_t *kto = W.ktoff + (int64_t)b * (L.nt + 1);
-        const int k0 = (int)kto[t], k1 = (int)kto[t + 1];
+        uint32_t *tb = dyn;                  // kept positions in the tile
+        uint32_t *wpre = dyn + nw;           // set bits before each word
+        const int k0 = (int)min(k0r, (uint32_t)KMAX);
+        const int k1 = (int)min(max(k1r, (uint32_t)k0), (uint32_t)KMAX);
         const uint64_t *kl = W.klist + (int64_t)b * KMAX;
-        for (int w = tid; w < nw; w += NT) S.tb[w] = 0u;
-        for (int i = k0 + tid; i < k1; i += NT) S.kv[i - k0] = kl[i];
-        __syncthreads();
-        const int nk = k1 - k0;
-        for (int i = tid; i < nk; i += NT) {
-            const int r = (int)cidx(S.kv[i]) - t0;
-            atomicOr(&S.tb[r >> 5], 1u << (r & 31));
+        // the tile's kept entries (the merge grouped them by tile), at most
+        // KMAX / NT per thread
+        constexpr int KR = KMAX / NT;
+        uint64_t kv[KR];
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const int i = k0 + r * NT + tid;
+            kv[r] = i < k1 ? kl[i] : 0ull;
         }
+        for (int w = tid; w < nw; w += NT) tb[w] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+            if (k0 + r * NT + tid < k1) {
+                const int rr = (int)cidx(kv[r]) - t0;
+                atomicOr(&tb[rr >> 5], 1u << (rr & 31));
+            }
         __syncthreads();
         // ranks: set bits before each word (words split evenly over threads)
         const int per = (nw + NT - 1) / NT;
         uint32_t cnt = 0;
         for (int i = 0; i < per; ++i) {
             const int w = tid * per + i;
-            if (w < nw) cnt += __popc(S.tb[w]);
+            if (w < nw) cnt += __popc(tb[w]);
         }
         uint32_t tot;
         uint32_t run = wg_excl_scan_u32<NT>(cnt, S.sc, tot);
         for (int i = 0; i < per; ++i) {
             const int w = tid * per + i;
             if (w < nw) {
-                S.wpre[w] = run;
-                run += __popc(S.tb[w]);
+                wpre[w] = run;
+                run += __popc(tb[w]);
             }
         }
         __syncthreads();
-        for (int i = tid; i < nk; i += NT) {
-            const uint64_t cv = S.kv[i];
-            const int r = (int)cidx(cv) - t0;
-            const uint32_t below = S.tb[r >> 5] & ((1u << (r & 31)) - 1u);
-            S.lval[S.wpre[r >> 5] + __popc(below)] = cval(cv);
-        }
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+            if (k0 + r * NT + tid < k1) {
+                const int rr = (int)cidx(kv[r]) - t0;
+                const uint32_t below = tb[rr >> 5] & ((1u << (rr & 31)) - 1u);
+                S.lval[wpre[rr >> 5] + __popc(below)] = cval(kv[r]);
+            }
         __syncthreads();
         // whole lines: each lane writes 8 consecutive floats (two 16-byte
         // stores), the pattern that sustains the highest write rate
@@ -2720,13 +2882,13 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
             const int j = t0 + r0;
             const int nv = group_nv(j, t1);
             if (nv == 0) continue;
-            const uint32_t word = S.tb[r0 >> 5];
+            const uint32_t word = tb[r0 >> 5];
             const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
             float xv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[i] = -INFINITY;
             if (bits) {
-                uint32_t k = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
+                uint32_t k = wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     if ((bits >> i) & 1u) xv[i] = S.lval[k++];
@@ -2744,6 +2906,7 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
     }
     if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
     // K = { comp >= T } (T = 0 keeps the whole row): re-read the tile
+    uint32_t *bm = dyn;
     if (XF && P.pen) build_bitmap<NT>(bm, t0, t1 - t0, P, b);
     const void *rowp = row_ptr(P, DT, b);
     const uint64_t T = info.T;
@@ -2812,7 +2975,8 @@ hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dty
 hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                       hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)p.B), block(SEL_THREADS);
+    constexpr int RPW = SEL_THREADS / 64;  // rows per workgroup
+    dim3 grid((unsigned)((p.B + RPW - 1) / RPW)), block(SEL_THREADS);
     size_t sh = p.pen ? (size_t)(K3_SEG / 32) * 4 : 0;
     return SMP_PICK(k_fix, grid, block, sh);
 }
@@ -2825,7 +2989,9 @@ hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStre
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                            hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)p.B), block(K3_THREADS);
+    // one workgroup per CU (its LDS allows no more); queued rows are spread
+    // over them, none queued costs one read per workgroup
+    dim3 grid((unsigned)std::min(p.B, 256)), block(K3_THREADS);
     return SMP_PICK(k_fallback, grid, block, 0);
 }
 
@@ -2833,7 +2999,7 @@ hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dt
                         hipStream_t s) {
     const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(DENSE_THREADS);
-    size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
+    size_t sh = (size_t)((l.seg + 31) / 32) * 2 * 4;  // tile bitmap + ranks
     return SMP_PICK(k_dense, grid, block, sh);
 }
 
