@@ -1,3 +1,4 @@
+#include <algorithm>
 // C ABI of the batched logits sampler: argument checks, workspace, planning
 // and kernel launches.  The operation itself is defined in sampler.h.
 #include <math.h>
@@ -17,6 +18,7 @@ constexpr int PROF_RING = 64;
 
 struct sampler_s {
     int32_t max_batch;
+    int32_t rows_per_launch;  // 0 = automatic
     int32_t vocab;
     int32_t dtype;
     int32_t guess;
@@ -70,15 +72,17 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     *h = nullptr;
     if (max_batch < 1 || vocab < 1 || vocab > SAMPLER_VOCAB_MAX) return SAMPLER_EINVAL;
     if (dtype != SAMPLER_F32 && dtype != SAMPLER_BF16) return SAMPLER_EINVAL;
-    int32_t guess = DEFAULT_GUESS, seg = SEG_DEFAULT;
+    int32_t guess = DEFAULT_GUESS, seg = SEG_DEFAULT, rpl = 0;
     if (opts) {
         if (opts->topk_guess < 0 || opts->topk_guess > SAMPLER_TOPK_MAX) return SAMPLER_EINVAL;
         if (opts->segment_len != 0 &&
             (opts->segment_len < SEG_MIN || opts->segment_len > SEG_MAX ||
              opts->segment_len % SEG_MIN != 0))
             return SAMPLER_EINVAL;
+        if (opts->rows_per_launch < 0) return SAMPLER_EINVAL;
         if (opts->topk_guess) guess = opts->topk_guess;
         if (opts->segment_len) seg = opts->segment_len;
+        rpl = opts->rows_per_launch;
     }
     const KPlan plan = make_plan(vocab, seg);
 
@@ -89,6 +93,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->dtype = dtype;
     s->guess = guess;
     s->seg = seg;
+    s->rows_per_launch = rpl;
     if (hipGetDevice(&s->device) != hipSuccess) {
         delete s;
         return SAMPLER_EHIP;
@@ -225,37 +230,53 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     };
     const bool filtering = a->top_k != nullptr || a->top_p != nullptr;
 
-    hipError_t e;
+    // Rows go in chunks small enough for every grid (at most 2^23 workgroups
+    // of at most 1024 threads); each kernel runs over all chunks before the
+    // next kernel starts, so the per-kernel profile spans stay contiguous.
+    const int64_t max_wg = (int64_t)1 << 23;
+    int64_t lim = std::max<int64_t>(1, max_wg / l.nt);
+    if (h->rows_per_launch > 0) lim = std::min<int64_t>(lim, h->rows_per_launch);
+    const int chunk = (int)std::min<int64_t>(batch, lim);
+    auto each = [&](auto &&launcher) -> bool {
+        for (int c0 = 0; c0 < batch; c0 += chunk) {
+            KParams pc = p;
+            pc.b0 = c0;
+            pc.B = std::min(chunk, batch - c0);
+            if (launcher(pc) != hipSuccess) return false;
+        }
+        return true;
+    };
+
     mark(0);
     if (filtering) {
-        e = launch_plan(p, l, h->ws, h->dtype, al, st);
-        if (e != hipSuccess) return SAMPLER_EHIP;
+        if (!each([&](const KParams &pc) { return launch_plan(pc, l, h->ws, h->dtype, al, st); }))
+            return SAMPLER_EHIP;
         launched[0] = true;
     }
     mark(1);
-    e = launch_pass(p, l, h->ws, h->dtype, al, st);
-    if (e != hipSuccess) return SAMPLER_EHIP;
+    if (!each([&](const KParams &pc) { return launch_pass(pc, l, h->ws, h->dtype, al, st); }))
+        return SAMPLER_EHIP;
     launched[1] = true;
     mark(2);
     if (filtering) {
-        e = launch_fix(p, l, h->ws, h->dtype, al, st);
-        if (e != hipSuccess) return SAMPLER_EHIP;
+        if (!each([&](const KParams &pc) { return launch_fix(pc, l, h->ws, h->dtype, al, st); }))
+            return SAMPLER_EHIP;
         launched[2] = true;
     }
     mark(3);
-    e = launch_rows(p, l, h->ws, st);
-    if (e != hipSuccess) return SAMPLER_EHIP;
+    if (!each([&](const KParams &pc) { return launch_rows(pc, l, h->ws, st); }))
+        return SAMPLER_EHIP;
     launched[3] = true;
     mark(4);
     if (a->top_p != nullptr) {
-        e = launch_fallback(p, l, h->ws, h->dtype, al, st);
-        if (e != hipSuccess) return SAMPLER_EHIP;
+        // one launch over the queue the merge filled, whatever the chunks
+        if (launch_fallback(p, l, h->ws, h->dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
         launched[4] = true;
     }
     mark(5);
     if (p.out_probs || (p.out_logits && filtering)) {
-        e = launch_dense(p, l, h->ws, h->dtype, al, st);
-        if (e != hipSuccess) return SAMPLER_EHIP;
+        if (!each([&](const KParams &pc) { return launch_dense(pc, l, h->ws, h->dtype, al, st); }))
+            return SAMPLER_EHIP;
         launched[5] = true;
     }
     mark(6);

@@ -950,7 +950,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
     if (threadIdx.x == 0) {
         W.rowkey[b] = 0u;
         W.rmask[b] = 0u;
-        if (blockIdx.x == 0) *W.fbcnt = 0u;  // the full-row search queue
+        if (b == 0) *W.fbcnt = 0u;  // the full-row search queue (first chunk)
     }
     float smax;
     bool active;
@@ -2252,6 +2252,15 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         v4[i] = p < nsel ? S.srt[p] : 0ull;
         mxv = v4[i] > mxv ? v4[i] : mxv;
     }
+    // a sampling row without top-p keeps the whole selection: q at its
+    // entries is requested now, so that the gather overlaps what follows
+    const bool early_q = md.sm && !md.tp;
+    float qv4[4];
+    if (early_q) {
+        const float *rowq = P.q + (int64_t)b * P.V;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv4[i] = (4 * tid + i < nsel) ? rowq[cidx(v4[i])] : 1.0f;
+    }
     const uint64_t top = wg_max_u64<NT>(mxv, S.sc64);
     const float x0 = cval(top);
     double loc = 0.0;
@@ -2377,12 +2386,27 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     uint64_t *kl = W.klist + (int64_t)b * KMAX;
     constexpr int KR = KMAX / NT;
     float qv[KR];
-    if (md.sm) {
+    if (md.sm && !early_q) {
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const uint32_t p = (uint32_t)(r * NT + tid);
             qv[r] = p < nK ? P.q[(int64_t)b * P.V + cidx(kp[p])] : 1.0f;
         }
+    }
+    if (early_q) {
+        // K is the whole selection: each thread races its own entries
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * tid + i < nsel) {
+                const uint32_t id = cidx(v4[i]);
+                const double ei = exp((double)cval(v4[i]) - (double)x0);
+                const double den = (double)qv4[i] + (double)P.eps;
+                const double rr = (ei == 0.0) ? 0.0 : ei / den;
+                if (rr > rbest || (rr == rbest && id < ibest)) {
+                    rbest = rr;
+                    ibest = id;
+                }
+            }
     }
     // the kept list goes out grouped by tile (any order within a tile), so
     // that each dense-writer workgroup reads only its own entries; toff (no
@@ -2425,7 +2449,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             const uint32_t id = cidx(v);
             const double ei = exp((double)cval(v) - (double)x0);
             zk += ei;
-            if (md.sm) {
+            if (md.sm && !early_q) {
                 const double den = (double)qv[r] + (double)P.eps;
                 const double rr = (ei == 0.0) ? 0.0 : ei / den;
                 if (rr > rbest || (rr == rbest && id < ibest)) {

@@ -34,7 +34,8 @@ class SamplerError(RuntimeError):
 
 
 class sampler_opts(ctypes.Structure):
-    _fields_ = [("topk_guess", ctypes.c_int32), ("segment_len", ctypes.c_int32)]
+    _fields_ = [("topk_guess", ctypes.c_int32), ("segment_len", ctypes.c_int32),
+                ("rows_per_launch", ctypes.c_int32)]
 
 
 class sampler_args(ctypes.Structure):
@@ -96,11 +97,11 @@ def sampler_strerror(code: int) -> str:
 
 
 def sampler_create(max_batch: int, vocab: int, dtype: int, topk_guess: int = 0,
-                   segment_len: int = 0) -> ctypes.c_void_p:
+                   segment_len: int = 0, rows_per_launch: int = 0) -> ctypes.c_void_p:
     """sampler_create on the current HIP device; returns the handle."""
     lib = load_library()
     h = ctypes.c_void_p()
-    opts = sampler_opts(int(topk_guess), int(segment_len))
+    opts = sampler_opts(int(topk_guess), int(segment_len), int(rows_per_launch))
     rc = lib.sampler_create(ctypes.byref(h), int(max_batch), int(vocab), int(dtype),
                             ctypes.byref(opts))
     if rc != SAMPLER_OK:
@@ -196,13 +197,14 @@ class Sampler:
     """Owns one handle; ``run`` marshals tensors and calls sampler_run."""
 
     def __init__(self, max_batch: int, vocab: int, dtype, topk_guess: int = 0,
-                 segment_len: int = 0):
+                 segment_len: int = 0, rows_per_launch: int = 0):
         import torch
 
         dt = SAMPLER_BF16 if dtype in (torch.bfloat16, SAMPLER_BF16, "bf16") else SAMPLER_F32
         self.vocab = int(vocab)
         self.dtype = dt
-        self.handle = sampler_create(max_batch, vocab, dt, topk_guess, segment_len)
+        self.handle = sampler_create(max_batch, vocab, dt, topk_guess, segment_len,
+                                     rows_per_launch)
 
     def run(self, logits, out_idx, stream=None, **kw) -> None:
         args = make_args(logits, out_idx, **kw)

@@ -81,6 +81,10 @@ typedef struct sampler_opts {
      * Ascend page's rolling top-k uses segments of 8192).  0 = default
      * (8192); otherwise a multiple of 1024 in [1024, 32768]. */
     int32_t segment_len;
+    /* Most rows per kernel launch: a call with more rows runs each kernel
+     * over consecutive chunks of rows (in order, on the same stream).  0 =
+     * automatic (as many as the launch limits allow); otherwise >= 1. */
+    int32_t rows_per_launch;
 } sampler_opts;
 
 /*

@@ -46,7 +46,7 @@ def device_inputs(W, ld_pad=0):
 
 
 def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sampler=None,
-            inputs=None):
+            inputs=None, rpl=0):
     import torch
 
     from decode_token_sampling_row_amd.sampler import Sampler
@@ -58,7 +58,7 @@ def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sam
     out_l = torch.full((B, V), 12345.0, dtype=torch.float32, device=dev) if need_logits else None
     out_p = torch.full((B, V), -1.0, dtype=torch.float32, device=dev) if need_probs else None
     s = sampler or Sampler(max(B, 1), V, torch.bfloat16 if W.dtype == wl.BF16 else torch.float32,
-                           topk_guess=guess, segment_len=seg)
+                           topk_guess=guess, segment_len=seg, rows_per_launch=rpl)
     s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"], eps=W.eps,
           temperature=W.temperature, repetition_penalty=W.penalty,
           penalty_ids=d["penalty_ids"], penalty_offsets=d["penalty_offsets"],

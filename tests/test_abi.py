@@ -50,6 +50,8 @@ def test_args_struct_layout_matches_header():
     #define O(f) printf("%zu ", offsetof(sampler_args, f))
     int main(void) {
       printf("%zu %zu ", sizeof(sampler_args), sizeof(sampler_opts));
+      printf("%zu %zu %zu ", offsetof(sampler_opts, topk_guess), offsetof(sampler_opts, segment_len),
+             offsetof(sampler_opts, rows_per_launch));
       O(logits); O(ld); O(top_k); O(top_p); O(q); O(eps); O(temperature);
       O(repetition_penalty); O(penalty_ids); O(penalty_offsets); O(row_flags);
       O(flags); O(out_idx); O(out_logits); O(out_probs);
@@ -64,8 +66,9 @@ def test_args_struct_layout_matches_header():
         got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
                                               check=True).stdout.split()]
     A = smp.sampler_args
-    want = [ctypes.sizeof(A), ctypes.sizeof(smp.sampler_opts)] + [getattr(A, f).offset
-                                                                   for f, _ in A._fields_]
+    O = smp.sampler_opts
+    want = ([ctypes.sizeof(A), ctypes.sizeof(O)] + [getattr(O, f).offset for f, _ in O._fields_]
+            + [getattr(A, f).offset for f, _ in A._fields_])
     assert got == want
 
 
@@ -89,8 +92,9 @@ def test_create_rejects_bad_arguments_before_touching_the_gpu(lib):
     bad = [(0, 10, 0), (-1, 10, 0), (4, 0, 0), (4, (1 << 21) + 1, 0), (4, 10, 2), (4, 10, -1)]
     for mb, v, dt in bad:
         assert lib.sampler_create(ctypes.byref(h), mb, v, dt, None) == smp.SAMPLER_EINVAL
-    for g, c in [(-1, 0), (1025, 0), (0, 512), (0, -1024), (0, 1500), (0, 33792)]:
-        o = smp.sampler_opts(g, c)
+    for g, c, r in [(-1, 0, 0), (1025, 0, 0), (0, 512, 0), (0, -1024, 0), (0, 1500, 0),
+                    (0, 33792, 0), (0, 0, -1)]:
+        o = smp.sampler_opts(g, c, r)
         assert lib.sampler_create(ctypes.byref(h), 4, 100, 0, ctypes.byref(o)) == smp.SAMPLER_EINVAL
     assert lib.sampler_create(None, 4, 100, 0, None) == smp.SAMPLER_EINVAL
 

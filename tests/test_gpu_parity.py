@@ -164,6 +164,23 @@ def test_knobs_do_not_change_results(guess, seg):
     np.testing.assert_allclose(base["probs"], other["probs"], rtol=1e-6, atol=1e-12)
 
 
+@pytest.mark.parametrize("rpl", [1, 5])
+def test_rows_per_launch_changes_nothing(rpl):
+    # flat top-p rows (the full-row search queue fills across chunks), rows
+    # whose sample overstates the row (exact re-selection), greedy and
+    # sample-only rows, in chunks of rpl rows
+    W = wl.make(3, B=12, V=20000, seed=9)
+    W.row_flags = np.array([2, 6, 3, 7, 0, 4, 1, 5, 2, 6, 2, 6], np.uint8)
+    W.top_k = np.array([0, 0, 40, 1024, 0, 0, 77, 5, 0, 0, 0, 0], np.int32)
+    print(f"[case] rows_per_launch={rpl} B={W.B} V={W.V}", flush=True)
+    base = run_hip(W, need_logits=True, need_probs=True)
+    other = run_hip(W, need_logits=True, need_probs=True, rpl=rpl)
+    np.testing.assert_array_equal(base["idx"], other["idx"])
+    np.testing.assert_array_equal(base["logits"].view(np.uint32), other["logits"].view(np.uint32))
+    np.testing.assert_array_equal(base["probs"].view(np.uint32), other["probs"].view(np.uint32))
+    compare(W, other, run_oracle(W, need_logits=True), label=f"rpl={rpl}")
+
+
 def test_repeated_runs_bit_identical():
     import torch
 
