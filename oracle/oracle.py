@@ -49,7 +49,7 @@ def _load():
         lib.oracle_run.restype = ctypes.c_int
         lib.oracle_run.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64,
-            P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P,
+            P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P, P,
             ctypes.c_uint32, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32]
         _lib = lib
     return _lib
@@ -67,13 +67,15 @@ def _arr(a, dtype):
 
 def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
         temperature=1.0, penalty=1.0, ids=None, offsets=None, row_flags=None,
-        need_logits=True, need_probs=False, rows=None, threads=1):
+        need_logits=True, need_probs=False, rows=None, threads=1, u=None):
     """Run the oracle.
 
     logits: [B, ld] float32 (dtype F32) or uint16 bf16 bit patterns (BF16);
     vocab: V <= ld (default ld).
     rows: optional iterable of row indices to compute (others are left as
     zeros / -1); used to sample rows of large workloads.
+    u: optional [B] uniforms; sampling rows then draw by inverse CDF (and
+    ``gap`` holds that decision's margin) instead of racing with q.
     Returns a dict with idx [B] int64, logits [B, V] float32 or None,
     probs [B, V] float32 or None, nkept [B] int32, margin [B], gap [B].
     """
@@ -90,6 +92,9 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
     top_k = _arr(top_k, np.int32)
     top_p = _arr(top_p, np.float32)
     q = _arr(q, np.float32)
+    u = _arr(u, np.float32)
+    if u is not None:
+        assert u.shape == (B,)
     ids = _arr(ids, np.int32)
     offsets = _arr(offsets, np.int64)
     row_flags = _arr(row_flags, np.uint8)
@@ -104,7 +109,7 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
 
     def call(r0, r1):
         rc = lib.oracle_run(B, V, dtype, _ptr(logits), ld, _ptr(top_k), _ptr(top_p),
-                            _ptr(q), eps, temperature, penalty, _ptr(ids),
+                            _ptr(q), _ptr(u), eps, temperature, penalty, _ptr(ids),
                             _ptr(offsets), _ptr(row_flags), flags, _ptr(out_idx),
                             _ptr(out_logits), _ptr(out_probs), _ptr(nkept),
                             _ptr(margin), _ptr(gap), r0, r1)

@@ -41,6 +41,14 @@
  *       (Ascend page, Sample section: probs/(q+eps), argmax, gather through
  *       logits_idx; q paired with candidates by vocab id -- a reading).
  *       Sampling off: the output is K_0, the greedy argmax (MiniMind 10.8).
+ *   O9' sample by inverse CDF instead (row bit2 and uniforms u given; q is
+ *       not used): the output is K_{n-1} for the least n >= 1 whose
+ *       inclusive cumulative probability S_n = sum_{i<n} pi_i reaches u[b];
+ *       u <= 0 or NaN gives n = 1, and when rounding leaves S_|K| below u
+ *       the last element of K is taken.  (MiniMind sec. 10.8 draws the
+ *       token from the filtered softmax with torch.multinomial; with the
+ *       caller's uniform this is that draw made by inverse CDF in the
+ *       order of O4 -- a reading of how the draw is made.)
  *   O10 dense filtered logits: x_j at K, -inf elsewhere  (Ascend page,
  *       logits_top_kp_select scatter; MiniMind -inf masking)
  *   O11 dense probabilities: fp32(pi) at K, 0 elsewhere.
@@ -50,7 +58,9 @@
  *   margin  top-p decision margin min(S_n* - p, p - S_{n*-1}) (n* > 1),
  *           S_1 - p (n* = 1), +inf when top-p is off
  *   gap     (r1 - r2) / r1 over the two largest ratios, +inf when there is
- *           no sampling or a single candidate
+ *           no sampling or a single candidate; for inverse-CDF sampling the
+ *           decision margin min(S_n - u, u - S_{n-1}) instead (+inf when
+ *           n = 1 by u <= 0)
  *
  * Build:  gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
  *         -o liboracle.so sampler_oracle.c -lm
@@ -129,13 +139,15 @@ static void row_transform(float *x, int32_t V, int32_t dtype, const void *logits
 /*
  * Process rows [row_begin, row_end).  Pointers are host pointers with the
  * layouts of the library's sampler_args: logits [B, ld] (fp32 or bf16 bits),
- * top_k [B], top_p [B], q [B, V], ids/offsets CSR history, row_flags [B]
+ * top_k [B], top_p [B], q [B, V], u [B] (NULL = sampling by the exponential
+ * race with q), ids/offsets CSR history, row_flags [B]
  * (NULL = all stages on), out_idx [B], out_logits / out_probs [B, V] (may be
  * NULL), nkept / margin / gap [B] (may be NULL).
  * Returns 0, or -1 on an allocation failure or a bad argument.
  */
 int oracle_run(int32_t B, int32_t V, int32_t dtype, const void *logits, int64_t ld,
-               const int32_t *top_k, const float *top_p, const float *q, float eps,
+               const int32_t *top_k, const float *top_p, const float *q, const float *u,
+               float eps,
                float temperature, float rho, const int32_t *ids,
                const int64_t *offsets, const uint8_t *row_flags, uint32_t flags,
                int64_t *out_idx, float *out_logits, float *out_probs,
@@ -210,10 +222,29 @@ int oracle_run(int32_t B, int32_t V, int32_t dtype, const void *logits, int64_t 
         double ZK = 0.0;
         for (int32_t i = 0; i < nK; i++) ZK += e[i];
 
-        /* O9: exponential-race sample, or greedy K_0. */
+        /* O9: exponential-race sample, O9': inverse-CDF sample, or greedy K_0. */
         int64_t idx = ord[0].id;
         double g = INFINITY;
-        if ((rf & ROW_SAMPLE) && q != NULL) {
+        if ((rf & ROW_SAMPLE) && u != NULL) {
+            double uu = (double)u[b];
+            int32_t n = 1;
+            if (uu > 0.0) {
+                double S = 0.0, S_prev = 0.0;
+                n = nK;
+                for (int32_t i = 1; i <= nK; i++) {
+                    S_prev = S;
+                    S += e[i - 1] / ZK;
+                    if (S >= uu) {
+                        n = i;
+                        break;
+                    }
+                }
+                g = S - uu;
+                if (n > 1 && uu - S_prev < g) g = uu - S_prev;
+                if (g < 0.0) g = 0.0; /* rounding left S_|K| below u */
+            }
+            idx = ord[n - 1].id;
+        } else if ((rf & ROW_SAMPLE) && q != NULL) {
             double r1 = -1.0, r2 = -1.0;
             int32_t best = -1;
             for (int32_t i = 0; i < nK; i++) {

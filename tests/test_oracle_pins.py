@@ -343,6 +343,78 @@ def test_exponential_race_law(k, p):
     assert ok, (stat, counts, pk * n)
 
 
+@pytest.mark.parametrize("k,p", [(0, 1.0), (3, 1.0), (4, 0.7)])
+def test_inverse_cdf_law(k, p):
+    """With u ~ U(0, 1), the inverse-CDF draw picks i with probability pi_i
+    (MiniMind sec. 10.8: a multinomial draw from the filtered softmax)."""
+    x = np.array([1.0, 0.5, 0.0, -0.5, 2.0, 0.25], np.float32)
+    n = 60000
+    rng = np.random.default_rng(610)
+    X = np.tile(x, (n, 1))
+    u = rng.random(n).astype(np.float32)
+    flags = SAMPLE | (TOPK if k else 0) | (TOPP if p < 1 else 0)
+    r = run_f32(X, flags, top_k=k, top_p=p, u=u, need_logits=False, threads=4)
+    order = sorted(range(x.size), key=lambda i: (-x[i], i))
+    cand = order[:k] if k else order
+    w = np.exp(x[cand].astype(np.float64) - x[cand[0]])
+    mass = np.cumsum(w) / w.sum()
+    nk = len(cand) if p >= 1 else int(np.argmax(mass >= p)) + 1
+    keep = cand[:nk]
+    pk = w[:nk] / w[:nk].sum()
+    counts = np.array([np.sum(r["idx"] == i) for i in keep], np.float64)
+    assert counts.sum() == n
+    ok, stat = _chi2_ok(counts, pk, n)
+    assert ok, (stat, counts, pk * n)
+
+
+def test_inverse_cdf_maps_u_intervals_of_length_pi():
+    """Sweeping u over a fine grid, each kept element is drawn on one interval
+    of u, in the row's order, whose length is its probability."""
+    rng = np.random.default_rng(611)
+    x = rng.normal(0.0, 1.0, 40).astype(np.float32)
+    x[[3, 9, 17]] = x[5]  # ties: equal values go to the smaller id first
+    g = 20001
+    u = ((np.arange(g) + 0.5) / g).astype(np.float32)
+    X = np.tile(x, (g, 1))
+    r = run_f32(X, TOPK | SAMPLE, top_k=12, u=u, need_logits=False, need_probs=True)
+    order = sorted(range(x.size), key=lambda i: (-x[i], i))
+    pos = {v: n for n, v in enumerate(order)}
+    drawn = np.array([pos[int(i)] for i in r["idx"]])
+    assert np.all(np.diff(drawn) >= 0)  # non-decreasing position in the order
+    assert drawn.max() <= 11
+    probs = r["probs"][0]
+    for n, i in enumerate(order[:12]):
+        width = np.sum(drawn == n) / g
+        assert abs(width - probs[i]) <= 2.0 / g, (n, width, probs[i])
+
+
+def test_inverse_cdf_endpoints_and_greedy_cases():
+    rng = np.random.default_rng(612)
+    B, V = 30, 200
+    x = rng.integers(-4, 5, size=(B, V)).astype(np.float32)  # heavy ties
+    greedy = np.argmax(x, axis=1)
+    for uv in [0.0, -0.5, float("nan")]:
+        r = run_f32(x, TOPK | TOPP | SAMPLE, top_k=50, top_p=0.9,
+                    u=np.full(B, uv, np.float32), need_logits=False)
+        np.testing.assert_array_equal(r["idx"], greedy)
+    # k = 1: the draw is the argmax whatever u is
+    r = run_f32(x, TOPK | SAMPLE, top_k=1, u=rng.random(B).astype(np.float32),
+                need_logits=False)
+    np.testing.assert_array_equal(r["idx"], greedy)
+    # u just below 1: the last element of K (here the k-th of the order)
+    r = run_f32(x, TOPK | SAMPLE, top_k=7, u=np.full(B, np.nextafter(np.float32(1), 0)),
+                need_logits=True)
+    for b in range(B):
+        order = sorted(range(V), key=lambda i: (-x[b, i], i))
+        assert r["idx"][b] == order[6]
+    # equal values: K is uniform, the draw for u in ((n-1)/|K|, n/|K|) is
+    # the n-th smallest id of K
+    xe = np.zeros((8, 50), np.float32)
+    ue = ((np.arange(8) + 0.5) / 10.0).astype(np.float32)
+    r = run_f32(xe, TOPK | SAMPLE, top_k=10, u=ue, need_logits=False)
+    np.testing.assert_array_equal(r["idx"], np.arange(8))
+
+
 def test_k1_and_constant_q_and_sample_off_are_greedy():
     rng = np.random.default_rng(700)
     B, V = 40, 300
