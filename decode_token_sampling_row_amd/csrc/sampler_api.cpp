@@ -174,7 +174,7 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
     if ((a->flags & SAMPLER_NEED_LOGITS) && a->out_logits == nullptr) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_NEED_PROBS) && a->out_probs == nullptr) return SAMPLER_EINVAL;
     if ((a->penalty_ids == nullptr) != (a->penalty_offsets == nullptr)) return SAMPLER_EINVAL;
-    if (a->row_flags == nullptr && a->q == nullptr) return SAMPLER_EINVAL;
+    if (a->row_flags == nullptr && a->q == nullptr && a->u == nullptr) return SAMPLER_EINVAL;
     return SAMPLER_OK;
 }
 
@@ -191,6 +191,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.top_k = a->top_k;
     p.top_p = a->top_p;
     p.q = a->q;
+    p.u = a->u;
     p.ids = a->penalty_ids;
     p.offsets = a->penalty_offsets;
     p.row_flags = a->row_flags;
@@ -268,7 +269,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         return SAMPLER_EHIP;
     launched[3] = true;
     mark(4);
-    if (a->top_p != nullptr) {
+    if (a->top_p != nullptr || a->u != nullptr) {
         // one launch over the queue the merge filled, whatever the chunks
         if (launch_fallback(p, l, h->ws, h->dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
         launched[4] = true;

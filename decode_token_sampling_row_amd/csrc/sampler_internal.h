@@ -65,6 +65,7 @@ struct KParams {
     const int32_t *top_k;
     const float *top_p;
     const float *q;
+    const float *u;  // [B] uniforms of inverse-CDF sampling, or null (race with q)
     const int32_t *ids;
     const int64_t *offsets;
     const uint8_t *row_flags;

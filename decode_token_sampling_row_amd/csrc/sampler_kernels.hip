@@ -87,7 +87,9 @@ __device__ __forceinline__ float cval(uint64_t c) { return key2f((uint32_t)(c >>
 // ---------------------------------------------------------------- row mode
 
 struct Mode {
-    bool tk, tp, sm;
+    bool tk, tp;
+    bool sm;   // samples by the exponential race with q
+    bool inv;  // samples by inverse CDF with the caller's uniform u
     int k;
     float p;
 };
@@ -103,7 +105,8 @@ __device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
     md.k = md.tk ? k : 0;
     md.tp = (rf & 2u) && P.top_p && p < 1.0f;  // NaN compares false: stage off
     md.p = md.tp ? p : 1.0f;
-    md.sm = (rf & 4u) && P.q;
+    md.sm = (rf & 4u) && P.q && !P.u;
+    md.inv = (rf & 4u) && P.u;
     return md;
 }
 
@@ -950,7 +953,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
     if (threadIdx.x == 0) {
         W.rowkey[b] = 0u;
         W.rmask[b] = 0u;
-        if (b == 0) *W.fbcnt = 0u;  // the full-row search queue (first chunk)
     }
     float smax;
     bool active;
@@ -1816,6 +1818,7 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
             if (nv > 0) load4<DT, AL>(rowp, j, nv, ring[d]);
         }
     const Mode md = row_mode(P, b);
+    if (b == 0 && t == 0 && threadIdx.x == 0) *W.fbcnt = 0u;  // the full-row search queue
     const bool filtering = P.top_k || P.top_p;  // the planning kernel ran
     const float traw = filtering ? W.rowthr[b] : 0.0f;
     const float ref = filtering ? W.rowref[b] : 0.0f;
@@ -2031,6 +2034,36 @@ __device__ void radix_select_any(uint32_t n, uint32_t kk, G &&get, uint32_t *his
     pmask_out = pmask;
 }
 
+// Inverse-CDF position over a[0..n), n <= 4 NT, in the row's order (largest
+// first): the least position whose inclusive mass sum of exp(x - x0) reaches
+// u times the total; 0 when u <= 0 or NaN, n - 1 when rounding leaves the
+// total short of the target.  Every thread returns it.
+template <int NT>
+__device__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t n, float x0, float u, double *scd,
+                                    uint32_t *sc) {
+    if (!(u > 0.0f) || n <= 1) return 0u;
+    double e[4];
+    double loc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = 4 * threadIdx.x + i;
+        e[i] = p < n ? exp((double)cval(a[p]) - (double)x0) : 0.0;
+        loc += e[i];
+    }
+    double tot;
+    double run = wg_excl_scan_f64<NT>(loc, scd, tot);
+    const double target = (double)u * tot;
+    uint32_t first = NONE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = 4 * threadIdx.x + i;
+        run += e[i];
+        if (p < n && first == NONE && run >= target) first = p;
+    }
+    first = wg_min_u32<NT>(first, sc);
+    return first == NONE ? n - 1 : first;
+}
+
 __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork W) {
     __shared__ RowsShared S;
     extern __shared__ uint32_t toff[];  // per-tile candidate offsets, L.nt + 1
@@ -2129,11 +2162,14 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 }
             am = wg_max_u64<NT>(am, S.sc64);
             idx = am ? cidx(am) : NONE;
+            if (md.inv && am) info.m = cval(am);  // the row maximum, for the search
         }
         info.idx0 = idx;
         if (tid == 0) {
             P.out_idx[b] = (int64_t)idx;
             W.info[b] = info;
+            // inverse-CDF draw over the whole row: the full-row search finds it
+            if (md.inv && idx != NONE) W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
         }
         return;
     }
@@ -2278,6 +2314,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     uint32_t nK = nsel;
     bool settled = true;
     bool use_nuc = false;  // K is S.nuc[0..nK), else S.srt[0..nK)
+    bool srt_sorted = false;  // srt is in the row's order
     if (md.tp) {
         const double pZ = (double)md.p * Zc;
         double at = 0.0, below = 0.0;
@@ -2314,6 +2351,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
             __syncthreads();
             bitonic_desc<NT>(S.srt, npad);
+            srt_sorted = true;
             double e[4];
             double l2 = 0.0;
 #pragma unroll
@@ -2377,9 +2415,23 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     }
     __syncthreads();
 
+    // ---- inverse-CDF draw over K, in the row's order (srt is sorted first
+    // when no top-p cut ordered it; then K is the whole selection)
+    uint32_t inv_pos = 0;
+    if (md.inv) {
+        if (!use_nuc && !srt_sorted && nK > 1) {
+            const int npad = pow2_ceil((int)nsel);
+            for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
+            __syncthreads();
+            bitonic_desc<NT>(S.srt, npad);
+        }
+        inv_pos = inverse_cdf_pos<NT>(use_nuc ? S.nuc : S.srt, nK, x0, P.u[b], S.scd, S.sc);
+    }
+
     // ---- exponential race over K (or greedy), and the kept list
     const uint64_t *kp = use_nuc ? S.nuc : S.srt;
     uint32_t idx = cidx(top);
+    if (md.inv) idx = cidx(kp[inv_pos]);
     double zk = 0.0;
     double rbest = -1.0;
     uint32_t ibest = NONE;
@@ -2605,12 +2657,11 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     const Mode md = row_mode(P, b);
     const double m = (double)info.m;
 
-    uint64_t Tstar;
-    double ZK;
-    if (md.p <= 0.0f) {
-        Tstar = mkcomp(info.m, info.idx0);
-        ZK = 1.0;
-    } else {
+    // The least element T* (a composite) of the row's order at which the mass
+    // exp(x - m) summed from the top reaches the target -- tval times the
+    // row's total (found on the first pass) when frac, else tval itself --
+    // and ZKo, the mass through T*.
+    auto search = [&](double tval, bool frac, uint64_t &Tst, double &ZKo) {
         double above = 0.0, target = 0.0;
         int nlev = 0;
         int path = 0;  // 1 collect, 2 ties
@@ -2651,7 +2702,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             });
             if (level == 0) {
                 double Z = wg_sum_f64<K3_THREADS>(zt, S.scd);
-                target = (double)md.p * Z;
+                target = frac ? tval * Z : tval;
             }
             find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
             const uint32_t fb = S.found[0];
@@ -2723,7 +2774,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             }
             uint32_t fi = wg_min_u32<K3_THREADS>(first, S.sc);
             if (fi == NONE) fi = (uint32_t)(n > 0 ? n - 1 : 0);  // rounding: whole bucket
-            Tstar = (n > 0) ? S.coll[fi] : mkcomp(info.m, info.idx0);
+            Tst = (n > 0) ? S.coll[fi] : mkcomp(info.m, info.idx0);
             // ZK: mass of every kept element = above + bucket prefix through fi
             double s = 0.0;
 #pragma unroll
@@ -2731,7 +2782,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 int i = tid * PER + t;
                 if (i <= (int)fi && i < n) s += ei[t];
             }
-            ZK = above + wg_sum_f64<K3_THREADS>(s, S.scd);
+            ZKo = above + wg_sum_f64<K3_THREADS>(s, S.scd);
         } else {
             // every bucket member has the same value: take the c members with
             // the smallest vocab ids
@@ -2780,9 +2831,47 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 }
                 __syncthreads();
             }
-            Tstar = mkcomp(xt, S.found[1]);
-            ZK = above + (double)cneed * et;
+            Tst = mkcomp(xt, S.found[1]);
+            ZKo = above + (double)cneed * et;
         }
+    };
+
+    // Up to two searches, from one call site: (0) the top-p cut at p -- or,
+    // for a row queued only for an inverse-CDF draw over the whole row, that
+    // draw at u; (1) the draw inside the cut at u ZK.  A level <= 0 (or NaN)
+    // stands for the first element of the order.
+    const bool whole = info.kind == KIND_UNFILTERED;
+    const uint64_t top = mkcomp(info.m, info.idx0);
+    uint64_t Tstar = top;  // the cut (or the whole-row draw)
+    double ZK = 1.0;       // mass of the cut, exp(x - m) summed
+    uint64_t Tdraw = top;  // the draw inside the cut
+    for (int job = 0; job < 2; ++job) {
+        double tval;
+        bool frac;
+        if (job == 0) {
+            const double level = whole ? (double)P.u[b] : (double)md.p;
+            if (!(level > 0.0)) continue;
+            tval = level;
+            frac = true;
+        } else {
+            if (whole || !md.inv || !(P.u[b] > 0.0f)) break;
+            tval = (double)P.u[b] * ZK;
+            frac = false;
+        }
+        uint64_t Tj;
+        double Zj;
+        search(tval, frac, Tj, Zj);
+        if (job == 0) {
+            Tstar = Tj;
+            ZK = Zj;
+        } else {
+            Tdraw = Tj < Tstar ? Tstar : Tj;  // inside the cut whatever the rounding
+        }
+    }
+    if (whole) {
+        if (tid == 0) P.out_idx[b] = (int64_t)cidx(Tstar);
+        __syncthreads();  // the next row reuses the shared buffers
+        continue;
     }
 
     // ---- exponential race over K = { comp >= T* }, or greedy
@@ -2796,6 +2885,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         });
         Race r = wg_race<K3_THREADS>(rc, S.scx, S.scq, S.sci);
         idx = r.idx;
+    } else if (md.inv) {
+        idx = cidx(Tdraw);
     }
     if (tid == 0) {
         P.out_idx[b] = (int64_t)idx;

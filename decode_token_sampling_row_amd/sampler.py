@@ -55,6 +55,7 @@ class sampler_args(ctypes.Structure):
         ("out_idx", ctypes.c_void_p),
         ("out_logits", ctypes.c_void_p),
         ("out_probs", ctypes.c_void_p),
+        ("u", ctypes.c_void_p),
     ]
 
 
@@ -132,7 +133,7 @@ def _ptr(t, dtype=None, what=""):
 def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
               temperature=1.0, repetition_penalty=1.0, penalty_ids=None,
               penalty_offsets=None, row_flags=None, out_logits=None, out_probs=None,
-              profile=False) -> sampler_args:
+              profile=False, u=None) -> sampler_args:
     """Marshal torch tensors into a sampler_args struct."""
     import torch
 
@@ -166,6 +167,7 @@ def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
     a.out_idx = _ptr(out_idx, torch.int64, "out_idx")
     a.out_logits = _ptr(out_logits, torch.float32, "out_logits")
     a.out_probs = _ptr(out_probs, torch.float32, "out_probs")
+    a.u = _ptr(u, torch.float32, "u")
     return a
 
 

@@ -23,6 +23,11 @@
  *      exact ties -- q is paired with candidates by vocabulary id; without it
  *      the output is the first kept token, i.e. the greedy argmax (Ascend
  *      page, Sample section; MiniMind sec. 10.8);
+ *   6'. or, when the caller passes uniforms u instead, a multinomial draw
+ *      from softmax_K made by inverse CDF: the kept token at which the
+ *      cumulative probability, summed in the order of step 3, first reaches
+ *      u[row] (MiniMind sec. 10.8, torch.multinomial over the filtered
+ *      softmax);
  *   7. optional dense outputs: the filtered logits (x at kept ids, -inf
  *      elsewhere; the Ascend page's logits_top_kp_select) and the
  *      probabilities renormalised over the kept set (0 elsewhere).
@@ -109,6 +114,14 @@ typedef struct sampler_args {
     int64_t *out_idx;          /* [B] sampled (or greedy) vocab id          */
     float *out_logits;         /* [B, V] row stride V; iff NEED_LOGITS      */
     float *out_probs;          /* [B, V] row stride V; iff NEED_PROBS       */
+    const float *u;            /* [B] uniforms for inverse-CDF sampling, or
+                                  NULL.  When given, rows with the sample bit
+                                  draw the kept token whose inclusive
+                                  cumulative probability (in the order of
+                                  step 3) first reaches u[b] -- u <= 0 or NaN
+                                  gives the first kept token, u beyond what
+                                  rounding lets the sum reach gives the last
+                                  -- and q is not read (it may be NULL).     */
 } sampler_args;
 
 /*
@@ -129,7 +142,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
  * ld < V, temperature or penalty not finite and > 0, eps negative or not
  * finite, a requested dense output with a NULL buffer, exactly one of the
  * penalty arrays NULL, unknown flag bits, or row_flags == NULL (every row
- * samples) with q == NULL.
+ * samples) with both q and u NULL.
  * Per-row values are never errors: k outside [1, min(V, 1024)] skips top-k,
  * p >= 1 or NaN skips top-p, history ids outside [0, V) are ignored.
  */

@@ -6,7 +6,9 @@ path) and through the CPU oracle, and compare them with the parity rules:
   top-p boundary ties (a prefix mass within 1e-9 of p); those are counted;
 * the dense filtered logits are bit-exact (so the kept sets are too) on every
   row that is not a top-p boundary tie;
-* probabilities agree within 1e-5 absolute.
+* probabilities agree within 1e-5 absolute;
+* with inverse-CDF sampling (uniforms u) the output id is bit-exact except
+  where u lies within 1e-9 of a cumulative-probability boundary (counted).
 """
 import numpy as np
 
@@ -15,6 +17,7 @@ from oracle import oracle as orc
 
 GAP_TIE = 1e-5
 MARGIN_TIE = 1e-9
+U_TIE = 1e-9
 PROB_ATOL = 1e-5
 
 
@@ -46,7 +49,7 @@ def device_inputs(W, ld_pad=0):
 
 
 def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sampler=None,
-            inputs=None, rpl=0):
+            inputs=None, rpl=0, u=None, drop_q=False):
     import torch
 
     from decode_token_sampling_row_amd.sampler import Sampler
@@ -59,7 +62,9 @@ def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sam
     out_p = torch.full((B, V), -1.0, dtype=torch.float32, device=dev) if need_probs else None
     s = sampler or Sampler(max(B, 1), V, torch.bfloat16 if W.dtype == wl.BF16 else torch.float32,
                            topk_guess=guess, segment_len=seg, rows_per_launch=rpl)
-    s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"], eps=W.eps,
+    ud = None if u is None else torch.from_numpy(np.ascontiguousarray(u, np.float32)).to(dev)
+    s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"],
+          q=None if drop_q else d["q"], u=ud, eps=W.eps,
           temperature=W.temperature, repetition_penalty=W.penalty,
           penalty_ids=d["penalty_ids"], penalty_offsets=d["penalty_offsets"],
           row_flags=d["row_flags"], out_logits=out_l, out_probs=out_p)
@@ -70,20 +75,23 @@ def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sam
     return res
 
 
-def run_oracle(W, need_logits=True, need_probs=False, rows=None, threads=8):
+def run_oracle(W, need_logits=True, need_probs=False, rows=None, threads=8, u=None):
     return orc.run(W.logits, orc.BF16 if W.dtype == wl.BF16 else orc.F32, vocab=W.V,
                    top_k=W.top_k, top_p=W.top_p, q=W.q, eps=W.eps, temperature=W.temperature,
                    penalty=W.penalty, ids=W.ids, offsets=W.offsets, row_flags=W.row_flags,
-                   need_logits=need_logits, need_probs=need_probs, rows=rows, threads=threads)
+                   need_logits=need_logits, need_probs=need_probs, rows=rows, threads=threads,
+                   u=u)
 
 
-def compare(W, hip, ref, rows=None, label=""):
-    """Assert the parity rules on `rows` (default all); returns tie counts."""
+def compare(W, hip, ref, rows=None, label="", inverse=False):
+    """Assert the parity rules on `rows` (default all); returns tie counts.
+    inverse: the runs sampled by inverse CDF (ref["gap"] is then the u
+    margin)."""
     rows = np.arange(W.B) if rows is None else np.asarray(rows)
     flags = W.row_flags if W.row_flags is not None else np.full(W.B, 7, np.uint8)
-    sampling = ((flags & 4) != 0) & (W.q is not None)
+    sampling = ((flags & 4) != 0) & (inverse or W.q is not None)
     margin_tie = ref["margin"] < MARGIN_TIE
-    near = sampling & (ref["gap"] <= GAP_TIE)
+    near = sampling & (ref["gap"] <= (U_TIE if inverse else GAP_TIE))
     n_margin = int(margin_tie[rows].sum())
     n_near = int(near[rows].sum())
     check_idx = rows[~margin_tie[rows] & ~near[rows]]

@@ -54,7 +54,7 @@ def test_args_struct_layout_matches_header():
              offsetof(sampler_opts, rows_per_launch));
       O(logits); O(ld); O(top_k); O(top_p); O(q); O(eps); O(temperature);
       O(repetition_penalty); O(penalty_ids); O(penalty_offsets); O(row_flags);
-      O(flags); O(out_idx); O(out_logits); O(out_probs);
+      O(flags); O(out_idx); O(out_logits); O(out_probs); O(u);
       return 0;
     }
     """

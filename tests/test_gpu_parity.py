@@ -181,6 +181,26 @@ def test_rows_per_launch_changes_nothing(rpl):
     compare(W, other, run_oracle(W, need_logits=True), label=f"rpl={rpl}")
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_inverse_cdf_sampling(cfg):
+    # the caller's uniforms replace q: listed rows draw in k_rows, unfiltered
+    # rows and rows whose guess failed draw through the full-row search
+    sizes = {1: (4, 32000), 2: (16, 30000), 3: (12, 20000), 4: (64, 6400), 5: (24, 40000)}
+    B, V = sizes[cfg]
+    W = wl.make(cfg, B=B, V=V, seed=21)
+    if W.row_flags is None:
+        W.row_flags = np.full(W.B, 7, np.uint8)
+    u = np.random.default_rng(77 + cfg).random(W.B).astype(np.float32)
+    u[0] = 0.0  # the first kept token
+    if W.B > 1:
+        u[1] = np.nextafter(np.float32(1), np.float32(0))  # the last kept token
+    print(f"[case] inverse CDF cfg{cfg} B={W.B} V={W.V}", flush=True)
+    hip = run_hip(W, need_logits=True, u=u, drop_q=True)
+    ref = run_oracle(W, need_logits=True, u=u)
+    stats = compare(W, hip, ref, label=f"inverse cfg{cfg}", inverse=True)
+    print(f"[case] inverse cfg{cfg}: {stats}", flush=True)
+
+
 def test_repeated_runs_bit_identical():
     import torch
 
