@@ -25,7 +25,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 F32 = 0
 BF16 = 1
 ROW_TOPK, ROW_TOPP, ROW_SAMPLE = 1, 2, 4
-NEED_LOGITS, NEED_PROBS = 1, 2
+NEED_LOGITS, NEED_PROBS, TOPK_TIES = 1, 2, 4
 
 _lib = None
 
@@ -67,7 +67,7 @@ def _arr(a, dtype):
 
 def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
         temperature=1.0, penalty=1.0, ids=None, offsets=None, row_flags=None,
-        need_logits=True, need_probs=False, rows=None, threads=1, u=None):
+        need_logits=True, need_probs=False, rows=None, threads=1, u=None, topk_ties=False):
     """Run the oracle.
 
     logits: [B, ld] float32 (dtype F32) or uint16 bf16 bit patterns (BF16);
@@ -76,6 +76,7 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
     zeros / -1); used to sample rows of large workloads.
     u: optional [B] uniforms; sampling rows then draw by inverse CDF (and
     ``gap`` holds that decision's margin) instead of racing with q.
+    topk_ties: top-k keeps every element equal to the k-th value too.
     Returns a dict with idx [B] int64, logits [B, V] float32 or None,
     probs [B, V] float32 or None, nkept [B] int32, margin [B], gap [B].
     """
@@ -98,7 +99,8 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
     ids = _arr(ids, np.int32)
     offsets = _arr(offsets, np.int64)
     row_flags = _arr(row_flags, np.uint8)
-    flags = (NEED_LOGITS if need_logits else 0) | (NEED_PROBS if need_probs else 0)
+    flags = ((NEED_LOGITS if need_logits else 0) | (NEED_PROBS if need_probs else 0)
+             | (TOPK_TIES if topk_ties else 0))
 
     out_idx = np.full(B, -1, dtype=np.int64)
     out_logits = np.zeros((B, V), dtype=np.float32) if need_logits else None

@@ -28,6 +28,11 @@
  *   O5  top-k active iff row bit0 and 1 <= k <= min(V, 1024): C = first k
  *       of the order, else C = whole row      (Ascend page, topK, range
  *                                             rule and Card(top_k_value)=k)
+ *   O5' with the TOPK_TIES call flag, C also takes every element equal to
+ *       the k-th value: C = { j : x_j >= the k-th largest value }
+ *                                             (MiniMind sec. 10.5: logits
+ *                                             below the k-th value of topk
+ *                                             are masked, so ties stay)
  *   O6  e_i = exp(x_Ci - x_C0), Z = sum e_i   (softmax over the survivors,
  *                                             Ascend page, topK/topP)
  *   O7  top-p active iff row bit1 and p < 1 (NaN -> inactive): keep the
@@ -79,6 +84,7 @@
 
 #define NEED_LOGITS 1u
 #define NEED_PROBS 2u
+#define TOPK_TIES 4u
 
 #define TOPK_CAP 1024
 
@@ -188,7 +194,11 @@ int oracle_run(int32_t B, int32_t V, int32_t dtype, const void *logits, int64_t 
         if ((rf & ROW_TOPK) && top_k != NULL) {
             int32_t k = top_k[b];
             int32_t kmax = V < TOPK_CAP ? V : TOPK_CAP;
-            if (k >= 1 && k <= kmax) nC = k;
+            if (k >= 1 && k <= kmax) {
+                nC = k;
+                if (flags & TOPK_TIES)
+                    while (nC < V && ord[nC].x == ord[k - 1].x) nC++;
+            }
         }
 
         /* O6: softmax over C in double. */

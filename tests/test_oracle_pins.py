@@ -171,6 +171,26 @@ def test_topk_brute_force_with_ties(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
+def test_topk_keeping_ties_matches_minimind_topk(seed):
+    """TOPK_TIES reading: the MiniMind chapter's own top-k line (mask the
+    logits below the k-th value of torch.topk) gives the kept set, ties at
+    the k-th value included."""
+    rng = np.random.default_rng(150 + seed)
+    B, V = 6, int(rng.integers(5, 60))
+    x = rng.integers(-3, 4, size=(B, V)).astype(np.float32)  # many exact ties
+    for k in sorted({1, 2, V // 3 + 1, V // 2 + 1, V}):
+        r = run_f32(x, TOPK, top_k=k, topk_ties=True)
+        for b in range(B):
+            mm = _minimind_chain(x[b], k, 1.0)
+            assert kept_set(r["logits"][b]) == set(np.nonzero(np.isfinite(mm))[0].tolist())
+            kth = np.sort(x[b])[::-1][k - 1]
+            assert r["nkept"][b] == int(np.sum(x[b] >= kth))
+    # without the flag exactly k survive
+    r = run_f32(x, TOPK, top_k=3)
+    assert np.all(r["nkept"] == 3)
+
+
+@pytest.mark.parametrize("seed", range(12))
 def test_topp_brute_force(seed):
     rng = np.random.default_rng(200 + seed)
     V = int(rng.integers(2, 10))
