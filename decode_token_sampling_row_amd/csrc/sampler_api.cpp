@@ -169,7 +169,8 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
     if (!(a->repetition_penalty > 0.0f) || !isfinite(a->repetition_penalty))
         return SAMPLER_EINVAL;
     if (!(a->eps >= 0.0f) || !isfinite(a->eps)) return SAMPLER_EINVAL;
-    const uint32_t known = SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_PROFILE;
+    const uint32_t known =
+        SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_TOPK_TIES | SAMPLER_PROFILE;
     if (a->flags & ~known) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_NEED_LOGITS) && a->out_logits == nullptr) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_NEED_PROBS) && a->out_probs == nullptr) return SAMPLER_EINVAL;
@@ -201,7 +202,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.eps = a->eps;
     p.temperature = a->temperature;
     p.rho = a->repetition_penalty;
-    p.flags = a->flags & (SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS);
+    p.flags = a->flags & (SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_TOPK_TIES);
     p.B = batch;
     p.V = h->vocab;
     p.guess = h->guess;
@@ -269,7 +270,8 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         return SAMPLER_EHIP;
     launched[3] = true;
     mark(4);
-    if (a->top_p != nullptr || a->u != nullptr) {
+    if (a->top_p != nullptr || a->u != nullptr ||
+        (a->top_k != nullptr && (a->flags & SAMPLER_TOPK_TIES))) {
         // one launch over the queue the merge filled, whatever the chunks
         if (launch_fallback(p, l, h->ws, h->dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
         launched[4] = true;

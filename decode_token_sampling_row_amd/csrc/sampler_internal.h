@@ -56,7 +56,7 @@ struct RowInfo {
     float m;       // row max (transformed)
     float xmin;    // row min finite
     uint32_t idx0; // id of the row maximum (first in order)
-    uint32_t pad;
+    float vfloor;  // full-row search: only values >= vfloor take part (-inf: all)
 };
 
 struct KParams {

@@ -58,6 +58,7 @@ namespace {
 
 constexpr uint32_t NONE = 0xffffffffu;
 constexpr uint32_t NEED_PROBS = 2u;
+constexpr uint32_t TOPK_TIES = 4u;  // top-k keeps the ties at the k-th value
 // top-p decisions taken from a guess must clear the cutoff by this much
 // (relative to the row's total mass); the row's total is accumulated from
 // fp32 exponentials, good to about 1e-6.  Rows inside the margin take the
@@ -2117,7 +2118,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.m = -INFINITY;
     info.xmin = INFINITY;
     info.idx0 = NONE;
-    info.pad = 0;
+    info.vfloor = -INFINITY;
 
     if (!filtered) {
         // merge the tiles' winners: the race by ratio (lowest id on a tie),
@@ -2218,8 +2219,15 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // to RCAP candidates are held in registers, RCAP / NT per thread, loaded
     // before the statistics are merged so that their latency overlaps it;
     // more (rare) are selected by passes over the slots themselves.
-    const uint32_t nsel = min(kk, N);
+    uint32_t nsel = min(kk, N);
     const bool inreg = N <= (uint32_t)RCAP;
+    // top-k keeping the ties at the k-th value: the selection grows to every
+    // candidate with that value (the candidates hold all of them unless the
+    // row was selected again exactly); a row where that cannot be done here
+    // goes to the full-row search with the k-th value as its floor
+    const bool ties = md.tk && (P.flags & TOPK_TIES) != 0;
+    bool to_search = false;
+    uint32_t kmin = 0;  // value key of the k-th largest (ties rows)
     constexpr int R = RCAP / NT;
     uint64_t v[R];
     uint32_t vm = 0;
@@ -2261,6 +2269,25 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             for (int r = 0; r < R; ++r)
                 if (((vm >> r) & 1u) && (v[r] & pmask) >= prefix) km |= 1u << r;
         }
+        if (ties) {
+            uint32_t lo = ~0u;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if ((km >> r) & 1u) lo = min(lo, (uint32_t)(v[r] >> 32));
+            kmin = wg_min_u32<NT>(lo, S.sc);
+            uint32_t km2 = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (((vm >> r) & 1u) && (uint32_t)(v[r] >> 32) >= kmin) km2 |= 1u << r;
+            uint32_t n1;
+            (void)wg_excl_scan_u32<NT>(__popc(km2), S.sc, n1);
+            if (redone || n1 > (uint32_t)KMAX) {
+                to_search = true;
+            } else {
+                km = km2;
+                nsel = n1;
+            }
+        }
         uint32_t tot;
         uint32_t off = wg_excl_scan_u32<NT>(__popc(km), S.sc, tot);
 #pragma unroll
@@ -2274,6 +2301,13 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         for (uint32_t e = tid; e < N; e += NT) {
             const uint64_t c = gget(e);
             if ((c & pmask) >= prefix) S.srt[atomicAdd(&S.cnt, 1u)] = c;
+        }
+        to_search = ties;  // (many candidates: rare) the full-row search does it
+        if (ties) {
+            __syncthreads();
+            uint32_t lo = ~0u;
+            for (uint32_t i = tid; i < nsel; i += NT) lo = min(lo, (uint32_t)(S.srt[i] >> 32));
+            kmin = wg_min_u32<NT>(lo, S.sc);
         }
     }
     __syncthreads();
@@ -2299,6 +2333,17 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     }
     const uint64_t top = wg_max_u64<NT>(mxv, S.sc64);
     const float x0 = cval(top);
+    if (to_search) {
+        info.kind = KIND_FALLBACK;
+        info.m = x0;
+        info.idx0 = cidx(top);
+        info.vfloor = key2f(kmin);
+        if (tid == 0) {
+            W.info[b] = info;
+            W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
+        }
+        return;
+    }
     double loc = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -2656,6 +2701,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     RowInfo info = W.info[b];
     const Mode md = row_mode(P, b);
     const double m = (double)info.m;
+    const float vfloor = info.vfloor;  // values below take no part (top-k floor)
 
     // The least element T* (a composite) of the row's order at which the mass
     // exp(x - m) summed from the top reaches the target -- tval times the
@@ -2689,7 +2735,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             __syncthreads();
             double zt = 0.0;
             row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-                if (!(x > -INFINITY)) return;
+                if (!(x > -INFINITY) || x < vfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
                 double e = exp((double)x - m);
@@ -2742,7 +2788,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (tid == 0) S.counter = 0;
             __syncthreads();
             row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-                if (!(x > -INFINITY)) return;
+                if (!(x > -INFINITY) || x < vfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
                 uint32_t pos = atomicAdd(&S.counter, 1u);
@@ -2845,10 +2891,21 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     uint64_t Tstar = top;  // the cut (or the whole-row draw)
     double ZK = 1.0;       // mass of the cut, exp(x - m) summed
     uint64_t Tdraw = top;  // the draw inside the cut
+    const bool floor_only = !whole && !md.tp;  // a top-k row keeping its ties
+    if (floor_only) {
+        // the cut is every value >= the floor
+        Tstar = (uint64_t)f2key(vfloor) << 32;
+        double z = 0.0;
+        row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
+            if (x >= vfloor) z += exp((double)x - m);
+        });
+        ZK = wg_sum_f64<K3_THREADS>(z, S.scd);
+    }
     for (int job = 0; job < 2; ++job) {
         double tval;
         bool frac;
         if (job == 0) {
+            if (floor_only) continue;
             const double level = whole ? (double)P.u[b] : (double)md.p;
             if (!(level > 0.0)) continue;
             tval = level;

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libsampler.so")
 SAMPLER_OK, SAMPLER_EINVAL, SAMPLER_ENOMEM, SAMPLER_EHIP = 0, -1, -2, -3
 SAMPLER_F32, SAMPLER_BF16 = 0, 1
 SAMPLER_ROW_TOPK, SAMPLER_ROW_TOPP, SAMPLER_ROW_SAMPLE, SAMPLER_ROW_ALL = 1, 2, 4, 7
-SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_PROFILE = 1, 2, 256
+SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_TOPK_TIES, SAMPLER_PROFILE = 1, 2, 4, 256
 SAMPLER_TOPK_MAX = 1024
 SAMPLER_VOCAB_MAX = 1 << 21
 
@@ -133,7 +133,7 @@ def _ptr(t, dtype=None, what=""):
 def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
               temperature=1.0, repetition_penalty=1.0, penalty_ids=None,
               penalty_offsets=None, row_flags=None, out_logits=None, out_probs=None,
-              profile=False, u=None) -> sampler_args:
+              profile=False, u=None, topk_ties=False) -> sampler_args:
     """Marshal torch tensors into a sampler_args struct."""
     import torch
 
@@ -151,6 +151,8 @@ def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
         flags |= SAMPLER_NEED_PROBS
     if profile:
         flags |= SAMPLER_PROFILE
+    if topk_ties:
+        flags |= SAMPLER_TOPK_TIES
     a = sampler_args()
     a.logits = _ptr(logits, None, "logits")
     a.ld = logits.stride(0)

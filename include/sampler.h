@@ -12,7 +12,9 @@
  *   3. top-k: when the row's top-k bit is set and 1 <= k <= min(vocab, 1024),
  *      keep exactly the k largest logits, ties broken by the smaller vocab id;
  *      any other k skips the stage (Ascend torch_npu npu_top_k_top_p_sample
- *      page, topK section: valid range and Card(top_k_value) = top_k);
+ *      page, topK section: valid range and Card(top_k_value) = top_k); with
+ *      SAMPLER_TOPK_TIES, every logit equal to the k-th value is kept too
+ *      (MiniMind sec. 10.5);
  *   4. softmax over the survivors (same page, topK/topP sections);
  *   5. top-p: when the row's top-p bit is set and p < 1, keep the shortest
  *      prefix of the survivors (in the order of step 3) whose probability
@@ -64,6 +66,10 @@ extern "C" {
 /* ---- call flags (sampler_args.flags) ------------------------------------- */
 #define SAMPLER_NEED_LOGITS 1u  /* write out_logits                          */
 #define SAMPLER_NEED_PROBS 2u   /* write out_probs (debug; re-reads logits)  */
+#define SAMPLER_TOPK_TIES 4u    /* top-k also keeps every logit equal to the
+                                   k-th largest value (MiniMind sec. 10.5:
+                                   only logits below the k-th value of topk
+                                   are masked), so more than k may survive  */
 #define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
                                    averages with sampler_profile             */
 #define SAMPLER_PROFILE_SLOTS 6
@@ -110,7 +116,7 @@ typedef struct sampler_args {
     const int32_t *penalty_ids;     /* [nnz] history ids, or NULL          */
     const int64_t *penalty_offsets; /* [B+1] CSR offsets into penalty_ids */
     const uint8_t *row_flags;  /* [B] SAMPLER_ROW_* bits, NULL = all on     */
-    uint32_t flags;            /* SAMPLER_NEED_LOGITS | _NEED_PROBS | _PROFILE */
+    uint32_t flags;            /* SAMPLER_NEED_LOGITS | _NEED_PROBS | _TOPK_TIES | _PROFILE */
     int64_t *out_idx;          /* [B] sampled (or greedy) vocab id          */
     float *out_logits;         /* [B, V] row stride V; iff NEED_LOGITS      */
     float *out_probs;          /* [B, V] row stride V; iff NEED_PROBS       */

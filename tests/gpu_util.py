@@ -49,7 +49,7 @@ def device_inputs(W, ld_pad=0):
 
 
 def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sampler=None,
-            inputs=None, rpl=0, u=None, drop_q=False):
+            inputs=None, rpl=0, u=None, drop_q=False, ties=False):
     import torch
 
     from decode_token_sampling_row_amd.sampler import Sampler
@@ -67,7 +67,7 @@ def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sam
           q=None if drop_q else d["q"], u=ud, eps=W.eps,
           temperature=W.temperature, repetition_penalty=W.penalty,
           penalty_ids=d["penalty_ids"], penalty_offsets=d["penalty_offsets"],
-          row_flags=d["row_flags"], out_logits=out_l, out_probs=out_p)
+          row_flags=d["row_flags"], out_logits=out_l, out_probs=out_p, topk_ties=ties)
     torch.cuda.synchronize()
     res = {"idx": out_idx.cpu().numpy(),
            "logits": out_l.cpu().numpy() if need_logits else None,
@@ -75,12 +75,13 @@ def run_hip(W, need_logits=True, need_probs=False, guess=0, seg=0, ld_pad=0, sam
     return res
 
 
-def run_oracle(W, need_logits=True, need_probs=False, rows=None, threads=8, u=None):
+def run_oracle(W, need_logits=True, need_probs=False, rows=None, threads=8, u=None,
+               ties=False):
     return orc.run(W.logits, orc.BF16 if W.dtype == wl.BF16 else orc.F32, vocab=W.V,
                    top_k=W.top_k, top_p=W.top_p, q=W.q, eps=W.eps, temperature=W.temperature,
                    penalty=W.penalty, ids=W.ids, offsets=W.offsets, row_flags=W.row_flags,
                    need_logits=need_logits, need_probs=need_probs, rows=rows, threads=threads,
-                   u=u)
+                   u=u, topk_ties=ties)
 
 
 def compare(W, hip, ref, rows=None, label="", inverse=False):

@@ -82,7 +82,8 @@ def test_constants_match_header():
     for name in ["SAMPLER_OK", "SAMPLER_EINVAL", "SAMPLER_ENOMEM", "SAMPLER_EHIP",
                  "SAMPLER_F32", "SAMPLER_BF16", "SAMPLER_ROW_TOPK", "SAMPLER_ROW_TOPP",
                  "SAMPLER_ROW_SAMPLE", "SAMPLER_ROW_ALL", "SAMPLER_NEED_LOGITS",
-                 "SAMPLER_NEED_PROBS", "SAMPLER_PROFILE", "SAMPLER_PROFILE_SLOTS",
+                 "SAMPLER_NEED_PROBS", "SAMPLER_TOPK_TIES", "SAMPLER_PROFILE",
+                 "SAMPLER_PROFILE_SLOTS",
                  "SAMPLER_TOPK_MAX"]:
         assert getattr(smp, name) == val(name), name
 

@@ -271,6 +271,36 @@ def test_unrepresentative_sample(case, dtype):
     _check(W, f"sample {case} {dtype}")
 
 
+@pytest.mark.parametrize("case", ["ties", "ties_inverse", "redone"])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_topk_keeping_ties(case, dtype):
+    """SAMPLER_TOPK_TIES: top-k keeps every value equal to the k-th.  Integer
+    logits make large tie groups: small k stay within a list (the row merge
+    extends the selection), k near 1024 exceed it and go to the full-row
+    search with the k-th value as floor, as do rows selected again exactly."""
+    rng = np.random.default_rng(31)
+    if case == "redone":
+        B, V = 16, 262144
+        x = np.round(rng.standard_normal((B, V)) * 2.0).astype(np.float32)
+        for b in range(B):
+            x[b, _sample_runs(V, b)] += 6.0  # the sample overstates the row
+        k = np.array([1024, 50, 1, 7, 1024, 300, 2, 1000] * 2)
+    else:
+        B, V = 32, 30000
+        x = rng.integers(-20, 21, size=(B, V)).astype(np.float32)
+        k = np.array([1, 5, 50, 300, 1000, 1024, 2, 0] * 4)
+    W = _custom(x, top_k=k, top_p=0.9, flags=_all_combos(B), dtype=dtype)
+    u = rng.random(B).astype(np.float32) if case == "ties_inverse" else None
+    label = f"topk ties {case} {dtype}"
+    print(f"[case] {label} B={W.B} V={W.V}", flush=True)
+    hip = run_hip(W, need_logits=True, need_probs=True, ties=True, u=u, drop_q=u is not None)
+    ref = run_oracle(W, need_logits=True, need_probs=True, ties=True, u=u)
+    _log(label, compare(W, hip, ref, label=label, inverse=u is not None))
+    # more than k survive where the k-th value is tied
+    tk = (W.row_flags & 1) != 0
+    assert np.any(ref["nkept"][tk & ((W.row_flags & 2) == 0)] > k[tk & ((W.row_flags & 2) == 0)])
+
+
 def test_flat_rows_force_full_row_search():
     rng = np.random.default_rng(11)
     B, V = 8, 128256
