@@ -21,7 +21,7 @@ constexpr int SEL_LIMIT = 1536;    // exact pass: most entries a cut-back keeps
 constexpr int VEC = 8;             // elements per group in the exact pass
 // Row admission estimate: EST_SEGS runs of EST_SEG logits.
 constexpr int EST_SEGS = 16;
-constexpr int EST_SEG = 1024;
+constexpr int EST_SEG = 512;
 constexpr int EST_N = EST_SEGS * EST_SEG;
 constexpr int K1_THREADS = 256;    // estimate workgroup
 // Row kernels.

@@ -3,7 +3,7 @@
 // Pipeline of one call (all on the caller's stream):
 //
 //   k_plan      grid = B.  Rows with top-k / top-p: an admission value from a
-//               sample of the row (16 staggered runs of 1024 logits), below
+//               sample of the row (16 staggered runs of 512 logits), below
 //               which no element can be among the row's kk largest with high
 //               probability; the sample maximum as the reference for sums of
 //               exponentials.

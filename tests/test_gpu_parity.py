@@ -229,17 +229,18 @@ def test_fallback_with_huge_tie_block():
 
 
 def _sample_runs(V, b):
-    """Positions of the 16 runs of 1024 logits of row b that the select pass
+    """Positions of the 16 runs of 512 logits of row b that the select pass
     estimates its admission value from: run s lies in the s-th sixteenth of
     the row (bounds rounded down to multiples of 8), at one of 16 staggered
     offsets."""
+    run = 512
     pos = []
     for s in range(16):
         seg0 = (s * V // 16) & ~7
         seg1 = ((s + 1) * V // 16) & ~7
-        step = ((seg1 - seg0 - 1024) // 16) & ~7
+        step = ((seg1 - seg0 - run) // 16) & ~7
         a = seg0 + ((s * 5 + b * 3) & 15) * step
-        pos.append(np.arange(a, a + 1024))
+        pos.append(np.arange(a, a + run))
     return np.concatenate(pos)
 
 
