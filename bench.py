@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at batch x vocab"
-KERNELS = ["k_plan", "k_pass", "k_fix", "k_rows", "k_fallback", "k_dense"]
+KERNELS = ["k_plan", "k_pass", "k_rows", "k_fallback", "k_dense"]
 
 
 def parse():
@@ -94,8 +94,7 @@ def model_bytes(W, kept):
         ndense += int(filtered.sum()) * 4 * V         # filtered rows: written after the merge
     npass += int(nids.sum()) * 4
     rows = int((kept[sm & filtered]).sum()) * 4 + B * (8 + 9)
-    return {"k_plan": 0, "k_pass": npass, "k_fix": 0, "k_rows": rows, "k_fallback": 0,
-            "k_dense": ndense}
+    return {"k_plan": 0, "k_pass": npass, "k_rows": rows, "k_fallback": 0, "k_dense": ndense}
 
 
 def counted_traffic(kernel):

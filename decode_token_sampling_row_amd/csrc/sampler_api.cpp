@@ -113,18 +113,10 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
     const size_t o_ktoff = off;
     off = align_up(off + B * ((size_t)plan.nt + 1) * sizeof(uint32_t), 256);
-    const size_t o_rowkey = off;
-    off = align_up(off + B * sizeof(uint32_t), 256);
     const size_t o_rowthr = off;
     off = align_up(off + B * sizeof(float), 256);
     const size_t o_rowref = off;
     off = align_up(off + B * sizeof(float), 256);
-    const size_t o_rcand = off;
-    off = align_up(off + B * SLOT * sizeof(uint64_t), 256);
-    const size_t o_rcnt = off;
-    off = align_up(off + B * sizeof(int32_t), 256);
-    const size_t o_rmask = off;
-    off = align_up(off + B * sizeof(uint32_t), 256);
     const size_t o_fbcnt = off;
     off = align_up(off + sizeof(uint32_t), 256);
     const size_t o_fblist = off;
@@ -144,12 +136,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.info = (RowInfo *)(c + o_info);
     s->ws.klist = (uint64_t *)(c + o_klist);
     s->ws.ktoff = (uint32_t *)(c + o_ktoff);
-    s->ws.rowkey = (uint32_t *)(c + o_rowkey);
     s->ws.rowthr = (float *)(c + o_rowthr);
     s->ws.rowref = (float *)(c + o_rowref);
-    s->ws.rcand = (uint64_t *)(c + o_rcand);
-    s->ws.rcnt = (int32_t *)(c + o_rcnt);
-    s->ws.rmask = (uint32_t *)(c + o_rmask);
     s->ws.fbcnt = (uint32_t *)(c + o_fbcnt);
     s->ws.fblist = (uint32_t *)(c + o_fblist);
     s->events_made = false;
@@ -260,29 +248,22 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         return SAMPLER_EHIP;
     launched[1] = true;
     mark(2);
-    if (filtering) {
-        if (!each([&](const KParams &pc) { return launch_fix(pc, l, h->ws, h->dtype, al, st); }))
-            return SAMPLER_EHIP;
-        launched[2] = true;
-    }
-    mark(3);
     if (!each([&](const KParams &pc) { return launch_rows(pc, l, h->ws, st); }))
         return SAMPLER_EHIP;
-    launched[3] = true;
-    mark(4);
-    if (a->top_p != nullptr || a->u != nullptr ||
-        (a->top_k != nullptr && (a->flags & SAMPLER_TOPK_TIES))) {
+    launched[2] = true;
+    mark(3);
+    if (filtering || a->u != nullptr) {
         // one launch over the queue the merge filled, whatever the chunks
         if (launch_fallback(p, l, h->ws, h->dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
-        launched[4] = true;
+        launched[3] = true;
     }
-    mark(5);
+    mark(4);
     if (p.out_probs || (p.out_logits && filtering)) {
         if (!each([&](const KParams &pc) { return launch_dense(pc, l, h->ws, h->dtype, al, st); }))
             return SAMPLER_EHIP;
-        launched[5] = true;
+        launched[4] = true;
     }
-    mark(6);
+    mark(5);
     if (prof) ++h->nprof;
     return SAMPLER_OK;
 }

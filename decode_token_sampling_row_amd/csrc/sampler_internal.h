@@ -14,11 +14,7 @@ constexpr int ROWCAP = 8192;       // candidate entries per row, over all its ti
 constexpr int TCAP_MAX = 2048;     // candidate entries per tile (its four waves)
 constexpr int WCAP_MAX = TCAP_MAX / 4;  // candidate entries per wave
 constexpr int KMAX = 1024;         // largest k / guess
-constexpr int SLOT = 2048;         // entries of a row's exact re-selection
-constexpr int SEL_CAP = 2048;      // entries per half of the exact pass's LDS buffer
-constexpr int SEL_SOFT = 1536;     // exact pass: cut a half back above this fill
-constexpr int SEL_LIMIT = 1536;    // exact pass: most entries a cut-back keeps
-constexpr int VEC = 8;             // elements per group in the exact pass
+constexpr int VEC = 8;             // elements per group of the row helpers
 // Row admission estimate: EST_SEGS runs of EST_SEG logits.
 constexpr int EST_SEGS = 16;
 constexpr int EST_SEG = 512;
@@ -51,12 +47,13 @@ struct ChunkStat {
 struct RowInfo {
     int32_t kind;
     int32_t nK;
-    uint64_t T;    // threshold composite key (KIND_THRESH)
+    uint64_t T;    // threshold composite key (KIND_THRESH); for KIND_FALLBACK a
+                   // floor of the search (0: none; only composites >= T count)
     double ZK;     // sum exp(x - m) over K
     float m;       // row max (transformed)
     float xmin;    // row min finite
     uint32_t idx0; // id of the row maximum (first in order)
-    float vfloor;  // full-row search: only values >= vfloor take part (-inf: all)
+    uint32_t pad;
 };
 
 struct KParams {
@@ -96,12 +93,8 @@ struct KWork {
     RowInfo *info;    // [maxB]
     uint64_t *klist;  // [maxB][KMAX] kept list of rows with a list, grouped by tile
     uint32_t *ktoff;  // [maxB][nt + 1] start of each tile's group in klist
-    uint32_t *rowkey; // [maxB] exact admission key of the row's re-selection
     float *rowthr;    // [maxB] estimated admission value of the row
     float *rowref;    // [maxB] transformed sample maximum (reference for exponentials)
-    uint64_t *rcand;  // [maxB][SLOT] exact re-selection of a row
-    int32_t *rcnt;    // [maxB] entries in rcand
-    uint32_t *rmask;  // [maxB] nonzero: the row's candidates are rcand
     uint32_t *fbcnt;  // [1] rows queued for the full-row top-p search
     uint32_t *fblist; // [maxB] those rows
 };
@@ -111,8 +104,6 @@ hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dty
                        hipStream_t s);
 hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
                        hipStream_t s);
-hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
-                      hipStream_t s);
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                            bool aligned, hipStream_t s);

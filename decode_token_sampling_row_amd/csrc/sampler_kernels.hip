@@ -22,22 +22,24 @@
 //                   tile, q streamed alongside;
 //                 - greedy rows: the argmax;
 //                 - the dense output of rows without a filter.
-//   k_fix       grid = B / 8, one row checked per wave.  A row whose wave
-//               overflowed its sub-slot, or whose handed-over entries above
-//               the admission value number fewer than kk, is selected again
-//               exactly (the page's rolling top-k, LDS buffer cut back by
-//               radix select).
-//   k_rows      grid = B.  Per row: exact top-kk of the candidates by radix
-//               select, softmax in double, the shortest prefix reaching p
-//               (top-k guess accepted with a margin), exponential race over
-//               the kept set (gather of q at the kept ids), output id, the
-//               kept list grouped by tile.  Rows whose guess does not settle
-//               top-p are queued.
-//   k_fallback  grid = min(B, 256) over the queue.  Full-row top-p cutoff: a
-//               value-space mass histogram, then key-space refinement, then
+//   k_rows      grid = B.  Per row: the completeness check of what the pass
+//               handed over (no wave overflowed its sub-slot, and at least kk
+//               entries lie above the admission value's transform -- every
+//               element left out lies at or below it); exact top-kk of the
+//               candidates by radix select, softmax in double, the shortest
+//               prefix reaching p (top-k guess accepted with a margin), the
+//               exponential race over the kept set (gather of q at the kept
+//               ids) or the inverse-CDF draw, output id, the kept list
+//               grouped by tile.  Rows that fail the check, whose guess does
+//               not settle top-p, or that draw by inverse CDF over the whole
+//               row are queued.
+//   k_fallback  grid = min(B, 256) over the queue.  The full-row search: a
+//               value-space histogram of exp masses (or of counts, for the
+//               exact kk-th element of a top-k row), key-space refinement,
 //               an exact sort of the boundary bucket in LDS (or a rank among
-//               ties by vocab id), then the race over the kept set.  This is
-//               the page's full-sort fallback reached without a full sort.
+//               ties by vocab id); then the race or the draw over the kept
+//               set.  This is the page's full-sort fallback reached without a
+//               full sort.
 //   k_dense     grid = B x tiles.  Writes the dense filtered logits (and the
 //               optional probabilities) of filtered rows with full-line
 //               stores, composing each tile in LDS from the kept list.
@@ -121,14 +123,6 @@ __device__ __forceinline__ float xform(float x, uint32_t hit, const KParams &P) 
         if (P.temperature != 1.0f) x = x / P.temperature;
     }
     return x + 0.0f;
-}
-
-// Penalty bits of the 8 elements starting at row-relative offset r (a
-// multiple of 8) of a bitmap that starts at offset 0.
-template <bool XF>
-__device__ __forceinline__ uint32_t pen_bits(const uint32_t *bm, int r, const KParams &P) {
-    if (!XF || !P.pen) return 0u;
-    return (bm[r >> 5] >> (r & 31)) & 0xffu;
 }
 
 // Row index of workgroup i in a grid of n row-workgroups: consecutive
@@ -621,10 +615,7 @@ __device__ __forceinline__ const void *row_ptr(const KParams &P, int dt, int b) 
     return (const char *)P.logits + (int64_t)b * P.ld * (dt == 1 ? 2 : 4);
 }
 
-// ================================================================== chunk passes
-
-constexpr int SEL_THREADS = 512;  // exact selection workgroup
-constexpr int SEL_DEPTH = 4;      // exact selection: batches in flight
+// ================================================================== row helpers
 
 __device__ __forceinline__ int group_nv(int j, int end) {
     const int rem = end - j;
@@ -694,36 +685,6 @@ __device__ __forceinline__ void unpack_raw(const Raw<DT> &r, float (&x)[8]) {
         const Raw<0> &f = reinterpret_cast<const Raw<0> &>(r);
         x[0] = f.a.x; x[1] = f.a.y; x[2] = f.a.z; x[3] = f.a.w;
         x[4] = f.b.x; x[5] = f.b.y; x[6] = f.b.z; x[7] = f.b.w;
-    }
-}
-
-// Issue the loads of one batch (UU groups per thread; row-relative offsets).
-template <int DT, bool AL, int NT, int UU>
-__device__ __forceinline__ void issue_batch(const void *rowp, int base, int c1,
-                                            Raw<DT> (&raw)[UU]) {
-#pragma unroll
-    for (int u = 0; u < UU; ++u) {
-        const int j = base + (u * NT + (int)threadIdx.x) * VEC;
-        load_raw<DT, AL>(rowp, j, group_nv(j, c1), raw[u]);
-    }
-}
-
-// Widen and transform a loaded batch.  FULL: the whole batch lies inside the
-// chunk (no per-element bounds).
-template <int DT, int NT, int UU, bool XF, bool FULL, bool CANON = true>
-__device__ __forceinline__ void finish_batch(const Raw<DT> (&raw)[UU], int base, int c0, int c1,
-                                             const uint32_t *bm, const KParams &P,
-                                             float (&x)[UU][8], int (&jb)[UU], int (&nv)[UU]) {
-#pragma unroll
-    for (int u = 0; u < UU; ++u) {
-        jb[u] = base + (u * NT + (int)threadIdx.x) * VEC;
-        nv[u] = FULL ? 8 : group_nv(jb[u], c1);
-        unpack_raw<DT>(raw[u], x[u]);
-        const uint32_t bits = (FULL || nv[u] > 0) ? pen_bits<XF>(bm, jb[u] - c0, P) : 0u;
-        if (XF || CANON) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[u][i] = xform<XF>(x[u][i], (bits >> i) & 1u, P);
-        }
     }
 }
 
@@ -835,9 +796,9 @@ struct StreamShared {
 // smax receives the sample maximum (raw); active whether the row has top-k
 // or top-p at all (the sample is requested before the row's stages are
 // known, so that the two latencies overlap).
-// Only the speed of the select pass depends on t: that pass checks that what
-// it admitted holds the row's kk largest and redoes the row exactly when it
-// does not.
+// Only the speed depends on t: the row merge checks that what the pass
+// admitted holds the row's kk largest and sends the row to the full-row
+// search when it does not.
 // First element of sample run s of row b (V > EST_N): inside the s-th of
 // EST_SEGS equal segments, at one of 16 offsets that depend on s and b, a
 // multiple of 8.  Staggered so that the runs of all rows do not start at
@@ -944,17 +905,12 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamSha
     return -INFINITY;
 }
 
-// One workgroup per row, before the pass: clears the row's exact-pass key
-// and redo mask, and for rows with top-k or top-p writes the admission
-// estimate.
+// One workgroup per row, before the pass: for rows with top-k or top-p, the
+// admission estimate and the reference of the exponential sums.
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W) {
     __shared__ StreamShared S;
     const int b = P.b0 + (int)blockIdx.x;
-    if (threadIdx.x == 0) {
-        W.rowkey[b] = 0u;
-        W.rmask[b] = 0u;
-    }
     float smax;
     bool active;
     const float t = row_estimate<DT, AL>(P, b, S, smax, active);
@@ -963,416 +919,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
         W.rowthr[b] = t;
         W.rowref[b] = xform<XF>(smax, 0u, P);
     }
-}
-
-// ---------------------------------------------------------------- exact selection
-// Used by k_fix for what the fast pass leaves open.  Keeps a superset of a
-// chunk's kk largest (kk = k, or the top-k guess G for top-p rows without
-// top-k) in an LDS buffer: an element enters when its value key is >= the
-// admission key; when the buffer fills it is cut back to a superset of its kk
-// largest -- with a 256-bin value histogram (the kept part is every entry at
-// or above the bin where the count from the top reaches kk), or an exact
-// radix select when one bin holds too many equal or near-equal values -- and
-// the admission key becomes the smallest kept value.  This is the rolling,
-// prefiltered top-k of the Ascend npu_top_k_top_p_sample page (topK section)
-// with the exact cut deferred to the row merge.
-
-struct SelShared {
-    uint64_t buf[2][SEL_CAP];  // candidate buffer, two halves used in turn
-    uint32_t hist[256];
-    uint32_t sel[4];
-    uint32_t sc[16];
-    uint64_t sc64[16];
-    double scd[16];
-    float scf[16];
-    uint32_t cnt;    // reserved entries of the active half
-    uint32_t ffail;  // first reservation that did not fit
-    uint32_t kcnt;   // entries written by a compaction
-    uint32_t rkey;   // admission key published by the row's other chunks
-    float shi[SEL_THREADS / 64];  // per-wave largest appended value
-};
-
-__device__ __forceinline__ uint32_t bin256(float x, float lo, float scale) {
-    float t = (x - lo) * scale;
-    if (!(t >= 0.0f)) return 0u;
-    if (t >= 255.0f) return 255u;
-    return (uint32_t)t;
-}
-
-__device__ __forceinline__ uint32_t lane_rank(uint64_t bal) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-}
-
-// Workgroup reduction of (count, finite min, max) over SEL_THREADS threads.
-__device__ __forceinline__ void sel_span(SelShared &S, uint32_t &cnt, float &lo, float &hi) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        cnt += shx(cnt, s);
-        lo = fminf(lo, shxf(lo, s));
-        hi = fmaxf(hi, shxf(hi, s));
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        S.sc[w] = cnt;
-        S.scf[w] = lo;
-        S.scf[8 + w] = hi;
-    }
-    __syncthreads();
-    cnt = S.sc[0];
-    lo = S.scf[0];
-    hi = S.scf[8];
-#pragma unroll
-    for (int i = 1; i < SEL_THREADS / 64; ++i) {
-        cnt += S.sc[i];
-        lo = fminf(lo, S.scf[i]);
-        hi = fmaxf(hi, S.scf[8 + i]);
-    }
-    __syncthreads();
-}
-
-// Exact radix select over the entries of src[0..n) whose value key is >=
-// tkey (distinct composites, 1 <= kk < their count), read from LDS in every
-// pass: (v & pmask) >= prefix holds for exactly the kk largest of them.
-// Common high bits are skipped first.
-template <int NT>
-__device__ void radix_select_lds(const uint64_t *src, uint32_t n, uint32_t tkey, uint32_t kk,
-                                 SelShared &S, uint64_t &prefix_out, uint64_t &pmask_out) {
-    uint64_t mn = ~0ull, mx = 0ull;
-    for (uint32_t i = threadIdx.x; i < n; i += NT) {
-        const uint64_t v = src[i];
-        if ((uint32_t)(v >> 32) >= tkey) {
-            mn = v < mn ? v : mn;
-            mx = v > mx ? v : mx;
-        }
-    }
-    mn = wg_min_u64<NT>(mn, S.sc64);
-    mx = wg_max_u64<NT>(mx, S.sc64);
-    const uint64_t diff = mn ^ mx;
-    if (diff == 0) {
-        prefix_out = mx;
-        pmask_out = ~0ull;
-        return;
-    }
-    int hi = 63 - __clzll(diff);
-    uint64_t pmask = (hi == 63) ? 0ull : (~0ull << (hi + 1));
-    uint64_t prefix = mx & pmask;
-    uint32_t need = kk;
-    for (;;) {
-        const int width = hi + 1 < 8 ? hi + 1 : 8;
-        const int shift = hi + 1 - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n; i += NT) {
-            const uint64_t v = src[i];
-            if ((uint32_t)(v >> 32) >= tkey && (v & pmask) == prefix)
-                atomicAdd(&S.hist[(uint32_t)(v >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        wave0_find_bin(S.hist, need, S.sel);
-        __syncthreads();
-        const uint32_t d = S.sel[0], above = S.sel[1], cntd = S.sel[2];
-        need -= above;
-        prefix |= (uint64_t)d << shift;
-        pmask |= (uint64_t)dmask << shift;
-        if (cntd == need || shift == 0) break;
-        hi = shift - 1;
-    }
-    prefix_out = prefix;
-    pmask_out = pmask;
-}
-
-// Cut S.buf[half][0..n) (n > kk) back to a superset of the kk largest of its
-// entries whose value key is >= tkey, holding at most `limit` entries (limit
-// >= kk): every such entry at or above the 256-bin value-histogram bin where
-// the count from the top reaches kk -- bins span [value(tkey), hi], hi an
-// upper bound of the buffer -- or exactly the kk largest when that bin is too
-// full.  The survivors go to the other half.  Returns their count; when at
-// least kk survive, tkey rises to the smallest surviving key.
-__device__ uint32_t sel_reduce(SelShared &S, int half, uint32_t n, uint32_t kk, uint32_t limit,
-                               uint32_t &tkey, float hi) {
-    constexpr int NT = SEL_THREADS;
-    const uint64_t *src = S.buf[half];
-    uint64_t *dst = S.buf[half ^ 1];
-    float lo = key2f(tkey);
-    if (tkey == 0u) {
-        // no floor yet: take the smallest finite value in the buffer
-        lo = INFINITY;
-        for (uint32_t i = threadIdx.x; i < n; i += NT) {
-            const float xv = cval(src[i]);
-            if (xv > -INFINITY) lo = fminf(lo, xv);
-        }
-        uint32_t dummy = 0;
-        float dh = -INFINITY;
-        sel_span(S, dummy, lo, dh);
-    }
-    if (threadIdx.x == 0) S.kcnt = 0;
-    bool exact = true;
-    uint32_t bstar = 0;
-    float scale = 0.0f;
-    if (hi > lo && lo > -INFINITY) {
-        scale = 256.0f / (hi - lo);
-        for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n; i += NT) {
-            const uint64_t v = src[i];
-            if ((uint32_t)(v >> 32) >= tkey) atomicAdd(&S.hist[bin256(cval(v), lo, scale)], 1u);
-        }
-        __syncthreads();
-        // fewer than kk entries at or above the floor: keep them all
-        uint32_t tot = 0;
-        if (threadIdx.x < 64) {
-            const uint32_t t4 = S.hist[4 * threadIdx.x] + S.hist[4 * threadIdx.x + 1] +
-                                S.hist[4 * threadIdx.x + 2] + S.hist[4 * threadIdx.x + 3];
-            tot = t4;
-#pragma unroll
-            for (int sft = 32; sft >= 1; sft >>= 1) tot += shx(tot, sft);
-            if (threadIdx.x == 0) S.sel[3] = tot;
-        }
-        __syncthreads();
-        tot = S.sel[3];
-        if (tot <= kk) {
-            bstar = 0;
-            exact = false;
-        } else {
-            wave0_find_bin(S.hist, kk, S.sel);
-            __syncthreads();
-            bstar = S.sel[0];
-            exact = S.sel[1] + S.sel[2] > limit;
-        }
-    }
-    uint64_t prefix = 0, pmask = 0;
-    if (exact) {
-        uint32_t cnt = 0;
-        for (uint32_t i = threadIdx.x; i < n; i += NT) cnt += (uint32_t)(src[i] >> 32) >= tkey;
-        float l2 = 0.0f, h2 = 0.0f;
-        sel_span(S, cnt, l2, h2);
-        if (cnt > kk) {
-            radix_select_lds<NT>(src, n, tkey, kk, S, prefix, pmask);
-        } else {
-            exact = false;  // keep every entry at or above the floor
-            bstar = 0;
-            scale = 0.0f;
-            lo = 0.0f;
-        }
-    }
-    const int lane = threadIdx.x & 63;
-    uint32_t mk = NONE;
-    const uint32_t rounds = (n + NT - 1) / NT;
-    for (uint32_t rd = 0; rd < rounds; ++rd) {
-        const uint32_t i = rd * NT + threadIdx.x;
-        const uint64_t v = (i < n) ? src[i] : 0ull;
-        bool keep = i < n && (uint32_t)(v >> 32) >= tkey;
-        if (keep) keep = exact ? ((v & pmask) >= prefix) : (bin256(cval(v), lo, scale) >= bstar);
-        const uint64_t bal = __ballot(keep);
-        if (bal == 0) continue;
-        uint32_t wbase = 0;
-        if (lane == 0) wbase = atomicAdd(&S.kcnt, (uint32_t)__popcll(bal));
-        wbase = (uint32_t)__shfl((int)wbase, 0, 64);
-        if (keep) {
-            dst[wbase + lane_rank(bal)] = v;
-            const uint32_t k = (uint32_t)(v >> 32);
-            mk = k < mk ? k : mk;
-        }
-    }
-    mk = wg_min_u32<NT>(mk, S.sc);
-    const uint32_t kept = S.kcnt;
-    if (kept >= kk && mk != NONE && mk > tkey) tkey = mk;
-    return kept;
-}
-
-// Append the elements of one group of 8 (values x[], first id j, nv valid)
-// with x >= tval to the active half: one LDS reservation per wave, slots
-// placed with ballots; hi tracks the largest value appended.  Returns true
-// when the wave's reservation did not fit (nothing written; the group stays
-// pending).
-template <bool FULL>
-__device__ __forceinline__ bool sel_append(SelShared &S, int half, const float (&x)[8], uint32_t j,
-                                           int nv, float tval, float &hi) {
-    const int lane = threadIdx.x & 63;
-    uint64_t bal[8];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        bal[i] = __ballot((FULL || i < nv) && x[i] >= tval);
-        tot += (uint32_t)__popcll(bal[i]);
-    }
-    if (tot == 0) return false;
-    uint32_t wbase = 0;
-    if (lane == 0) wbase = atomicAdd(&S.cnt, tot);
-    wbase = (uint32_t)__shfl((int)wbase, 0, 64);
-    if (wbase + tot > (uint32_t)SEL_CAP) {
-        if (lane == 0) atomicMin(&S.ffail, wbase);
-        return true;
-    }
-    uint64_t *dst = S.buf[half];
-    uint32_t off = wbase;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (bal[i] == 0) continue;
-        if ((bal[i] >> lane) & 1ull) {
-            const float xc = x[i] + 0.0f;  // -0 -> +0 before the key
-            dst[off + lane_rank(bal[i])] = mkcomp(xc, j + i);
-            hi = fmaxf(hi, xc);
-        }
-        off += (uint32_t)__popcll(bal[i]);
-    }
-    return false;
-}
-
-__device__ __forceinline__ float key_floor(uint32_t tkey) {
-    return tkey ? key2f(tkey) : -INFINITY;
-}
-
-// Admission key from one group of 8 per thread held in registers (the first
-// batch of a chunk): a value key k such that at least kk of the batch's
-// elements have key >= k, taken at the 256-bin histogram bin where the
-// count from the top reaches kk.  0 (admit everything) when the batch has
-// fewer than kk elements.
-__device__ uint32_t batch_key(SelShared &S, const float (&x)[8], int nv, uint32_t kk) {
-    uint32_t cnt = 0;
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (i < nv) {
-            ++cnt;
-            if (x[i] > -INFINITY) {
-                lo = fminf(lo, x[i]);
-                hi = fmaxf(hi, x[i]);
-            }
-        }
-    sel_span(S, cnt, lo, hi);
-    if (cnt < kk || !(hi > lo)) return 0u;
-    const float scale = 256.0f / (hi - lo);
-    for (int i = threadIdx.x; i < 256; i += SEL_THREADS) S.hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (i < nv) atomicAdd(&S.hist[bin256(x[i], lo, scale)], 1u);
-    __syncthreads();
-    wave0_find_bin(S.hist, kk, S.sel);
-    __syncthreads();
-    const uint32_t bstar = S.sel[0];
-    uint32_t mk = NONE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (i < nv && bin256(x[i], lo, scale) >= bstar) mk = min(mk, f2key(x[i] + 0.0f));
-    mk = wg_min_u32<SEL_THREADS>(mk, S.sc);
-    return mk == NONE ? 0u : mk;
-}
-
-// One batch before the workgroup barrier: widen/transform, top-p statistics,
-// the first batch's admission key, and the append.  Returns true when this
-// wave's append did not fit.
-template <int DT, bool XF, bool FULL>
-__device__ __forceinline__ bool select_front(SelShared &S, const Raw<DT> &cur, int base, int c0,
-                                             int c1, const uint32_t *bm, const KParams &P,
-                                             bool do_stats, Stats &st, bool &first, uint32_t kk,
-                                             uint32_t &tkey, uint32_t &rk_seen, uint32_t *rowkey,
-                                             int half, float &hi, float (&xo)[8], int &j0,
-                                             int &nv0) {
-    float x[1][8];
-    int jb[1], nv[1];
-    finish_batch<DT, SEL_THREADS, 1, XF, FULL, false>(*(const Raw<DT>(*)[1]) & cur, base, c0, c1,
-                                                      bm, P, x, jb, nv);
-    if (do_stats) stats_batch(st, x, nv);
-    if (first) {
-        // the first batch sets the admission key from its own values
-        first = false;
-        tkey = batch_key(S, x[0], nv[0], kk);
-        if (threadIdx.x == 0 && tkey) rk_seen = atomicMax(rowkey, tkey);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xo[i] = x[0][i];
-    j0 = jb[0];
-    nv0 = nv[0];
-    return sel_append<FULL>(S, half, x[0], (uint32_t)j0, nv0, key_floor(tkey), hi);
-}
-
-// Exact selection over the chunk [c0, c1) of row b, appended to the `valid`
-// entries already in S.buf[half] (hi: an upper bound of their values, or
-// -inf): on return S.buf[half] holds `valid` entries, and every element of
-// the chunk and of the earlier entries that is among their kk largest, or
-// whose value key is >= the returned tkey (tkey only rises), is among them.
-// tkey on entry is a valid admission key for the row (0 = none).  The
-// penalty bitmap bm must describe [c0, c1).
-template <int DT, bool AL, bool XF>
-__device__ void select_exact(SelShared &S, const KParams &P, const uint32_t *bm,
-                             const void *rowp, int c0, int c1, uint32_t kk, bool do_stats,
-                             Stats &st, uint32_t *rowkey, uint32_t &tkey, int &half,
-                             uint32_t &valid, float &hi) {
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        S.cnt = valid;
-        S.ffail = NONE;
-    }
-    __syncthreads();
-    uint32_t rk_seen = 0;  // thread 0: row key returned by the last publication
-    bool first = true;
-    constexpr int BATCH = SEL_THREADS * VEC;
-    Raw<DT> ring[SEL_DEPTH];
-#pragma unroll
-    for (int d = 0; d < SEL_DEPTH; ++d)
-        if (c0 + d * BATCH < c1)
-            issue_batch<DT, AL, SEL_THREADS, 1>(rowp, c0 + d * BATCH, c1, *(Raw<DT>(*)[1]) & ring[d]);
-    for (int base = c0; base < c1; base += BATCH) {
-        const Raw<DT> cur = ring[0];
-#pragma unroll
-        for (int d = 0; d + 1 < SEL_DEPTH; ++d) ring[d] = ring[d + 1];
-        if (base + SEL_DEPTH * BATCH < c1)
-            issue_batch<DT, AL, SEL_THREADS, 1>(rowp, base + SEL_DEPTH * BATCH, c1,
-                                               *(Raw<DT>(*)[1]) & ring[SEL_DEPTH - 1]);
-        float x[8];
-        int j0, nv0;
-        const uint32_t tk_in = tkey;
-        bool pending =
-            (base + BATCH <= c1)
-                ? select_front<DT, XF, true>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
-                                             tkey, rk_seen, rowkey, half, hi, x, j0, nv0)
-                : select_front<DT, XF, false>(S, cur, base, c0, c1, bm, P, do_stats, st, first, kk,
-                                              tkey, rk_seen, rowkey, half, hi, x, j0, nv0);
-        tkey = max(tkey, tk_in);
-        __syncthreads();
-        uint32_t ff = S.ffail;
-        valid = min(S.cnt, ff);
-        bool ovf = ff != NONE;
-        while (ovf || valid > (uint32_t)SEL_SOFT) {
-            // adopt the key the row's other chunks have published, cut back
-            float h = hi;
-#pragma unroll
-            for (int sft = 32; sft >= 1; sft >>= 1) h = fmaxf(h, shxf(h, sft));
-            if ((tid & 63) == 0) S.shi[tid >> 6] = h;
-            if (tid == 0) S.rkey = rk_seen;
-            __syncthreads();
-            tkey = max(tkey, S.rkey);
-            h = S.shi[0];
-#pragma unroll
-            for (int i = 1; i < SEL_THREADS / 64; ++i) h = fmaxf(h, S.shi[i]);
-            const uint32_t kept = sel_reduce(S, half, valid, kk, SEL_LIMIT, tkey, h);
-            half ^= 1;
-            if (tid == 0) {
-                S.cnt = kept;
-                S.ffail = NONE;
-                rk_seen = atomicMax(rowkey, tkey);
-            }
-            __syncthreads();
-            valid = kept;
-            if (!ovf) break;
-            if (pending) pending = sel_append<false>(S, half, x, (uint32_t)j0, nv0, key_floor(tkey), hi);
-            __syncthreads();
-            ff = S.ffail;
-            valid = min(S.cnt, ff);
-            ovf = ff != NONE;
-        }
-    }
-    // the latest row key bounds every chunk's output
-    if (tid == 0)
-        S.rkey = max(rk_seen,
-                     (uint32_t)__hip_atomic_load(rowkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    __syncthreads();
-    tkey = max(tkey, S.rkey);
-    __syncthreads();
 }
 
 // ---------------------------------------------------------------- k_pass
@@ -1389,7 +935,8 @@ __device__ void select_exact(SelShared &S, const KParams &P, const uint32_t *bm,
 //    row_estimate), each wave appending to its own sub-slot, and statistics
 //    for rows without top-k; their dense output is written once the kept
 //    set is known (k_dense), in whole lines.  A wave whose admissions exceed
-//    its sub-slot (L.wcap) marks it overflowed; k_fix then redoes the row.
+//    its sub-slot (L.wcap) marks it overflowed; the row merge then sends the
+//    row to the full-row search.
 
 constexpr int PASS_THREADS = 256;
 constexpr int PASS_WAVES = PASS_THREADS / 64;
@@ -1475,6 +1022,12 @@ template <bool XF>
 __device__ __forceinline__ uint32_t pen_bits4(const uint32_t *bm, int r, const KParams &P) {
     if (!XF || !P.pen) return 0u;
     return (bm[r >> 5] >> (r & 31)) & 0xfu;
+}
+
+// Rank of this lane among the lanes set in a wave ballot.
+__device__ __forceinline__ uint32_t lane_rank(uint64_t bal) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
 // ---- wave-level reductions (every lane gets the result)
@@ -1832,102 +1385,6 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
         pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
 }
 
-// ---------------------------------------------------------------- k_fix
-// Exact selection, one workgroup per top-k / top-p row, for what the pass
-// could not settle: a row with a wave that overflowed its sub-slot, or a row
-// where fewer than kk of the handed-over entries lie above the estimate's
-// transform yt (so its kk-th largest may be an element left out; those all
-// have y <= yt).  The whole row is selected again, segment by segment, into
-// the row's redo slot, which then replaces its tiles.
-
-// Copy the entries of S.buf[half][0..n) whose value key is >= tkey to dst;
-// their number ends in S.kcnt.
-__device__ void copy_out(SelShared &S, int half, uint32_t n, uint32_t tkey, uint64_t *dst) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    if (tid == 0) S.kcnt = 0;
-    __syncthreads();
-    const uint32_t rounds = (n + SEL_THREADS - 1) / SEL_THREADS;
-    for (uint32_t rd = 0; rd < rounds; ++rd) {
-        const uint32_t i = rd * SEL_THREADS + tid;
-        const uint64_t v = (i < n) ? S.buf[half][i] : 0ull;
-        const bool keep = i < n && (uint32_t)(v >> 32) >= tkey;
-        const uint64_t bal = __ballot(keep);
-        if (bal == 0) continue;
-        uint32_t wbase = 0;
-        if (lane == 0) wbase = atomicAdd(&S.kcnt, (uint32_t)__popcll(bal));
-        wbase = (uint32_t)__shfl((int)wbase, 0, 64);
-        if (keep) dst[wbase + lane_rank(bal)] = v;
-    }
-    __syncthreads();
-}
-
-template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(SEL_THREADS, 4) void k_fix(KParams P, KPlan L, KWork W) {
-    __shared__ SelShared S;
-    extern __shared__ uint32_t bm[];  // penalty bitmap of one segment
-    constexpr int RPW = SEL_THREADS / 64;  // rows per workgroup, one checked per wave
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int ns = L.nt * PASS_WAVES;  // wave sub-slots of a row
-    {
-        // wave w checks row RPW * blockIdx + w: its sub-slots read in
-        // parallel for the overflow flag and the strict count
-        const int rb = (int)blockIdx.x * RPW + (tid >> 6);
-        uint32_t redo = 0;
-        if (rb < P.B) {
-            const int b = P.b0 + rb;
-            const Mode md = row_mode(P, b);
-            if (md.tk || md.tp) {
-                uint32_t o = 0, st_cnt = 0;
-                for (int i = lane; i < ns; i += 64) {
-                    const uint32_t v = W.wcnt[(int64_t)b * ns + i];
-                    if (v == 0xffffffffu) o = 1;
-                    else st_cnt += v >> 16;
-                }
-#pragma unroll
-                for (int sft = 32; sft >= 1; sft >>= 1) {
-                    o |= shx(o, sft);
-                    st_cnt += shx(st_cnt, sft);
-                }
-                const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-                const float traw = W.rowthr[b];
-                // with traw = -inf every element was admitted, so no check
-                redo = (o != 0u || (traw > -INFINITY && st_cnt < kk)) ? 1u : 0u;
-            }
-        }
-        if (lane == 0) S.sc[tid >> 6] = redo;
-    }
-    __syncthreads();
-    uint32_t flags = 0;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) flags |= (S.sc[i] != 0u ? 1u : 0u) << i;
-    __syncthreads();
-    // the rows to redo, one after another with the whole workgroup
-    for (int i = 0; i < RPW; ++i) {
-        if (!((flags >> i) & 1u)) continue;
-        const int b = P.b0 + (int)blockIdx.x * RPW + i;
-        const Mode md = row_mode(P, b);
-        const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-        const void *rowp = row_ptr(P, DT, b);
-        Stats st;  // unused: the tile statistics come from the pass
-        st.m = -INFINITY; st.xmin = INFINITY; st.z = 0.0;
-        uint32_t tkey = 0, valid = 0;
-        int half = 0;
-        float hi = -INFINITY;
-        for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
-            const int s1 = min(s0 + K3_SEG, P.V);
-            if (XF && P.pen) build_bitmap<SEL_THREADS>(bm, s0, s1 - s0, P, b);
-            select_exact<DT, AL, XF>(S, P, bm, rowp, s0, s1, kk, false, st, W.rowkey + b, tkey,
-                                     half, valid, hi);
-        }
-        copy_out(S, half, valid, tkey, W.rcand + (int64_t)b * SLOT);
-        if (tid == 0) {
-            W.rcnt[b] = (int32_t)S.kcnt;
-            W.rmask[b] = 1u;
-        }
-        __syncthreads();  // the next row reuses the shared buffers
-    }
-}
-
 // ================================================================== k_rows
 // Per row, one workgroup of ROWS_THREADS: the exact kk largest of the row's
 // candidates (held in registers, radix select), ordered only as far as top-p
@@ -2118,7 +1575,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.m = -INFINITY;
     info.xmin = INFINITY;
     info.idx0 = NONE;
-    info.vfloor = -INFINITY;
+    info.pad = 0;
 
     if (!filtered) {
         // merge the tiles' winners: the race by ratio (lowest id on a tie),
@@ -2175,21 +1632,43 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         return;
     }
 
-    // ---- candidates of the row: the waves' sub-slots, or the redo slot
+    // ---- candidates of the row: the waves' sub-slots
     const uint32_t kk = md.tk ? (uint32_t)md.k : (uint32_t)min(P.guess, P.V);
-    const bool redone = W.rmask[b] != 0u;
+    const float traw = W.rowthr[b];
     const uint64_t *rowc = W.cand + (int64_t)b * ROWCAP;
-    const uint64_t *redc = W.rcand + (int64_t)b * SLOT;
     uint32_t N;
-    if (redone) {
-        N = (uint32_t)W.rcnt[b];
-    } else {
-        // exclusive prefix of the sub-slot counts (none overflowed here)
+    {
+        // the sub-slot counts: exclusive prefix, overflows, and the entries
+        // above the estimate's transform
         const int per = (nt + NT - 1) / NT;
-        uint32_t loc = 0;
+        uint32_t loc = 0, chk = 0;  // chk: strict count + overflows << 16
         for (int i = 0; i < per; ++i) {
             const int t = tid * per + i;
-            if (t < nt) loc += W.wcnt[b * nt + t] & 0xffffu;
+            if (t < nt) {
+                const uint32_t v = W.wcnt[b * nt + t];
+                if (v == 0xffffffffu) {
+                    chk += 1u << 16;
+                } else {
+                    loc += v & 0xffffu;
+                    chk += v >> 16;
+                }
+            }
+        }
+        uint32_t tchk;
+        (void)wg_excl_scan_u32<NT>(chk, S.sc, tchk);
+        // The fast result is complete iff no wave overflowed and, unless the
+        // estimate admitted everything, at least kk handed-over entries lie
+        // above its transform (every element left out lies at or below it).
+        // Otherwise the full-row search selects the row exactly.
+        if ((tchk >> 16) != 0u || (traw > -INFINITY && (tchk & 0xffffu) < kk)) {
+            info.kind = KIND_FALLBACK;
+            info.idx0 = NONE;  // the row maximum is found by the search
+            info.T = 0;
+            if (tid == 0) {
+                W.info[b] = info;
+                W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
+            }
+            return;
         }
         uint32_t run = wg_excl_scan_u32<NT>(loc, S.sc, N);
         for (int i = 0; i < per; ++i) {
@@ -2203,9 +1682,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         __syncthreads();
     }
     const uint32_t tcap = (uint32_t)L.wcap;
-    // entry e of the row's candidates, wherever it lives
+    // entry e of the row's candidates
     auto gget = [&](uint32_t e) -> uint64_t {
-        if (redone) return redc[e];
         int lo = 0, hi = nt;  // toff[lo] <= e < toff[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -2222,9 +1700,10 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     uint32_t nsel = min(kk, N);
     const bool inreg = N <= (uint32_t)RCAP;
     // top-k keeping the ties at the k-th value: the selection grows to every
-    // candidate with that value (the candidates hold all of them unless the
-    // row was selected again exactly); a row where that cannot be done here
-    // goes to the full-row search with the k-th value as its floor
+    // candidate with that value (the candidates hold all of them: every
+    // element left out lies at or below the estimate's transform, below the
+    // k-th value); a group too large for the list goes to the full-row
+    // search with the k-th value as its floor
     const bool ties = md.tk && (P.flags & TOPK_TIES) != 0;
     bool to_search = false;
     uint32_t kmin = 0;  // value key of the k-th largest (ties rows)
@@ -2232,20 +1711,18 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     uint64_t v[R];
     uint32_t vm = 0;
     if (inreg) {
-        if (!redone) {
-            // where candidate e lives, written slot by slot (a lookup per
-            // candidate instead of a search over the slot offsets)
-            for (int t = tid; t < nt; t += NT) {
-                const uint32_t e0 = toff[t], e1 = toff[t + 1];
-                for (uint32_t e = e0; e < e1; ++e) S.addr[e] = (uint32_t)t * tcap + (e - e0);
-            }
-            __syncthreads();
+        // where candidate e lives, written slot by slot (a lookup per
+        // candidate instead of a search over the slot offsets)
+        for (int t = tid; t < nt; t += NT) {
+            const uint32_t e0 = toff[t], e1 = toff[t + 1];
+            for (uint32_t e = e0; e < e1; ++e) S.addr[e] = (uint32_t)t * tcap + (e - e0);
         }
+        __syncthreads();
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t e = (uint32_t)(r * NT + tid);
             if (e < N) {
-                v[r] = redone ? redc[e] : rowc[S.addr[e]];
+                v[r] = rowc[S.addr[e]];
                 vm |= 1u << r;
             } else {
                 v[r] = 0ull;
@@ -2281,7 +1758,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 if (((vm >> r) & 1u) && (uint32_t)(v[r] >> 32) >= kmin) km2 |= 1u << r;
             uint32_t n1;
             (void)wg_excl_scan_u32<NT>(__popc(km2), S.sc, n1);
-            if (redone || n1 > (uint32_t)KMAX) {
+            if (n1 > (uint32_t)KMAX) {
                 to_search = true;
             } else {
                 km = km2;
@@ -2337,7 +1814,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         info.kind = KIND_FALLBACK;
         info.m = x0;
         info.idx0 = cidx(top);
-        info.vfloor = key2f(kmin);
+        info.T = (uint64_t)kmin << 32;  // the floor: every value >= the k-th
         if (tid == 0) {
             W.info[b] = info;
             W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
@@ -2700,14 +2177,27 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     const int b = (int)W.fblist[qi];
     RowInfo info = W.info[b];
     const Mode md = row_mode(P, b);
+    if (info.idx0 == NONE) {
+        // a row the merge found incomplete: its maximum (the first element of
+        // the order) from one pass over the row
+        uint64_t mx = 0;
+        row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
+            const uint64_t c = mkcomp(x, j);
+            mx = c > mx ? c : mx;
+        });
+        mx = wg_max_u64<K3_THREADS>(mx, S.sc64);
+        info.m = cval(mx);
+        info.idx0 = cidx(mx);
+    }
     const double m = (double)info.m;
-    const float vfloor = info.vfloor;  // values below take no part (top-k floor)
+    uint64_t cfloor = info.T;  // only composites >= cfloor take part (0: all)
 
-    // The least element T* (a composite) of the row's order at which the mass
-    // exp(x - m) summed from the top reaches the target -- tval times the
-    // row's total (found on the first pass) when frac, else tval itself --
-    // and ZKo, the mass through T*.
-    auto search = [&](double tval, bool frac, uint64_t &Tst, double &ZKo) {
+    // The least element T* (a composite) of the row's order at which the
+    // weight summed from the top reaches the target -- tval times the total
+    // weight (found on the first pass) when frac, else tval itself -- and
+    // ZKo, the weight through T*.  The weight of an element is exp(x - m), or
+    // 1 when count (then -inf values count too).
+    auto search = [&](double tval, bool frac, bool count, uint64_t &Tst, double &ZKo) {
         double above = 0.0, target = 0.0;
         int nlev = 0;
         int path = 0;  // 1 collect, 2 ties
@@ -2735,10 +2225,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             __syncthreads();
             double zt = 0.0;
             row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-                if (!(x > -INFINITY) || x < vfloor) return;
+                if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
-                double e = exp((double)x - m);
+                double e = count ? 1.0 : exp((double)x - m);
                 if (level == 0) zt += e;
                 uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, span);
                 atomicAdd(&S.hm[bi], e);
@@ -2788,7 +2278,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (tid == 0) S.counter = 0;
             __syncthreads();
             row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-                if (!(x > -INFINITY) || x < vfloor) return;
+                if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
                 uint32_t pos = atomicAdd(&S.counter, 1u);
@@ -2806,7 +2296,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 #pragma unroll
             for (int t = 0; t < PER; ++t) {
                 int i = tid * PER + t;
-                ei[t] = (i < n) ? exp((double)cval(S.coll[i]) - m) : 0.0;
+                ei[t] = (i < n) ? (count ? 1.0 : exp((double)cval(S.coll[i]) - m)) : 0.0;
                 loc += ei[t];
             }
             double tot;
@@ -2833,7 +2323,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             // every bucket member has the same value: take the c members with
             // the smallest vocab ids
             const float xt = key2f(bklo);
-            const double et = exp((double)xt - m);
+            const double et = count ? 1.0 : exp((double)xt - m);
             double cnt_need = ceil((target - above) / et);
             uint32_t cneed = (cnt_need < 1.0) ? 1u : (cnt_need > (double)bcnt ? bcnt : (uint32_t)cnt_need);
             // c-th smallest index among elements equal to xt: scan in index order
@@ -2882,30 +2372,36 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
     };
 
-    // Up to two searches, from one call site: (0) the top-p cut at p -- or,
-    // for a row queued only for an inverse-CDF draw over the whole row, that
-    // draw at u; (1) the draw inside the cut at u ZK.  A level <= 0 (or NaN)
-    // stands for the first element of the order.
+    // Up to three searches, from one call site: (0) for a top-k row without a
+    // known floor, its kk-th element by count, which becomes the floor (its
+    // value, when ties are kept); (1) the top-p cut at p -- or, for a row
+    // queued only for an inverse-CDF draw over the whole row, that draw at u;
+    // (2) the draw inside the cut at u ZK.  A level <= 0 (or NaN) stands for
+    // the first element of the order.
     const bool whole = info.kind == KIND_UNFILTERED;
     const uint64_t top = mkcomp(info.m, info.idx0);
     uint64_t Tstar = top;  // the cut (or the whole-row draw)
     double ZK = 1.0;       // mass of the cut, exp(x - m) summed
     uint64_t Tdraw = top;  // the draw inside the cut
-    const bool floor_only = !whole && !md.tp;  // a top-k row keeping its ties
-    if (floor_only) {
-        // the cut is every value >= the floor
-        Tstar = (uint64_t)f2key(vfloor) << 32;
-        double z = 0.0;
-        row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-            if (x >= vfloor) z += exp((double)x - m);
-        });
-        ZK = wg_sum_f64<K3_THREADS>(z, S.scd);
-    }
-    for (int job = 0; job < 2; ++job) {
+    for (int job = 0; job < 3; ++job) {
         double tval;
-        bool frac;
+        bool frac, count = false;
         if (job == 0) {
-            if (floor_only) continue;
+            if (whole || !md.tk || cfloor != 0) continue;
+            tval = (double)md.k;
+            frac = false;
+            count = true;
+        } else if (job == 1) {
+            if (!whole && !md.tp) {
+                // top-k alone: the cut is the floor
+                Tstar = cfloor;
+                double z = 0.0;
+                row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
+                    if (mkcomp(x, j) >= cfloor) z += exp((double)x - m);
+                });
+                ZK = wg_sum_f64<K3_THREADS>(z, S.scd);
+                continue;
+            }
             const double level = whole ? (double)P.u[b] : (double)md.p;
             if (!(level > 0.0)) continue;
             tval = level;
@@ -2917,8 +2413,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
         uint64_t Tj;
         double Zj;
-        search(tval, frac, Tj, Zj);
+        search(tval, frac, count, Tj, Zj);
         if (job == 0) {
+            cfloor = (P.flags & TOPK_TIES) ? (Tj >> 32) << 32 : Tj;
+        } else if (job == 1) {
             Tstar = Tj;
             ZK = Zj;
         } else {
@@ -3142,15 +2640,6 @@ hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dty
     dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(PASS_THREADS);
     size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
     return SMP_PICK(k_pass, grid, block, sh);
-}
-
-hipError_t launch_fix(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
-                      hipStream_t s) {
-    const bool xf = any_transform(p);
-    constexpr int RPW = SEL_THREADS / 64;  // rows per workgroup
-    dim3 grid((unsigned)((p.B + RPW - 1) / RPW)), block(SEL_THREADS);
-    size_t sh = p.pen ? (size_t)(K3_SEG / 32) * 4 : 0;
-    return SMP_PICK(k_fix, grid, block, sh);
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {

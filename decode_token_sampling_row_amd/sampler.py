@@ -24,7 +24,7 @@ SAMPLER_VOCAB_MAX = 1 << 21
 
 EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_profile",
            "sampler_destroy", "sampler_strerror")
-SAMPLER_PROFILE_SLOTS = 6
+SAMPLER_PROFILE_SLOTS = 5
 
 
 class SamplerError(RuntimeError):

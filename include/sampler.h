@@ -72,7 +72,7 @@ extern "C" {
                                    are masked), so more than k may survive  */
 #define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
                                    averages with sampler_profile             */
-#define SAMPLER_PROFILE_SLOTS 6
+#define SAMPLER_PROFILE_SLOTS 5
 
 /* Largest k of the top-k stage and largest top-k guess. */
 #define SAMPLER_TOPK_MAX 1024
@@ -133,7 +133,7 @@ typedef struct sampler_args {
 /*
  * Create a handle for batches of at most max_batch rows of vocab V logits of
  * the given storage type on the current HIP device.  Allocates the device
- * workspace (about 100 KiB per row at the default segment length).  opts
+ * workspace (about 80 KiB per row at the default segment length).  opts
  * may be NULL.
  * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
  * (max_batch < 1, V < 1 or > SAMPLER_VOCAB_MAX, unknown dtype, bad opts),
@@ -169,9 +169,9 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
  * with SAMPLER_PROFILE since the previous sampler_profile call (the last 64
  * of them if there were more), in launch order: [0] per-row planning (the
  * admission estimate of top-k / top-p rows), [1] the streaming pass over the
- * logits (every row), [2] exact selection of what the pass left open, [3]
- * row merge / cutoff / sample, [4] full-row top-p cutoff (rows whose guess
- * failed), [5] dense probabilities.  Each time runs from an event recorded
+ * logits (every row), [2] row merge / cutoff / sample, [3] full-row search
+ * (rows the pass could not settle, top-p rows whose guess failed, inverse-CDF
+ * draws over whole rows), [4] dense outputs of filtered rows.  Each time runs from an event recorded
  * on the call's stream just before the kernel to one recorded just after
  * it.  Kernels that were not launched count 0.  Waits for the last profiled
  * call to finish, then forgets the calls it averaged.
