@@ -114,6 +114,19 @@ def test_segment_boundaries(V):
     _check(W, f"segments V={V}")
 
 
+@pytest.mark.parametrize("seg", [0, 1024])
+def test_largest_vocab(seg):
+    """V = 2^21, the largest the library accepts; with 1024-element tiles a
+    wave's sub-slot holds a single candidate, so many rows overflow and take
+    the full-row search."""
+    rng = np.random.default_rng(41)
+    B, V = 8, 1 << 21
+    x = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+    k = np.array([1024, 7, 1, 0, 1024, 300, 0, 1000])
+    W = _custom(x, top_k=k, top_p=0.9, flags=_all_combos(B), dtype=wl.BF16)
+    _check(W, f"V=2^21 seg={seg}", need_probs=False, seg=seg)
+
+
 def test_k_equals_vocab_and_cap():
     rng = np.random.default_rng(3)
     for V, ks in [(700, [700, 699, 1, 701]), (1024, [1024, 1023]), (5000, [1024, 1025])]:
