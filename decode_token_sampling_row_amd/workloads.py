@@ -210,3 +210,58 @@ def make(cfg: int, B: Optional[int] = None, V: Optional[int] = None, seed: int =
         args["V"] = V
     args.update(kw)
     return fn(seed=seed, **args)
+
+
+@dataclass
+class DecodeLoop:
+    """Inputs of several decode steps over one batch (the MiniMind generation
+    loop's shape: one logits row per sequence and step, a history that grows
+    by one id per step).  Per step, logits[s] is [B, V] in the storage dtype
+    and q[s] / u[s] are fresh random numbers; the history is a CSR of slots
+    (prompt ids first, then filler ids that are not history), with per-row
+    capacities, a few rows already finished, and an EOS logit that rises
+    over the steps at a row-dependent rate so that rows end at different
+    steps."""
+    B: int
+    V: int
+    dtype: str
+    eos: int
+    logits: list
+    q: list
+    u: list
+    top_k: np.ndarray
+    top_p: np.ndarray
+    row_flags: np.ndarray
+    ids: np.ndarray
+    offsets: np.ndarray
+    lens: np.ndarray
+    finished: np.ndarray
+
+
+def decode_loop(B: int, V: int, dtype: str = F32, steps: int = 8, prompt: int = 6,
+                eos: int = 2, seed: int = 0) -> DecodeLoop:
+    """Seeded decode-loop inputs: per-row base logits N(0, 2^2) plus N(0, 0.3^2)
+    step noise (so that a row's likely tokens recur and the penalty matters),
+    EOS logit -4 + 2.5 s (b mod 7 + 1) / 7 at step s, k in [0, min(V, 1024)],
+    p in [0.5, 1), every stage combination; every fifth row's slot holds only
+    prompt + 3 ids, every seventh row starts finished."""
+    g = _rng(99, S_LOGITS, seed)
+    base = g.standard_normal((B, V)).astype(np.float32) * 2
+    rate = ((np.arange(B) % 7) + 1) / 7.0
+    logits, q, u = [], [], []
+    for s in range(steps):
+        x = base + g.standard_normal((B, V)).astype(np.float32) * np.float32(0.3)
+        x[:, eos] = np.float32(-4.0) + (2.5 * s * rate).astype(np.float32)
+        logits.append(_store(x, dtype))
+        q.append(g.standard_exponential((B, V)).astype(np.float32))
+        u.append(g.random(B).astype(np.float32))
+    top_k = g.integers(0, min(V, 1024) + 1, size=B).astype(np.int32)
+    top_p = g.uniform(0.5, 1.0, size=B).astype(np.float32)
+    row_flags = (np.arange(B) % 8).astype(np.uint8)
+    cap = np.where(np.arange(B) % 5 == 4, prompt + 3, prompt + steps).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
+    ids = g.integers(0, V, size=int(offsets[-1])).astype(np.int32)  # prompt + filler
+    lens = np.full(B, prompt, np.int32)
+    finished = np.where(np.arange(B) % 7 == 6, 1 + (np.arange(B) % 3), 0).astype(np.uint8)
+    return DecodeLoop(B, V, dtype, eos, logits, q, u, top_k, top_p, row_flags, ids, offsets,
+                      lens, finished)

@@ -6,7 +6,8 @@ it, and it imports nothing from the product package.
 
 ``run`` takes numpy arrays shaped like the library's arguments and returns the
 oracle outputs plus per-row diagnostics (kept-set size, top-p decision margin,
-sampling ratio gap).  Rows can be processed on several host threads; ctypes
+sampling ratio gap).  ``decode_epilogue`` is the decode-step epilogue (EOS
+forcing, finished flags, history append), written in plain Python.  Rows can be processed on several host threads; ctypes
 drops the GIL while the C code runs.
 """
 from __future__ import annotations
@@ -67,7 +68,8 @@ def _arr(a, dtype):
 
 def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
         temperature=1.0, penalty=1.0, ids=None, offsets=None, row_flags=None,
-        need_logits=True, need_probs=False, rows=None, threads=1, u=None, topk_ties=False):
+        need_logits=True, need_probs=False, rows=None, threads=1, u=None, topk_ties=False,
+        lens=None):
     """Run the oracle.
 
     logits: [B, ld] float32 (dtype F32) or uint16 bf16 bit patterns (BF16);
@@ -77,6 +79,8 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
     u: optional [B] uniforms; sampling rows then draw by inverse CDF (and
     ``gap`` holds that decision's margin) instead of racing with q.
     topk_ties: top-k keeps every element equal to the k-th value too.
+    lens: optional [B] history lengths: row b's history is then the first
+    clamp(lens[b], 0, slot size) ids of its CSR slot instead of the whole slot.
     Returns a dict with idx [B] int64, logits [B, V] float32 or None,
     probs [B, V] float32 or None, nkept [B] int32, margin [B], gap [B].
     """
@@ -98,6 +102,15 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
         assert u.shape == (B,)
     ids = _arr(ids, np.int32)
     offsets = _arr(offsets, np.int64)
+    if lens is not None and ids is not None:
+        # the filled part of every slot, as a CSR of its own
+        parts, offs = [], [0]
+        for b in range(B):
+            n = min(max(int(lens[b]), 0), max(int(offsets[b + 1] - offsets[b]), 0))
+            parts.append(ids[offsets[b]:offsets[b] + n])
+            offs.append(offs[-1] + n)
+        ids = np.ascontiguousarray(np.concatenate(parts) if parts else ids[:0], dtype=np.int32)
+        offsets = np.asarray(offs, dtype=np.int64)
     row_flags = _arr(row_flags, np.uint8)
     flags = ((NEED_LOGITS if need_logits else 0) | (NEED_PROBS if need_probs else 0)
              | (TOPK_TIES if topk_ties else 0))
@@ -137,3 +150,46 @@ def run(logits, dtype, vocab=None, top_k=None, top_p=None, q=None, eps=1e-20,
             call(*rr)
     return {"idx": out_idx, "logits": out_logits, "probs": out_probs,
             "nkept": nkept, "margin": margin, "gap": gap}
+
+
+def decode_epilogue(idx, finished=None, eos_id=None, ids=None, offsets=None, lens=None,
+                    append=False):
+    """The decode-step epilogue of the MiniMind generation loop, row by row.
+
+    MiniMind generation chapter, sec. 10.9 (EOS batch handling), in its order:
+      1. a row already finished outputs EOS instead of its draw;
+      2. a row whose output is EOS becomes finished (a nonzero flag stays);
+      3. the output is concatenated onto the row's sequence -- here written
+         at position lens[b] of its history slot ids[offsets[b]:offsets[b+1]]
+         (sec. 10.7 penalises every id of that sequence), unless the slot is
+         full;
+      4. the rows not yet finished are counted (the loop ends at zero).
+    Returns new arrays (inputs untouched): idx, finished, ids, lens and
+    counts = [unfinished rows, appends that found a full slot].
+    """
+    idx = np.array(idx, dtype=np.int64)
+    B = idx.shape[0]
+    fin = None if finished is None else np.array(finished, dtype=np.uint8)
+    ids = None if ids is None else np.array(ids, dtype=np.int32)
+    lens = None if lens is None else np.array(lens, dtype=np.int32)
+    unfinished, full = 0, 0
+    for b in range(B):
+        if fin is not None:
+            if fin[b] != 0:
+                idx[b] = eos_id
+            elif idx[b] == eos_id:
+                fin[b] = 1
+            if fin[b] == 0:
+                unfinished += 1
+        else:
+            unfinished += 1
+        if append:
+            start, cap = int(offsets[b]), int(offsets[b + 1] - offsets[b])
+            n = max(int(lens[b]), 0)
+            if n < cap:
+                ids[start + n] = idx[b]
+                lens[b] = n + 1
+            else:
+                full += 1
+    return {"idx": idx, "finished": fin, "ids": ids, "lens": lens,
+            "counts": np.array([unfinished, full], dtype=np.int32)}

@@ -544,3 +544,123 @@ def test_topk_range_boundary():
     y = x[:700]
     assert run_f32(y, TOPK, top_k=700)["nkept"][0] == 700
     assert run_f32(y, TOPK, top_k=699)["nkept"][0] == 699
+
+
+# ---------------------------------------------------------------- decode-step epilogue
+
+def _history(prompt, cap, junk):
+    """CSR history slots: row b holds prompt[b] then junk up to cap ids."""
+    B = len(prompt)
+    ids = np.zeros(B * cap, np.int32)
+    for b in range(B):
+        ids[b * cap:(b + 1) * cap] = junk[b]
+        ids[b * cap:b * cap + len(prompt[b])] = prompt[b]
+    offsets = np.arange(B + 1, dtype=np.int64) * cap
+    lens = np.array([len(p) for p in prompt], np.int32)
+    return ids, offsets, lens
+
+
+def test_eos_batch_table():
+    """The batch illustration of the EOS section: greedy draws that name the
+    table's tokens (a non-EOS token where the table shows a forced EOS), run
+    through the oracle and its epilogue, reproduce every cell, the finished
+    column, and the loop's end after step 6."""
+    g = _golden("minimind_eos_batch_table.json")
+    eos, V, B = g["eos_token_id"], 32, 3
+    tok = {f"tok_{c}": 10 + i for i, c in enumerate("abcdefghi")}
+    prompt = [[5, 6, 7]] * B
+    ids, offsets, lens = _history(prompt, 3 + len(g["steps"]), [31] * B)
+    fin = np.zeros(B, np.uint8)
+    for st in g["steps"]:
+        raw = [20 + st["step"] if st["forced"][b] else (eos if st["tokens"][b] == "EOS" else tok[st["tokens"][b]])
+               for b in range(B)]
+        x = np.zeros((B, V), np.float32)
+        x[np.arange(B), raw] = 5.0
+        r = run_f32(x, 0)
+        assert r["idx"].tolist() == raw
+        e = orc.decode_epilogue(r["idx"], fin, eos, ids, offsets, lens, append=True)
+        want = [eos if t == "EOS" else tok[t] for t in st["tokens"]]
+        assert e["idx"].tolist() == want
+        assert [bool(f) for f in e["finished"]] == st["finished"]
+        assert (e["counts"][0] == 0) == (st["step"] == g["loop_ends_after_step"])
+        assert e["counts"][1] == 0
+        fin, ids, lens = e["finished"], e["ids"], e["lens"]
+    for b in range(B):
+        col = [eos if s["tokens"][b] == "EOS" else tok[s["tokens"][b]] for s in g["steps"]]
+        assert ids[offsets[b]:offsets[b] + lens[b]].tolist() == prompt[b] + col
+
+
+def _minimind_greedy_loop(step_logits, prompt, rho, temperature, eos):
+    """The MiniMind generate loop with do_sample=False, in torch: temperature,
+    penalty over torch.unique of the whole sequence, argmax, EOS forcing,
+    concatenation, finished update and the all-finished break."""
+    import torch
+
+    input_ids = torch.tensor(prompt, dtype=torch.int64)
+    finished = torch.zeros(input_ids.shape[0], dtype=torch.bool)
+    for x in step_logits:
+        logits = torch.from_numpy(x.copy()) / temperature
+        for i in range(input_ids.shape[0]):
+            seen = torch.unique(input_ids[i])
+            score = logits[i, seen]
+            logits[i, seen] = torch.where(score > 0, score / rho, score * rho)
+        nxt = torch.argmax(logits, dim=-1, keepdim=True)
+        nxt = torch.where(finished.unsqueeze(-1), nxt.new_full((nxt.shape[0], 1), eos), nxt)
+        input_ids = torch.cat([input_ids, nxt], dim=-1)
+        finished |= nxt.squeeze(-1).eq(eos)
+        if finished.all():
+            break
+    return input_ids.numpy()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_decode_loop_matches_minimind_loop(seed):
+    """Several decode steps of the oracle with its epilogue (penalty reads
+    only the filled part of each history slot, the slot's tail holds ids
+    that must not be penalised) against the MiniMind loop in torch.  The
+    temperature is a power of two, so that its division commutes exactly
+    with the penalty (the loop divides first, the library penalises first)."""
+    rng = np.random.default_rng(1300 + seed)
+    B, V, P, S, eos = 6, 40, 5, 14, 2
+    base = rng.standard_normal((B, V)).astype(np.float32) * 2
+    base[:, eos] = -4.0
+    steps = []
+    for s in range(S):
+        x = base + rng.standard_normal((B, V)).astype(np.float32) * 0.3
+        x[:, eos] += np.float32(0.6) * s * (1 + np.arange(B)) / B
+        steps.append(x.astype(np.float32))
+    prompt = rng.integers(3, V, (B, P)).tolist()
+    junk = [int(np.argmax(base[b])) for b in range(B)]  # would change the draws if read
+    ids, offsets, lens = _history(prompt, P + S, junk)
+    want = _minimind_greedy_loop(steps, prompt, 1.3, 0.5, eos)
+    fin = np.zeros(B, np.uint8)
+    n = 0
+    for x in steps:
+        r = run_f32(x, 0, temperature=0.5, penalty=1.3, ids=ids, offsets=offsets, lens=lens)
+        e = orc.decode_epilogue(r["idx"], fin, eos, ids, offsets, lens, append=True)
+        fin, ids, lens = e["finished"], e["ids"], e["lens"]
+        n += 1
+        if e["counts"][0] == 0:
+            break
+    assert want.shape[1] == P + n
+    assert n < S or not fin.all()
+    for b in range(B):
+        assert ids[offsets[b]:offsets[b] + lens[b]].tolist() == want[b].tolist()
+
+
+def test_epilogue_full_slots_and_no_eos():
+    """Appends to a full slot are dropped and counted; without finished
+    flags every row counts as unfinished and no output is replaced."""
+    idx = np.array([4, 2, 9, 2])
+    ids = np.arange(8, dtype=np.int32)
+    offsets = np.array([0, 2, 4, 6, 8])
+    lens = np.array([2, 1, 5, -3], np.int32)  # full, room, beyond cap, negative -> 0
+    e = orc.decode_epilogue(idx, None, None, ids, offsets, lens, append=True)
+    assert e["idx"].tolist() == idx.tolist()
+    assert e["counts"].tolist() == [4, 2]
+    assert e["lens"].tolist() == [2, 2, 5, 1]
+    assert e["ids"].tolist() == [0, 1, 2, 2, 4, 5, 2, 7]
+    e = orc.decode_epilogue(idx, np.array([0, 0, 3, 0], np.uint8), 9)
+    assert e["idx"].tolist() == [4, 2, 9, 2]
+    assert e["finished"].tolist() == [0, 0, 3, 0]
+    assert e["counts"].tolist() == [3, 0]
