@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at batch x vocab"
-KERNELS = ["k_plan", "k_pass", "k_rows", "k_fallback", "k_dense"]
+KERNELS = ["k_plan", "k_pass", "k_rows", "k_fallback", "k_dense", "k_epilogue"]
 
 
 def parse():
@@ -94,7 +94,8 @@ def model_bytes(W, kept):
         ndense += int(filtered.sum()) * 4 * V         # filtered rows: written after the merge
     npass += int(nids.sum()) * 4
     rows = int((kept[sm & filtered]).sum()) * 4 + B * (8 + 9)
-    return {"k_plan": 0, "k_pass": npass, "k_rows": rows, "k_fallback": 0, "k_dense": ndense}
+    return {"k_plan": 0, "k_pass": npass, "k_rows": rows, "k_fallback": 0, "k_dense": ndense,
+            "k_epilogue": 0}
 
 
 def counted_traffic(kernel):

@@ -157,12 +157,15 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
     if (!(a->repetition_penalty > 0.0f) || !isfinite(a->repetition_penalty))
         return SAMPLER_EINVAL;
     if (!(a->eps >= 0.0f) || !isfinite(a->eps)) return SAMPLER_EINVAL;
-    const uint32_t known =
-        SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_TOPK_TIES | SAMPLER_PROFILE;
+    const uint32_t known = SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_TOPK_TIES |
+                           SAMPLER_APPEND_HISTORY | SAMPLER_PROFILE;
     if (a->flags & ~known) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_NEED_LOGITS) && a->out_logits == nullptr) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_NEED_PROBS) && a->out_probs == nullptr) return SAMPLER_EINVAL;
     if ((a->penalty_ids == nullptr) != (a->penalty_offsets == nullptr)) return SAMPLER_EINVAL;
+    if (a->penalty_len != nullptr && a->penalty_ids == nullptr) return SAMPLER_EINVAL;
+    if ((a->flags & SAMPLER_APPEND_HISTORY) && a->penalty_len == nullptr) return SAMPLER_EINVAL;
+    if (a->finished != nullptr && (a->eos_id < 0 || a->eos_id >= h->vocab)) return SAMPLER_EINVAL;
     if (a->row_flags == nullptr && a->q == nullptr && a->u == nullptr) return SAMPLER_EINVAL;
     return SAMPLER_OK;
 }
@@ -183,6 +186,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.u = a->u;
     p.ids = a->penalty_ids;
     p.offsets = a->penalty_offsets;
+    p.plen = a->penalty_len;
     p.row_flags = a->row_flags;
     p.out_idx = a->out_idx;
     p.out_logits = (a->flags & SAMPLER_NEED_LOGITS) ? a->out_logits : nullptr;
@@ -264,6 +268,23 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         launched[4] = true;
     }
     mark(5);
+    const bool append = (a->flags & SAMPLER_APPEND_HISTORY) != 0;
+    if (a->finished || append || a->counts) {
+        // after every kernel that reads the history or writes out_idx
+        EpiParams e;
+        e.out_idx = a->out_idx;
+        e.finished = a->finished;
+        e.eos = a->eos_id;
+        e.ids = a->penalty_ids;
+        e.offsets = a->penalty_offsets;
+        e.len = a->penalty_len;
+        e.counts = a->counts;
+        e.B = batch;
+        e.append = append ? 1 : 0;
+        if (launch_epilogue(e, st) != hipSuccess) return SAMPLER_EHIP;
+        launched[5] = true;
+    }
+    mark(6);
     if (prof) ++h->nprof;
     return SAMPLER_OK;
 }

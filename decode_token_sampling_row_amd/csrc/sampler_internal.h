@@ -65,6 +65,7 @@ struct KParams {
     const float *u;  // [B] uniforms of inverse-CDF sampling, or null (race with q)
     const int32_t *ids;
     const int64_t *offsets;
+    const int32_t *plen;  // [B] history lengths within the slots, or null (whole slots)
     const uint8_t *row_flags;
     int64_t *out_idx;
     float *out_logits;
@@ -99,6 +100,20 @@ struct KWork {
     uint32_t *fblist; // [maxB] those rows
 };
 
+// Decode-step epilogue over all rows of a call (one workgroup).
+struct EpiParams {
+    int64_t *out_idx;
+    uint8_t *finished;       // or null
+    int64_t eos;
+    int32_t *ids;            // history slots (written when append is set)
+    const int64_t *offsets;
+    int32_t *len;            // history lengths (read / written when append is set)
+    int32_t *counts;         // [2] or null
+    int32_t B;
+    int32_t append;
+};
+constexpr int EPI_THREADS = 1024;
+
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
 hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
                        hipStream_t s);
@@ -109,5 +124,6 @@ hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int
                            bool aligned, hipStream_t s);
 hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                         bool aligned, hipStream_t s);
+hipError_t launch_epilogue(const EpiParams &e, hipStream_t s);
 
 }  // namespace smp

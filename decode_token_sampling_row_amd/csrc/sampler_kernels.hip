@@ -43,6 +43,11 @@
 //   k_dense     grid = B x tiles.  Writes the dense filtered logits (and the
 //               optional probabilities) of filtered rows with full-line
 //               stores, composing each tile in LDS from the kept list.
+//   k_epilogue  one workgroup, when asked for.  The decode-step epilogue of
+//               the MiniMind generation loop (sec. 10.9): finished rows
+//               output EOS, rows that output EOS become finished, the output
+//               is appended to the row's history slot, and the unfinished
+//               rows are counted.
 //
 // Order and keys: a transformed logit x and its vocab id j form the 64-bit
 // composite  (orderkey(x) << 32) | ~j ; larger composite = earlier in the
@@ -603,7 +608,12 @@ __device__ __forceinline__ void build_bitmap(uint32_t *bm, int64_t seg0, int64_t
     __syncthreads();
     for (int w = threadIdx.x; w < nw; w += NT) bm[w] = 0u;
     __syncthreads();
-    const int64_t i0 = P.offsets[b], i1 = P.offsets[b + 1];
+    const int64_t i0 = P.offsets[b];
+    int64_t i1 = P.offsets[b + 1];
+    if (P.plen) {  // only the filled part of the slot is history
+        const int64_t n = P.plen[b] < 0 ? 0 : P.plen[b];
+        if (i0 + n < i1) i1 = i0 + n;
+    }
     for (int64_t t = i0 + threadIdx.x; t < i1; t += NT) {
         int64_t r = (int64_t)P.ids[t] - seg0;
         if (r >= 0 && r < len) atomicOr(&bm[r >> 5], 1u << (r & 31));
@@ -2603,6 +2613,61 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
     }
 }
 
+// ================================================================== k_epilogue
+// The decode-step epilogue, in the order of the MiniMind loop (sec. 10.9):
+// force EOS on finished rows, mark rows whose output is EOS, append the
+// output to the history (the loop's concatenation onto the sequence), count
+// the rows still running (the loop's all-finished test).  One workgroup
+// strides over every row of the call, so the counts need no zeroed memory
+// and no atomics.
+__global__ __launch_bounds__(EPI_THREADS) void k_epilogue(EpiParams E) {
+    __shared__ uint32_t red[2][EPI_THREADS / 64];
+    uint32_t unf = 0, full = 0;
+    for (int b = threadIdx.x; b < E.B; b += EPI_THREADS) {
+        int64_t t = E.out_idx[b];
+        if (E.finished) {
+            uint8_t f = E.finished[b];
+            if (f) {
+                t = E.eos;
+                E.out_idx[b] = t;
+            } else if (t == E.eos) {
+                f = 1;
+                E.finished[b] = f;
+            }
+            unf += f == 0;
+        } else {
+            ++unf;
+        }
+        if (E.append) {
+            const int64_t i0 = E.offsets[b], cap = E.offsets[b + 1] - i0;
+            const int64_t n = E.len[b] < 0 ? 0 : E.len[b];
+            if (n < cap) {
+                E.ids[i0 + n] = (int32_t)t;
+                E.len[b] = (int32_t)(n + 1);
+            } else {
+                ++full;
+            }
+        }
+    }
+    unf = wave_sum_u32(unf);
+    full = wave_sum_u32(full);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][w] = unf;
+        red[1][w] = full;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && E.counts) {
+        uint32_t a = 0, c = 0;
+        for (int i = 0; i < EPI_THREADS / 64; ++i) {
+            a += red[0][i];
+            c += red[1][i];
+        }
+        E.counts[0] = (int32_t)a;
+        E.counts[1] = (int32_t)c;
+    }
+}
+
 template <class K>
 hipError_t launch(K kern, dim3 grid, dim3 block, size_t shmem, hipStream_t s, const KParams &p,
                   const KPlan &l, const KWork &w) {
@@ -2665,5 +2730,10 @@ hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dt
 }
 
 #undef SMP_PICK
+
+hipError_t launch_epilogue(const EpiParams &e, hipStream_t s) {
+    hipLaunchKernelGGL(k_epilogue, dim3(1), dim3(EPI_THREADS), 0, s, e);
+    return hipGetLastError();
+}
 
 }  // namespace smp

@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(PKG, "libsampler.so")
 SAMPLER_OK, SAMPLER_EINVAL, SAMPLER_ENOMEM, SAMPLER_EHIP = 0, -1, -2, -3
 SAMPLER_F32, SAMPLER_BF16 = 0, 1
 SAMPLER_ROW_TOPK, SAMPLER_ROW_TOPP, SAMPLER_ROW_SAMPLE, SAMPLER_ROW_ALL = 1, 2, 4, 7
-SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_TOPK_TIES, SAMPLER_PROFILE = 1, 2, 4, 256
+SAMPLER_NEED_LOGITS, SAMPLER_NEED_PROBS, SAMPLER_TOPK_TIES = 1, 2, 4
+SAMPLER_APPEND_HISTORY, SAMPLER_PROFILE = 8, 256
 SAMPLER_TOPK_MAX = 1024
 SAMPLER_VOCAB_MAX = 1 << 21
 
 EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_profile",
            "sampler_destroy", "sampler_strerror")
-SAMPLER_PROFILE_SLOTS = 5
+SAMPLER_PROFILE_SLOTS = 6
 
 
 class SamplerError(RuntimeError):
@@ -56,6 +57,10 @@ class sampler_args(ctypes.Structure):
         ("out_logits", ctypes.c_void_p),
         ("out_probs", ctypes.c_void_p),
         ("u", ctypes.c_void_p),
+        ("penalty_len", ctypes.c_void_p),
+        ("finished", ctypes.c_void_p),
+        ("eos_id", ctypes.c_int64),
+        ("counts", ctypes.c_void_p),
     ]
 
 
@@ -133,8 +138,16 @@ def _ptr(t, dtype=None, what=""):
 def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
               temperature=1.0, repetition_penalty=1.0, penalty_ids=None,
               penalty_offsets=None, row_flags=None, out_logits=None, out_probs=None,
-              profile=False, u=None, topk_ties=False) -> sampler_args:
-    """Marshal torch tensors into a sampler_args struct."""
+              profile=False, u=None, topk_ties=False, penalty_len=None, finished=None,
+              eos_id=None, counts=None, append_history=False) -> sampler_args:
+    """Marshal torch tensors into a sampler_args struct.
+
+    The decode-step epilogue: ``finished`` (uint8 [B], updated in place) with
+    ``eos_id``; ``append_history`` appends the output ids to the history
+    slots ``penalty_ids`` / ``penalty_offsets`` filled up to ``penalty_len``
+    (int32 [B], advanced in place); ``counts`` (int32 [2]) receives the
+    unfinished rows and the appends that found a full slot.
+    """
     import torch
 
     if logits.dim() != 2 or logits.stride(1) != 1:
@@ -153,6 +166,10 @@ def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
         flags |= SAMPLER_PROFILE
     if topk_ties:
         flags |= SAMPLER_TOPK_TIES
+    if append_history:
+        flags |= SAMPLER_APPEND_HISTORY
+    if finished is not None and eos_id is None:
+        raise ValueError("finished needs eos_id")
     a = sampler_args()
     a.logits = _ptr(logits, None, "logits")
     a.ld = logits.stride(0)
@@ -170,6 +187,10 @@ def make_args(logits, out_idx, *, top_k=None, top_p=None, q=None, eps=1e-20,
     a.out_logits = _ptr(out_logits, torch.float32, "out_logits")
     a.out_probs = _ptr(out_probs, torch.float32, "out_probs")
     a.u = _ptr(u, torch.float32, "u")
+    a.penalty_len = _ptr(penalty_len, torch.int32, "penalty_len")
+    a.finished = _ptr(finished, torch.uint8, "finished")
+    a.eos_id = int(eos_id) if eos_id is not None else 0
+    a.counts = _ptr(counts, torch.int32, "counts")
     return a
 
 

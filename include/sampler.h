@@ -32,7 +32,13 @@
  *      softmax);
  *   7. optional dense outputs: the filtered logits (x at kept ids, -inf
  *      elsewhere; the Ascend page's logits_top_kp_select) and the
- *      probabilities renormalised over the kept set (0 elsewhere).
+ *      probabilities renormalised over the kept set (0 elsewhere);
+ *   8. optional decode-step epilogue (MiniMind sec. 10.9, EOS batch
+ *      handling): a row already marked finished outputs the EOS id instead
+ *      of its draw, a row whose output is EOS becomes finished, the output
+ *      is appended to the row's history (the sequence the penalty of the
+ *      next step reads, sec. 10.7), and the rows still unfinished are
+ *      counted so that the caller's loop can stop when none is left.
  *
  * Every step runs in hand-written HIP kernels on the caller's stream; the
  * library never copies data to the host and never synchronises in
@@ -70,9 +76,11 @@ extern "C" {
                                    k-th largest value (MiniMind sec. 10.5:
                                    only logits below the k-th value of topk
                                    are masked), so more than k may survive  */
+#define SAMPLER_APPEND_HISTORY 8u /* step 8: append out_idx[b] to row b's
+                                   history (needs penalty_len)              */
 #define SAMPLER_PROFILE 256u    /* time each kernel with HIP events; read the
                                    averages with sampler_profile             */
-#define SAMPLER_PROFILE_SLOTS 5
+#define SAMPLER_PROFILE_SLOTS 6
 
 /* Largest k of the top-k stage and largest top-k guess. */
 #define SAMPLER_TOPK_MAX 1024
@@ -113,10 +121,13 @@ typedef struct sampler_args {
     float eps;                 /* >= 0, added to q                         */
     float temperature;         /* > 0; 1 = stage off                        */
     float repetition_penalty;  /* > 0; 1 = stage off                        */
-    const int32_t *penalty_ids;     /* [nnz] history ids, or NULL          */
+    int32_t *penalty_ids;      /* [nnz] history ids, or NULL; row b's slot is
+                                  penalty_ids[offsets[b] .. offsets[b+1]).
+                                  Written only with SAMPLER_APPEND_HISTORY */
     const int64_t *penalty_offsets; /* [B+1] CSR offsets into penalty_ids */
     const uint8_t *row_flags;  /* [B] SAMPLER_ROW_* bits, NULL = all on     */
-    uint32_t flags;            /* SAMPLER_NEED_LOGITS | _NEED_PROBS | _TOPK_TIES | _PROFILE */
+    uint32_t flags;            /* SAMPLER_NEED_LOGITS | _NEED_PROBS | _TOPK_TIES |
+                                  _APPEND_HISTORY | _PROFILE */
     int64_t *out_idx;          /* [B] sampled (or greedy) vocab id          */
     float *out_logits;         /* [B, V] row stride V; iff NEED_LOGITS      */
     float *out_probs;          /* [B, V] row stride V; iff NEED_PROBS       */
@@ -128,6 +139,28 @@ typedef struct sampler_args {
                                   gives the first kept token, u beyond what
                                   rounding lets the sum reach gives the last
                                   -- and q is not read (it may be NULL).     */
+    /* ---- step 8, the decode-step epilogue; every part optional ---------- */
+    int32_t *penalty_len;      /* [B] or NULL.  Given: row b's history is the
+                                  first n_b = clamp(penalty_len[b], 0, cap_b)
+                                  ids of its slot (cap_b = offsets[b+1] -
+                                  offsets[b]); NULL: the whole slot.  With
+                                  SAMPLER_APPEND_HISTORY the call writes the
+                                  output id at position n_b of the slot and
+                                  sets penalty_len[b] = n_b + 1; a full slot
+                                  (n_b >= cap_b) is left as it is and the row
+                                  is counted in counts[1].                  */
+    uint8_t *finished;         /* [B] in/out, or NULL (no EOS handling).  A
+                                  row with finished[b] != 0 outputs eos_id;
+                                  then finished[b] = 1 where the output is
+                                  eos_id and finished[b] was 0 (a nonzero
+                                  value is kept).  The draw and the dense
+                                  outputs of a finished row are still made. */
+    int64_t eos_id;            /* the EOS id, in [0, V) when finished is set */
+    int32_t *counts;           /* [2] or NULL, written by every call with
+                                  batch >= 1: [0] rows with finished[b] == 0
+                                  after the call (batch when finished is
+                                  NULL; 0 = every row has ended), [1] rows
+                                  whose append found a full slot.            */
 } sampler_args;
 
 /*
@@ -147,8 +180,9 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
  * or SAMPLER_EINVAL: batch outside [0, max_batch], logits / out_idx NULL,
  * ld < V, temperature or penalty not finite and > 0, eps negative or not
  * finite, a requested dense output with a NULL buffer, exactly one of the
- * penalty arrays NULL, unknown flag bits, or row_flags == NULL (every row
- * samples) with both q and u NULL.
+ * penalty arrays NULL, penalty_len without them, SAMPLER_APPEND_HISTORY
+ * without all three, finished with eos_id outside [0, V), unknown flag bits,
+ * or row_flags == NULL (every row samples) with both q and u NULL.
  * Per-row values are never errors: k outside [1, min(V, 1024)] skips top-k,
  * p >= 1 or NaN skips top-p, history ids outside [0, V) are ignored.
  */
@@ -160,6 +194,7 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a);
  * sampler_check first.  The handle's workspace is reused by every call, so
  * calls with one handle must be ordered on one stream (not thread-safe).
  * Rows whose logits are NaN, or entirely -inf, are outside the contract.
+ * A call with batch 0 launches nothing and writes nothing.
  * Returns SAMPLER_OK, SAMPLER_EINVAL or SAMPLER_EHIP (launch failure).
  */
 int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream);
@@ -171,7 +206,8 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
  * admission estimate of top-k / top-p rows), [1] the streaming pass over the
  * logits (every row), [2] row merge / cutoff / sample, [3] full-row search
  * (rows the pass could not settle, top-p rows whose guess failed, inverse-CDF
- * draws over whole rows), [4] dense outputs of filtered rows.  Each time runs from an event recorded
+ * draws over whole rows), [4] dense outputs of filtered rows, [5] the
+ * decode-step epilogue.  Each time runs from an event recorded
  * on the call's stream just before the kernel to one recorded just after
  * it.  Kernels that were not launched count 0.  Waits for the last profiled
  * call to finish, then forgets the calls it averaged.

@@ -54,7 +54,8 @@ def test_args_struct_layout_matches_header():
              offsetof(sampler_opts, rows_per_launch));
       O(logits); O(ld); O(top_k); O(top_p); O(q); O(eps); O(temperature);
       O(repetition_penalty); O(penalty_ids); O(penalty_offsets); O(row_flags);
-      O(flags); O(out_idx); O(out_logits); O(out_probs); O(u);
+      O(flags); O(out_idx); O(out_logits); O(out_probs); O(u); O(penalty_len);
+      O(finished); O(eos_id); O(counts);
       return 0;
     }
     """
@@ -82,7 +83,8 @@ def test_constants_match_header():
     for name in ["SAMPLER_OK", "SAMPLER_EINVAL", "SAMPLER_ENOMEM", "SAMPLER_EHIP",
                  "SAMPLER_F32", "SAMPLER_BF16", "SAMPLER_ROW_TOPK", "SAMPLER_ROW_TOPP",
                  "SAMPLER_ROW_SAMPLE", "SAMPLER_ROW_ALL", "SAMPLER_NEED_LOGITS",
-                 "SAMPLER_NEED_PROBS", "SAMPLER_TOPK_TIES", "SAMPLER_PROFILE",
+                 "SAMPLER_NEED_PROBS", "SAMPLER_TOPK_TIES", "SAMPLER_APPEND_HISTORY",
+                 "SAMPLER_PROFILE",
                  "SAMPLER_PROFILE_SLOTS",
                  "SAMPLER_TOPK_MAX"]:
         assert getattr(smp, name) == val(name), name

@@ -365,7 +365,7 @@ def test_empty_batch_and_argument_checks():
     smp.sampler_run(s.handle, 0, smp.sampler_args())  # empty batch: no-op
     assert smp.sampler_check(s.handle, 5, good) == smp.SAMPLER_EINVAL
     for field, val in [("temperature", 0.0), ("temperature", float("inf")),
-                       ("repetition_penalty", -1.0), ("eps", -1e-3), ("flags", 8),
+                       ("repetition_penalty", -1.0), ("eps", -1e-3), ("flags", 16),
                        ("ld", 99), ("out_idx", None), ("logits", None)]:
         a = smp.make_args(x, idx, q=q)
         setattr(a, field, val)
@@ -380,6 +380,20 @@ def test_empty_batch_and_argument_checks():
     assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL
     with pytest.raises(smp.SamplerError):
         smp.sampler_run(s.handle, 4, a)
+    hist = torch.zeros(8, dtype=torch.int32, device="cuda")
+    offs = torch.arange(5, dtype=torch.int64, device="cuda") * 2
+    lens = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fin = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    a = smp.make_args(x, idx, q=q, penalty_len=lens)  # lengths without a history
+    assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL
+    a = smp.make_args(x, idx, q=q, penalty_ids=hist, penalty_offsets=offs, append_history=True)
+    assert smp.sampler_check(s.handle, 4, a) == smp.SAMPLER_EINVAL  # append needs lengths
+    a = smp.make_args(x, idx, q=q, penalty_ids=hist, penalty_offsets=offs, penalty_len=lens,
+                      append_history=True)
+    assert smp.sampler_check(s.handle, 4, a) == 0
+    for eos, rc in [(-1, smp.SAMPLER_EINVAL), (100, smp.SAMPLER_EINVAL), (0, 0), (99, 0)]:
+        a = smp.make_args(x, idx, q=q, finished=fin, eos_id=eos)
+        assert smp.sampler_check(s.handle, 4, a) == rc, eos
     s.close()
     del lib, ctypes
 
@@ -400,12 +414,15 @@ def test_profile_reports_kernel_times():
         s.run(d["logits"], out_idx, top_k=d["top_k"], top_p=d["top_p"], q=d["q"],
               row_flags=d["row_flags"], out_logits=out_l, profile=True)
     ms = s.profile()
-    assert len(ms) == 5 and all(t > 0 for t in ms)
+    assert len(ms) == 6 and all(t > 0 for t in ms[:5]) and ms[5] == 0
     # without top-k / top-p, uniforms and dense outputs, neither the planning,
     # the full-row search nor the dense writer is launched
     s.run(d["logits"], out_idx, q=d["q"], row_flags=d["row_flags"], profile=True)
     ms = s.profile()
-    assert ms[1] > 0 and ms[2] > 0 and ms[0] == ms[3] == ms[4] == 0
+    assert ms[1] > 0 and ms[2] > 0 and ms[0] == ms[3] == ms[4] == ms[5] == 0
+    counts = torch.zeros(2, dtype=torch.int32, device="cuda")
+    s.run(d["logits"], out_idx, q=d["q"], row_flags=d["row_flags"], counts=counts, profile=True)
+    assert s.profile()[5] > 0  # the epilogue
     with pytest.raises(SamplerError):
         s.profile()  # the averaged calls are forgotten
     s.close()
