@@ -117,6 +117,8 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + B * sizeof(float), 256);
     const size_t o_rowref = off;
     off = align_up(off + B * sizeof(float), 256);
+    const size_t o_rowlo = off;
+    off = align_up(off + B * sizeof(float), 256);
     const size_t o_fbcnt = off;
     off = align_up(off + sizeof(uint32_t), 256);
     const size_t o_fblist = off;
@@ -138,6 +140,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->ws.ktoff = (uint32_t *)(c + o_ktoff);
     s->ws.rowthr = (float *)(c + o_rowthr);
     s->ws.rowref = (float *)(c + o_rowref);
+    s->ws.rowlo = (float *)(c + o_rowlo);
     s->ws.fbcnt = (uint32_t *)(c + o_fbcnt);
     s->ws.fblist = (uint32_t *)(c + o_fblist);
     s->events_made = false;

@@ -96,6 +96,7 @@ struct KWork {
     uint32_t *ktoff;  // [maxB][nt + 1] start of each tile's group in klist
     float *rowthr;    // [maxB] estimated admission value of the row
     float *rowref;    // [maxB] transformed sample maximum (reference for exponentials)
+    float *rowlo;     // [maxB] transformed smallest value of the estimate sample
     uint32_t *fbcnt;  // [1] rows queued for the full-row top-p search
     uint32_t *fblist; // [maxB] those rows
 };

@@ -309,6 +309,19 @@ __device__ __forceinline__ uint64_t wg_min_u64(uint64_t v, uint64_t *sc) {
 }
 
 template <int NT>
+__device__ __forceinline__ float wg_min_f32(float v, float *sc) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, shxf(v, m));
+    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t = fminf(t, sc[i]);
+    __syncthreads();
+    return t;
+}
+
+template <int NT>
 __device__ __forceinline__ uint32_t wg_min_u32(uint32_t v, uint32_t *sc) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = min(v, shx(v, m));
@@ -799,10 +812,14 @@ struct StreamShared {
 // row when it is shorter than EST_N -- r
 // being the sample rank expected for the row's kk-th largest plus four
 // standard deviations of it plus 8.  The sample's order keys are binned by
-// their distance below the sample maximum, first in steps of 2^16 (one bf16
-// ulp), and in steps of 2^24 when the 255 top bins hold fewer than r; only
-// the top 255 bins are counted, so the bins stay sparse and the LDS atomics
-// rarely collide.  -inf (admit everything) when r would exceed the sample.
+// their distance below the sample maximum in steps of 2^16 (one bf16 ulp);
+// only the top 255 bins are counted, so the bins stay sparse and the LDS
+// atomics rarely collide.  When those bins hold fewer than r keys (a few
+// samples far above the rest stretch the range: spikes, or one large
+// extreme value), the r-th key is found in two steps instead: its bin of
+// 2^24 (256 fine steps), then its fine bin inside that one, so the value
+// keeps the same resolution whatever the spread above it.  -inf (admit
+// everything) when r would exceed the sample.
 // smax receives the sample maximum (raw); active whether the row has top-k
 // or top-p at all (the sample is requested before the row's stages are
 // known, so that the two latencies overlap).
@@ -824,7 +841,7 @@ __device__ __forceinline__ int est_run_start(int s, int b, int V) {
 
 template <int DT, bool AL>
 __device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamShared &S,
-                                              float &smax, bool &active) {
+                                              float &smax, float &smin, bool &active) {
     constexpr int NT = K1_THREADS;
     constexpr int PER = EST_N / (NT * VEC);  // groups of 8 per thread
     constexpr int GPS = EST_SEG / VEC;       // groups per run
@@ -857,26 +874,45 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamSha
     const double r0 = (double)kk * (double)n / (double)V;
     const double rr = ceil(r0 + 4.0 * sqrt(r0) + 8.0);
     const uint32_t r = rr < (double)n ? (uint32_t)rr : 0u;  // 0: admit everything
-    // the sample maximum
-    uint32_t mx = 0;
+    // the sample maximum and smallest finite value
+    const uint32_t kninf = f2key(-INFINITY);
+    uint32_t mx = 0, mn = ~0u;
 #pragma unroll
     for (int g = 0; g < PER; ++g) {
         float x[8];
         unpack_raw<DT>(raw[g], x);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (i < nv[g]) mx = max(mx, f2key(x[i]));
+            if (i < nv[g]) {
+                const uint32_t k = f2key(x[i]);
+                mx = max(mx, k);
+                if (k > kninf) mn = min(mn, k);
+            }
     }
 #pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) mx = max(mx, shx(mx, sft));
-    if ((threadIdx.x & 63) == 0) S.sci[threadIdx.x >> 6] = mx;
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+        mx = max(mx, shx(mx, sft));
+        mn = min(mn, shx(mn, sft));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        S.sci[threadIdx.x >> 6] = mx;
+        S.sci[8 + (threadIdx.x >> 6)] = mn;
+    }
     __syncthreads();
     mx = S.sci[0];
+    mn = S.sci[8];
 #pragma unroll
-    for (int i = 1; i < NT / 64; ++i) mx = max(mx, S.sci[i]);
+    for (int i = 1; i < NT / 64; ++i) {
+        mx = max(mx, S.sci[i]);
+        mn = min(mn, S.sci[8 + i]);
+    }
     smax = key2f(mx);
+    smin = mn == ~0u ? INFINITY : key2f(mn);
     if (r == 0) return -INFINITY;
-    for (int shift = 16; shift <= 24; shift += 8) {
+    // histogram of the keys whose distance below the maximum, in steps of
+    // 2^shift and counted from `base` steps, is below `nb`; bin 255 - d
+    // holds distance base + d.  Returns the number of keys counted.
+    auto fill = [&](int shift, uint32_t base, uint32_t nb) -> uint32_t {
         for (int i = threadIdx.x; i < 256; i += NT) S.hist[i] = 0;
         __syncthreads();
 #pragma unroll
@@ -885,34 +921,42 @@ __device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamSha
             unpack_raw<DT>(raw[g], x);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t d = (mx - f2key(x[i])) >> shift;
-                if (i < nv[g] && d < 255u) atomicAdd(&S.hist[255 - d], 1u);
+                const uint32_t d = ((mx - f2key(x[i])) >> shift) - base;
+                if (i < nv[g] && d < nb) atomicAdd(&S.hist[255 - d], 1u);
             }
         }
         __syncthreads();
-        uint32_t tot = 0;
         if (threadIdx.x < 64) {
-            tot = S.hist[4 * threadIdx.x] + S.hist[4 * threadIdx.x + 1] +
-                  S.hist[4 * threadIdx.x + 2] + S.hist[4 * threadIdx.x + 3];
+            uint32_t tot = S.hist[4 * threadIdx.x] + S.hist[4 * threadIdx.x + 1] +
+                           S.hist[4 * threadIdx.x + 2] + S.hist[4 * threadIdx.x + 3];
 #pragma unroll
             for (int sft = 32; sft >= 1; sft >>= 1) tot += shx(tot, sft);
             if (threadIdx.x == 0) S.sel[3] = tot;
         }
         __syncthreads();
-        tot = S.sel[3];
-        if (tot >= r || shift == 24) {
-            if (tot < r) return -INFINITY;  // unreachable: 255 * 2^24 spans every key
-            wave0_find_bin(S.hist, r, S.sel);
-            __syncthreads();
-            const uint32_t d = 255u - S.sel[0];
-            // every key of bins 0..d, i.e. key > mx - (d + 1) * 2^shift
-            const uint64_t lo = (uint64_t)mx - (((uint64_t)d + 1) << shift) + 1;
-            const uint32_t fk = lo > (uint64_t)mx ? 0u : (uint32_t)lo;
-            return fk <= f2key(-INFINITY) ? -INFINITY : key2f(fk);
-        }
+        return S.sel[3];
+    };
+    // the fine bin (distance from the maximum, in steps of 2^16) holding the
+    // need-th largest key of the histogram just filled, given `base`
+    auto pick = [&](uint32_t need, uint32_t base) -> float {
+        wave0_find_bin(S.hist, need, S.sel);
         __syncthreads();
-    }
-    return -INFINITY;
+        const uint32_t d = base + (255u - S.sel[0]);
+        // every key of fine bins 0..d, i.e. key > mx - (d + 1) * 2^16
+        const uint64_t lo = (uint64_t)mx - (((uint64_t)d + 1) << 16) + 1;
+        const uint32_t fk = lo > (uint64_t)mx ? 0u : (uint32_t)lo;
+        return fk <= f2key(-INFINITY) ? -INFINITY : key2f(fk);
+    };
+    if (fill(16, 0u, 255u) >= r) return pick(r, 0u);
+    // spread-out top: the coarse bin of the r-th key, then its fine bin
+    if (fill(24, 0u, 255u) < r) return -INFINITY;  // unreachable: 255 * 2^24 spans every key
+    wave0_find_bin(S.hist, r, S.sel);
+    __syncthreads();
+    const uint32_t dc = 255u - S.sel[0];
+    const uint32_t above = S.sel[1];
+    __syncthreads();
+    (void)fill(16, dc << 8, 256u);
+    return pick(r - above, dc << 8);
 }
 
 // One workgroup per row, before the pass: for rows with top-k or top-p, the
@@ -921,13 +965,14 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W) {
     __shared__ StreamShared S;
     const int b = P.b0 + (int)blockIdx.x;
-    float smax;
+    float smax, smin;
     bool active;
-    const float t = row_estimate<DT, AL>(P, b, S, smax, active);
+    const float t = row_estimate<DT, AL>(P, b, S, smax, smin, active);
     if (!active) return;
     if (threadIdx.x == 0) {
         W.rowthr[b] = t;
         W.rowref[b] = xform<XF>(smax, 0u, P);
+        W.rowlo[b] = smin < INFINITY ? xform<XF>(smin, 0u, P) : INFINITY;
     }
 }
 
@@ -2068,7 +2113,7 @@ struct FallbackShared {
     float lv_lo, lv_scale;
     uint32_t lv_bin[8];
     uint32_t lv_klo[8];
-    uint64_t lv_span[8];
+    uint32_t lv_sh[8];
     uint32_t sc[16];
     uint64_t sc64[16];
     double scd[16];
@@ -2086,9 +2131,18 @@ __device__ __forceinline__ uint32_t bin_value(float x, float lo, float scale) {
     if (t >= (float)(K3_BINS - 1)) return K3_BINS - 1;
     return (uint32_t)t;
 }
-__device__ __forceinline__ uint32_t bin_key(uint32_t key, uint32_t klo, uint64_t span) {
-    uint64_t bi = ((uint64_t)(key - klo) * (uint64_t)K3_BINS) / span;
-    return bi < (uint64_t)K3_BINS ? (uint32_t)bi : (uint32_t)(K3_BINS - 1);
+// Key bins of a refinement level: keys from klo on, 2^sh keys per bin (sh
+// makes the parent bucket's key range fit the K3_BINS bins).
+__device__ __forceinline__ uint32_t bin_key(uint32_t key, uint32_t klo, uint32_t sh) {
+    const uint32_t bi = (key - klo) >> sh;
+    return bi < (uint32_t)K3_BINS ? bi : (uint32_t)(K3_BINS - 1);
+}
+// Smallest sh with (span - 1) >> sh < K3_BINS, for a key range of `span` keys.
+__device__ __forceinline__ uint32_t bin_shift(uint64_t span) {
+    const int bits = span > 1 ? 64 - __clzll((long long)(span - 1)) : 0;
+    constexpr int BB = 11;  // log2(K3_BINS)
+    static_assert((1 << BB) == K3_BINS, "K3_BINS is a power of two");
+    return bits > BB ? (uint32_t)(bits - BB) : 0u;
 }
 
 // Boundary bucket of a mass histogram: walking the bins from the top, the
@@ -2147,7 +2201,7 @@ __device__ __forceinline__ bool in_play(const FallbackShared &S, float x, uint32
     if (nlev == 0) return true;
     if (bin_value(x, S.lv_lo, S.lv_scale) != S.lv_bin[0]) return false;
     for (int l = 1; l < nlev; ++l)
-        if (bin_key(k, S.lv_klo[l], S.lv_span[l]) != S.lv_bin[l]) return false;
+        if (bin_key(k, S.lv_klo[l], S.lv_sh[l]) != S.lv_bin[l]) return false;
     return true;
 }
 
@@ -2201,6 +2255,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     }
     const double m = (double)info.m;
     uint64_t cfloor = info.T;  // only composites >= cfloor take part (0: all)
+    // low end of the first histogram level: the smallest value of the row's
+    // estimate sample (rows with top-k / top-p; elements below it share bin
+    // 0, which later levels refine like any other bin)
+    const float rowlo = (md.tk || md.tp) ? W.rowlo[b] : INFINITY;
 
     // The least element T* (a composite) of the row's order at which the
     // weight summed from the top reaches the target -- tval times the total
@@ -2215,16 +2273,21 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         for (int level = 0; level < 6; ++level) {
             // bin function of this level
             float lo = 0.0f, scale = 0.0f;
-            uint32_t klo = 0;
-            uint64_t span = 1;
+            uint32_t klo = 0, sh = 0;
             if (level == 0) {
-                // bins over the 128 below the row maximum; smaller values (whose
-                // mass is below 1e-55 of the maximum's) fall in bin 0
+                // bins over the values that take part: from about the row
+                // minimum (or the floor's value) to the maximum, at most 128
+                // below it; smaller values (whose mass is below 1e-55 of the
+                // maximum's) fall in bin 0
                 lo = info.m - 128.0f;
-                scale = (float)K3_BINS / 128.0f;
+                if (rowlo <= info.m) lo = fmaxf(lo, rowlo);
+                if (cfloor != 0) lo = fmaxf(lo, key2f((uint32_t)(cfloor >> 32)));
+                const float w = info.m - lo;
+                scale = w > 0.0f ? (float)K3_BINS / w : 1.0f;
+                if (!(scale < INFINITY)) scale = 1.0f;  // a one-value range
             } else {
                 klo = S.lv_klo[level];
-                span = S.lv_span[level];
+                sh = S.lv_sh[level];
             }
             for (int i = tid; i < K3_BINS; i += K3_THREADS) {
                 S.hm[i] = 0.0;
@@ -2240,7 +2303,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 if (!in_play(S, x, k, nlev)) return;
                 double e = count ? 1.0 : exp((double)x - m);
                 if (level == 0) zt += e;
-                uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, span);
+                uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, sh);
                 atomicAdd(&S.hm[bi], e);
                 atomicAdd(&S.hc[bi], 1u);
                 atomicMin(&S.hlo[bi], k);
@@ -2268,7 +2331,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 S.lv_bin[level] = fb;
                 if (level + 1 < 8) {
                     S.lv_klo[level + 1] = bklo;
-                    S.lv_span[level + 1] = (uint64_t)(bkhi - bklo) + 1ull;
+                    S.lv_sh[level + 1] = bin_shift((uint64_t)(bkhi - bklo) + 1ull);
                 }
             }
             __syncthreads();
