@@ -1453,6 +1453,7 @@ constexpr int ROWS_THREADS = 256;
 
 constexpr int RCAP = 4096;       // candidates held in registers by the merge
 constexpr int NUC_STEPS = 16;    // top-p prefixes found without a sort, at most
+constexpr int WAVE_TOPP = 256;   // selections this small: top-p by one wave, in registers
 
 struct RowsShared {
     uint32_t addr[RCAP];      // slot address of each candidate (in-register path)
@@ -1467,6 +1468,42 @@ struct RowsShared {
     uint32_t cnt;
     double fd[2];
 };
+
+// Descending bitonic sort of 256 keys held by one wave, key 4 lane + r in
+// v[r]: partners in the same lane swap registers, partners in other lanes
+// are exchanged with shuffles.  No LDS and no barrier.
+__device__ __forceinline__ void wave_bitonic_desc256(uint64_t (&v)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 256; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j >= 1; j >>= 1) {
+            if (j >= 4) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = 4 * lane + r;
+                    const uint64_t o = shx64(v[r], j >> 2);
+                    // in a descending block the lower index keeps the larger key
+                    const bool keep_max = ((e & k) == 0) == ((e & j) == 0);
+                    v[r] = keep_max ? (o > v[r] ? o : v[r]) : (o < v[r] ? o : v[r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rp = r ^ j;
+                    if (rp > r) {
+                        const bool desc = ((4 * lane + r) & k) == 0;
+                        const uint64_t a = v[r], c = v[rp];
+                        if (desc ? (c > a) : (c < a)) {
+                            v[r] = c;
+                            v[rp] = a;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
 
 template <int NT>
 __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double *scd,
@@ -1886,8 +1923,10 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     else Zc = (Z != 0.0) ? Z * exp((double)M - (double)x0) : tot_e;
 
     // ---- top-p.  The kept set is the shortest prefix, in the order, whose
-    // mass reaches p Zc.  Short prefixes (the usual case) are found by taking
-    // the maxima one at a time; longer ones by sorting every candidate.
+    // mass reaches p Zc.  Selections of at most WAVE_TOPP entries are sorted
+    // and scanned by one wave; in larger ones short prefixes (the usual case)
+    // are found by taking the maxima one at a time, longer ones by sorting
+    // every candidate.
     uint32_t nK = nsel;
     bool settled = true;
     bool use_nuc = false;  // K is S.nuc[0..nK), else S.srt[0..nK)
@@ -1896,68 +1935,51 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         const double pZ = (double)md.p * Zc;
         double at = 0.0, below = 0.0;
         bool found = false;
-        {
-            uint32_t rem = 0;  // positions of this thread already taken
-            double cum = 0.0;
-            for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
-                uint64_t mx = 0;
+        if (nsel <= (uint32_t)WAVE_TOPP) {
+            // wave 0 holds the whole selection (positions 4 tid + i, tid <
+            // 64): it sorts it in registers, scans the masses in double and
+            // finds the first position whose running mass reaches pZ
+            if (tid < 64) {
+                uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};
+                wave_bitonic_desc256(w);
+                double e[4];
+                double l = 0.0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
-                mx = wg_max_u64<NT>(mx, S.sc64);
+                for (int i = 0; i < 4; ++i) {
+                    e[i] = 4 * tid + i < nsel ? exp((double)cval(w[i]) - (double)x0) : 0.0;
+                    l += e[i];
+                }
+                double inc = l;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
-                const double em = exp((double)cval(mx) - (double)x0);
-                below = cum;
-                cum += em;
-                if (tid == 0) S.nuc[it] = mx;
-                if (cum >= pZ) {
-                    found = true;
-                    at = cum;
-                    nK = it + 1;
-                    break;
+                for (int d = 1; d < 64; d <<= 1) {
+                    const double o = __shfl_up(inc, d, 64);
+                    if (tid >= d) inc += o;
+                }
+                double run = inc - l, a_ = 0.0, b_ = 0.0;
+                uint32_t first = NONE;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t p = 4 * tid + i;
+                    run += e[i];
+                    if (p < nsel && first == NONE && run >= pZ) {
+                        first = p;
+                        a_ = run;
+                        b_ = run - e[i];
+                    }
+                    if (p < nsel) S.srt[p] = w[i];
+                }
+                const uint64_t hit = __ballot(first != NONE);
+                if (hit == 0ull) {
+                    if (tid == 0) S.sel[0] = NONE;
+                } else if (tid == __ffsll((long long)hit) - 1) {
+                    S.sel[0] = first;
+                    S.fd[0] = a_;
+                    S.fd[1] = b_;
                 }
             }
-        }
-        if (found) {
-            use_nuc = true;
-        } else {
-            // the whole order: sort, then prefix masses by position
-            const int npad = pow2_ceil((int)nsel);
-            for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
             __syncthreads();
-            bitonic_desc<NT>(S.srt, npad);
             srt_sorted = true;
-            double e[4];
-            double l2 = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t p = 4 * tid + i;
-                e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
-                l2 += e[i];
-            }
-            double t2;
-            const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
-            uint32_t first = NONE;
-            double run = before, a_ = 0.0, b_ = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t p = 4 * tid + i;
-                run += e[i];
-                if (p < nsel && first == NONE && run >= pZ) {
-                    first = p;
-                    a_ = run;
-                    b_ = run - e[i];
-                }
-            }
-            const uint32_t mine = first;
-            first = wg_min_u32<NT>(first, S.sc);
-            if (first != NONE && mine == first) {
-                S.fd[0] = a_;
-                S.fd[1] = b_;
-            }
-            __syncthreads();
+            const uint32_t first = S.sel[0];
             if (first != NONE) {
                 found = true;
                 nK = first + 1;
@@ -1965,6 +1987,77 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 below = S.fd[1];
             }
             __syncthreads();
+        } else {
+            {
+                uint32_t rem = 0;  // positions of this thread already taken
+                double cum = 0.0;
+                for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
+                    uint64_t mx = 0;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
+                    mx = wg_max_u64<NT>(mx, S.sc64);
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
+                    const double em = exp((double)cval(mx) - (double)x0);
+                    below = cum;
+                    cum += em;
+                    if (tid == 0) S.nuc[it] = mx;
+                    if (cum >= pZ) {
+                        found = true;
+                        at = cum;
+                        nK = it + 1;
+                        break;
+                    }
+                }
+            }
+            if (found) {
+                use_nuc = true;
+            } else {
+                // the whole order: sort, then prefix masses by position
+                const int npad = pow2_ceil((int)nsel);
+                for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
+                __syncthreads();
+                bitonic_desc<NT>(S.srt, npad);
+                srt_sorted = true;
+                double e[4];
+                double l2 = 0.0;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t p = 4 * tid + i;
+                    e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                    l2 += e[i];
+                }
+                double t2;
+                const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
+                uint32_t first = NONE;
+                double run = before, a_ = 0.0, b_ = 0.0;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t p = 4 * tid + i;
+                    run += e[i];
+                    if (p < nsel && first == NONE && run >= pZ) {
+                        first = p;
+                        a_ = run;
+                        b_ = run - e[i];
+                    }
+                }
+                const uint32_t mine = first;
+                first = wg_min_u32<NT>(first, S.sc);
+                if (first != NONE && mine == first) {
+                    S.fd[0] = a_;
+                    S.fd[1] = b_;
+                }
+                __syncthreads();
+                if (first != NONE) {
+                    found = true;
+                    nK = first + 1;
+                    at = S.fd[0];
+                    below = S.fd[1];
+                }
+                __syncthreads();
+            }
         }
         if (md.tk) {
             if (!found) nK = nsel;  // rounding: the whole top-k set
