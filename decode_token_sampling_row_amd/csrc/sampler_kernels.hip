@@ -1454,6 +1454,7 @@ constexpr int ROWS_THREADS = 256;
 constexpr int RCAP = 4096;       // candidates held in registers by the merge
 constexpr int NUC_STEPS = 16;    // top-p prefixes found without a sort, at most
 constexpr int WAVE_TOPP = 256;   // selections this small: top-p by one wave, in registers
+constexpr int WAVE_NUC = 4;      // maxima the wave looks at before it sorts (fixed: 4)
 
 struct RowsShared {
     uint32_t addr[RCAP];      // slot address of each candidate (in-register path)
@@ -1468,6 +1469,36 @@ struct RowsShared {
     uint32_t cnt;
     double fd[2];
 };
+
+__device__ __forceinline__ void cx_desc(uint64_t &a, uint64_t &b) {
+    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+}
+// The 4 largest of the 256 keys one wave holds (4 per lane), in descending
+// order, in every lane: each lane sorts its own 4, then 6 exchange steps
+// merge two sorted lists of 4 and keep the larger half (compare position i
+// with the partner's position 3 - i, then sort the bitonic result).
+__device__ __forceinline__ void wave_top4(const uint64_t (&v)[4], uint64_t (&t)[4]) {
+    t[0] = v[0]; t[1] = v[1]; t[2] = v[2]; t[3] = v[3];
+    cx_desc(t[0], t[1]);
+    cx_desc(t[2], t[3]);
+    cx_desc(t[0], t[2]);
+    cx_desc(t[1], t[3]);
+    cx_desc(t[1], t[2]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = shx64(t[i], m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = t[i] > o[3 - i] ? t[i] : o[3 - i];
+        cx_desc(t[0], t[2]);
+        cx_desc(t[1], t[3]);
+        cx_desc(t[0], t[1]);
+        cx_desc(t[2], t[3]);
+    }
+}
 
 // Descending bitonic sort of 256 keys held by one wave, key 4 lane + r in
 // v[r]: partners in the same lane swap registers, partners in other lanes
@@ -1937,10 +1968,32 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         bool found = false;
         if (nsel <= (uint32_t)WAVE_TOPP) {
             // wave 0 holds the whole selection (positions 4 tid + i, tid <
-            // 64): it sorts it in registers, scans the masses in double and
-            // finds the first position whose running mass reaches pZ
+            // 64).  It takes the first maxima one at a time (a short prefix
+            // is the usual case); if they do not reach pZ it sorts the
+            // selection in registers, scans the masses in double and finds
+            // the first position whose running mass reaches pZ
             if (tid < 64) {
-                uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};
+                uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};  // 0 beyond nsel
+                uint64_t t4[4];
+                wave_top4(w, t4);
+                double cum = 0.0, prev = 0.0;
+                uint32_t nfound = 0;
+#pragma unroll
+                for (int it = 0; it < WAVE_NUC; ++it) {
+                    if (nfound || (uint32_t)it >= nsel) break;
+                    prev = cum;
+                    cum += exp((double)cval(t4[it]) - (double)x0);
+                    if (tid == 0) S.nuc[it] = t4[it];
+                    if (cum >= pZ) nfound = it + 1;
+                }
+                if (nfound) {
+                    if (tid == 0) {
+                        S.sel[0] = nfound - 1;
+                        S.sel[1] = 1u;  // K is S.nuc[0 .. nfound)
+                        S.fd[0] = cum;
+                        S.fd[1] = prev;
+                    }
+                } else {
                 wave_bitonic_desc256(w);
                 double e[4];
                 double l = 0.0;
@@ -1969,6 +2022,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                     if (p < nsel) S.srt[p] = w[i];
                 }
                 const uint64_t hit = __ballot(first != NONE);
+                if (tid == 0) S.sel[1] = 0u;  // K is S.srt[0 .. nK), sorted
                 if (hit == 0ull) {
                     if (tid == 0) S.sel[0] = NONE;
                 } else if (tid == __ffsll((long long)hit) - 1) {
@@ -1976,10 +2030,12 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                     S.fd[0] = a_;
                     S.fd[1] = b_;
                 }
+                }
             }
             __syncthreads();
-            srt_sorted = true;
             const uint32_t first = S.sel[0];
+            if (S.sel[1]) use_nuc = true;
+            else srt_sorted = true;
             if (first != NONE) {
                 found = true;
                 nK = first + 1;
