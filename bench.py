@@ -1,6 +1,7 @@
 """Benchmark of the batched logits sampler on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
+    python bench.py --latency [--steps K] [--warmup W]
 
 A step is one sampler_run over one batch: the whole hot path (penalty,
 temperature, top-k, softmax, top-p, exponential race, dense filtered
@@ -12,6 +13,12 @@ Prints one JSON line: rows/s (value), ms per step, achieved HBM GB/s of the
 path's algorithmic bytes, a roofline entry for the dominant kernel (timed with
 HIP events on the stream it runs on), and the CPU oracle timed on a bounded
 sample of the same rows.
+
+--latency instead times single calls of each of the five workloads (batch x
+vocab 4 x 32000 up to 1024 x 262144, each with its own stage mix) and prints
+one JSON line per workload: the median, p10 and p90 per-call time from HIP
+events around each call, with a 1 GiB buffer written between calls so that
+the small workloads' inputs are not served from the 256 MB last-level cache.
 """
 from __future__ import annotations
 
@@ -42,6 +49,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--latency", action="store_true",
+                    help="per-call latency of every workload (one JSON line each)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) a few times: "
                          "the reference for scaling HBM byte counters")
@@ -116,6 +125,62 @@ def counted_traffic(kernel):
     return None
 
 
+def latency(args):
+    """Per-call latency of each workload, caches flushed between calls."""
+    import torch
+
+    from decode_token_sampling_row_amd import workloads as wl
+    from decode_token_sampling_row_amd.sampler import Sampler
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for cfg in sorted(wl.CONFIGS):
+        W = wl.make(cfg, seed=args.seed)
+        if W.dtype == wl.BF16:
+            logits = torch.from_numpy(W.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            logits = torch.from_numpy(W.logits).to(dev)
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        out_idx = torch.empty(W.B, dtype=torch.int64, device=dev)
+        out_l = torch.empty((W.B, W.V), dtype=torch.float32, device=dev)
+        s = Sampler(W.B, W.V, torch.bfloat16 if W.dtype == wl.BF16 else torch.float32)
+        kw = dict(top_k=t(W.top_k), top_p=t(W.top_p), q=t(W.q), eps=W.eps,
+                  temperature=W.temperature, repetition_penalty=W.penalty,
+                  penalty_ids=t(W.ids), penalty_offsets=t(W.offsets), row_flags=t(W.row_flags),
+                  out_logits=out_l if W.need_logits else None)
+        # kept-set sizes for the byte model, from an untimed call with the dense output
+        s.run(logits, out_idx, **dict(kw, out_logits=out_l))
+        torch.cuda.synchronize()
+        kept = torch.isfinite(out_l).sum(dim=1).cpu().numpy()
+        for _ in range(args.warmup):
+            s.run(logits, out_idx, **kw)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(float(i))
+            a.record(stream)
+            s.run(logits, out_idx, **kw)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        med = float(np.median(us))
+        nbytes = sum(model_bytes(W, kept).values())
+        print(json.dumps({
+            "workload": W.name, "batch": W.B, "vocab": W.V, "logits_dtype": W.dtype,
+            "calls": args.steps, "us_per_call_median": med,
+            "us_per_call_p10": float(np.percentile(us, 10)),
+            "us_per_call_p90": float(np.percentile(us, 90)),
+            "rows_per_s": W.B / (med * 1e-6), "model_bytes": int(nbytes),
+            "hbm_gbps": nbytes / (med * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "caches": "1 GiB written between calls"}), flush=True)
+        s.close()
+        del out_l, logits
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +190,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.latency:
+        latency(args)
         return
 
     import torch

@@ -1536,6 +1536,46 @@ __device__ __forceinline__ void wave_bitonic_desc256(uint64_t (&v)[4]) {
     }
 }
 
+// Sorts srt[0 .. n) in descending order, n <= 4 NT = 1024 (NT = 256): each
+// wave sorts its 256 positions in registers; a key's place is then its
+// position in its own run plus, in each other run, the number of keys above
+// it (a binary search).  runs: LDS scratch for 4 NT keys.  Composite keys are
+// distinct and never 0, so 0 pads the runs.  Starts reading srt without a
+// barrier (its writers must have passed one); ends with a barrier.
+template <int NT>
+__device__ __attribute__((noinline)) void wg_sort_desc(uint64_t *srt, uint32_t n, uint64_t *runs) {
+    static_assert(NT == 256, "four waves of 64 lanes, 4 keys per lane");
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    {
+        uint64_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (uint32_t)(4 * tid + i) < n ? srt[4 * tid + i] : 0ull;
+        wave_bitonic_desc256(v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) runs[4 * tid + i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t k = runs[4 * tid + i];
+        if (k == 0ull) continue;
+        uint32_t rank = (uint32_t)(4 * lane + i);
+#pragma unroll 1
+        for (int o = 0; o < 4; ++o) {
+            if (o == w) continue;
+            const uint64_t *r = runs + 256 * o;
+            // keys above k form a prefix of the descending run
+            uint32_t c = 0;
+#pragma unroll
+            for (uint32_t step = 256; step >= 1; step >>= 1)
+                if (c + step <= 256u && r[c + step - 1] > k) c += step;
+            rank += c;
+        }
+        srt[rank] = k;
+    }
+    __syncthreads();
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double *scd,
                                                   uint32_t *sci) {
@@ -2049,11 +2089,11 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 double cum = 0.0;
                 for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
                     uint64_t mx = 0;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
                     mx = wg_max_u64<NT>(mx, S.sc64);
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
                     const double em = exp((double)cval(mx) - (double)x0);
@@ -2072,14 +2112,11 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 use_nuc = true;
             } else {
                 // the whole order: sort, then prefix masses by position
-                const int npad = pow2_ceil((int)nsel);
-                for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
-                __syncthreads();
-                bitonic_desc<NT>(S.srt, npad);
+                wg_sort_desc<NT>(S.srt, nsel, reinterpret_cast<uint64_t *>(S.addr));
                 srt_sorted = true;
                 double e[4];
                 double l2 = 0.0;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t p = 4 * tid + i;
                     e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
@@ -2089,7 +2126,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
                 uint32_t first = NONE;
                 double run = before, a_ = 0.0, b_ = 0.0;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t p = 4 * tid + i;
                     run += e[i];
@@ -2145,12 +2182,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // when no top-p cut ordered it; then K is the whole selection)
     uint32_t inv_pos = 0;
     if (md.inv) {
-        if (!use_nuc && !srt_sorted && nK > 1) {
-            const int npad = pow2_ceil((int)nsel);
-            for (int i = nsel + tid; i < npad; i += NT) S.srt[i] = 0ull;
-            __syncthreads();
-            bitonic_desc<NT>(S.srt, npad);
-        }
+        if (!use_nuc && !srt_sorted && nK > 1)
+            wg_sort_desc<NT>(S.srt, nsel, reinterpret_cast<uint64_t *>(S.addr));
         inv_pos = inverse_cdf_pos<NT>(use_nuc ? S.nuc : S.srt, nK, x0, P.u[b], S.scd, S.sc);
     }
 
