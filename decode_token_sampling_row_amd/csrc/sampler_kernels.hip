@@ -2413,6 +2413,51 @@ __device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
     __syncthreads();
 }
 
+// row_pass with the row's q as well, f(x, q, j), in groups of 4: the 4
+// logits and the 4 q of a group are requested as vectors one group ahead of
+// the visitors, so a visitor that needs q only for some elements does not
+// wait for each load in turn (and 4-wide groups keep the register count
+// down).
+template <int DT, bool AL, bool XF, class F>
+__device__ void row_pass_q(const KParams &P, int b, uint32_t *bm, const float *rowq, F &&f) {
+    const void *rowp = row_ptr(P, DT, b);
+    const int V = P.V;
+    for (int s0 = 0; s0 < V; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, V);
+        if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
+        // one group in flight ahead of the one being visited
+        int j = s0 + (int)threadIdx.x * 4;
+        Raw4<DT> rx;
+        Raw4<0> rq;
+        if (j < s1) {
+            const int nv0 = s1 - j >= 4 ? 4 : s1 - j;
+            load4<DT, AL>(rowp, j, nv0, rx);
+            load4<0, AL>(rowq, j, nv0, rq);
+        }
+        for (; j < s1; j += K3_THREADS * 4) {
+            const int nv = s1 - j >= 4 ? 4 : s1 - j;
+            float x[4], qx[4];
+            unpack4<DT>(rx, x);
+            unpack4<0>(rq, qx);
+            const int jn = j + K3_THREADS * 4;
+            if (jn < s1) {
+                const int nvn = s1 - jn >= 4 ? 4 : s1 - jn;
+                load4<DT, AL>(rowp, jn, nvn, rx);
+                load4<0, AL>(rowq, jn, nvn, rq);
+            }
+            uint32_t bits = 0;
+            if (P.pen) {
+                const int r = j - s0;
+                bits = (bm[r >> 5] >> (r & 31)) & 0xfu;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nv) f(xform<XF>(x[i], (bits >> i) & 1u, P), qx[i], (uint32_t)(j + i));
+        }
+    }
+    __syncthreads();
+}
+
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
@@ -2690,8 +2735,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         Race rc;
         rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
         const float *rowq = P.q + (int64_t)b * P.V;
-        row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-            if (mkcomp(x, j) >= Tstar) race_offer(rc, x, rowq[j] + P.eps, j);
+        row_pass_q<DT, AL, XF>(P, b, S.bm, rowq, [&](float x, float qj, uint32_t j) {
+            if (mkcomp(x, j) >= Tstar) race_offer(rc, x, qj + P.eps, j);
         });
         Race r = wg_race<K3_THREADS>(rc, S.scx, S.scq, S.sci);
         idx = r.idx;
