@@ -2387,26 +2387,32 @@ __device__ __forceinline__ bool in_play(const FallbackShared &S, float x, uint32
     return true;
 }
 
-// Visit every element (x transformed, id j) of row b; f(x, j).
+// Visit every element (x transformed, id j) of row b; f(x, j).  Groups of 4
+// per thread, the next group requested before the current one is visited,
+// so that each thread keeps a load in flight while its visitors run.
 template <int DT, bool AL, bool XF, class F>
 __device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
     const void *rowp = row_ptr(P, DT, b);
-    const int64_t V = P.V;
-    for (int64_t s0 = 0; s0 < V; s0 += K3_SEG) {
-        const int64_t s1 = min(s0 + (int64_t)K3_SEG, V);
+    const int V = P.V;
+    for (int s0 = 0; s0 < V; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, V);
         if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
-        for (int64_t j = s0 + (int64_t)threadIdx.x * VEC; j < s1; j += (int64_t)K3_THREADS * VEC) {
-            int64_t rem = s1 - j;
-            int nv = rem >= 8 ? 8 : (int)rem;
-            float x[8];
-            load8<DT, AL>(rowp, j, nv, x);
+        int j = s0 + (int)threadIdx.x * 4;
+        Raw4<DT> rx;
+        if (j < s1) load4<DT, AL>(rowp, j, s1 - j >= 4 ? 4 : s1 - j, rx);
+        for (; j < s1; j += K3_THREADS * 4) {
+            const int nv = s1 - j >= 4 ? 4 : s1 - j;
+            float x[4];
+            unpack4<DT>(rx, x);
+            const int jn = j + K3_THREADS * 4;
+            if (jn < s1) load4<DT, AL>(rowp, jn, s1 - jn >= 4 ? 4 : s1 - jn, rx);
             uint32_t bits = 0;
             if (P.pen) {
-                int64_t r = j - s0;
-                bits = (bm[r >> 5] >> (r & 31)) & 0xffu;
+                const int r = j - s0;
+                bits = (bm[r >> 5] >> (r & 31)) & 0xfu;
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 4; ++i)
                 if (i < nv) f(xform<XF>(x[i], (bits >> i) & 1u, P), (uint32_t)(j + i));
         }
     }
