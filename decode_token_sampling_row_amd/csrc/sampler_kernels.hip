@@ -2539,8 +2539,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, sh);
                 atomicAdd(&S.hm[bi], e);
                 atomicAdd(&S.hc[bi], 1u);
-                atomicMin(&S.hlo[bi], k);
-                atomicMax(&S.hhi[bi], k);
+                if (level != 0) {  // level 0: the key range follows from the bin edges
+                    atomicMin(&S.hlo[bi], k);
+                    atomicMax(&S.hhi[bi], k);
+                }
             });
             if (level == 0) {
                 double Z = wg_sum_f64<K3_THREADS>(zt, S.scd);
@@ -2554,7 +2556,19 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             bsel = fb;
             bcnt = S.hc[fb];
             bklo = S.hlo[fb];
-            const uint32_t bkhi = S.hhi[fb];
+            uint32_t bkhi = S.hhi[fb];
+            if (level == 0) {
+                // keys of the bin's value range, half a bin wider on each side
+                // than its edges (rounding in bin_value moves an edge by far
+                // less); bin 0 also holds everything below lo (-inf included),
+                // the last bin everything up to the maximum.  Membership is
+                // still decided by the bin itself, so a wider range is safe.
+                const float w = 1.0f / scale;
+                bklo = fb == 0 ? 0u : f2key(lo + ((float)fb - 0.5f) * w);
+                bkhi = fb == (uint32_t)(K3_BINS - 1) ? f2key(info.m)
+                                                     : f2key(fminf(lo + ((float)fb + 1.5f) * w, info.m));
+                if (bkhi < bklo) bkhi = bklo;
+            }
             __syncthreads();
             if (tid == 0) {
                 if (level == 0) {
