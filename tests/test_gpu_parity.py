@@ -214,6 +214,32 @@ def test_inverse_cdf_sampling(cfg):
     print(f"[case] inverse cfg{cfg}: {stats}", flush=True)
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("draw", ["race", "inverse"])
+def test_topp_selection_sizes(dtype, draw):
+    """Top-p over selections on both sides of the row merge's size limits:
+    at most 256 entries are cut by one wave (4 largest first, then a register
+    sort), larger ones by maxima extraction and then the workgroup sort.
+    Near-flat rows make the nuclei long enough to reach the sorts; bf16
+    rows add ties inside the selection."""
+    rng = np.random.default_rng(31 if dtype == wl.F32 else 32)
+    ks = [3, 4, 5, 255, 256, 257, 511, 1024]
+    ps = [0.2, 0.6, 0.9, 0.999]
+    B, V = len(ks) * len(ps), 20000
+    x = (rng.standard_normal((B, V)) * 0.3).astype(np.float32)
+    k = np.repeat(ks, len(ps))
+    p = np.tile(ps, len(ks)).astype(np.float32)
+    W = _custom(x, top_k=k, top_p=p, flags=7, dtype=dtype, seed=33)
+    u = rng.random(B).astype(np.float32) if draw == "inverse" else None
+    print(f"[case] top-p selection sizes {dtype} {draw} B={B} V={V}", flush=True)
+    hip = run_hip(W, need_logits=True, need_probs=True, u=u, drop_q=u is not None)
+    ref = run_oracle(W, need_logits=True, need_probs=True, u=u)
+    _log(f"top-p sizes {dtype} {draw}", compare(W, hip, ref, label="top-p sizes",
+                                                inverse=u is not None))
+    # every selection size and p produced a non-trivial cut somewhere
+    assert (ref["nkept"] > 8).any() and (ref["nkept"] < k).any()
+
+
 def test_repeated_runs_bit_identical():
     import torch
 
