@@ -1536,46 +1536,6 @@ __device__ __forceinline__ void wave_bitonic_desc256(uint64_t (&v)[4]) {
     }
 }
 
-// Sorts srt[0 .. n) in descending order, n <= 4 NT = 1024 (NT = 256): each
-// wave sorts its 256 positions in registers; a key's place is then its
-// position in its own run plus, in each other run, the number of keys above
-// it (a binary search).  runs: LDS scratch for 4 NT keys.  Composite keys are
-// distinct and never 0, so 0 pads the runs.  Starts reading srt without a
-// barrier (its writers must have passed one); ends with a barrier.
-template <int NT>
-__device__ __attribute__((noinline)) void wg_sort_desc(uint64_t *srt, uint32_t n, uint64_t *runs) {
-    static_assert(NT == 256, "four waves of 64 lanes, 4 keys per lane");
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    {
-        uint64_t v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (uint32_t)(4 * tid + i) < n ? srt[4 * tid + i] : 0ull;
-        wave_bitonic_desc256(v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) runs[4 * tid + i] = v[i];
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int i = 0; i < 4; ++i) {
-        const uint64_t k = runs[4 * tid + i];
-        if (k == 0ull) continue;
-        uint32_t rank = (uint32_t)(4 * lane + i);
-#pragma unroll 1
-        for (int o = 0; o < 4; ++o) {
-            if (o == w) continue;
-            const uint64_t *r = runs + 256 * o;
-            // keys above k form a prefix of the descending run
-            uint32_t c = 0;
-#pragma unroll
-            for (uint32_t step = 256; step >= 1; step >>= 1)
-                if (c + step <= 256u && r[c + step - 1] > k) c += step;
-            rank += c;
-        }
-        srt[rank] = k;
-    }
-    __syncthreads();
-}
-
 template <int NT>
 __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double *scd,
                                                   uint32_t *sci) {
@@ -2000,22 +1960,19 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // every candidate.
     uint32_t nK = nsel;
     bool settled = true;
-    bool use_nuc = false;  // K is S.nuc[0..nK), else S.srt[0..nK)
-    bool srt_sorted = false;  // srt is in the row's order
+    bool use_nuc = false;     // K is S.nuc[0..nK), else S.srt[0..nK)
+    const bool small = nsel <= (uint32_t)WAVE_TOPP;  // all in wave 0 (positions 4 tid + i)
+    const double pZ = md.tp ? (double)md.p * Zc : 0.0;
+    double at = 0.0, below = 0.0;
+    bool found = false;
+    // ---- top-p, step 1: a short prefix (the usual case).  Small selections
+    // take their 4 largest from one wave reduction; larger ones up to
+    // NUC_STEPS maxima, one at a time, by the workgroup.
     if (md.tp) {
-        const double pZ = (double)md.p * Zc;
-        double at = 0.0, below = 0.0;
-        bool found = false;
-        if (nsel <= (uint32_t)WAVE_TOPP) {
-            // wave 0 holds the whole selection (positions 4 tid + i, tid <
-            // 64).  It takes the first maxima one at a time (a short prefix
-            // is the usual case); if they do not reach pZ it sorts the
-            // selection in registers, scans the masses in double and finds
-            // the first position whose running mass reaches pZ
+        if (small) {
             if (tid < 64) {
-                uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};  // 0 beyond nsel
                 uint64_t t4[4];
-                wave_top4(w, t4);
+                wave_top4(v4, t4);  // v4 is 0 beyond nsel
                 double cum = 0.0, prev = 0.0;
                 uint32_t nfound = 0;
 #pragma unroll
@@ -2026,15 +1983,92 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                     if (tid == 0) S.nuc[it] = t4[it];
                     if (cum >= pZ) nfound = it + 1;
                 }
-                if (nfound) {
-                    if (tid == 0) {
-                        S.sel[0] = nfound - 1;
-                        S.sel[1] = 1u;  // K is S.nuc[0 .. nfound)
-                        S.fd[0] = cum;
-                        S.fd[1] = prev;
-                    }
-                } else {
-                wave_bitonic_desc256(w);
+                if (tid == 0) {
+                    S.sel[0] = nfound ? nfound - 1 : NONE;
+                    S.fd[0] = cum;
+                    S.fd[1] = prev;
+                }
+            }
+            __syncthreads();
+            if (S.sel[0] != NONE) {
+                found = true;
+                nK = S.sel[0] + 1;
+                at = S.fd[0];
+                below = S.fd[1];
+            }
+            __syncthreads();
+        } else {
+            uint32_t rem = 0;  // positions of this thread already taken
+            double cum = 0.0;
+            for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
+                uint64_t mx = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
+                mx = wg_max_u64<NT>(mx, S.sc64);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
+                const double em = exp((double)cval(mx) - (double)x0);
+                below = cum;
+                cum += em;
+                if (tid == 0) S.nuc[it] = mx;
+                if (cum >= pZ) {
+                    found = true;
+                    at = cum;
+                    nK = it + 1;
+                    break;
+                }
+            }
+        }
+        use_nuc = found;
+    }
+    // ---- step 2: the selection in the row's order, when top-p needs more
+    // than a short prefix, or for an inverse-CDF draw over the whole
+    // selection.  Each wave sorts its 256 positions in registers; a small
+    // selection is then wholly in wave 0, a larger one merges the four runs:
+    // a key's place is its position in its run plus, in each other run, the
+    // number of keys above it (a binary search; composite keys are distinct
+    // and never 0, so 0 pads).  Then, for top-p, the shortest prefix whose
+    // running mass (in double) reaches pZ.
+    if (md.tp ? !found : (md.inv && nsel > 1)) {
+        uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};
+        wave_bitonic_desc256(w);
+        if (small) {
+            if (tid < 64) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((uint32_t)(4 * tid + i) < nsel) S.srt[4 * tid + i] = w[i];
+            }
+        } else {
+            uint64_t *runs = reinterpret_cast<uint64_t *>(S.addr);  // free by now
+#pragma unroll
+            for (int i = 0; i < 4; ++i) runs[4 * tid + i] = w[i];
+            __syncthreads();
+            const int wv = tid >> 6;
+#pragma unroll 1
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t k = runs[4 * tid + i];
+                if (k == 0ull) continue;
+                uint32_t rank = (uint32_t)(4 * (tid & 63) + i);
+#pragma unroll 1
+                for (int o = 0; o < 4; ++o) {
+                    if (o == wv) continue;
+                    const uint64_t *r = runs + 256 * o;
+                    uint32_t c = 0;  // keys above k: a prefix of the run
+#pragma unroll
+                    for (uint32_t step = 256; step >= 1; step >>= 1)
+                        if (c + step <= 256u && r[c + step - 1] > k) c += step;
+                    rank += c;
+                }
+                S.srt[rank] = k;
+            }
+        }
+        __syncthreads();
+        if (md.tp && small) {
+            // wave 0: masses of its sorted registers, a shuffle scan, the
+            // first position reaching pZ by ballot
+            if (tid < 64) {
                 double e[4];
                 double l = 0.0;
 #pragma unroll
@@ -2059,10 +2093,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                         a_ = run;
                         b_ = run - e[i];
                     }
-                    if (p < nsel) S.srt[p] = w[i];
                 }
                 const uint64_t hit = __ballot(first != NONE);
-                if (tid == 0) S.sel[1] = 0u;  // K is S.srt[0 .. nK), sorted
                 if (hit == 0ull) {
                     if (tid == 0) S.sel[0] = NONE;
                 } else if (tid == __ffsll((long long)hit) - 1) {
@@ -2070,12 +2102,47 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                     S.fd[0] = a_;
                     S.fd[1] = b_;
                 }
-                }
             }
             __syncthreads();
-            const uint32_t first = S.sel[0];
-            if (S.sel[1]) use_nuc = true;
-            else srt_sorted = true;
+            if (S.sel[0] != NONE) {
+                found = true;
+                nK = S.sel[0] + 1;
+                at = S.fd[0];
+                below = S.fd[1];
+            }
+            __syncthreads();
+        } else if (md.tp) {
+            // workgroup: masses by position, an exclusive scan, the least
+            // position reaching pZ
+            double e[4];
+            double l2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                l2 += e[i];
+            }
+            double t2;
+            const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
+            uint32_t first = NONE;
+            double run = before, a_ = 0.0, b_ = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                run += e[i];
+                if (p < nsel && first == NONE && run >= pZ) {
+                    first = p;
+                    a_ = run;
+                    b_ = run - e[i];
+                }
+            }
+            const uint32_t mine = first;
+            first = wg_min_u32<NT>(first, S.sc);
+            if (first != NONE && mine == first) {
+                S.fd[0] = a_;
+                S.fd[1] = b_;
+            }
+            __syncthreads();
             if (first != NONE) {
                 found = true;
                 nK = first + 1;
@@ -2083,75 +2150,9 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 below = S.fd[1];
             }
             __syncthreads();
-        } else {
-            {
-                uint32_t rem = 0;  // positions of this thread already taken
-                double cum = 0.0;
-                for (uint32_t it = 0; it < (uint32_t)NUC_STEPS && it < nsel; ++it) {
-                    uint64_t mx = 0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!((rem >> i) & 1u) && 4 * tid + i < nsel) mx = v4[i] > mx ? v4[i] : mx;
-                    mx = wg_max_u64<NT>(mx, S.sc64);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
-                    const double em = exp((double)cval(mx) - (double)x0);
-                    below = cum;
-                    cum += em;
-                    if (tid == 0) S.nuc[it] = mx;
-                    if (cum >= pZ) {
-                        found = true;
-                        at = cum;
-                        nK = it + 1;
-                        break;
-                    }
-                }
-            }
-            if (found) {
-                use_nuc = true;
-            } else {
-                // the whole order: sort, then prefix masses by position
-                wg_sort_desc<NT>(S.srt, nsel, reinterpret_cast<uint64_t *>(S.addr));
-                srt_sorted = true;
-                double e[4];
-                double l2 = 0.0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t p = 4 * tid + i;
-                    e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
-                    l2 += e[i];
-                }
-                double t2;
-                const double before = wg_excl_scan_f64<NT>(l2, S.scd, t2);
-                uint32_t first = NONE;
-                double run = before, a_ = 0.0, b_ = 0.0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t p = 4 * tid + i;
-                    run += e[i];
-                    if (p < nsel && first == NONE && run >= pZ) {
-                        first = p;
-                        a_ = run;
-                        b_ = run - e[i];
-                    }
-                }
-                const uint32_t mine = first;
-                first = wg_min_u32<NT>(first, S.sc);
-                if (first != NONE && mine == first) {
-                    S.fd[0] = a_;
-                    S.fd[1] = b_;
-                }
-                __syncthreads();
-                if (first != NONE) {
-                    found = true;
-                    nK = first + 1;
-                    at = S.fd[0];
-                    below = S.fd[1];
-                }
-                __syncthreads();
-            }
         }
+    }
+    if (md.tp) {
         if (md.tk) {
             if (!found) nK = nsel;  // rounding: the whole top-k set
         } else if (!found) {
@@ -2178,14 +2179,11 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     }
     __syncthreads();
 
-    // ---- inverse-CDF draw over K, in the row's order (srt is sorted first
-    // when no top-p cut ordered it; then K is the whole selection)
+    // ---- inverse-CDF draw over K, in the row's order (K is a prefix of
+    // the sorted selection, or the short prefix in S.nuc)
     uint32_t inv_pos = 0;
-    if (md.inv) {
-        if (!use_nuc && !srt_sorted && nK > 1)
-            wg_sort_desc<NT>(S.srt, nsel, reinterpret_cast<uint64_t *>(S.addr));
+    if (md.inv)
         inv_pos = inverse_cdf_pos<NT>(use_nuc ? S.nuc : S.srt, nK, x0, P.u[b], S.scd, S.sc);
-    }
 
     // ---- exponential race over K (or greedy), and the kept list
     const uint64_t *kp = use_nuc ? S.nuc : S.srt;
