@@ -215,6 +215,22 @@ def test_inverse_cdf_sampling(cfg):
 
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_far_spikes_in_the_estimate_sample(dtype):
+    """A few logits far above the rest (1e4 over a N(0, 2^2) bulk) put the
+    estimate sample's maximum so far up that the r-th sampled key lies
+    outside the fine bins below it; the estimate then finds it in two steps
+    (coarse bin, then fine bin inside)."""
+    rng = np.random.default_rng(41)
+    B, V = 24, 100000
+    x = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+    for r in range(B):
+        x[r, rng.choice(V, size=40, replace=False)] += np.float32(1e4)
+    k = np.array([1024, 300, 0, 50] * 6)
+    W = _custom(x, top_k=k, top_p=0.9, flags=_all_combos(B), dtype=dtype, seed=42)
+    _check(W, f"far spikes {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("draw", ["race", "inverse"])
 def test_topp_selection_sizes(dtype, draw):
     """Top-p over selections on both sides of the row merge's size limits:
