@@ -309,19 +309,6 @@ __device__ __forceinline__ uint64_t wg_min_u64(uint64_t v, uint64_t *sc) {
 }
 
 template <int NT>
-__device__ __forceinline__ float wg_min_f32(float v, float *sc) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, shxf(v, m));
-    if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float t = INFINITY;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) t = fminf(t, sc[i]);
-    __syncthreads();
-    return t;
-}
-
-template <int NT>
 __device__ __forceinline__ uint32_t wg_min_u32(uint32_t v, uint32_t *sc) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = min(v, shx(v, m));
@@ -578,35 +565,6 @@ __device__ void bitonic_desc(uint64_t *s, int n) {
     }
 }
 
-// Descending bitonic sort of s[0..n), n a power of two <= NT: one element per
-// thread, partners closer than 64 exchanged with lane shuffles, farther ones
-// through LDS.  Callers barrier before; ends with a barrier.
-template <int NT>
-__device__ void bitonic_desc_reg(uint64_t *s, int n) {
-    const int i = threadIdx.x;
-    uint64_t v = (i < n) ? s[i] : 0ull;
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t o;
-            if (j >= 64) {
-                __syncthreads();
-                if (i < n) s[i] = v;
-                __syncthreads();
-                o = (i < n) ? s[i ^ j] : 0ull;
-            } else {
-                o = shx64(v, j);
-            }
-            const bool desc = (i & k) == 0;
-            const bool lower = (i & j) == 0;
-            const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
-            v = (desc == lower) ? mx : mn;
-        }
-    }
-    __syncthreads();
-    if (i < n) s[i] = v;
-    __syncthreads();
-}
-
 __device__ __forceinline__ int pow2_ceil(int n) {
     int p = 1;
     while (p < n) p <<= 1;
@@ -748,34 +706,6 @@ __device__ __forceinline__ void stats_batch(Stats &st, const float (&x)[UU][N], 
             st.z += (double)zs;
         }
     }
-}
-
-// Workgroup merge of per-thread Stats into one ChunkStat's m / z / xmin.
-template <int NT>
-__device__ __forceinline__ void stats_reduce(const Stats &st, float *scf, double *scd, ChunkStat &cs) {
-    float m = st.m;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, shxf(m, s));
-    if ((threadIdx.x & 63) == 0) scf[threadIdx.x >> 6] = m;
-    __syncthreads();
-    float M = scf[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, scf[i]);
-    __syncthreads();
-    double z = (st.z != 0.0) ? st.z * exp((double)st.m - (double)M) : 0.0;
-    z = wg_sum_f64<NT>(z, scd);
-    float mn = st.xmin;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) mn = fminf(mn, shxf(mn, s));
-    if ((threadIdx.x & 63) == 0) scf[threadIdx.x >> 6] = mn;
-    __syncthreads();
-    float MN = scf[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) MN = fminf(MN, scf[i]);
-    __syncthreads();
-    cs.m = M;
-    cs.z = z;
-    cs.xmin = MN;
 }
 
 __device__ __forceinline__ ChunkStat empty_stat() {
