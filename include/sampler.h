@@ -203,8 +203,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
  * Kernel times, in milliseconds, averaged over the sampler_run calls made
  * with SAMPLER_PROFILE since the previous sampler_profile call (the last 64
  * of them if there were more), in launch order: [0] per-row planning (the
- * admission estimate of top-k / top-p rows; not launched when a row fits one
- * tile of the pass, which then makes the estimate), [1] the streaming pass over the
+ * admission estimate of top-k / top-p rows), [1] the streaming pass over the
  * logits (every row), [2] row merge / cutoff / sample, [3] full-row search
  * (rows the pass could not settle, top-p rows whose guess failed, inverse-CDF
  * draws over whole rows), [4] dense outputs of filtered rows, [5] the
