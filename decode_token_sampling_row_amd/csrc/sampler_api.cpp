@@ -244,16 +244,14 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         return true;
     };
 
-    // rows of a single tile: the pass makes their admission estimate itself
-    const bool fused = filtering && l.nt == 1;
     mark(0);
-    if (filtering && !fused) {
+    if (filtering) {
         if (!each([&](const KParams &pc) { return launch_plan(pc, l, h->ws, h->dtype, al, st); }))
             return SAMPLER_EHIP;
         launched[0] = true;
     }
     mark(1);
-    if (!each([&](const KParams &pc) { return launch_pass(pc, l, h->ws, h->dtype, al, st, fused); }))
+    if (!each([&](const KParams &pc) { return launch_pass(pc, l, h->ws, h->dtype, al, st); }))
         return SAMPLER_EHIP;
     launched[1] = true;
     mark(2);

@@ -118,10 +118,8 @@ constexpr int EPI_THREADS = 1024;
 // Launchers (sampler_kernels.hip).  Return hipSuccess or the launch error.
 hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
                        hipStream_t s);
-// fused: rows are one tile long and the pass makes the admission estimate
-// itself (launch_plan is then not called).
 hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool aligned,
-                       hipStream_t s, bool fused);
+                       hipStream_t s);
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s);
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype,
                            bool aligned, hipStream_t s);

@@ -1337,8 +1337,8 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     }
 }
 
-template <int DT, bool AL, bool XF, bool FUSE>
-__device__ __forceinline__ void pass_body(const KParams &P, const KPlan &L, const KWork &W) {
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
     __shared__ uint64_t wbufs[PASS_WAVES][WCAP_MAX];  // each wave's candidates
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
     const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
@@ -1358,27 +1358,9 @@ __device__ __forceinline__ void pass_body(const KParams &P, const KPlan &L, cons
         }
     const Mode md = row_mode(P, b);
     if (b == 0 && t == 0 && threadIdx.x == 0) *W.fbcnt = 0u;  // the full-row search queue
-    float traw = 0.0f, ref = 0.0f;
-    if (FUSE) {
-        // one tile is the whole row: its admission estimate is made here,
-        // from the row itself, instead of by the planning kernel
-        __shared__ StreamShared ES;
-        float smax, smin;
-        bool act;
-        const float te = row_estimate<DT, AL>(P, b, ES, smax, smin, act);
-        if (act) {
-            traw = te;
-            ref = xform<XF>(smax, 0u, P);
-            if (threadIdx.x == 0) {
-                W.rowthr[b] = traw;
-                W.rowref[b] = ref;
-                W.rowlo[b] = smin < INFINITY ? xform<XF>(smin, 0u, P) : INFINITY;
-            }
-        }
-    } else if (P.top_k || P.top_p) {  // the planning kernel ran
-        traw = W.rowthr[b];
-        ref = W.rowref[b];
-    }
+    const bool filtering = P.top_k || P.top_p;  // the planning kernel ran
+    const float traw = filtering ? W.rowthr[b] : 0.0f;
+    const float ref = filtering ? W.rowref[b] : 0.0f;
     if (XF && P.pen) build_bitmap<PASS_THREADS>(bm, c0, c1 - c0, P, b);
     if (md.tk || md.tp)
         pass_tile<DT, AL, XF, 2>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
@@ -1386,18 +1368,6 @@ __device__ __forceinline__ void pass_body(const KParams &P, const KPlan &L, cons
         pass_tile<DT, AL, XF, 1>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
     else
         pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
-}
-
-template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
-    pass_body<DT, AL, XF, false>(P, L, W);
-}
-
-// Rows of one tile (vocab <= tile length) with top-k / top-p: the pass
-// makes the admission estimate itself, so no planning kernel runs.
-template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(PASS_THREADS) void k_pass_fused(KParams P, KPlan L, KWork W) {
-    pass_body<DT, AL, XF, true>(P, L, W);
 }
 
 // ================================================================== k_rows
@@ -2968,11 +2938,10 @@ hipError_t launch_plan(const KParams &p, const KPlan &l, const KWork &w, int dty
 }
 
 hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
-                       hipStream_t s, bool fused) {
+                       hipStream_t s) {
     const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(PASS_THREADS);
     size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
-    if (fused) return SMP_PICK(k_pass_fused, grid, block, sh);
     return SMP_PICK(k_pass, grid, block, sh);
 }
 
