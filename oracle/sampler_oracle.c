@@ -45,6 +45,9 @@
  *       output is the vocab id of the largest r, lowest id on exact ties
  *       (Ascend page, Sample section: probs/(q+eps), argmax, gather through
  *       logits_idx; q paired with candidates by vocab id -- a reading).
+ *       With eps = 0 and q = 0 the ratio of a finite logit is +inf (IEEE
+ *       positive / 0; the probability of a finite logit is positive even
+ *       where its double exponential underflows); -inf logits have ratio 0.
  *       Sampling off: the output is K_0, the greedy argmax (MiniMind 10.8).
  *   O9' sample by inverse CDF instead (row bit2 and uniforms u given; q is
  *       not used): the output is K_{n-1} for the least n >= 1 whose
@@ -63,7 +66,8 @@
  *   margin  top-p decision margin min(S_n* - p, p - S_{n*-1}) (n* > 1),
  *           S_1 - p (n* = 1), +inf when top-p is off
  *   gap     (r1 - r2) / r1 over the two largest ratios, +inf when there is
- *           no sampling or a single candidate; for inverse-CDF sampling the
+ *           no sampling, a single candidate, or an infinite largest ratio
+ *           (q + eps == 0 exactly); for inverse-CDF sampling the
  *           decision margin min(S_n - u, u - S_{n-1}) instead (+inf when
  *           n = 1 by u <= 0)
  *
@@ -261,7 +265,14 @@ int oracle_run(int32_t B, int32_t V, int32_t dtype, const void *logits, int64_t 
                 double pi = e[i] / ZK;
                 int32_t id = ord[i].id;
                 double den = (double)q[(int64_t)b * V + id] + (double)eps;
-                double r = (pi == 0.0) ? 0.0 : pi / den;
+                /* a -inf logit has probability 0 and is never drawn; every
+                 * finite logit has a positive probability (however far its
+                 * double exponential underflows), so a zero denominator
+                 * gives it an infinite ratio, as positive / 0 does in IEEE */
+                double r;
+                if (!(ord[i].x > -INFINITY)) r = 0.0;
+                else if (den == 0.0) r = INFINITY;
+                else r = pi / den;
                 if (r > r1 || (r == r1 && id < best)) {
                     if (best >= 0) r2 = r1;
                     r1 = r;
@@ -271,7 +282,11 @@ int oracle_run(int32_t B, int32_t V, int32_t dtype, const void *logits, int64_t 
                 }
             }
             idx = best;
-            if (nK > 1 && r2 >= 0.0) g = (r1 > 0.0) ? (r1 - r2) / r1 : 0.0;
+            /* infinite ratios come only from exact zeros of q + eps, and
+             * their ties go to the lowest id: that decision has no
+             * rounding in it, so it is not a near tie */
+            if (nK > 1 && r2 >= 0.0)
+                g = (r1 == INFINITY) ? INFINITY : (r1 > 0.0) ? (r1 - r2) / r1 : 0.0;
         }
         out_idx[b] = idx;
         if (nkept) nkept[b] = nK;

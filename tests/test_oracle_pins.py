@@ -664,3 +664,120 @@ def test_epilogue_full_slots_and_no_eos():
     assert e["idx"].tolist() == [4, 2, 9, 2]
     assert e["finished"].tolist() == [0, 0, 3, 0]
     assert e["counts"].tolist() == [3, 0]
+
+
+# ---------------------------------------------------------------- the gap diagnostic
+#
+# The GPU parity tests exempt a sampling row from the id check only when the
+# oracle's `gap` says the decision is a near tie, so `gap` itself is pinned
+# here against an independent numpy statement of the same quantities: the
+# kept set from a lexicographic sort, the ratios pi / (q + eps) over it
+# (Ascend page, Sample section), and for inverse-CDF draws the distance of u
+# to the nearest cumulative-probability boundary.
+
+def _numpy_kept(x, k, p):
+    """Kept ids of one row in the order (value desc, id asc), numpy only."""
+    V = x.size
+    order = np.lexsort((np.arange(V), -x.astype(np.float64)))
+    if 1 <= k <= min(V, 1024):
+        order = order[:k]
+    if p < 1.0:
+        e = np.exp(x[order].astype(np.float64) - float(x[order[0]]))
+        S = np.cumsum(e) / e.sum()
+        n = int(np.searchsorted(S >= p, True)) + 1 if (S >= p).any() else order.size
+        order = order[:n]
+    return order
+
+
+def _numpy_race_gap(x, q, eps, kept):
+    e = np.exp(x[kept].astype(np.float64) - float(x[kept[0]]))
+    den = q[kept].astype(np.float64) + float(eps)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(np.isneginf(x[kept]), 0.0,
+                     np.where(den == 0.0, np.inf, (e / e.sum()) / den))
+    best = int(kept[np.lexsort((kept, -r))[0]])
+    if kept.size < 2:
+        return best, np.inf
+    r1, r2 = np.sort(r)[::-1][:2]
+    if np.isinf(r1):
+        return best, np.inf
+    return best, (r1 - r2) / r1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gap_is_the_relative_ratio_gap(seed):
+    rng = np.random.default_rng(500 + seed)
+    B, V = 24, 700
+    x = (rng.standard_normal((B, V)) * (0.5 + seed)).astype(np.float32)
+    if seed % 2:
+        x = np.round(x * 2) / 2  # many exact value ties
+    q = rng.standard_exponential((B, V)).astype(np.float32)
+    # a few rows with two candidates at an almost equal ratio
+    q[3, :] = 1.0
+    x[3, 10] = x[3].max() + 1.0
+    x[3, 11] = x[3, 10]
+    k = rng.integers(0, 40, size=B).astype(np.int32)
+    p = rng.uniform(0.3, 1.0, size=B).astype(np.float32)
+    eps = 1e-20
+    r = run_f32(x, 7, top_k=k, top_p=p, q=q, eps=eps)
+    for b in range(B):
+        kept = _numpy_kept(x[b], int(k[b]), float(p[b]))
+        assert r["nkept"][b] == kept.size
+        idx, gap = _numpy_race_gap(x[b], q[b], eps, kept)
+        assert r["idx"][b] == idx
+        if np.isinf(gap):
+            assert np.isinf(r["gap"][b])
+        else:
+            assert r["gap"][b] == pytest.approx(gap, rel=1e-9, abs=1e-15), b
+    assert r["gap"][3] == 0.0  # exact tie: exempt on the GPU side
+
+
+def test_gap_with_zero_denominators():
+    """eps = 0 and exact zeros in q: a finite logit's ratio is +inf there,
+    ties among them go to the lowest id and count as decided (gap +inf); a
+    -inf logit never wins whatever its q."""
+    rng = np.random.default_rng(77)
+    B, V = 8, 300
+    x = (rng.standard_normal((B, V)) * 20).astype(np.float32)
+    q = rng.standard_exponential((B, V)).astype(np.float32)
+    q[0, [17, 250]] = 0.0           # two zero-q tokens: the lower id wins
+    q[1, 5] = 0.0                   # one, far down the order
+    x[1, 5] = x[1].min() - 900.0    # its double exponential underflows
+    q[2, 9] = 0.0
+    x[2, 9] = -np.inf               # probability 0: never drawn
+    r = run_f32(x, SAMPLE, q=q, eps=0.0)
+    assert r["idx"][0] == 17 and np.isinf(r["gap"][0])
+    assert r["idx"][1] == 5 and np.isinf(r["gap"][1])
+    assert r["idx"][2] != 9
+    for b in range(B):
+        kept = np.lexsort((np.arange(V), -x[b].astype(np.float64)))
+        idx, gap = _numpy_race_gap(x[b], q[b], 0.0, kept)
+        assert r["idx"][b] == idx
+        if np.isfinite(gap):
+            assert r["gap"][b] == pytest.approx(gap, rel=1e-9)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_inverse_cdf_gap_is_the_distance_to_the_nearest_boundary(seed):
+    rng = np.random.default_rng(600 + seed)
+    B, V = 16, 400
+    x = (rng.standard_normal((B, V)) * 1.5).astype(np.float32)
+    k = rng.integers(0, 60, size=B).astype(np.int32)
+    p = rng.uniform(0.4, 1.0, size=B).astype(np.float32)
+    u = rng.random(B).astype(np.float32)
+    u[0] = 0.0
+    r = run_f32(x, 7, top_k=k, top_p=p, u=u)
+    for b in range(B):
+        kept = _numpy_kept(x[b], int(k[b]), float(p[b]))
+        e = np.exp(x[b, kept].astype(np.float64) - float(x[b, kept[0]]))
+        S = np.cumsum(e / e.sum())
+        uu = float(u[b])
+        if uu <= 0.0:
+            assert r["idx"][b] == kept[0] and np.isinf(r["gap"][b])
+            continue
+        hit = np.nonzero(S >= uu)[0]
+        n = int(hit[0]) + 1 if hit.size else kept.size
+        assert r["idx"][b] == kept[n - 1]
+        below = S[n - 2] if n > 1 else None
+        want = S[n - 1] - uu if below is None else min(S[n - 1] - uu, uu - below)
+        assert r["gap"][b] == pytest.approx(max(want, 0.0), rel=1e-6, abs=1e-12), b
