@@ -76,10 +76,10 @@ def model_bytes(W, kept):
     logits once (V * elem), the dense fp32 output (4V) when requested, q
     where the method reads it (all V for rows that sample without a filter,
     4 |K| gathered for filtered sampling rows), history ids (4 each), the
-    output id (8) and the per-row k, p, flags (9).  The pass streams the
-    logits, q of unfiltered sampling rows and the dense output of unfiltered
-    rows; the merge gathers q at K; the dense writer writes the filtered
-    rows' dense output."""
+    output id (8) and the per-row k, p, flags (9).  The pass reads every
+    row's logits and history ids, q of unfiltered sampling rows, and writes
+    the dense output of unfiltered rows; the merge gathers q at K; the dense
+    writer writes the filtered rows' dense output."""
     B, V = W.B, W.V
     flags = W.row_flags if W.row_flags is not None else np.full(B, 7, np.uint8)
     kmax = min(V, 1024)

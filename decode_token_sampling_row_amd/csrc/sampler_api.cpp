@@ -23,6 +23,7 @@ struct sampler_s {
     int32_t dtype;
     int32_t guess;
     int32_t seg;
+    int32_t cus;  // compute units of the device
     int device;
     KWork ws;
     void *ws_base;
@@ -42,13 +43,16 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-KPlan make_plan(int32_t vocab, int32_t seg) {
+KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
     KPlan l;
+    l.cus = cus;
     const int64_t V = vocab;
     l.seg = seg;
     l.nt = (int32_t)((V + seg - 1) / seg);
     const int64_t tc = ROWCAP / l.nt;
     l.wcap = (int32_t)((tc < TCAP_MAX ? tc : TCAP_MAX) / 4);
+    const int64_t ngr = (V + 2047) / 2048;  // dense group-rows
+    l.ntd = (int32_t)((ngr + DGR_PER_TILE - 1) / DGR_PER_TILE);
     return l;
 }
 
@@ -84,7 +88,6 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
         if (opts->segment_len) seg = opts->segment_len;
         rpl = opts->rows_per_launch;
     }
-    const KPlan plan = make_plan(vocab, seg);
 
     sampler_s *s = new (std::nothrow) sampler_s();
     if (!s) return SAMPLER_ENOMEM;
@@ -94,10 +97,14 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     s->guess = guess;
     s->seg = seg;
     s->rows_per_launch = rpl;
-    if (hipGetDevice(&s->device) != hipSuccess) {
+    if (hipGetDevice(&s->device) != hipSuccess ||
+        hipDeviceGetAttribute(&s->cus, hipDeviceAttributeMultiprocessorCount, s->device) !=
+            hipSuccess) {
         delete s;
         return SAMPLER_EHIP;
     }
+    if (s->cus < 1) s->cus = 1;
+    const KPlan plan = make_plan(vocab, seg, s->cus);
     const size_t B = (size_t)max_batch;
     size_t off = 0;
     const size_t NTL = (size_t)plan.nt * 4;  // wave sub-slots per row
@@ -112,7 +119,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     const size_t o_klist = off;
     off = align_up(off + B * KMAX * sizeof(uint64_t), 256);
     const size_t o_ktoff = off;
-    off = align_up(off + B * ((size_t)plan.nt + 1) * sizeof(uint32_t), 256);
+    off = align_up(off + B * ((size_t)plan.ntd + 1) * sizeof(uint32_t), 256);
     const size_t o_rowthr = off;
     off = align_up(off + B * sizeof(float), 256);
     const size_t o_rowref = off;
@@ -203,7 +210,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.guess = h->guess;
     p.pen = (a->repetition_penalty != 1.0f && a->penalty_ids != nullptr) ? 1 : 0;
 
-    const KPlan l = make_plan(h->vocab, h->seg);
+    const KPlan l = make_plan(h->vocab, h->seg, h->cus);
     const int esize = h->dtype == SAMPLER_BF16 ? 2 : 4;
     const bool al = aligned16(a->logits) && ((a->ld * esize) % 16) == 0 &&
                     (h->vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
@@ -231,7 +238,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     // of at most 1024 threads); each kernel runs over all chunks before the
     // next kernel starts, so the per-kernel profile spans stay contiguous.
     const int64_t max_wg = (int64_t)1 << 23;
-    int64_t lim = std::max<int64_t>(1, max_wg / l.nt);
+    int64_t lim = std::max<int64_t>(1, max_wg / std::max(l.nt, l.ntd));
     if (h->rows_per_launch > 0) lim = std::min<int64_t>(lim, h->rows_per_launch);
     const int chunk = (int)std::min<int64_t>(batch, lim);
     auto each = [&](auto &&launcher) -> bool {

@@ -25,6 +25,8 @@ constexpr int K3_THREADS = 1024;
 constexpr int K3_BINS = 2048;      // value-space histogram bins
 constexpr int K3_COLLECT = 4096;   // bucket members sorted in LDS
 constexpr int K3_SEG = 65536;      // penalty-bitmap segment
+// Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
+constexpr int DGR_PER_TILE = 4;
 
 // Row kinds written by the merge kernel.
 enum RowKind : int32_t {
@@ -53,7 +55,8 @@ struct RowInfo {
     float m;       // row max (transformed)
     float xmin;    // row min finite
     uint32_t idx0; // id of the row maximum (first in order)
-    uint32_t pad;
+    uint32_t done; // 1: the dense filtered logits are complete (KIND_LIST rows
+                   // filled by the pass whose kept values the merge wrote)
 };
 
 struct KParams {
@@ -85,6 +88,8 @@ struct KPlan {
     int32_t seg;   // elements per pass tile (a multiple of 1024)
     int32_t nt;    // tiles per row
     int32_t wcap;  // candidate entries per wave sub-slot (4 nt wcap <= ROWCAP)
+    int32_t ntd;   // dense tiles per row: ceil(ceil(V / 2048) / DGR_PER_TILE)
+    int32_t cus;   // compute units of the device
 };
 
 struct KWork {
@@ -93,7 +98,7 @@ struct KWork {
     ChunkStat *cstat; // [maxB][nt][4] per-wave statistics / winners
     RowInfo *info;    // [maxB]
     uint64_t *klist;  // [maxB][KMAX] kept list of rows with a list, grouped by tile
-    uint32_t *ktoff;  // [maxB][nt + 1] start of each tile's group in klist
+    uint32_t *ktoff;  // [maxB][ntd + 1] start of each dense tile's group in klist
     float *rowthr;    // [maxB] estimated admission value of the row
     float *rowref;    // [maxB] transformed sample maximum (reference for exponentials)
     float *rowlo;     // [maxB] transformed smallest value of the estimate sample

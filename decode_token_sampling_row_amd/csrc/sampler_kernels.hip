@@ -40,9 +40,9 @@
 //               ties by vocab id); then the race or the draw over the kept
 //               set.  This is the page's full-sort fallback reached without a
 //               full sort.
-//   k_dense     grid = B x tiles.  Writes the dense filtered logits (and the
-//               optional probabilities) of filtered rows with full-line
-//               stores, composing each tile in LDS from the kept list.
+//   k_dense     grid = B x tiles, only when probabilities are asked for.
+//               Writes them with full-line stores, composing each tile in
+//               LDS from the kept list.
 //   k_epilogue  one workgroup, when asked for.  The decode-step epilogue of
 //               the MiniMind generation loop (sec. 10.9): finished rows
 //               output EOS, rows that output EOS become finished, the output
@@ -117,6 +117,14 @@ __device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
     md.inv = (rf & 4u) && P.u;
     return md;
 }
+
+// A filtered row whose dense filtered logits the pass fills with -inf while
+// it streams the row, the row merge then writing the kept values: rows with
+// top-p, whose kept sets are the short nuclei in the usual case.  Scattered
+// writes of single values cost a read-modify-write of their line each, so
+// rows with top-k alone (kept sets of up to 1024) get their dense output
+// composed in whole lines by the dense writer instead.
+__device__ __forceinline__ bool dense_filled(const Mode &md) { return md.tp; }
 
 // Penalty, temperature, -0 -> +0 (adding +0 maps -0 to +0 and leaves every
 // other value unchanged).  Division is IEEE correctly rounded.  XF = false
@@ -322,29 +330,95 @@ __device__ __forceinline__ uint32_t wg_min_u32(uint32_t v, uint32_t *sc) {
 }
 
 // Exponential race: is candidate a (logit xa, q+eps qa) ahead of b?
-// e_a / qa > e_b / qb  <=>  exp(xa - xb) * qb > qa.  Equal -> smaller id.
+// e_a / qa > e_b / qb  <=>  (xa - xb) log2(e) > log2(qa) - log2(qb).  Equal
+// ratios -> smaller id.  A zero q + eps gives a finite logit an infinite
+// ratio (positive / 0); -inf logits never enter a race.
 struct Race {
     float x, qe;
     uint32_t idx;
+    float lq;  // log2(qe) when qe is a normal number in [2^-120, 2^120], else NaN
 };
-// The exponentials use the hardware exp2 (relative error ~1e-6 where the
-// two logits are far apart, where the comparison is never close).
+
+constexpr float LOG2E_F = 1.4426950408889634f;
+// The fp32 decision quantity D = (xa - xb) log2 e - (log2 qa - log2 qb) is
+// trusted when |D| exceeds this: with |xa - xb| <= 256 and |log2 q| <= 120
+// its rounding error stays below 2^-10 (hardware log2 is good to a few ulp,
+// the subtraction and the product to half an ulp each).  Closer calls are
+// decided in double.
+constexpr float RACE_BAND = 0.00390625f;  // 2^-8
+constexpr float RACE_DMAX = 256.0f;
+
+__device__ __forceinline__ float race_lq(float qe) {
+    return (qe >= 7.52316385e-37f && qe <= 1.32922800e36f) ? __builtin_amdgcn_logf(qe)
+                                                          : __builtin_nanf("");
+}
+
+// ln 2 as hi + lo, hi with 15 significant bits: k * hi is exact for |k| < 512
+// (every exponent difference of two floats).
+constexpr float LN2_HI = 0x1.62e4p-1f;
+constexpr float LN2_LO = 0x1.7f7d1cp-20f;
+
+// The close call, to about 1e-7 absolute in L = (xa - xb) - ln(qa / qb):
+// zero denominators first (an infinite ratio; two of them tie), then xa - xb
+// exactly as a two-term sum, ln(qa / qb) as the exponent difference times
+// ln 2 (exact products) plus the log of the mantissa ratio, which lies in
+// (0.5, 2) so that its absolute error stays at a few 1e-8.  Equal -> the
+// smaller id.
+__device__ __forceinline__ bool race_ahead_exact(float xa, float qa, uint32_t ia, float xb, float qb,
+                                                 uint32_t ib) {
+    const bool za = qa == 0.0f, zb = qb == 0.0f;
+    if (za || zb) return (za && zb) ? ia < ib : za;
+    const float nb = -xb;
+    const float dh = xa + nb;
+    const float bb = dh - xa;
+    const float dl = (xa - (dh - bb)) + (nb - bb);
+    int ea, eb;
+    const float ma = frexpf(qa, &ea), mb = frexpf(qb, &eb);
+    const float k = (float)(ea - eb);
+    const float A = dh - k * LN2_HI;
+    const float B = dl - k * LN2_LO;
+    const float L = (A - logf(ma / mb)) + B;
+    return L > 0.0f || (L == 0.0f && ia < ib);
+}
+
 __device__ __forceinline__ bool race_ahead(const Race &a, const Race &b) {
     if (a.idx == NONE) return false;
     if (b.idx == NONE) return true;
-    float f = __expf(a.x - b.x) * b.qe;
-    if (f > a.qe) return true;
-    if (f < a.qe) return false;
-    return a.idx < b.idx;
+    const float d = a.x - b.x;
+    const float D = d * LOG2E_F - (race_lq(a.qe) - race_lq(b.qe));
+    if (fabsf(d) <= RACE_DMAX) {
+        if (D > RACE_BAND) return true;
+        if (D < -RACE_BAND) return false;
+    }
+    return race_ahead_exact(a.x, a.qe, a.idx, b.x, b.qe, b.idx);
 }
+
+// Offer element (x, q + eps, id j) to a lane's running winner.  The usual
+// candidate loses by far more than the band and costs a log2, a multiply
+// and two compares.
 __device__ __forceinline__ void race_offer(Race &best, float x, float qe, uint32_t j) {
     if (!(x > -INFINITY)) return;  // probability 0: never drawn
-    if (best.idx == NONE || __expf(x - best.x) * best.qe > qe) {
-        best.x = x;
-        best.qe = qe;
-        best.idx = j;
+    const float lq = race_lq(qe);
+    if (best.idx != NONE) {
+        const float d = x - best.x;
+        const float D = d * LOG2E_F - (lq - best.lq);
+        const bool fast = fabsf(d) <= RACE_DMAX;
+        if (fast && D < -RACE_BAND) return;
+        if (!(fast && D > RACE_BAND) && !race_ahead_exact(x, qe, j, best.x, best.qe, best.idx))
+            return;
     }
+    best.x = x;
+    best.qe = qe;
+    best.idx = j;
+    best.lq = lq;
 }
+// A candidate's race ratio in double, e = exp(x - max) over q + eps: 0 for a
+// -inf logit (never drawn), +inf for a finite logit over a zero denominator.
+__device__ __forceinline__ double race_ratio(float x, double e, double den) {
+    if (!(x > -INFINITY)) return 0.0;
+    return den == 0.0 ? (double)INFINITY : e / den;
+}
+
 template <int NT>
 __device__ __forceinline__ Race wg_race(Race r, float *scx, float *scq, uint32_t *sci) {
 #pragma unroll
@@ -353,6 +427,7 @@ __device__ __forceinline__ Race wg_race(Race r, float *scx, float *scq, uint32_t
         o.x = shxf(r.x, m);
         o.qe = shxf(r.qe, m);
         o.idx = shx(r.idx, m);
+        o.lq = 0.0f;
         if (race_ahead(o, r)) r = o;
     }
     const int w = threadIdx.x >> 6;
@@ -366,12 +441,14 @@ __device__ __forceinline__ Race wg_race(Race r, float *scx, float *scq, uint32_t
     t.x = scx[0];
     t.qe = scq[0];
     t.idx = sci[0];
+    t.lq = 0.0f;
 #pragma unroll
     for (int i = 1; i < NT / 64; ++i) {
         Race o;
         o.x = scx[i];
         o.qe = scq[i];
         o.idx = sci[i];
+        o.lq = 0.0f;
         if (race_ahead(o, t)) t = o;
     }
     __syncthreads();
@@ -1038,6 +1115,7 @@ __device__ __forceinline__ Race wave_race(Race r) {
         o.x = shxf(r.x, m);
         o.qe = shxf(r.qe, m);
         o.idx = shx(r.idx, m);
+        o.lq = 0.0f;
         if (race_ahead(o, r)) r = o;
     }
     return r;
@@ -1214,10 +1292,16 @@ __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, 
             if (g < ng) {
                 const int j = j0 + g * PGROUP;
                 const int nv = FULL ? 4 : nv4(j, c1);
-                if (KIND == 2)
+                if (KIND == 2) {
                     sel_group<DT, XF, FULL, STATS>(ring[d], j, nv, c0, bm, P, rs, ws, wbuf, wcap,
                                                    ref, traw, yt);
-                else
+                    // a top-p row's dense output starts as -inf here; the row
+                    // merge writes its (usually few) kept values over it
+                    if (rowo && (FULL || nv > 0)) {
+                        const float ninf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                        store4<AL>(rowo, j, FULL ? 4 : nv, ninf);
+                    }
+                } else
                     stream_group<DT, AL, XF, FULL, STATS, KIND == 1>(ring[d], qring[d % QD], j, nv,
                                                                      c0, bm, P, rowo, ss);
                 const int gn = g + PASS_D;
@@ -1254,7 +1338,10 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     const bool full = c0 + ng * PGROUP <= c1;        // every group whole
     const void *rowp = row_ptr(P, DT, b);
     const float *rowq = KIND == 1 ? P.q + (int64_t)b * P.V : nullptr;
-    float *rowo = (KIND != 2 && P.out_logits) ? P.out_logits + (int64_t)b * P.V : nullptr;
+    // the pass writes the dense output of unfiltered rows, and the -inf fill
+    // of top-p rows (dense_filled)
+    float *rowo = (P.out_logits && (KIND != 2 || dense_filled(md)))
+                      ? P.out_logits + (int64_t)b * P.V : nullptr;
     const bool do_stats = KIND == 2 ? !md.tk : (P.flags & NEED_PROBS) != 0;
     const int j0 = c0 + tid * 4;
     const int wslot = (b * L.nt + t) * PASS_WAVES + (tid >> 6);
@@ -1263,7 +1350,7 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     const float yt = KIND == 2 ? xform<XF>(traw, 0u, P) : 0.0f;
     StreamState ss;
     ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
-    ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE;
+    ss.rc.x = -INFINITY; ss.rc.qe = 1.0f; ss.rc.idx = NONE; ss.rc.lq = 0.0f;
     ss.bx = -INFINITY;
     ss.bj = j0 < c1 ? (uint32_t)j0 : NONE;  // kept if every value is -inf
     RefSum rs;
@@ -1370,6 +1457,21 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
         pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
 }
 
+// Dense tiles (see k_dense), used by the row merge to group its kept list.
+constexpr int DENSE_THREADS = 256;
+constexpr int DGR_LOG2 = 11;
+constexpr int DGR = 1 << DGR_LOG2;  // elements per group-row: 256 lanes x 8
+constexpr int DTILE = DGR * DGR_PER_TILE;
+static_assert(DGR == DENSE_THREADS * VEC, "a group-row is one group of 8 per lane");
+
+// Dense tile of vocab id j, and j's position inside that tile.
+__device__ __forceinline__ uint32_t dense_tile(uint32_t j, uint32_t ntd) {
+    return (j >> DGR_LOG2) % ntd;
+}
+__device__ __forceinline__ uint32_t dense_pos(uint32_t j, uint32_t ntd) {
+    return (((j >> DGR_LOG2) / ntd) << DGR_LOG2) | (j & (uint32_t)(DGR - 1));
+}
+
 // ================================================================== k_rows
 // Per row, one workgroup of ROWS_THREADS: the exact kk largest of the row's
 // candidates (held in registers, radix select), ordered only as far as top-p
@@ -1395,6 +1497,7 @@ struct RowsShared {
     uint32_t sc[16];
     uint64_t sc64[16];
     double scd[16];
+    float scx[16], scq[16];
     uint32_t sci[16];
     uint32_t cnt;
     double fd[2];
@@ -1628,7 +1731,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.m = -INFINITY;
     info.xmin = INFINITY;
     info.idx0 = NONE;
-    info.pad = 0;
+    info.done = 0;
 
     if (!filtered) {
         // merge the tiles' winners: the race by ratio (lowest id on a tie),
@@ -1641,29 +1744,22 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         info.xmin = XMIN;
         uint32_t idx;
         if (md.sm) {
-            float xr_loc = -INFINITY;
-            for (int t = tid; t < nt; t += NT)
-                if (cst[t].ridx != NONE) xr_loc = fmaxf(xr_loc, cst[t].rx);
-#pragma unroll
-            for (int sft = 32; sft >= 1; sft >>= 1) xr_loc = fmaxf(xr_loc, shxf(xr_loc, sft));
-            if ((tid & 63) == 0) S.scd[tid >> 6] = xr_loc;
-            __syncthreads();
-            float xr = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < NT / 64; ++i) xr = fmaxf(xr, (float)S.scd[i]);
-            __syncthreads();
-            double br = -1.0;
-            uint32_t bi = NONE;
+            // the waves' race winners, compared exactly as inside the waves
+            Race best;
+            best.x = -INFINITY;
+            best.qe = 1.0f;
+            best.idx = NONE;
+            best.lq = 0.0f;
             for (int t = tid; t < nt; t += NT) {
                 const ChunkStat cs = cst[t];
-                if (cs.ridx == NONE) continue;
-                const double r = exp((double)cs.rx - (double)xr) / (double)cs.rqe;
-                if (r > br || (r == br && cs.ridx < bi)) {
-                    br = r;
-                    bi = cs.ridx;
-                }
+                Race o;
+                o.x = cs.rx;
+                o.qe = cs.rqe;
+                o.idx = cs.ridx;
+                o.lq = 0.0f;
+                if (race_ahead(o, best)) best = o;
             }
-            idx = wg_best_ratio<NT>(br, bi, S.scd, S.sci);
+            idx = wg_race<NT>(best, S.scx, S.scq, S.sci).idx;
         } else {
             uint64_t am = 0;
             for (int t = tid; t < nt; t += NT)
@@ -2139,27 +2235,31 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             if (4 * tid + i < nsel) {
                 const uint32_t id = cidx(v4[i]);
                 const double ei = exp((double)cval(v4[i]) - (double)x0);
-                const double den = (double)qv4[i] + (double)P.eps;
-                const double rr = (ei == 0.0) ? 0.0 : ei / den;
+                const double rr = race_ratio(cval(v4[i]), ei, (double)qv4[i] + (double)P.eps);
                 if (rr > rbest || (rr == rbest && id < ibest)) {
                     rbest = rr;
                     ibest = id;
                 }
             }
     }
-    // the kept list goes out grouped by tile (any order within a tile), so
-    // that each dense-writer workgroup reads only its own entries; toff (no
-    // longer needed for the candidates) counts them per tile
-    const int ntile = L.nt;
-    for (int i = tid; i <= ntile; i += NT) toff[i] = 0u;
-    __syncthreads();
+    // for the dense outputs, the kept list goes out grouped by tile (any
+    // order within a tile), so that each dense-writer workgroup reads only
+    // its own entries; toff (no longer needed for the candidates) counts them
+    // per tile
+    const int ntile = L.ntd;
+    // the pass filled this row's dense logits with -inf: the kept values go
+    // straight over the fill
+    const bool scatter = P.out_logits != nullptr && dense_filled(md);
+    const bool group = P.out_probs != nullptr || (P.out_logits != nullptr && !scatter);
+    if (group) {
+        for (int i = tid; i <= ntile; i += NT) toff[i] = 0u;
+        __syncthreads();
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-        const uint32_t p = (uint32_t)(r * NT + tid);
-        if (p < nK) atomicAdd(&toff[cidx(kp[p]) / (uint32_t)L.seg], 1u);
-    }
-    __syncthreads();
-    {
+        for (int r = 0; r < KR; ++r) {
+            const uint32_t p = (uint32_t)(r * NT + tid);
+            if (p < nK) atomicAdd(&toff[dense_tile(cidx(kp[p]), (uint32_t)ntile)], 1u);
+        }
+        __syncthreads();
         const int per = (ntile + NT - 1) / NT;
         uint32_t lc = 0;
         for (int i = 0; i < per; ++i) {
@@ -2189,14 +2289,14 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
             const double ei = exp((double)cval(v) - (double)x0);
             zk += ei;
             if (md.sm && !early_q) {
-                const double den = (double)qv[r] + (double)P.eps;
-                const double rr = (ei == 0.0) ? 0.0 : ei / den;
+                const double rr = race_ratio(cval(v), ei, (double)qv[r] + (double)P.eps);
                 if (rr > rbest || (rr == rbest && id < ibest)) {
                     rbest = rr;
                     ibest = id;
                 }
             }
-            kl[atomicAdd(&toff[id / (uint32_t)L.seg], 1u)] = v;
+            if (group) kl[atomicAdd(&toff[dense_tile(id, (uint32_t)ntile)], 1u)] = v;
+            if (scatter) P.out_logits[(int64_t)b * P.V + id] = cval(v);
         }
     }
     if (md.sm) idx = wg_best_ratio<NT>(rbest, ibest, S.scd, S.sci);
@@ -2204,6 +2304,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.kind = KIND_LIST;
     info.nK = (int32_t)nK;
     info.ZK = zk;
+    info.done = scatter ? 1u : 0u;
     if (tid == 0) {
         P.out_idx[b] = (int64_t)idx;
         W.info[b] = info;
@@ -2681,7 +2782,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     uint32_t idx = info.idx0;
     if (md.sm) {
         Race rc;
-        rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE;
+        rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE; rc.lq = 0.0f;
         const float *rowq = P.q + (int64_t)b * P.V;
         row_pass_q<DT, AL, XF>(P, b, S.bm, rowq, [&](float x, float qj, uint32_t j) {
             if (mkcomp(x, j) >= Tstar) race_offer(rc, x, qj + P.eps, j);
@@ -2704,52 +2805,63 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 
 // ================================================================== k_dense
 
-// Dense outputs of one tile (the pass's tiles) of one row, in whole lines:
-// the filtered logits of rows with top-k / top-p (x at the kept ids, -inf
-// elsewhere; rows without a filter got theirs from the pass) and, when asked
-// for, the probabilities (pi at the kept ids, 0 elsewhere).  Rows with a
-// kept list place the tile's kept values through a bitmap of their positions
-// and their ranks among the set bits, without reading the logits; threshold
-// rows (after the full-row search) and unfiltered rows re-read the tile.
-
-constexpr int DENSE_THREADS = 256;
+// Dense outputs of one dense tile of one row, in whole lines: the filtered
+// logits of rows with top-k / top-p (x at the kept ids, -inf elsewhere; rows
+// without a filter got theirs from the pass) and, when asked for, the
+// probabilities (pi at the kept ids, 0 elsewhere).  A dense tile is
+// DGR_PER_TILE group-rows of DGR elements spaced ntd group-rows apart: group-
+// row g of the row belongs to tile g mod ntd.  Spreading a workgroup's
+// stores over the row in this way writes faster than one contiguous span per
+// workgroup.  Rows with a kept list place the tile's kept values through a
+// bitmap of their tile positions and their ranks among the set bits, without
+// reading the logits; threshold rows (after the full-row search) and
+// unfiltered rows re-read the tile's logits.
 
 struct DenseShared {
-    float lval[KMAX];  // the tile's kept values by rank
+    float lval[KMAX];           // the tile's kept values by rank
+    uint32_t tb[DTILE / 32];    // kept positions (or penalised positions) of the tile
+    uint32_t wpre[DTILE / 32];  // set bits before each word
     uint32_t sc[16];
 };
 
+// What a dense tile needs before its stores: the row's kind and the range of
+// the kept list, requested one tile ahead.
+struct DenseMeta {
+    RowInfo info;
+    uint32_t k0, k1;
+};
+
+__device__ __forceinline__ DenseMeta dense_meta(const KParams &P, const KWork &W, int ntd, int i) {
+    const int b = P.b0 + i / ntd, t = i % ntd;
+    const uint32_t *kto = W.ktoff + (int64_t)b * (ntd + 1);
+    DenseMeta dm;
+    dm.info = W.info[b];
+    dm.k0 = kto[t];
+    dm.k1 = kto[t + 1];
+    return dm;
+}
+
+// One dense tile: tile t of row b, metadata dm.
 template <int DT, bool AL, bool XF>
-__global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
-    __shared__ DenseShared S;
-    // tile bitmap and per-word ranks of listed rows (2 x seg / 32 words), or
-    // the penalty bitmap of threshold rows
-    extern __shared__ uint32_t dyn[];
+__device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &W, int ntd, int b,
+                                                 int t, const DenseMeta &dm, DenseShared &S) {
     constexpr int NT = DENSE_THREADS;
     const int tid = threadIdx.x;
-    const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
-    const int t0 = t * L.seg, t1 = min(t0 + L.seg, P.V);
-    // the tile's range of the kept list, requested with the row's kind (a
-    // row without a list ignores it)
-    const uint32_t *kto = W.ktoff + (int64_t)b * (L.nt + 1);
-    const uint32_t k0r = kto[t], k1r = kto[t + 1];
-    const RowInfo info = W.info[b];
-    float *ol = (P.out_logits && info.kind != KIND_UNFILTERED)
+    const int ngr = (P.V + DGR - 1) / DGR;
+    const RowInfo &info = dm.info;
+    float *ol = (P.out_logits && info.kind != KIND_UNFILTERED && !info.done)
                     ? P.out_logits + (int64_t)b * P.V : nullptr;
     float *op = P.out_probs ? P.out_probs + (int64_t)b * P.V : nullptr;
     if (!ol && !op) return;
     const double m = (double)info.m, ZK = info.ZK;
-    const int ng = (t1 - t0 + PGROUP - 1) / PGROUP;
+    constexpr int NW = DTILE / 32;  // bitmap words
 
     if (info.kind == KIND_LIST) {
-        const int nw = (t1 - t0 + 31) / 32;  // bitmap words
-        uint32_t *tb = dyn;                  // kept positions in the tile
-        uint32_t *wpre = dyn + nw;           // set bits before each word
-        const int k0 = (int)min(k0r, (uint32_t)KMAX);
-        const int k1 = (int)min(max(k1r, (uint32_t)k0), (uint32_t)KMAX);
+        const int k0 = (int)min(dm.k0, (uint32_t)KMAX);
+        const int k1 = (int)min(max(dm.k1, (uint32_t)k0), (uint32_t)KMAX);
         const uint64_t *kl = W.klist + (int64_t)b * KMAX;
-        // the tile's kept entries (the merge grouped them by tile), at most
-        // KMAX / NT per thread
+        // the tile's kept entries (the merge grouped them by dense tile), at
+        // most KMAX / NT per thread
         constexpr int KR = KMAX / NT;
         uint64_t kv[KR];
 #pragma unroll
@@ -2757,98 +2869,131 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
             const int i = k0 + r * NT + tid;
             kv[r] = i < k1 ? kl[i] : 0ull;
         }
-        for (int w = tid; w < nw; w += NT) tb[w] = 0u;
+        for (int w = tid; w < NW; w += NT) S.tb[w] = 0u;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KR; ++r)
             if (k0 + r * NT + tid < k1) {
-                const int rr = (int)cidx(kv[r]) - t0;
-                atomicOr(&tb[rr >> 5], 1u << (rr & 31));
+                const uint32_t rr = dense_pos(cidx(kv[r]), (uint32_t)ntd);
+                atomicOr(&S.tb[rr >> 5], 1u << (rr & 31));
             }
         __syncthreads();
         // ranks: set bits before each word (words split evenly over threads)
-        const int per = (nw + NT - 1) / NT;
+        constexpr int PER = (NW + NT - 1) / NT;
         uint32_t cnt = 0;
-        for (int i = 0; i < per; ++i) {
-            const int w = tid * per + i;
-            if (w < nw) cnt += __popc(tb[w]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int w = tid * PER + i;
+            if (w < NW) cnt += __popc(S.tb[w]);
         }
         uint32_t tot;
         uint32_t run = wg_excl_scan_u32<NT>(cnt, S.sc, tot);
-        for (int i = 0; i < per; ++i) {
-            const int w = tid * per + i;
-            if (w < nw) {
-                wpre[w] = run;
-                run += __popc(tb[w]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int w = tid * PER + i;
+            if (w < NW) {
+                S.wpre[w] = run;
+                run += __popc(S.tb[w]);
             }
         }
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KR; ++r)
             if (k0 + r * NT + tid < k1) {
-                const int rr = (int)cidx(kv[r]) - t0;
-                const uint32_t below = tb[rr >> 5] & ((1u << (rr & 31)) - 1u);
-                S.lval[wpre[rr >> 5] + __popc(below)] = cval(kv[r]);
+                const uint32_t rr = dense_pos(cidx(kv[r]), (uint32_t)ntd);
+                const uint32_t below = S.tb[rr >> 5] & ((1u << (rr & 31)) - 1u);
+                S.lval[S.wpre[rr >> 5] + __popc(below)] = cval(kv[r]);
             }
         __syncthreads();
-        // whole lines: each lane writes 8 consecutive floats (two 16-byte
-        // stores), the pattern that sustains the highest write rate
-        constexpr int DGROUP = NT * VEC;
-        const int ng8 = (t1 - t0 + DGROUP - 1) / DGROUP;
-        for (int g = 0; g < ng8; ++g) {
-            const int r0 = g * DGROUP + tid * VEC;
-            const int j = t0 + r0;
-            const int nv = group_nv(j, t1);
+        // each lane writes 8 consecutive floats (two 16-byte stores) of each
+        // of the tile's group-rows
+#pragma unroll
+        for (int i = 0; i < DGR_PER_TILE; ++i) {
+            const int g = t + i * ntd;
+            if (g >= ngr) break;
+            const int r0 = i * DGR + tid * VEC;
+            const int j = g * DGR + tid * VEC;
+            const int nv = group_nv(j, P.V);
             if (nv == 0) continue;
-            const uint32_t word = tb[r0 >> 5];
+            const uint32_t word = S.tb[r0 >> 5];
             const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
             float xv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = -INFINITY;
+            for (int e = 0; e < 8; ++e) xv[e] = -INFINITY;
             if (bits) {
-                uint32_t k = wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
+                uint32_t k = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if ((bits >> i) & 1u) xv[i] = S.lval[k++];
+                for (int e = 0; e < 8; ++e)
+                    if ((bits >> e) & 1u) xv[e] = S.lval[k++];
             }
             if (ol) store8<AL>(ol, j, nv, xv);
             if (op) {
                 float o[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    o[i] = ((bits >> i) & 1u) ? (float)(exp((double)xv[i] - m) / ZK) : 0.0f;
+                for (int e = 0; e < 8; ++e)
+                    o[e] = ((bits >> e) & 1u) ? (float)(exp((double)xv[e] - m) / ZK) : 0.0f;
                 store8<AL>(op, j, nv, o);
             }
         }
+        // the next tile rewrites the bitmap, ranks and values
+        __syncthreads();
         return;
     }
     if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
     // K = { comp >= T } (T = 0 keeps the whole row): re-read the tile
-    uint32_t *bm = dyn;
-    if (XF && P.pen) build_bitmap<NT>(bm, t0, t1 - t0, P, b);
+    if (XF && P.pen) {
+        // the tile's penalised positions
+        for (int w = tid; w < NW; w += NT) S.tb[w] = 0u;
+        __syncthreads();
+        const int64_t i0 = P.offsets[b];
+        int64_t i1 = P.offsets[b + 1];
+        if (P.plen) {
+            const int64_t n = P.plen[b] < 0 ? 0 : P.plen[b];
+            if (i0 + n < i1) i1 = i0 + n;
+        }
+        for (int64_t h = i0 + tid; h < i1; h += NT) {
+            const int32_t id = P.ids[h];
+            if (id >= 0 && id < P.V && dense_tile((uint32_t)id, (uint32_t)ntd) == (uint32_t)t) {
+                const uint32_t rr = dense_pos((uint32_t)id, (uint32_t)ntd);
+                atomicOr(&S.tb[rr >> 5], 1u << (rr & 31));
+            }
+        }
+        __syncthreads();
+    }
     const void *rowp = row_ptr(P, DT, b);
     const uint64_t T = info.T;
-    for (int g = 0; g < ng; ++g) {
-        const int r0 = g * PGROUP + tid * 4;
-        const int j = t0 + r0;
-        const int nv = nv4(j, t1);
-        if (nv == 0) continue;
-        Raw4<DT> raw;
-        load4<DT, AL>(rowp, j, nv, raw);
-        float x[4];
-        unpack4<DT>(raw, x);
-        const uint32_t bits = pen_bits4<XF>(bm, r0, P);
-        float lo[4], po[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float xi = xform<XF>(x[i], (bits >> i) & 1u, P);
-            const bool in = mkcomp(xi, (uint32_t)(j + i)) >= T;
-            lo[i] = in ? xi : -INFINITY;
-            po[i] = in ? (float)(exp((double)xi - m) / ZK) : 0.0f;
+    for (int i = 0; i < DGR_PER_TILE; ++i) {
+        const int g = t + i * ntd;
+        if (g >= ngr) break;
+        const int r0 = i * DGR + tid * VEC;
+        const int j = g * DGR + tid * VEC;
+        const int nv = group_nv(j, P.V);
+        if (nv == 0) continue;
+        float x[8];
+        load8<DT, AL>(rowp, j, nv, x);
+        const uint32_t bits = (XF && P.pen) ? (S.tb[r0 >> 5] >> (r0 & 31)) & 0xffu : 0u;
+        float lo[8], po[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xi = xform<XF>(x[e], (bits >> e) & 1u, P);
+            const bool in = mkcomp(xi, (uint32_t)(j + e)) >= T;
+            lo[e] = in ? xi : -INFINITY;
+            po[e] = in ? (float)(exp((double)xi - m) / ZK) : 0.0f;
         }
-        if (ol) store4<AL>(ol, j, nv, lo);
-        if (op) store4<AL>(op, j, nv, po);
+        if (ol) store8<AL>(ol, j, nv, lo);
+        if (op) store8<AL>(op, j, nv, po);
     }
+    if (XF && P.pen) __syncthreads();  // the next tile rewrites the bitmap
+}
+
+// One dense tile per workgroup, B x ntd of them.
+template <int DT, bool AL, bool XF>
+__global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWork W) {
+    __shared__ DenseShared S;
+    const int ntd = L.ntd;
+    const int i = (int)blockIdx.x;
+    dense_tile_write<DT, AL, XF>(P, W, ntd, P.b0 + i / ntd, i % ntd, dense_meta(P, W, ntd, i), S);
 }
 
 // ================================================================== k_epilogue
@@ -2946,7 +3091,8 @@ hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dty
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {
-    const size_t sh = (size_t)(l.nt * PASS_WAVES + 1) * 4;  // per-sub-slot candidate offsets
+    // per-sub-slot candidate offsets, then per-dense-tile counts of the kept list
+    const size_t sh = (size_t)(std::max(l.nt * PASS_WAVES, l.ntd) + 1) * 4;
     return launch(k_rows, dim3((unsigned)p.B), dim3(ROWS_THREADS), sh, s, p, l, w);
 }
 
@@ -2962,9 +3108,8 @@ hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int
 hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                         hipStream_t s) {
     const bool xf = any_transform(p);
-    dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(DENSE_THREADS);
-    size_t sh = (size_t)((l.seg + 31) / 32) * 2 * 4;  // tile bitmap + ranks
-    return SMP_PICK(k_dense, grid, block, sh);
+    dim3 grid((unsigned)((int64_t)p.B * l.ntd)), block(DENSE_THREADS);
+    return SMP_PICK(k_dense, grid, block, 0);
 }
 
 #undef SMP_PICK

@@ -84,10 +84,14 @@ def run_oracle(W, need_logits=True, need_probs=False, rows=None, threads=8, u=No
                    u=u, topk_ties=ties)
 
 
-def compare(W, hip, ref, rows=None, label="", inverse=False):
+def compare(W, hip, ref, rows=None, label="", inverse=False, max_exempt=None):
     """Assert the parity rules on `rows` (default all); returns tie counts.
     inverse: the runs sampled by inverse CDF (ref["gap"] is then the u
-    margin)."""
+    margin).  The rows exempted from the id check (near ties and top-p
+    boundary ties, both decided by the oracle alone) may not exceed
+    max_exempt, by default 1 % of the compared rows rounded down (so none on
+    fewer than 100 rows): an exemption count above that would make the id
+    check vacuous."""
     rows = np.arange(W.B) if rows is None else np.asarray(rows)
     flags = W.row_flags if W.row_flags is not None else np.full(W.B, 7, np.uint8)
     sampling = ((flags & 4) != 0) & (inverse or W.q is not None)
@@ -95,6 +99,11 @@ def compare(W, hip, ref, rows=None, label="", inverse=False):
     near = sampling & (ref["gap"] <= (U_TIE if inverse else GAP_TIE))
     n_margin = int(margin_tie[rows].sum())
     n_near = int(near[rows].sum())
+    allowed = int(0.01 * rows.size) if max_exempt is None else int(max_exempt)
+    exempt = int((margin_tie[rows] | near[rows]).sum())
+    assert exempt <= allowed, (
+        f"{label}: {exempt} of {rows.size} rows exempted from the id check "
+        f"({n_near} near ties, {n_margin} top-p boundary ties), more than {allowed}")
     check_idx = rows[~margin_tie[rows] & ~near[rows]]
     bad = check_idx[hip["idx"][check_idx] != ref["idx"][check_idx]]
     assert bad.size == 0, (

@@ -54,17 +54,27 @@ def test_parity_every_row(label, cfg, B, V):
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_parity_full_size_sampled_rows(cfg):
+def test_parity_full_size_every_row(cfg):
+    """Every row of each workload at its full size, in the launch
+    configuration the benchmark times (one call over the whole batch); the
+    oracle and the comparison go in chunks of rows to bound host memory."""
     import torch
 
     W = wl.make(cfg, seed=0)
     print(f"[case] full cfg{cfg} B={W.B} V={W.V}", flush=True)
     hip = run_hip(W, need_logits=W.need_logits)
-    rng = np.random.default_rng(cfg)
-    rows = np.unique(np.concatenate([np.arange(min(W.B, 16)),
-                                     rng.choice(W.B, size=min(W.B, 16), replace=False)]))
-    ref = run_oracle(W, need_logits=W.need_logits, rows=rows)
-    _log(f"full cfg{cfg}", compare(W, hip, ref, rows=rows, label=f"full cfg{cfg}"))
+    chunk = 64
+    tot = {"near_ties": 0, "boundary_ties": 0, "rows": 0}
+    for r0 in range(0, W.B, chunk):
+        rows = np.arange(r0, min(W.B, r0 + chunk))
+        ref = run_oracle(W, need_logits=W.need_logits, rows=rows, threads=16)
+        st = compare(W, hip, ref, rows=rows, label=f"full cfg{cfg} rows {r0}..",
+                     max_exempt=rows.size)  # the bound applies to the whole batch below
+        for k in tot:
+            tot[k] += st[k]
+        del ref
+    _log(f"full cfg{cfg}", tot)
+    assert tot["near_ties"] + tot["boundary_ties"] <= int(0.01 * W.B)
     torch.cuda.empty_cache()
 
 
@@ -80,11 +90,11 @@ def _custom(x, top_k=None, top_p=None, flags=7, q=None, dtype=wl.F32, seed=0, **
                        bc(top_p, np.float32), bc(flags, np.uint8), **kw)
 
 
-def _check(W, label, need_probs=True, **kw):
+def _check(W, label, need_probs=True, max_exempt=None, **kw):
     print(f"[case] {label} B={W.B} V={W.V}", flush=True)
     hip = run_hip(W, need_logits=True, need_probs=need_probs, **kw)
     ref = run_oracle(W, need_logits=True, need_probs=need_probs)
-    _log(label, compare(W, hip, ref, label=label))
+    _log(label, compare(W, hip, ref, label=label, max_exempt=max_exempt))
     return hip, ref
 
 
@@ -139,10 +149,14 @@ def test_exact_ties_everywhere():
     B, V = 16, 30000
     x = np.zeros((B, V), np.float32)
     x[1::2] = np.round(np.random.default_rng(5).standard_normal((B // 2, V)) * 2) / 2
+    flags = _all_combos(B)
+    # an all-zero row whose top-p stage is on has its cutoff exactly at p =
+    # 0.5 (n / V reaches it at n = V / 2): a top-p boundary tie by
+    # construction, exempt from the checks
+    boundary = int(((flags & 2) != 0)[0::2].sum())
     for dt in (wl.F32, wl.BF16):
-        W = _custom(x, top_k=np.array([10, 1024, 1, 0] * 4), top_p=0.5, flags=_all_combos(B),
-                    dtype=dt)
-        _check(W, f"ties {dt}")
+        W = _custom(x, top_k=np.array([10, 1024, 1, 0] * 4), top_p=0.5, flags=flags, dtype=dt)
+        _check(W, f"ties {dt}", max_exempt=boundary)
 
 
 def test_signed_zero_and_neg_inf():
@@ -468,3 +482,46 @@ def test_profile_reports_kernel_times():
     with pytest.raises(SamplerError):
         s.profile()  # the averaged calls are forgotten
     s.close()
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_race_extreme_q_and_zero_eps(dtype):
+    """The exponential race where fp32 arithmetic is weakest: eps = 0 with
+    exact zeros in q (a finite logit over a zero denominator has an infinite
+    ratio; ties among those go to the lowest id), q spread over 28 decades
+    (exp of U[-60, 5]) and logits N(0, 20^2), so that the logit differences
+    the race compares reach 80 and more.  Sample-only rows race in the
+    streaming pass, filtered rows in the row merge, flat top-p rows in the
+    full-row search."""
+    rng = np.random.default_rng(51)
+    B, V = 48, 40000
+    x = (rng.standard_normal((B, V)) * 20.0).astype(np.float32)
+    x[40:] = (rng.standard_normal((8, V)) * 0.05).astype(np.float32)  # flat: full-row search
+    q = np.exp(rng.uniform(-60.0, 5.0, size=(B, V))).astype(np.float32)
+    order = np.argsort(-x, axis=1, kind="stable")
+    flags = np.array([4, 5, 6, 7] * 12, np.uint8)
+    k = np.array([0, 50, 0, 1024] * 12, np.int32)
+    p = np.array([1.0, 1.0, 0.9, 0.95] * 12, np.float32)
+    flags[40:], k[40:], p[40:] = 6, 0, 0.9  # flat rows: top-p alone, the full-row search
+    must_zero = []  # rows whose draw must land on a zero of q
+    for b in range(B):
+        if b >= 40:                     # flat rows, full-row search: two zeros inside K
+            q[b, order[b, [100, 5000]]] = 0.0
+            must_zero.append(b)
+        elif b % 8 == 0:                # sample only: two zeros near the top, lower id wins
+            q[b, order[b, [3, 7]]] = 0.0
+            must_zero.append(b)
+        elif b % 8 == 4:                # sample only: one zero far down the row
+            q[b, order[b, V - 10]] = 0.0
+            must_zero.append(b)
+        elif b % 4 == 1:                # top-k 50: two zeros inside the kept set
+            q[b, order[b, [10, 20]]] = 0.0
+            must_zero.append(b)
+        elif b % 4 == 2:                # zeros anywhere (mostly outside K)
+            q[b, rng.choice(V, size=3, replace=False)] = 0.0
+        else:                           # top-k 1024 + top-p: a zero at the third place
+            q[b, order[b, 2]] = 0.0
+    W = _custom(x, top_k=k, top_p=p, flags=flags, q=q, dtype=dtype, eps=0.0)
+    hip, ref = _check(W, f"race extremes {dtype}")
+    must_zero = np.array(must_zero)
+    assert (q[must_zero, ref["idx"][must_zero]] == 0.0).all()
