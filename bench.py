@@ -125,6 +125,50 @@ def counted_traffic(kernel):
     return None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, cpu_rows):
+    """The CPU oracle (plain C, one full sort per row, double precision) on a
+    bounded sample of the workload's rows: on the host threads this process
+    is given (OMP_NUM_THREADS, else every core) and on one thread.  A
+    reported baseline only."""
+    from oracle import oracle as orc
+
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(nproc, int(os.environ.get("OMP_NUM_THREADS", nproc))))
+
+    def timed(rows, nthreads, budget):
+        passes, spent = 0, 0.0
+        while passes < 8 and (passes == 0 or spent < budget):
+            c0 = time.perf_counter()
+            orc.run(W.logits, orc.BF16 if W.dtype == "bf16" else orc.F32, vocab=W.V,
+                    top_k=W.top_k, top_p=W.top_p, q=W.q, eps=W.eps,
+                    temperature=W.temperature, penalty=W.penalty, ids=W.ids,
+                    offsets=W.offsets, row_flags=W.row_flags, need_logits=W.need_logits,
+                    rows=rows, threads=nthreads)
+            spent += time.perf_counter() - c0
+            passes += 1
+        return passes, spent
+
+    n = min(W.B, cpu_rows)
+    passes, spent = timed(np.arange(n), threads, 10.0)
+    n1 = min(W.B, max(8, n // 8))  # one thread: an eighth of the rows
+    passes1, spent1 = timed(np.arange(n1), 1, 5.0)
+    return {"value": passes * n / spent, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "value_1thread": passes1 * n1 / spent1, "nproc": nproc, "cpu_model": cpu_model(),
+            "sample": f"rows 0..{n - 1} of the same workload (all stage combinations), "
+                      f"{passes} passes, {spent:.2f} s wall on {threads} threads; rows "
+                      f"0..{n1 - 1}, {passes1} passes, {spent1:.2f} s on 1 thread"}
+
+
 def latency(args):
     """Per-call latency of each workload, caches flushed between calls."""
     import torch
@@ -260,26 +304,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-
-        threads = max(1, min(16, os.cpu_count() or 1))
-        n = min(W.B, args.cpu_rows)
-        rows = np.arange(n)
-        # whole passes over the sample until about 10 s of CPU work (at most 8)
-        passes, spent = 0, 0.0
-        while passes < 8 and (passes == 0 or spent < 10.0):
-            c0 = time.perf_counter()
-            orc.run(W.logits, orc.BF16 if W.dtype == wl.BF16 else orc.F32, vocab=W.V,
-                    top_k=W.top_k, top_p=W.top_p, q=W.q, eps=W.eps,
-                    temperature=W.temperature, penalty=W.penalty, ids=W.ids,
-                    offsets=W.offsets, row_flags=W.row_flags, need_logits=W.need_logits,
-                    rows=rows, threads=threads)
-            spent += time.perf_counter() - c0
-            passes += 1
-        cpu = {"value": passes * n / spent, "unit": "rows/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"rows 0..{n - 1} of the same workload (all stage combinations), "
-                         f"{passes} passes, {spent:.2f} s wall on {threads} threads"}
+        cpu = cpu_baseline(W, args.cpu_rows)
 
     out = {
         "metric": METRIC,

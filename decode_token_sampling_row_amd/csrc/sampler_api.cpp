@@ -16,7 +16,8 @@ using namespace smp;
 constexpr int PROF_KERNELS = SAMPLER_PROFILE_SLOTS;
 constexpr int PROF_RING = 64;
 
-struct sampler_s {
+// The settings a call runs with (the handle's).
+struct Config {
     int32_t max_batch;
     int32_t rows_per_launch;  // 0 = automatic
     int32_t vocab;
@@ -24,6 +25,10 @@ struct sampler_s {
     int32_t guess;
     int32_t seg;
     int32_t cus;  // compute units of the device
+};
+
+struct sampler_s {
+    Config cfg;
     int device;
     KWork ws;
     void *ws_base;
@@ -56,27 +61,18 @@ KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
     return l;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *sampler_strerror(int code) {
-    switch (code) {
-        case SAMPLER_OK: return "ok";
-        case SAMPLER_EINVAL: return "invalid argument";
-        case SAMPLER_ENOMEM: return "device workspace allocation failed";
-        case SAMPLER_EHIP: return "HIP runtime error";
-        default: return "unknown error";
-    }
-}
-
-int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtype,
-                   const sampler_opts *opts) {
-    if (h == nullptr) return SAMPLER_EINVAL;
-    *h = nullptr;
+// Options and sizes of a handle.
+int make_config(Config &c, int32_t max_batch, int32_t vocab, int32_t dtype,
+                const sampler_opts *opts) {
     if (max_batch < 1 || vocab < 1 || vocab > SAMPLER_VOCAB_MAX) return SAMPLER_EINVAL;
     if (dtype != SAMPLER_F32 && dtype != SAMPLER_BF16) return SAMPLER_EINVAL;
-    int32_t guess = DEFAULT_GUESS, seg = SEG_DEFAULT, rpl = 0;
+    c.max_batch = max_batch;
+    c.vocab = vocab;
+    c.dtype = dtype;
+    c.guess = DEFAULT_GUESS;
+    c.seg = SEG_DEFAULT;
+    c.rows_per_launch = 0;
+    c.cus = 1;
     if (opts) {
         if (opts->topk_guess < 0 || opts->topk_guess > SAMPLER_TOPK_MAX) return SAMPLER_EINVAL;
         if (opts->segment_len != 0 &&
@@ -84,28 +80,16 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
              opts->segment_len % SEG_MIN != 0))
             return SAMPLER_EINVAL;
         if (opts->rows_per_launch < 0) return SAMPLER_EINVAL;
-        if (opts->topk_guess) guess = opts->topk_guess;
-        if (opts->segment_len) seg = opts->segment_len;
-        rpl = opts->rows_per_launch;
+        if (opts->topk_guess) c.guess = opts->topk_guess;
+        if (opts->segment_len) c.seg = opts->segment_len;
+        c.rows_per_launch = opts->rows_per_launch;
     }
+    return SAMPLER_OK;
+}
 
-    sampler_s *s = new (std::nothrow) sampler_s();
-    if (!s) return SAMPLER_ENOMEM;
-    s->max_batch = max_batch;
-    s->vocab = vocab;
-    s->dtype = dtype;
-    s->guess = guess;
-    s->seg = seg;
-    s->rows_per_launch = rpl;
-    if (hipGetDevice(&s->device) != hipSuccess ||
-        hipDeviceGetAttribute(&s->cus, hipDeviceAttributeMultiprocessorCount, s->device) !=
-            hipSuccess) {
-        delete s;
-        return SAMPLER_EHIP;
-    }
-    if (s->cus < 1) s->cus = 1;
-    const KPlan plan = make_plan(vocab, seg, s->cus);
-    const size_t B = (size_t)max_batch;
+// The workspace of B rows laid out from base (null: only sized).  Returns its
+// size in bytes.
+size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
     size_t off = 0;
     const size_t NTL = (size_t)plan.nt * 4;  // wave sub-slots per row
     const size_t o_cand = off;
@@ -130,39 +114,28 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     off = align_up(off + sizeof(uint32_t), 256);
     const size_t o_fblist = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
-    void *base = nullptr;
-    hipError_t e = hipMalloc(&base, off);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        delete s;
-        return e == hipErrorOutOfMemory ? SAMPLER_ENOMEM : SAMPLER_EHIP;
+    if (base) {
+        w->cand = (uint64_t *)(base + o_cand);
+        w->wcnt = (uint32_t *)(base + o_wcnt);
+        w->cstat = (ChunkStat *)(base + o_cstat);
+        w->info = (RowInfo *)(base + o_info);
+        w->klist = (uint64_t *)(base + o_klist);
+        w->ktoff = (uint32_t *)(base + o_ktoff);
+        w->rowthr = (float *)(base + o_rowthr);
+        w->rowref = (float *)(base + o_rowref);
+        w->rowlo = (float *)(base + o_rowlo);
+        w->fbcnt = (uint32_t *)(base + o_fbcnt);
+        w->fblist = (uint32_t *)(base + o_fblist);
     }
-    char *c = (char *)base;
-    s->ws_base = base;
-    s->ws.cand = (uint64_t *)(c + o_cand);
-    s->ws.wcnt = (uint32_t *)(c + o_wcnt);
-    s->ws.cstat = (ChunkStat *)(c + o_cstat);
-    s->ws.info = (RowInfo *)(c + o_info);
-    s->ws.klist = (uint64_t *)(c + o_klist);
-    s->ws.ktoff = (uint32_t *)(c + o_ktoff);
-    s->ws.rowthr = (float *)(c + o_rowthr);
-    s->ws.rowref = (float *)(c + o_rowref);
-    s->ws.rowlo = (float *)(c + o_rowlo);
-    s->ws.fbcnt = (uint32_t *)(c + o_fbcnt);
-    s->ws.fblist = (uint32_t *)(c + o_fblist);
-    s->events_made = false;
-    s->events_ok = false;
-    s->nprof = 0;
-    *h = s;
-    return SAMPLER_OK;
+    return off;
 }
 
-int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
-    if (h == nullptr || a == nullptr) return SAMPLER_EINVAL;
-    if (batch < 0 || batch > h->max_batch) return SAMPLER_EINVAL;
+int check_args(const Config &c, int32_t batch, const sampler_args *a) {
+    if (a == nullptr) return SAMPLER_EINVAL;
+    if (batch < 0 || batch > c.max_batch) return SAMPLER_EINVAL;
     if (batch == 0) return SAMPLER_OK;
     if (a->logits == nullptr || a->out_idx == nullptr) return SAMPLER_EINVAL;
-    if (a->ld < h->vocab) return SAMPLER_EINVAL;
+    if (a->ld < c.vocab) return SAMPLER_EINVAL;
     if (!(a->temperature > 0.0f) || !isfinite(a->temperature)) return SAMPLER_EINVAL;
     if (!(a->repetition_penalty > 0.0f) || !isfinite(a->repetition_penalty))
         return SAMPLER_EINVAL;
@@ -175,17 +148,26 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
     if ((a->penalty_ids == nullptr) != (a->penalty_offsets == nullptr)) return SAMPLER_EINVAL;
     if (a->penalty_len != nullptr && a->penalty_ids == nullptr) return SAMPLER_EINVAL;
     if ((a->flags & SAMPLER_APPEND_HISTORY) && a->penalty_len == nullptr) return SAMPLER_EINVAL;
-    if (a->finished != nullptr && (a->eos_id < 0 || a->eos_id >= h->vocab)) return SAMPLER_EINVAL;
+    if (a->finished != nullptr && (a->eos_id < 0 || a->eos_id >= c.vocab)) return SAMPLER_EINVAL;
     if (a->row_flags == nullptr && a->q == nullptr && a->u == nullptr) return SAMPLER_EINVAL;
     return SAMPLER_OK;
 }
 
-int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream) {
-    int rc = sampler_check(h, batch, a);
-    if (rc != SAMPLER_OK) return rc;
-    if (batch == 0) return SAMPLER_OK;
-    hipStream_t st = (hipStream_t)stream;
+// Per-kernel HIP events of a profiled call.
+struct Marks {
+    hipEvent_t *ev;  // PROF_KERNELS + 1 events, or null
+    bool *launched;  // PROF_KERNELS flags, or null
+    void mark(int i, hipStream_t st) const {
+        if (ev) (void)hipEventRecord(ev[i], st);
+    }
+    void done(int i) const {
+        if (launched) launched[i] = true;
+    }
+};
 
+// The launch sequence of one call over batch rows with workspace ws.
+int run_call(const Config &c, const KWork &ws, int32_t batch, const sampler_args *a,
+             hipStream_t st, const Marks &mk) {
     KParams p;
     memset(&p, 0, sizeof p);
     p.logits = a->logits;
@@ -206,32 +188,16 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     p.rho = a->repetition_penalty;
     p.flags = a->flags & (SAMPLER_NEED_LOGITS | SAMPLER_NEED_PROBS | SAMPLER_TOPK_TIES);
     p.B = batch;
-    p.V = h->vocab;
-    p.guess = h->guess;
+    p.V = c.vocab;
+    p.guess = c.guess;
     p.pen = (a->repetition_penalty != 1.0f && a->penalty_ids != nullptr) ? 1 : 0;
 
-    const KPlan l = make_plan(h->vocab, h->seg, h->cus);
-    const int esize = h->dtype == SAMPLER_BF16 ? 2 : 4;
+    const KPlan l = make_plan(c.vocab, c.seg, c.cus);
+    const int esize = c.dtype == SAMPLER_BF16 ? 2 : 4;
     const bool al = aligned16(a->logits) && ((a->ld * esize) % 16) == 0 &&
-                    (h->vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
+                    (c.vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
                     (p.out_logits == nullptr || aligned16(p.out_logits)) &&
                     (p.out_probs == nullptr || aligned16(p.out_probs));
-
-    bool prof = (a->flags & SAMPLER_PROFILE) != 0;
-    if (prof && !h->events_made) {
-        h->events_made = true;
-        h->events_ok = true;
-        for (int r = 0; r < PROF_RING; ++r)
-            for (int i = 0; i <= PROF_KERNELS; ++i)
-                if (hipEventCreate(&h->ev[r][i]) != hipSuccess) h->events_ok = false;
-    }
-    prof = prof && h->events_ok;
-    const int slot = h->nprof % PROF_RING;
-    bool *launched = h->launched[slot];
-    for (int i = 0; i < PROF_KERNELS; ++i) launched[i] = false;
-    auto mark = [&](int i) {
-        if (prof) (void)hipEventRecord(h->ev[slot][i], st);
-    };
     const bool filtering = a->top_k != nullptr || a->top_p != nullptr;
 
     // Rows go in chunks small enough for every grid (at most 2^23 workgroups
@@ -239,7 +205,7 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     // next kernel starts, so the per-kernel profile spans stay contiguous.
     const int64_t max_wg = (int64_t)1 << 23;
     int64_t lim = std::max<int64_t>(1, max_wg / std::max(l.nt, l.ntd));
-    if (h->rows_per_launch > 0) lim = std::min<int64_t>(lim, h->rows_per_launch);
+    if (c.rows_per_launch > 0) lim = std::min<int64_t>(lim, c.rows_per_launch);
     const int chunk = (int)std::min<int64_t>(batch, lim);
     auto each = [&](auto &&launcher) -> bool {
         for (int c0 = 0; c0 < batch; c0 += chunk) {
@@ -251,33 +217,32 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         return true;
     };
 
-    mark(0);
+    mk.mark(0, st);
     if (filtering) {
-        if (!each([&](const KParams &pc) { return launch_plan(pc, l, h->ws, h->dtype, al, st); }))
+        if (!each([&](const KParams &pc) { return launch_plan(pc, l, ws, c.dtype, al, st); }))
             return SAMPLER_EHIP;
-        launched[0] = true;
+        mk.done(0);
     }
-    mark(1);
-    if (!each([&](const KParams &pc) { return launch_pass(pc, l, h->ws, h->dtype, al, st); }))
+    mk.mark(1, st);
+    if (!each([&](const KParams &pc) { return launch_pass(pc, l, ws, c.dtype, al, st); }))
         return SAMPLER_EHIP;
-    launched[1] = true;
-    mark(2);
-    if (!each([&](const KParams &pc) { return launch_rows(pc, l, h->ws, st); }))
-        return SAMPLER_EHIP;
-    launched[2] = true;
-    mark(3);
+    mk.done(1);
+    mk.mark(2, st);
+    if (!each([&](const KParams &pc) { return launch_rows(pc, l, ws, st); })) return SAMPLER_EHIP;
+    mk.done(2);
+    mk.mark(3, st);
     if (filtering || a->u != nullptr) {
         // one launch over the queue the merge filled, whatever the chunks
-        if (launch_fallback(p, l, h->ws, h->dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
-        launched[3] = true;
+        if (launch_fallback(p, l, ws, c.dtype, al, st) != hipSuccess) return SAMPLER_EHIP;
+        mk.done(3);
     }
-    mark(4);
+    mk.mark(4, st);
     if (p.out_probs || (p.out_logits && filtering)) {
-        if (!each([&](const KParams &pc) { return launch_dense(pc, l, h->ws, h->dtype, al, st); }))
+        if (!each([&](const KParams &pc) { return launch_dense(pc, l, ws, c.dtype, al, st); }))
             return SAMPLER_EHIP;
-        launched[4] = true;
+        mk.done(4);
     }
-    mark(5);
+    mk.mark(5, st);
     const bool append = (a->flags & SAMPLER_APPEND_HISTORY) != 0;
     if (a->finished || append || a->counts) {
         // after every kernel that reads the history or writes out_idx
@@ -292,9 +257,90 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
         e.B = batch;
         e.append = append ? 1 : 0;
         if (launch_epilogue(e, st) != hipSuccess) return SAMPLER_EHIP;
-        launched[5] = true;
+        mk.done(5);
     }
-    mark(6);
+    mk.mark(6, st);
+    return SAMPLER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sampler_strerror(int code) {
+    switch (code) {
+        case SAMPLER_OK: return "ok";
+        case SAMPLER_EINVAL: return "invalid argument";
+        case SAMPLER_ENOMEM: return "device workspace allocation failed";
+        case SAMPLER_EHIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtype,
+                   const sampler_opts *opts) {
+    if (h == nullptr) return SAMPLER_EINVAL;
+    *h = nullptr;
+    Config cfg;
+    const int rc = make_config(cfg, max_batch, vocab, dtype, opts);
+    if (rc != SAMPLER_OK) return rc;
+
+    sampler_s *s = new (std::nothrow) sampler_s();
+    if (!s) return SAMPLER_ENOMEM;
+    if (hipGetDevice(&s->device) != hipSuccess ||
+        hipDeviceGetAttribute(&cfg.cus, hipDeviceAttributeMultiprocessorCount, s->device) !=
+            hipSuccess) {
+        delete s;
+        return SAMPLER_EHIP;
+    }
+    if (cfg.cus < 1) cfg.cus = 1;
+    s->cfg = cfg;
+    const KPlan plan = make_plan(vocab, cfg.seg, cfg.cus);
+    const size_t bytes = layout_workspace((size_t)max_batch, plan, nullptr, nullptr);
+    void *base = nullptr;
+    hipError_t e = hipMalloc(&base, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete s;
+        return e == hipErrorOutOfMemory ? SAMPLER_ENOMEM : SAMPLER_EHIP;
+    }
+    s->ws_base = base;
+    (void)layout_workspace((size_t)max_batch, plan, (char *)base, &s->ws);
+    s->events_made = false;
+    s->events_ok = false;
+    s->nprof = 0;
+    *h = s;
+    return SAMPLER_OK;
+}
+
+int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a) {
+    if (h == nullptr) return SAMPLER_EINVAL;
+    return check_args(h->cfg, batch, a);
+}
+
+int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream) {
+    int rc = sampler_check(h, batch, a);
+    if (rc != SAMPLER_OK) return rc;
+    if (batch == 0) return SAMPLER_OK;
+    hipStream_t st = (hipStream_t)stream;
+
+    bool prof = (a->flags & SAMPLER_PROFILE) != 0;
+    if (prof && !h->events_made) {
+        h->events_made = true;
+        h->events_ok = true;
+        for (int r = 0; r < PROF_RING; ++r)
+            for (int i = 0; i <= PROF_KERNELS; ++i)
+                if (hipEventCreate(&h->ev[r][i]) != hipSuccess) h->events_ok = false;
+    }
+    prof = prof && h->events_ok;
+    const int slot = h->nprof % PROF_RING;
+    bool *launched = h->launched[slot];
+    for (int i = 0; i < PROF_KERNELS; ++i) launched[i] = false;
+    Marks mk;
+    mk.ev = prof ? h->ev[slot] : nullptr;
+    mk.launched = launched;
+    rc = run_call(h->cfg, h->ws, batch, a, st, mk);
+    if (rc != SAMPLER_OK) return rc;
     if (prof) ++h->nprof;
     return SAMPLER_OK;
 }

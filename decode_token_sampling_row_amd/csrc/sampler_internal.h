@@ -55,8 +55,7 @@ struct RowInfo {
     float m;       // row max (transformed)
     float xmin;    // row min finite
     uint32_t idx0; // id of the row maximum (first in order)
-    uint32_t done; // 1: the dense filtered logits are complete (KIND_LIST rows
-                   // filled by the pass whose kept values the merge wrote)
+    uint32_t pad;
 };
 
 struct KParams {

@@ -55,8 +55,9 @@
 // distinct, so every selection below is exact and deterministic.
 
 #include <math.h>
-#include <algorithm>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "sampler_internal.h"
 
@@ -117,14 +118,6 @@ __device__ __forceinline__ Mode row_mode(const KParams &P, int b) {
     md.inv = (rf & 4u) && P.u;
     return md;
 }
-
-// A filtered row whose dense filtered logits the pass fills with -inf while
-// it streams the row, the row merge then writing the kept values: rows with
-// top-p, whose kept sets are the short nuclei in the usual case.  Scattered
-// writes of single values cost a read-modify-write of their line each, so
-// rows with top-k alone (kept sets of up to 1024) get their dense output
-// composed in whole lines by the dense writer instead.
-__device__ __forceinline__ bool dense_filled(const Mode &md) { return md.tp; }
 
 // Penalty, temperature, -0 -> +0 (adding +0 maps -0 to +0 and leaves every
 // other value unchanged).  Division is IEEE correctly rounded.  XF = false
@@ -537,7 +530,7 @@ __device__ __forceinline__ void wg_min_max_or_and(uint64_t &mn, uint64_t &mx, ui
 // comparison and the need-th largest becomes the exact boundary.  Needs
 // 1 <= kk < number of valid entries.
 template <int NT, int R>
-__device__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t kk,
+__device__ __forceinline__ void wg_radix_select(const uint64_t (&v)[R], uint32_t vmask, uint32_t kk,
                                 uint32_t *hist, uint32_t *sel, uint64_t *sc64, uint64_t *tie,
                                 uint32_t tcap, uint32_t *tcnt, uint64_t &prefix_out,
                                 uint64_t &pmask_out) {
@@ -1140,49 +1133,25 @@ struct RefSum {
 
 // What a wave of a select tile has collected so far.
 struct WaveSel {
-    uint32_t cnt;  // entries in the wave's buffer (uniform over the wave)
-    bool ovf;      // an append did not fit
+    uint32_t cnt;     // entries handed over so far (uniform over the wave)
+    bool ovf;         // the admissions did not fit the sub-slot
+    uint32_t mask;    // this lane's admitted elements of the current chunk:
+                      // bit 4 d + i = element i of its group in ring slot d
+    uint32_t strict;  // this lane's handed-over entries above the estimate
 };
 
-// Append the admitted elements of one group of 4 (c[i]: this lane's element
-// i is admitted; bal[i]: the wave's ballot of it) to the wave's buffer, in
-// ballot order.
-template <bool XF>
-__device__ __forceinline__ void sel_append4(const float (&x)[4], uint32_t bits, const bool (&c)[4],
-                                            const uint64_t (&bal)[4], int j, const KParams &P,
-                                            WaveSel &ws, uint64_t *wbuf, uint32_t wcap) {
-    const uint32_t n0 = (uint32_t)__popcll(bal[0]), n1 = (uint32_t)__popcll(bal[1]);
-    const uint32_t n2 = (uint32_t)__popcll(bal[2]), n3 = (uint32_t)__popcll(bal[3]);
-    const uint32_t tot = n0 + n1 + n2 + n3;
-    if (tot == 0) return;
-    if (ws.ovf || ws.cnt + tot > wcap) {
-        ws.ovf = true;
-        return;
-    }
-    const uint32_t nn[4] = {n0, n1, n2, n3};
-    uint32_t off = ws.cnt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (bal[i] == 0) continue;
-        if (c[i]) {
-            const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
-            wbuf[off + lane_rank(bal[i])] = mkcomp(y, (uint32_t)(j + i));
-        }
-        off += nn[i];
-    }
-    ws.cnt = off;
-}
-
-// One group of 4 (first id j, nv valid) of a select tile: admit
+// One group of 4 (first id j, nv valid, ring slot d) of a select tile: admit
 // non-penalised elements with raw x >= traw and penalised ones (and, for
 // rows that accumulate statistics, all of them) with transformed y >= yt,
 // where yt is the transform of traw; every element left out therefore has
-// y <= yt.
+// y <= yt.  The admitted elements only set bits of the lane's mask; a lane
+// that admits any keeps the raw group in its LDS staging slot, where the
+// chunk's compaction reads it back.
 template <int DT, bool XF, bool FULL, bool STATS>
-__device__ __forceinline__ void sel_group(const Raw4<DT> &raw, int j, int nv, int c0,
+__device__ __forceinline__ void sel_group(const Raw4<DT> &raw, int j, int nv, int c0, int d,
                                           const uint32_t *bm, const KParams &P, RefSum &rs,
-                                          WaveSel &ws, uint64_t *wbuf, uint32_t wcap, float ref,
-                                          float traw, float yt) {
+                                          WaveSel &ws, Raw4<DT> *stage, float ref, float traw,
+                                          float yt) {
     float x[4];
     unpack4<DT>(raw, x);
     const uint32_t bits = (FULL || nv > 0) ? pen_bits4<XF>(bm, j - c0, P) : 0u;
@@ -1206,11 +1175,62 @@ __device__ __forceinline__ void sel_group(const Raw4<DT> &raw, int j, int nv, in
                 if ((bits >> i) & 1u) c[i] = (FULL || i < nv) && xform<XF>(x[i], 1u, P) >= yt;
         }
     }
-    uint64_t bal[4];
+    const uint32_t cb = (uint32_t)c[0] | ((uint32_t)c[1] << 1) | ((uint32_t)c[2] << 2) |
+                        ((uint32_t)c[3] << 3);
+    if (cb) {
+        stage[d * 64 + (threadIdx.x & 63)] = raw;
+        ws.mask |= cb << (4 * d);
+    }
+}
+
+// Hand over a chunk's admitted elements: each lane's place in the wave's
+// sub-slot is the exclusive prefix of the lanes' counts (at most 32, so six
+// ballots of bit planes give it), and each lane then writes its entries,
+// reading their raw values back from its staging slots.  jd is the first id
+// of the lane's group in ring slot 0.
+template <int DT, bool XF>
+__device__ __forceinline__ void sel_compact(WaveSel &ws, const Raw4<DT> *stage, int jd, int c0,
+                                            const uint32_t *bm, const KParams &P, uint64_t *dst,
+                                            uint32_t wcap, float yt) {
+    uint32_t mask = ws.mask;
+    ws.mask = 0;
+    const uint32_t n = (uint32_t)__popc(mask);
+    uint32_t pre = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bal[i] = __ballot(c[i]);
-    if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;
-    sel_append4<XF>(x, bits, c, bal, j, P, ws, wbuf, wcap);
+    for (int bit = 0; bit < 6; ++bit) {
+        const uint64_t bal = __ballot((n >> bit) & 1u);
+        pre += lane_rank(bal) << bit;
+        tot += (uint32_t)__popcll(bal) << bit;
+    }
+    if (tot == 0) return;
+    if (ws.ovf || ws.cnt + tot > wcap) {
+        ws.ovf = true;
+        return;
+    }
+    uint32_t off = ws.cnt + pre;
+    const int lane = threadIdx.x & 63;
+    while (mask) {
+        const uint32_t e = (uint32_t)__ffs(mask) - 1u;
+        mask &= mask - 1u;
+        const uint32_t d = e >> 2, i = e & 3u;
+        float x;
+        if (DT == 1) {
+            const uint16_t *h = reinterpret_cast<const uint16_t *>(stage + d * 64 + lane);
+            x = __uint_as_float((uint32_t)h[i] << 16);
+        } else {
+            x = reinterpret_cast<const float *>(stage + d * 64 + lane)[i];
+        }
+        const int j = jd + (int)d * PGROUP + (int)i;
+        uint32_t pb = 0;
+        if (XF && P.pen) {
+            const int r = j - c0;
+            pb = (bm[r >> 5] >> (r & 31)) & 1u;
+        }
+        const float y = xform<XF>(x, pb, P);
+        dst[off++] = mkcomp(y, (uint32_t)j);
+        ws.strict += y > yt;
+    }
+    ws.cnt += tot;
 }
 
 // One group of 4 of a row without top-k / top-p: transform, dense store,
@@ -1272,8 +1292,8 @@ template <int DT, bool AL, bool XF, int KIND, bool FULL, bool STATS>
 __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, int c0, int c1,
                                           int ng, int j0, const void *rowp, const float *rowq,
                                           float *rowo, Raw4<DT> (&ring)[PASS_D], StreamState &ss,
-                                          RefSum &rs, WaveSel &ws, uint64_t *wbuf, uint32_t wcap,
-                                          float ref, float traw, float yt) {
+                                          RefSum &rs, WaveSel &ws, Raw4<DT> *stage, uint64_t *dst,
+                                          uint32_t wcap, float ref, float traw, float yt) {
     constexpr int QD = KIND == 1 ? PASS_D / 2 : 1;
     Raw4<0> qring[QD];
     if (KIND == 1) {
@@ -1292,16 +1312,10 @@ __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, 
             if (g < ng) {
                 const int j = j0 + g * PGROUP;
                 const int nv = FULL ? 4 : nv4(j, c1);
-                if (KIND == 2) {
-                    sel_group<DT, XF, FULL, STATS>(ring[d], j, nv, c0, bm, P, rs, ws, wbuf, wcap,
+                if (KIND == 2)
+                    sel_group<DT, XF, FULL, STATS>(ring[d], j, nv, c0, d, bm, P, rs, ws, stage,
                                                    ref, traw, yt);
-                    // a top-p row's dense output starts as -inf here; the row
-                    // merge writes its (usually few) kept values over it
-                    if (rowo && (FULL || nv > 0)) {
-                        const float ninf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                        store4<AL>(rowo, j, FULL ? 4 : nv, ninf);
-                    }
-                } else
+                else
                     stream_group<DT, AL, XF, FULL, STATS, KIND == 1>(ring[d], qring[d % QD], j, nv,
                                                                      c0, bm, P, rowo, ss);
                 const int gn = g + PASS_D;
@@ -1317,6 +1331,8 @@ __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, 
                 }
             }
         }
+        // the chunk's admissions go out while the next chunk is on its way
+        if (KIND == 2) sel_compact<DT, XF>(ws, stage, j0 + g0 * PGROUP, c0, bm, P, dst, wcap, yt);
     }
 }
 
@@ -1330,7 +1346,7 @@ template <int DT, bool AL, bool XF, int KIND>
 __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, const KPlan &L,
                                           const KWork &W, const Mode &md, int b, int t,
                                           float traw, float ref, Raw4<DT> (&ring)[PASS_D],
-                                          uint64_t (&wbufs)[PASS_WAVES][WCAP_MAX]) {
+                                          Raw4<DT> *stage) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int c0 = t * L.seg;
     const int c1 = min(c0 + L.seg, P.V);
@@ -1338,15 +1354,15 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     const bool full = c0 + ng * PGROUP <= c1;        // every group whole
     const void *rowp = row_ptr(P, DT, b);
     const float *rowq = KIND == 1 ? P.q + (int64_t)b * P.V : nullptr;
-    // the pass writes the dense output of unfiltered rows, and the -inf fill
-    // of top-p rows (dense_filled)
-    float *rowo = (P.out_logits && (KIND != 2 || dense_filled(md)))
-                      ? P.out_logits + (int64_t)b * P.V : nullptr;
+    // the pass writes the dense output of unfiltered rows; filtered rows get
+    // theirs from the dense writer once their kept sets are known
+    float *rowo = (KIND != 2 && P.out_logits) ? P.out_logits + (int64_t)b * P.V : nullptr;
     const bool do_stats = KIND == 2 ? !md.tk : (P.flags & NEED_PROBS) != 0;
     const int j0 = c0 + tid * 4;
     const int wslot = (b * L.nt + t) * PASS_WAVES + (tid >> 6);
     const uint32_t wcap = (uint32_t)L.wcap;
-    uint64_t *wbuf = wbufs[tid >> 6];
+    Raw4<DT> *wstage = stage ? stage + (tid >> 6) * (PASS_D * 64) : nullptr;
+    uint64_t *dst = W.cand + (int64_t)b * ROWCAP + (int64_t)(t * PASS_WAVES + (tid >> 6)) * wcap;
     const float yt = KIND == 2 ? xform<XF>(traw, 0u, P) : 0.0f;
     StreamState ss;
     ss.st.m = -INFINITY; ss.st.xmin = INFINITY; ss.st.z = 0.0;
@@ -1359,9 +1375,11 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     WaveSel ws;
     ws.cnt = 0;
     ws.ovf = false;
+    ws.mask = 0;
+    ws.strict = 0;
 #define SMP_TILE_LOOP(F, ST)                                                                    \
     tile_loop<DT, AL, XF, KIND, F, ST>(bm, P, c0, c1, ng, j0, rowp, rowq, rowo, ring, ss, rs, ws, \
-                                       wbuf, wcap, ref, traw, yt)
+                                       wstage, dst, wcap, ref, traw, yt)
     if (full) {
         if (do_stats) SMP_TILE_LOOP(true, true);
         else SMP_TILE_LOOP(true, false);
@@ -1382,18 +1400,8 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
                 cs.z = wave_sum_f64((double)rs.z);
             }
         }
-        // hand the entries over, counting those above yt
-        uint32_t strict = 0;
-        if (!ws.ovf) {
-            uint64_t *dst =
-                W.cand + (int64_t)b * ROWCAP + (int64_t)(t * PASS_WAVES + (tid >> 6)) * wcap;
-            for (uint32_t i = lane; i < ws.cnt; i += 64) {
-                const uint64_t v = wbuf[i];
-                dst[i] = v;
-                strict += cval(v) > yt;
-            }
-        }
-        strict = wave_sum_u32(strict);
+        // the entries went out chunk by chunk; count those above yt
+        const uint32_t strict = wave_sum_u32(ws.strict);
         if (lane == 0) {
             W.wcnt[wslot] = ws.ovf ? 0xffffffffu : (ws.cnt | (strict << 16));
             W.cstat[wslot] = cs;
@@ -1426,7 +1434,9 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
 
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
-    __shared__ uint64_t wbufs[PASS_WAVES][WCAP_MAX];  // each wave's candidates
+    // each wave's staging slots: the raw groups in which a lane admitted
+    // something, read back when the chunk is handed over
+    __shared__ Raw4<DT> stage[PASS_WAVES][PASS_D * 64];
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
     const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
     const int c0 = t * L.seg;
@@ -1449,12 +1459,13 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
     const float traw = filtering ? W.rowthr[b] : 0.0f;
     const float ref = filtering ? W.rowref[b] : 0.0f;
     if (XF && P.pen) build_bitmap<PASS_THREADS>(bm, c0, c1 - c0, P, b);
+    Raw4<DT> *st = &stage[0][0];
     if (md.tk || md.tp)
-        pass_tile<DT, AL, XF, 2>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+        pass_tile<DT, AL, XF, 2>(bm, P, L, W, md, b, t, traw, ref, ring, st);
     else if (md.sm)
-        pass_tile<DT, AL, XF, 1>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+        pass_tile<DT, AL, XF, 1>(bm, P, L, W, md, b, t, traw, ref, ring, st);
     else
-        pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, wbufs);
+        pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, st);
 }
 
 // Dense tiles (see k_dense), used by the row merge to group its kept list.
@@ -1603,7 +1614,7 @@ __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double
 // n): (prefix, pmask) such that exactly kk of them satisfy (v & pmask) >=
 // prefix.  Common high bits are skipped, then digits of up to 8 bits.
 template <int NT, class G>
-__device__ void radix_select_any(uint32_t n, uint32_t kk, G &&get, uint32_t *hist, uint32_t *sel,
+__device__ __forceinline__ void radix_select_any(uint32_t n, uint32_t kk, G &&get, uint32_t *hist, uint32_t *sel,
                                  uint64_t *sc64, uint64_t &prefix_out, uint64_t &pmask_out) {
     uint64_t mn = ~0ull, mx = 0ull;
     for (uint32_t i = threadIdx.x; i < n; i += NT) {
@@ -1653,7 +1664,7 @@ __device__ void radix_select_any(uint32_t n, uint32_t kk, G &&get, uint32_t *his
 // u times the total; 0 when u <= 0 or NaN, n - 1 when rounding leaves the
 // total short of the target.  Every thread returns it.
 template <int NT>
-__device__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t n, float x0, float u, double *scd,
+__device__ __forceinline__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t n, float x0, float u, double *scd,
                                     uint32_t *sc) {
     if (!(u > 0.0f) || n <= 1) return 0u;
     double e[4];
@@ -1678,9 +1689,98 @@ __device__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t n, float x0, flo
     return first == NONE ? n - 1 : first;
 }
 
+// The merge of an unfiltered row b (no top-k / top-p): its waves' maxima,
+// minima and sums of exponentials, and their race winners (by ratio, lowest
+// id on a tie) or argmax winners (by value, lowest id), over NT threads.
+// Writes the output id and the row's info; queues an inverse-CDF draw over
+// the whole row for the full-row search.  Scratch: 16 entries each.
+template <int NT>
+__device__ __forceinline__ void merge_unfiltered(const KParams &P, const KPlan &L, const KWork &W, int b,
+                                 const Mode &md, double *scd, uint64_t *sc64, float *scx,
+                                 float *scq, uint32_t *sci) {
+    static_assert(NT / 64 <= 16, "scratch of 16 entries");
+    const int tid = threadIdx.x;
+    const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
+    const ChunkStat *cst = W.cstat + (int64_t)b * nt;
+    float m_loc = -INFINITY, mn_loc = INFINITY;
+    for (int t = tid; t < nt; t += NT) {
+        m_loc = fmaxf(m_loc, cst[t].m);
+        mn_loc = fminf(mn_loc, cst[t].xmin);
+    }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+        m_loc = fmaxf(m_loc, shxf(m_loc, sft));
+        mn_loc = fminf(mn_loc, shxf(mn_loc, sft));
+    }
+    if ((tid & 63) == 0) {
+        scx[tid >> 6] = m_loc;
+        scq[tid >> 6] = mn_loc;
+    }
+    __syncthreads();
+    float M = -INFINITY, XMIN = INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        M = fmaxf(M, scx[i]);
+        XMIN = fminf(XMIN, scq[i]);
+    }
+    __syncthreads();
+    double z_loc = 0.0;
+    for (int t = tid; t < nt; t += NT) {
+        const ChunkStat cs = cst[t];
+        if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
+    }
+    const double Z = wg_sum_f64<NT>(z_loc, scd);
+    RowInfo info;
+    info.kind = KIND_UNFILTERED;
+    info.nK = P.V;
+    info.T = 0;
+    info.ZK = Z;
+    info.m = M;
+    info.xmin = XMIN;
+    info.pad = 0;
+    uint32_t idx;
+    if (md.sm) {
+        // the waves' race winners, compared exactly as inside the waves
+        Race best;
+        best.x = -INFINITY;
+        best.qe = 1.0f;
+        best.idx = NONE;
+        best.lq = 0.0f;
+        for (int t = tid; t < nt; t += NT) {
+            const ChunkStat cs = cst[t];
+            Race o;
+            o.x = cs.rx;
+            o.qe = cs.rqe;
+            o.idx = cs.ridx;
+            o.lq = 0.0f;
+            if (race_ahead(o, best)) best = o;
+        }
+        idx = wg_race<NT>(best, scx, scq, sci).idx;
+    } else {
+        uint64_t am = 0;
+        for (int t = tid; t < nt; t += NT)
+            if (cst[t].ridx != NONE) {
+                const uint64_t v = mkcomp(cst[t].rx, cst[t].ridx);
+                am = v > am ? v : am;
+            }
+        am = wg_max_u64<NT>(am, sc64);
+        idx = am ? cidx(am) : NONE;
+        if (md.inv && am) info.m = cval(am);  // the row maximum, for the search
+    }
+    info.idx0 = idx;
+    if (tid == 0) {
+        P.out_idx[b] = (int64_t)idx;
+        W.info[b] = info;
+        // inverse-CDF draw over the whole row: the full-row search finds it
+        if (md.inv && idx != NONE) W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
+    }
+}
+
 __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork W) {
     __shared__ RowsShared S;
-    extern __shared__ uint32_t toff[];  // per-tile candidate offsets, L.nt + 1
+    // per-tile candidate offsets (L.nt PASS_WAVES + 1), then per-dense-tile
+    // counts of the kept list (L.ntd + 1)
+    extern __shared__ uint32_t toff[];
     constexpr int NT = ROWS_THREADS;
     const int tid = threadIdx.x;
     const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
@@ -1731,53 +1831,10 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.m = -INFINITY;
     info.xmin = INFINITY;
     info.idx0 = NONE;
-    info.done = 0;
+    info.pad = 0;
 
     if (!filtered) {
-        // merge the tiles' winners: the race by ratio (lowest id on a tie),
-        // the argmax by (value, lowest id)
-        float M, XMIN;
-        double Z;
-        merge_stats(M, XMIN, Z);
-        info.ZK = Z;
-        info.m = M;
-        info.xmin = XMIN;
-        uint32_t idx;
-        if (md.sm) {
-            // the waves' race winners, compared exactly as inside the waves
-            Race best;
-            best.x = -INFINITY;
-            best.qe = 1.0f;
-            best.idx = NONE;
-            best.lq = 0.0f;
-            for (int t = tid; t < nt; t += NT) {
-                const ChunkStat cs = cst[t];
-                Race o;
-                o.x = cs.rx;
-                o.qe = cs.rqe;
-                o.idx = cs.ridx;
-                o.lq = 0.0f;
-                if (race_ahead(o, best)) best = o;
-            }
-            idx = wg_race<NT>(best, S.scx, S.scq, S.sci).idx;
-        } else {
-            uint64_t am = 0;
-            for (int t = tid; t < nt; t += NT)
-                if (cst[t].ridx != NONE) {
-                    const uint64_t v = mkcomp(cst[t].rx, cst[t].ridx);
-                    am = v > am ? v : am;
-                }
-            am = wg_max_u64<NT>(am, S.sc64);
-            idx = am ? cidx(am) : NONE;
-            if (md.inv && am) info.m = cval(am);  // the row maximum, for the search
-        }
-        info.idx0 = idx;
-        if (tid == 0) {
-            P.out_idx[b] = (int64_t)idx;
-            W.info[b] = info;
-            // inverse-CDF draw over the whole row: the full-row search finds it
-            if (md.inv && idx != NONE) W.fblist[atomicAdd(W.fbcnt, 1u)] = (uint32_t)b;
-        }
+        merge_unfiltered<NT>(P, L, W, b, md, S.scd, S.sc64, S.scx, S.scq, S.sci);
         return;
     }
 
@@ -2247,10 +2304,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // its own entries; toff (no longer needed for the candidates) counts them
     // per tile
     const int ntile = L.ntd;
-    // the pass filled this row's dense logits with -inf: the kept values go
-    // straight over the fill
-    const bool scatter = P.out_logits != nullptr && dense_filled(md);
-    const bool group = P.out_probs != nullptr || (P.out_logits != nullptr && !scatter);
+    const bool group = P.out_probs != nullptr || P.out_logits != nullptr;
     if (group) {
         for (int i = tid; i <= ntile; i += NT) toff[i] = 0u;
         __syncthreads();
@@ -2296,7 +2350,6 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 }
             }
             if (group) kl[atomicAdd(&toff[dense_tile(id, (uint32_t)ntile)], 1u)] = v;
-            if (scatter) P.out_logits[(int64_t)b * P.V + id] = cval(v);
         }
     }
     if (md.sm) idx = wg_best_ratio<NT>(rbest, ibest, S.scd, S.sci);
@@ -2304,7 +2357,6 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.kind = KIND_LIST;
     info.nK = (int32_t)nK;
     info.ZK = zk;
-    info.done = scatter ? 1u : 0u;
     if (tid == 0) {
         P.out_idx[b] = (int64_t)idx;
         W.info[b] = info;
@@ -2849,7 +2901,7 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
     const int tid = threadIdx.x;
     const int ngr = (P.V + DGR - 1) / DGR;
     const RowInfo &info = dm.info;
-    float *ol = (P.out_logits && info.kind != KIND_UNFILTERED && !info.done)
+    float *ol = (P.out_logits && info.kind != KIND_UNFILTERED)
                     ? P.out_logits + (int64_t)b * P.V : nullptr;
     float *op = P.out_probs ? P.out_probs + (int64_t)b * P.V : nullptr;
     if (!ol && !op) return;

@@ -218,8 +218,69 @@ def sampler_profile(h, n: int = SAMPLER_PROFILE_SLOTS):
     return [float(buf[i]) for i in range(rc)]
 
 
+def check_tensors(vocab: int, dtype: int, max_batch: int, logits, out_idx, *, top_k=None,
+                  top_p=None, q=None, penalty_ids=None, penalty_offsets=None, row_flags=None,
+                  out_logits=None, out_probs=None, u=None, penalty_len=None, finished=None,
+                  counts=None, **_):
+    """Reject, before any device access, tensors whose dtype or shape does not
+    match a handle of `vocab` and storage `dtype` (SAMPLER_F32 / _BF16): the
+    C side sees only pointers, so a wrong element type or a short buffer
+    would otherwise be read or written past its end.  Raises TypeError or
+    ValueError.  (The history ids cannot be checked against the offsets
+    without reading them; the caller keeps offsets[B] <= len(penalty_ids).)"""
+    import torch
+
+    want = torch.bfloat16 if dtype == SAMPLER_BF16 else torch.float32
+    if logits.dtype != want:
+        raise TypeError(f"logits: the handle was created for {want}, got {logits.dtype}")
+    if logits.dim() != 2 or logits.shape[1] != vocab:
+        raise ValueError(f"logits: expected [B, {vocab}], got {list(logits.shape)}")
+    B = logits.shape[0]
+    if B > max_batch:
+        raise ValueError(f"logits: batch {B} exceeds the handle's max_batch {max_batch}")
+
+    def vec(name, t, dt, n):
+        if t is None:
+            return
+        if t.dtype != dt:
+            raise TypeError(f"{name}: expected {dt}, got {t.dtype}")
+        if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous [{n}] tensor, got {list(t.shape)}")
+
+    def mat(name, t):
+        if t is None:
+            return
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name}: expected torch.float32, got {t.dtype}")
+        if list(t.shape) != [B, vocab] or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous [{B}, {vocab}] tensor, "
+                             f"got {list(t.shape)}")
+
+    vec("out_idx", out_idx, torch.int64, B)
+    vec("top_k", top_k, torch.int32, B)
+    vec("top_p", top_p, torch.float32, B)
+    vec("u", u, torch.float32, B)
+    vec("row_flags", row_flags, torch.uint8, B)
+    vec("penalty_len", penalty_len, torch.int32, B)
+    vec("finished", finished, torch.uint8, B)
+    vec("penalty_offsets", penalty_offsets, torch.int64, B + 1)
+    if penalty_ids is not None:
+        if penalty_ids.dtype != torch.int32:
+            raise TypeError(f"penalty_ids: expected torch.int32, got {penalty_ids.dtype}")
+        if penalty_ids.dim() != 1 or not penalty_ids.is_contiguous():
+            raise ValueError("penalty_ids: expected a contiguous 1-D tensor")
+    if counts is not None:
+        if counts.dtype != torch.int32:
+            raise TypeError(f"counts: expected torch.int32, got {counts.dtype}")
+        if counts.numel() < 2 or not counts.is_contiguous():
+            raise ValueError("counts: expected a contiguous tensor of at least 2 elements")
+    mat("q", q)
+    mat("out_logits", out_logits)
+    mat("out_probs", out_probs)
+
+
 class Sampler:
-    """Owns one handle; ``run`` marshals tensors and calls sampler_run."""
+    """Owns one handle; ``run`` checks and marshals tensors and calls sampler_run."""
 
     def __init__(self, max_batch: int, vocab: int, dtype, topk_guess: int = 0,
                  segment_len: int = 0, rows_per_launch: int = 0):
@@ -228,10 +289,12 @@ class Sampler:
         dt = SAMPLER_BF16 if dtype in (torch.bfloat16, SAMPLER_BF16, "bf16") else SAMPLER_F32
         self.vocab = int(vocab)
         self.dtype = dt
+        self.max_batch = int(max_batch)
         self.handle = sampler_create(max_batch, vocab, dt, topk_guess, segment_len,
                                      rows_per_launch)
 
     def run(self, logits, out_idx, stream=None, **kw) -> None:
+        check_tensors(self.vocab, self.dtype, self.max_batch, logits, out_idx, **kw)
         args = make_args(logits, out_idx, **kw)
         sampler_run(self.handle, logits.shape[0], args, stream)
 

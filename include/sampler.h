@@ -116,8 +116,16 @@ typedef struct sampler_args {
     int64_t ld;                /* row stride of logits in elements, >= V   */
     const int32_t *top_k;      /* [B] or NULL (top-k off for every row)    */
     const float *top_p;        /* [B] or NULL (top-p off for every row)    */
-    const float *q;            /* [B, V] fp32 sampling weights, row stride V;
-                                  NULL = sampling off for every row         */
+    const float *q;            /* [B, V] fp32 sampling weights, row stride V
+                                  (the Ascend page's q [batch, voc_size]);
+                                  NULL = no exponential race in this call:
+                                  rows with the sample bit then output their
+                                  first kept token (greedy), unless u is
+                                  given.  The per-row bits live in device
+                                  memory, which the host does not read, so a
+                                  sample bit without q cannot be an error;
+                                  only row_flags == NULL (every row samples)
+                                  with q and u both NULL is rejected.       */
     float eps;                 /* >= 0, added to q                         */
     float temperature;         /* > 0; 1 = stage off                        */
     float repetition_penalty;  /* > 0; 1 = stage off                        */
@@ -165,7 +173,8 @@ typedef struct sampler_args {
 
 /*
  * Create a handle for batches of at most max_batch rows of vocab V logits of
- * the given storage type on the current HIP device.  Allocates the device
+ * the given storage type on the current HIP device (the Ascend page's
+ * parameter list: logits [batch, voc_size] of float32 or bfloat16).  Allocates the device
  * workspace (about 80 KiB per row at the default segment length).  opts
  * may be NULL.
  * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
@@ -176,7 +185,10 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
                    const sampler_opts *opts);
 
 /*
- * Check the arguments of a call without touching the GPU.  Returns SAMPLER_OK
+ * Check the arguments of a call without touching the GPU (the Ascend page's
+ * parameter list and its value ranges: top_k in [1, min(voc_size, 1024)],
+ * top_p, q, eps; MiniMind sec. 10.4 and 10.7: temperature and penalty
+ * above 0).  Returns SAMPLER_OK
  * or SAMPLER_EINVAL: batch outside [0, max_batch], logits / out_idx NULL,
  * ld < V, temperature or penalty not finite and > 0, eps negative or not
  * finite, a requested dense output with a NULL buffer, exactly one of the
@@ -189,7 +201,10 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
 int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a);
 
 /*
- * Run one call on `stream` (a hipStream_t; NULL = the null stream).
+ * Run one call on `stream` (a hipStream_t; NULL = the null stream): steps 1
+ * to 8 above for every row (Ascend npu_top_k_top_p_sample page, calculation
+ * formula: topK, topP and Sample sections; MiniMind ch. 10, sec. 10.4 to
+ * 10.9).
  * Asynchronous: outputs are valid once the stream has completed.  Runs
  * sampler_check first.  The handle's workspace is reused by every call, so
  * calls with one handle must be ordered on one stream (not thread-safe).
@@ -200,7 +215,8 @@ int sampler_check(const sampler_t *h, int32_t batch, const sampler_args *a);
 int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream);
 
 /*
- * Kernel times, in milliseconds, averaged over the sampler_run calls made
+ * (Measurement, no passage of the pages.)  Kernel times, in milliseconds,
+ * averaged over the sampler_run calls made
  * with SAMPLER_PROFILE since the previous sampler_profile call (the last 64
  * of them if there were more), in launch order: [0] per-row planning (the
  * admission estimate of top-k / top-p rows), [1] the streaming pass over the
@@ -216,10 +232,12 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
  */
 int sampler_profile(sampler_t *h, float *ms, int32_t n);
 
-/* Free the workspace and the handle.  NULL is accepted. */
+/* Free the workspace and the handle (the ownership rule above: the handle owns
+ * only its workspace).  NULL is accepted. */
 int sampler_destroy(sampler_t *h);
 
-/* Static description of a return code. */
+/* Static description of a return code (SAMPLER_OK and the SAMPLER_E* codes
+ * above). */
 const char *sampler_strerror(int code);
 
 #ifdef __cplusplus

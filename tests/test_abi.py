@@ -124,3 +124,60 @@ def test_create_without_gpu_reports_hip_error(lib):
         pytest.skip("a GPU is present")
     h = ctypes.c_void_p()
     assert lib.sampler_create(ctypes.byref(h), 4, 100, 0, None) == smp.SAMPLER_EHIP
+
+
+def _good(B=3, V=10, bf16=False):
+    import torch
+
+    return dict(logits=torch.zeros((B, V), dtype=torch.bfloat16 if bf16 else torch.float32),
+                out_idx=torch.zeros(B, dtype=torch.int64),
+                top_k=torch.zeros(B, dtype=torch.int32), top_p=torch.ones(B),
+                q=torch.ones((B, V)), penalty_ids=torch.zeros(6, dtype=torch.int32),
+                penalty_offsets=torch.arange(B + 1, dtype=torch.int64) * 2,
+                row_flags=torch.zeros(B, dtype=torch.uint8), out_logits=torch.zeros((B, V)),
+                out_probs=torch.zeros((B, V)), u=torch.zeros(B),
+                penalty_len=torch.zeros(B, dtype=torch.int32),
+                finished=torch.zeros(B, dtype=torch.uint8),
+                counts=torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_rejects_mismatched_tensors_before_any_device_access():
+    """The binding checks dtypes and shapes against the handle before the C
+    call sees bare pointers (CPU tensors: no device is touched)."""
+    import torch
+
+    V, B = 10, 3
+    kw = _good(B, V)
+    smp.check_tensors(V, smp.SAMPLER_F32, 4, **kw)  # consistent: accepted
+    smp.check_tensors(V, smp.SAMPLER_BF16, 4, **_good(B, V, bf16=True))
+    with pytest.raises(TypeError):  # bf16 logits to an f32 handle: twice the bytes read
+        smp.check_tensors(V, smp.SAMPLER_F32, 4, **_good(B, V, bf16=True))
+    with pytest.raises(TypeError):
+        smp.check_tensors(V, smp.SAMPLER_BF16, 4, **kw)
+    with pytest.raises(ValueError):  # vocab mismatch
+        smp.check_tensors(V + 1, smp.SAMPLER_F32, 4, **kw)
+    with pytest.raises(ValueError):  # batch beyond the handle
+        smp.check_tensors(V, smp.SAMPLER_F32, 2, **kw)
+    bad = [("q", torch.ones((B, V - 1))), ("q", torch.ones((B - 1, V))),
+           ("out_logits", torch.zeros((B, V + 1))), ("out_probs", torch.zeros((B, V)).t()),
+           ("top_k", torch.zeros(B + 1, dtype=torch.int32)), ("top_p", torch.ones(B - 1)),
+           ("u", torch.zeros(B + 2)), ("row_flags", torch.zeros(B - 1, dtype=torch.uint8)),
+           ("penalty_offsets", torch.zeros(B, dtype=torch.int64)),
+           ("penalty_len", torch.zeros(B + 1, dtype=torch.int32)),
+           ("finished", torch.zeros(1, dtype=torch.uint8)),
+           ("counts", torch.zeros(1, dtype=torch.int32)),
+           ("out_idx", torch.zeros(B - 1, dtype=torch.int64))]
+    for name, t in bad:
+        with pytest.raises(ValueError):
+            smp.check_tensors(V, smp.SAMPLER_F32, 4, **dict(kw, **{name: t}))
+    wrong_type = [("q", torch.ones((B, V), dtype=torch.float64)),
+                  ("top_k", torch.zeros(B, dtype=torch.int64)),
+                  ("top_p", torch.ones(B, dtype=torch.float16)),
+                  ("row_flags", torch.zeros(B, dtype=torch.int32)),
+                  ("penalty_ids", torch.zeros(6, dtype=torch.int64)),
+                  ("penalty_offsets", torch.zeros(B + 1, dtype=torch.int32)),
+                  ("out_idx", torch.zeros(B, dtype=torch.int32)),
+                  ("counts", torch.zeros(2, dtype=torch.int64))]
+    for name, t in wrong_type:
+        with pytest.raises(TypeError):
+            smp.check_tensors(V, smp.SAMPLER_F32, 4, **dict(kw, **{name: t}))
