@@ -16,7 +16,8 @@ using namespace smp;
 constexpr int PROF_KERNELS = SAMPLER_PROFILE_SLOTS;
 constexpr int PROF_RING = 64;
 
-// The settings a call runs with (the handle's).
+// The settings a call runs with: the handle's, or those given to
+// sampler_run_static.
 struct Config {
     int32_t max_batch;
     int32_t rows_per_launch;  // 0 = automatic
@@ -61,7 +62,7 @@ KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
     return l;
 }
 
-// Options and sizes of a handle.
+// Options and sizes common to sampler_create and sampler_run_static.
 int make_config(Config &c, int32_t max_batch, int32_t vocab, int32_t dtype,
                 const sampler_opts *opts) {
     if (max_batch < 1 || vocab < 1 || vocab > SAMPLER_VOCAB_MAX) return SAMPLER_EINVAL;
@@ -153,7 +154,7 @@ int check_args(const Config &c, int32_t batch, const sampler_args *a) {
     return SAMPLER_OK;
 }
 
-// Per-kernel HIP events of a profiled call.
+// Per-kernel HIP events of a profiled call (none for sampler_run_static).
 struct Marks {
     hipEvent_t *ev;  // PROF_KERNELS + 1 events, or null
     bool *launched;  // PROF_KERNELS flags, or null
@@ -343,6 +344,35 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
     if (rc != SAMPLER_OK) return rc;
     if (prof) ++h->nprof;
     return SAMPLER_OK;
+}
+
+int sampler_run_static(int32_t batch, int32_t vocab, int32_t dtype, const sampler_opts *opts,
+                       const sampler_args *a, void *stream) {
+    Config cfg;
+    int rc = make_config(cfg, batch < 1 ? 1 : batch, vocab, dtype, opts);
+    if (rc != SAMPLER_OK) return rc;
+    if (batch < 0) return SAMPLER_EINVAL;
+    rc = check_args(cfg, batch, a);
+    if (rc != SAMPLER_OK) return rc;
+    if (a->flags & SAMPLER_PROFILE) return SAMPLER_EINVAL;  // no events: nothing is created
+    if (batch == 0) return SAMPLER_OK;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cfg.cus, hipDeviceAttributeMultiprocessorCount, device) !=
+            hipSuccess)
+        return SAMPLER_EHIP;
+    if (cfg.cus < 1) cfg.cus = 1;
+    const KPlan plan = make_plan(vocab, cfg.seg, cfg.cus);
+    const size_t bytes = layout_workspace((size_t)batch, plan, nullptr, nullptr);
+    if (bytes > (size_t)SAMPLER_STATIC_SCRATCH_BYTES) return SAMPLER_EINVAL;
+    void *base = nullptr;
+    if (static_scratch(device, &base) != hipSuccess) return SAMPLER_EHIP;
+    KWork ws;
+    (void)layout_workspace((size_t)batch, plan, (char *)base, &ws);
+    Marks mk;
+    mk.ev = nullptr;
+    mk.launched = nullptr;
+    return run_call(cfg, ws, batch, a, (hipStream_t)stream, mk);
 }
 
 int sampler_profile(sampler_t *h, float *ms, int32_t n) {

@@ -131,4 +131,9 @@ hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dt
                         bool aligned, hipStream_t s);
 hipError_t launch_epilogue(const EpiParams &e, hipStream_t s);
 
+// The device address of the library's static workspace on `device` (the
+// current device), SAMPLER_STATIC_SCRATCH_BYTES bytes; looked up once per
+// device.
+hipError_t static_scratch(int device, void **ptr);
+
 }  // namespace smp

@@ -58,6 +58,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
+
+#include "sampler.h"
 
 #include "sampler_internal.h"
 
@@ -3165,6 +3168,33 @@ hipError_t launch_dense(const KParams &p, const KPlan &l, const KWork &w, int dt
 }
 
 #undef SMP_PICK
+
+// The workspace of sampler_run_static: one array per device, in the code
+// object's device memory, held until the process ends.  Host code must not
+// pass `scratch` itself to a kernel (in host code the name is a stand-in, not
+// a device address); static_scratch looks the device address up once per
+// device and every use goes through that address.
+static __device__ __align__(256) unsigned char scratch[SAMPLER_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+void *scratch_addr[SCRATCH_DEVICES];
+std::mutex scratch_mu;
+}  // namespace
+
+hipError_t static_scratch(int device, void **ptr) {
+    if (device < 0 || device >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_addr[device] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_addr[device] = p;
+    }
+    *ptr = scratch_addr[device];
+    return hipSuccess;
+}
 
 hipError_t launch_epilogue(const EpiParams &e, hipStream_t s) {
     hipLaunchKernelGGL(k_epilogue, dim3(1), dim3(EPI_THREADS), 0, s, e);

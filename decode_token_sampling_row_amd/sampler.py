@@ -24,7 +24,8 @@ SAMPLER_TOPK_MAX = 1024
 SAMPLER_VOCAB_MAX = 1 << 21
 
 EXPORTS = ("sampler_create", "sampler_check", "sampler_run", "sampler_profile",
-           "sampler_destroy", "sampler_strerror")
+           "sampler_destroy", "sampler_strerror", "sampler_run_static")
+SAMPLER_STATIC_SCRATCH_BYTES = 32 << 20
 SAMPLER_PROFILE_SLOTS = 6
 
 
@@ -94,6 +95,10 @@ def load_library(path: str = LIB_PATH):
     lib.sampler_destroy.restype = ctypes.c_int
     lib.sampler_strerror.argtypes = [ctypes.c_int]
     lib.sampler_strerror.restype = ctypes.c_char_p
+    lib.sampler_run_static.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(sampler_opts),
+                                       ctypes.POINTER(sampler_args), P]
+    lib.sampler_run_static.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -207,6 +212,36 @@ def sampler_run(h, batch: int, args: sampler_args, stream: Optional[int] = None)
     rc = load_library().sampler_run(h, int(batch), ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != SAMPLER_OK:
         raise SamplerError(rc, "sampler_run")
+
+
+def sampler_run_static(batch: int, vocab: int, dtype: int, args: sampler_args,
+                       stream: Optional[int] = None, topk_guess: int = 0, segment_len: int = 0,
+                       rows_per_launch: int = 0) -> int:
+    """sampler_run_static: the call without a handle, on the library's static
+    per-GPU workspace (nothing is allocated).  Returns the C return code."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    opts = sampler_opts(int(topk_guess), int(segment_len), int(rows_per_launch))
+    return load_library().sampler_run_static(int(batch), int(vocab), int(dtype),
+                                             ctypes.byref(opts), ctypes.byref(args),
+                                             ctypes.c_void_p(stream))
+
+
+def run_static(logits, out_idx, stream=None, topk_guess=0, segment_len=0, rows_per_launch=0,
+               **kw) -> None:
+    """Check and marshal torch tensors, then sampler_run_static (raises on a
+    nonzero return code)."""
+    import torch
+
+    dt = SAMPLER_BF16 if logits.dtype == torch.bfloat16 else SAMPLER_F32
+    check_tensors(logits.shape[1], dt, logits.shape[0], logits, out_idx, **kw)
+    args = make_args(logits, out_idx, **kw)
+    rc = sampler_run_static(logits.shape[0], logits.shape[1], dt, args, stream, topk_guess,
+                            segment_len, rows_per_launch)
+    if rc != SAMPLER_OK:
+        raise SamplerError(rc, "sampler_run_static")
 
 
 def sampler_profile(h, n: int = SAMPLER_PROFILE_SLOTS):

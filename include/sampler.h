@@ -232,6 +232,31 @@ int sampler_run(sampler_t *h, int32_t batch, const sampler_args *a, void *stream
  */
 int sampler_profile(sampler_t *h, float *ms, int32_t n);
 
+/* Size of the library's static device workspace (per GPU), used by
+ * sampler_run_static instead of a handle's allocation. */
+#define SAMPLER_STATIC_SCRATCH_BYTES (32 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as sampler_run, on batch rows of vocab V logits of the given storage
+ * type with the given options (NULL = defaults), without a handle.  Nothing
+ * is allocated: the workspace is a static device array of
+ * SAMPLER_STATIC_SCRATCH_BYTES bytes per GPU, found once per device by its
+ * symbol and held until the process ends.  The workspace of a call grows
+ * with batch and with the number of tiles per row (about 78 KiB per row at
+ * vocab 262144 and the default tile length: some 420 rows); a call that
+ * does not fit returns SAMPLER_EINVAL, as do SAMPLER_PROFILE (no events are
+ * made) and every argument sampler_run rejects.  Every call on one GPU
+ * shares that GPU's workspace: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; calls ordered on one
+ * stream do not.  Nothing in the workspace has to start at zero (each call
+ * writes what it reads).  Returns SAMPLER_OK, SAMPLER_EINVAL or
+ * SAMPLER_EHIP.
+ */
+int sampler_run_static(int32_t batch, int32_t vocab, int32_t dtype, const sampler_opts *opts,
+                       const sampler_args *a, void *stream);
+
 /* Free the workspace and the handle (the ownership rule above: the handle owns
  * only its workspace).  NULL is accepted. */
 int sampler_destroy(sampler_t *h);
