@@ -49,19 +49,6 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
-    KPlan l;
-    l.cus = cus;
-    const int64_t V = vocab;
-    l.seg = seg;
-    l.nt = (int32_t)((V + seg - 1) / seg);
-    const int64_t tc = ROWCAP / l.nt;
-    l.wcap = (int32_t)((tc < TCAP_MAX ? tc : TCAP_MAX) / 4);
-    const int64_t ngr = (V + 2047) / 2048;  // dense group-rows
-    l.ntd = (int32_t)((ngr + DGR_PER_TILE - 1) / DGR_PER_TILE);
-    return l;
-}
-
 // Options and sizes common to sampler_create and sampler_run_static.
 int make_config(Config &c, int32_t max_batch, int32_t vocab, int32_t dtype,
                 const sampler_opts *opts) {

@@ -91,6 +91,49 @@ struct KPlan {
     int32_t cus;   // compute units of the device
 };
 
+// Index arithmetic shared by the host code, the kernels and the CPU checks of
+// its bounds (constexpr functions are callable on both sides).
+
+// The tiling of a row of V elements at tile length seg.
+constexpr KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
+    KPlan l{};
+    l.cus = cus;
+    l.seg = seg;
+    l.nt = (int32_t)(((int64_t)vocab + seg - 1) / seg);
+    const int64_t tc = ROWCAP / l.nt;
+    l.wcap = (int32_t)((tc < TCAP_MAX ? tc : TCAP_MAX) / 4);
+    const int64_t ngr = ((int64_t)vocab + 2047) / 2048;  // dense group-rows
+    l.ntd = (int32_t)((ngr + DGR_PER_TILE - 1) / DGR_PER_TILE);
+    return l;
+}
+
+// Dense writer tiles: group-row g (DGR elements) of a row belongs to tile
+// g mod ntd, at position (g / ntd) DGR inside it.
+constexpr int DGR_LOG2 = 11;
+constexpr int DGR = 1 << DGR_LOG2;
+constexpr int DTILE = DGR * DGR_PER_TILE;
+constexpr uint32_t dense_tile(uint32_t j, uint32_t ntd) { return (j >> DGR_LOG2) % ntd; }
+constexpr uint32_t dense_pos(uint32_t j, uint32_t ntd) {
+    return (((j >> DGR_LOG2) / ntd) << DGR_LOG2) | (j & (uint32_t)(DGR - 1));
+}
+
+// First element of sample run s (of EST_SEGS) of row b of a row of V >
+// EST_N elements: inside the s-th of EST_SEGS equal segments, at one of 16
+// offsets that depend on s and b, a multiple of VEC.
+constexpr int est_run_start(int s, int b, int V) {
+    const int64_t seg0 = ((int64_t)s * V / EST_SEGS) & ~(int64_t)(VEC - 1);
+    const int64_t seg1 = ((int64_t)(s + 1) * V / EST_SEGS) & ~(int64_t)(VEC - 1);
+    const int64_t room = seg1 - seg0 - EST_SEG;  // >= 0 when V > EST_N
+    const int64_t step = (room / 16) & ~(int64_t)(VEC - 1);
+    return (int)(seg0 + (int64_t)((s * 5 + b * 3) & 15) * step);
+}
+
+// Dynamic LDS words of the row merge: per-sub-slot candidate offsets, then
+// per-dense-tile counts of the kept list.
+constexpr int rows_lds_words(const KPlan &l) {
+    return (l.nt * 4 > l.ntd ? l.nt * 4 : l.ntd) + 1;
+}
+
 struct KWork {
     uint64_t *cand;   // [maxB][ROWCAP]; sub-slot s (tile t, wave w: 4t + w) at s * wcap
     uint32_t *wcnt;   // [maxB][nt][4] entries | strict count << 16 (all ones: overflow)

@@ -829,18 +829,9 @@ struct StreamShared {
 // Only the speed depends on t: the row merge checks that what the pass
 // admitted holds the row's kk largest and sends the row to the full-row
 // search when it does not.
-// First element of sample run s of row b (V > EST_N): inside the s-th of
-// EST_SEGS equal segments, at one of 16 offsets that depend on s and b, a
-// multiple of 8.  Staggered so that the runs of all rows do not start at
-// the same offsets modulo a large power of two, where they would all fall
-// on the same few memory channels.
-__device__ __forceinline__ int est_run_start(int s, int b, int V) {
-    const int64_t seg0 = ((int64_t)s * V / EST_SEGS) & ~(int64_t)(VEC - 1);
-    const int64_t seg1 = ((int64_t)(s + 1) * V / EST_SEGS) & ~(int64_t)(VEC - 1);
-    const int64_t room = seg1 - seg0 - EST_SEG;  // >= 0 when V > EST_N
-    const int64_t step = (room / 16) & ~(int64_t)(VEC - 1);
-    return (int)(seg0 + (int64_t)((s * 5 + b * 3) & 15) * step);
-}
+// The sample runs (est_run_start) are staggered so that the runs of all
+// rows do not start at the same offsets modulo a large power of two, where
+// they would all fall on the same few memory channels.
 
 template <int DT, bool AL>
 __device__ __forceinline__ float row_estimate(const KParams &P, int b, StreamShared &S,
@@ -1471,20 +1462,10 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
         pass_tile<DT, AL, XF, 0>(bm, P, L, W, md, b, t, traw, ref, ring, st);
 }
 
-// Dense tiles (see k_dense), used by the row merge to group its kept list.
+// Dense tiles (see k_dense and dense_tile), used by the row merge to group
+// its kept list.
 constexpr int DENSE_THREADS = 256;
-constexpr int DGR_LOG2 = 11;
-constexpr int DGR = 1 << DGR_LOG2;  // elements per group-row: 256 lanes x 8
-constexpr int DTILE = DGR * DGR_PER_TILE;
 static_assert(DGR == DENSE_THREADS * VEC, "a group-row is one group of 8 per lane");
-
-// Dense tile of vocab id j, and j's position inside that tile.
-__device__ __forceinline__ uint32_t dense_tile(uint32_t j, uint32_t ntd) {
-    return (j >> DGR_LOG2) % ntd;
-}
-__device__ __forceinline__ uint32_t dense_pos(uint32_t j, uint32_t ntd) {
-    return (((j >> DGR_LOG2) / ntd) << DGR_LOG2) | (j & (uint32_t)(DGR - 1));
-}
 
 // ================================================================== k_rows
 // Per row, one workgroup of ROWS_THREADS: the exact kk largest of the row's
@@ -3142,12 +3123,19 @@ hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dty
     const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(PASS_THREADS);
     size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
+    static_assert(sizeof(Raw4<0>) * PASS_WAVES * PASS_D * 64 + (SEG_MAX / 32) * 4 <= 65536,
+                  "pass LDS: staging and the penalty bitmap of the longest tile");
     return SMP_PICK(k_pass, grid, block, sh);
 }
 
 hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStream_t s) {
     // per-sub-slot candidate offsets, then per-dense-tile counts of the kept list
-    const size_t sh = (size_t)(std::max(l.nt * PASS_WAVES, l.ntd) + 1) * 4;
+    static_assert(PASS_WAVES == 4, "rows_lds_words counts four sub-slots per tile");
+    // the largest dynamic part is that of the longest row at the shortest tile
+    static_assert(sizeof(RowsShared) + 4 * rows_lds_words(make_plan(SAMPLER_VOCAB_MAX, SEG_MIN, 1)) <=
+                      65536,
+                  "row merge LDS");
+    const size_t sh = (size_t)rows_lds_words(l) * 4;
     return launch(k_rows, dim3((unsigned)p.B), dim3(ROWS_THREADS), sh, s, p, l, w);
 }
 
