@@ -2355,6 +2355,7 @@ struct FallbackShared {
     uint32_t hlo[K3_BINS];
     uint32_t hhi[K3_BINS];
     uint64_t coll[K3_COLLECT];
+    uint64_t rk[K3_BINS];  // first level: the best race key of each bin (race_key)
     uint32_t bm[K3_SEG / 32];
     // refinement levels: level 0 bins by value, later levels by key
     float lv_lo, lv_scale;
@@ -2390,6 +2391,23 @@ __device__ __forceinline__ uint32_t bin_shift(uint64_t span) {
     constexpr int BB = 11;  // log2(K3_BINS)
     static_assert((1 << BB) == K3_BINS, "K3_BINS is a power of two");
     return bits > BB ? (uint32_t)(bits - BB) : 0u;
+}
+
+// A race candidate as one 64-bit key that atomicMax can keep per bin: the
+// ratio e / den in double (0 for a -inf logit, +inf over a zero
+// denominator; a non-negative double orders like its bit pattern) cut to its
+// top 43 bits (relative steps of 2^-31), then ~id in the low 21 bits, so
+// that of two ratios that agree to that precision the smaller id wins.  Ids
+// are below SAMPLER_VOCAB_MAX = 2^21.
+constexpr int RK_ID_BITS = 21;
+static_assert((1 << RK_ID_BITS) >= SAMPLER_VOCAB_MAX, "ids fit the key's low bits");
+__device__ __forceinline__ uint64_t race_key(float x, double e, double den, uint32_t j) {
+    const double r = race_ratio(x, e, den);
+    const uint64_t hi = (uint64_t)__double_as_longlong(r) >> RK_ID_BITS;
+    return (hi << RK_ID_BITS) | (uint64_t)(~j & ((1u << RK_ID_BITS) - 1u));
+}
+__device__ __forceinline__ uint32_t race_key_id(uint64_t k) {
+    return ~(uint32_t)k & ((1u << RK_ID_BITS) - 1u);
 }
 
 // Boundary bucket of a mass histogram: walking the bins from the top, the
@@ -2563,7 +2581,17 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     // weight (found on the first pass) when frac, else tval itself -- and
     // ZKo, the weight through T*.  The weight of an element is exp(x - m), or
     // 1 when count (then -inf values count too).
-    auto search = [&](double tval, bool frac, bool count, uint64_t &Tst, double &ZKo) {
+    // With rk_on (the cut of a sampling row) the first level also keeps each
+    // bin's best race key, and when the search ends at that level (its
+    // boundary bucket collected) rk_top is the best key of the bins above the
+    // boundary and rk_fi the last kept position of the sorted bucket: the race
+    // over K then needs no pass of its own.
+    bool rk_done = false;
+    uint64_t rk_top = 0;
+    uint32_t rk_fi = 0;
+    const float *rowq = md.sm ? P.q + (int64_t)b * P.V : nullptr;
+    auto search = [&](double tval, bool frac, bool count, bool rk_on, uint64_t &Tst,
+                      double &ZKo) {
         double above = 0.0, target = 0.0;
         int nlev = 0;
         int path = 0;  // 1 collect, 2 ties
@@ -2587,15 +2615,17 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 klo = S.lv_klo[level];
                 sh = S.lv_sh[level];
             }
+            const bool rkl = rk_on && level == 0;
             for (int i = tid; i < K3_BINS; i += K3_THREADS) {
                 S.hm[i] = 0.0;
                 S.hc[i] = 0u;
                 S.hlo[i] = NONE;
                 S.hhi[i] = 0u;
+                if (rkl) S.rk[i] = 0ull;
             }
             __syncthreads();
             double zt = 0.0;
-            row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
+            auto visit = [&](float x, uint32_t j, float qj) {
                 if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
@@ -2608,7 +2638,14 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                     atomicMin(&S.hlo[bi], k);
                     atomicMax(&S.hhi[bi], k);
                 }
-            });
+                if (rkl) atomicMax(&S.rk[bi], race_key(x, e, (double)qj + (double)P.eps, j));
+            };
+            if (rkl)
+                row_pass_q<DT, AL, XF>(P, b, S.bm, rowq, [&](float x, float qj, uint32_t j) {
+                    visit(x, j, qj);
+                });
+            else
+                row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) { visit(x, j, 0.0f); });
             if (level == 0) {
                 double Z = wg_sum_f64<K3_THREADS>(zt, S.scd);
                 target = frac ? tval * Z : tval;
@@ -2616,6 +2653,13 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
             const uint32_t fb = S.found[0];
             const double bbefore = S.fd[0];
+            if (rkl) {
+                // the best key of the bins above the boundary (all of them in K)
+                uint64_t t = 0;
+                for (int i = tid; i < K3_BINS; i += K3_THREADS)
+                    if ((uint32_t)i > fb && S.rk[i] > t) t = S.rk[i];
+                rk_top = wg_max_u64<K3_THREADS>(t, S.sc64);
+            }
             __syncthreads();
             above += bbefore;
             bsel = fb;
@@ -2659,6 +2703,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
         (void)bsel;
         if (path == 0) path = 1;  // unreachable: a key range of 1 is reached by level 4
+        const bool rk_level0 = rk_on && nlev == 1 && path == 1;
         if (path == 1) {
             if (tid == 0) S.counter = 0;
             __syncthreads();
@@ -2696,6 +2741,10 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             uint32_t fi = wg_min_u32<K3_THREADS>(first, S.sc);
             if (fi == NONE) fi = (uint32_t)(n > 0 ? n - 1 : 0);  // rounding: whole bucket
             Tst = (n > 0) ? S.coll[fi] : mkcomp(info.m, info.idx0);
+            if (rk_level0 && n > 0) {
+                rk_done = true;
+                rk_fi = fi;
+            }
             // ZK: mass of every kept element = above + bucket prefix through fi
             double s = 0.0;
 #pragma unroll
@@ -2798,7 +2847,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
         uint64_t Tj;
         double Zj;
-        search(tval, frac, count, Tj, Zj);
+        search(tval, frac, count, job == 1 && md.sm && !whole, Tj, Zj);
         if (job == 0) {
             cfloor = (P.flags & TOPK_TIES) ? (Tj >> 32) << 32 : Tj;
         } else if (job == 1) {
@@ -2816,7 +2865,49 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 
     // ---- exponential race over K = { comp >= T* }, or greedy
     uint32_t idx = info.idx0;
-    if (md.sm) {
+    if (md.sm && rk_done) {
+        // K = the bins above the boundary (their best key) and the bucket's
+        // sorted members 0 .. rk_fi: the winner over both, ratios in double
+        double rr = -1.0;
+        uint32_t ri = NONE;
+        for (uint32_t i = tid; i <= rk_fi; i += K3_THREADS) {
+            const uint64_t c = S.coll[i];
+            const uint32_t id = cidx(c);
+            const float x = cval(c);
+            const double r = race_ratio(x, exp((double)x - m), (double)rowq[id] + (double)P.eps);
+            if (r > rr || (r == rr && id < ri)) {
+                rr = r;
+                ri = id;
+            }
+        }
+        if (rk_top != 0ull) {
+            // the key's candidate (the same id in every thread): its logit
+            // read again and transformed, the history searched by the whole
+            // workgroup for its penalty
+            const uint32_t id = race_key_id(rk_top);
+            int hit = 0;
+            if (XF && P.pen) {
+                const int64_t i0 = P.offsets[b];
+                int64_t i1 = P.offsets[b + 1];
+                if (P.plen) {
+                    const int64_t n = P.plen[b] < 0 ? 0 : P.plen[b];
+                    if (i0 + n < i1) i1 = i0 + n;
+                }
+                for (int64_t h = i0 + tid; h < i1; h += K3_THREADS) hit |= P.ids[h] == (int32_t)id;
+            }
+            hit = __syncthreads_or(hit);
+            if (tid == 0) {
+                const float x = xform<XF>(ld1<DT>(row_ptr(P, DT, b), id), hit ? 1u : 0u, P);
+                const double r =
+                    race_ratio(x, exp((double)x - m), (double)rowq[id] + (double)P.eps);
+                if (r > rr || (r == rr && id < ri)) {
+                    rr = r;
+                    ri = id;
+                }
+            }
+        }
+        idx = wg_best_ratio<K3_THREADS>(rr, ri, S.scd, S.sci);
+    } else if (md.sm) {
         Race rc;
         rc.x = -INFINITY; rc.qe = 1.0f; rc.idx = NONE; rc.lq = 0.0f;
         const float *rowq = P.q + (int64_t)b * P.V;

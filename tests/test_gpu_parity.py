@@ -381,6 +381,38 @@ def test_flat_rows_force_full_row_search():
     _check(W, "flat full-row search")
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_full_row_search_race_winner_penalised(dtype):
+    """Flat top-p rows (the full-row search) with a repetition penalty and a
+    temperature, q set so that the race winner is a penalised id near the top
+    of the row (far above the cut's boundary): the search keeps each value
+    bin's best race candidate and reads the winner's logit and history again,
+    so its transformed value must match the pass's.  Other rows put the
+    winner next to the cut (a zero of q at the ~k-th element, k from the
+    cut's size) or leave q random."""
+    rng = np.random.default_rng(61)
+    B, V = 12, 50021
+    x = (rng.standard_normal((B, V)) * 0.05).astype(np.float32)
+    x[:, 0] = 0.3  # a positive top entry that the penalty divides
+    q = rng.exponential(size=(B, V)).astype(np.float32)
+    order = np.argsort(-x, axis=1, kind="stable")
+    hist = []
+    for b in range(B):
+        h = rng.integers(0, V, size=400)
+        h[:3] = order[b, [0, 1, 4]]  # the top entries penalised
+        hist.append(h)
+        if b % 3 == 0:
+            q[b, order[b, 4]] = 1e-30      # a penalised top entry wins
+        elif b % 3 == 1:
+            q[b, order[b, int(V * 0.85)]] = 1e-30  # near the boundary of p = 0.9
+    ids = np.concatenate(hist).astype(np.int32)
+    offs = (np.arange(B + 1) * 400).astype(np.int64)
+    for rho in (1.3, 0.8):
+        W = _custom(x, top_k=0, top_p=0.9, flags=[6] * B, q=q, dtype=dtype, penalty=rho,
+                    temperature=0.7, ids=ids, offsets=offs)
+        _check(W, f"penalised winner rho={rho} {dtype}")
+
+
 def test_top_p_nonpositive_keeps_one():
     rng = np.random.default_rng(12)
     B, V = 8, 9000
