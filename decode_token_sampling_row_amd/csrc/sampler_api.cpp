@@ -102,6 +102,10 @@ size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
     off = align_up(off + sizeof(uint32_t), 256);
     const size_t o_fblist = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
+    const size_t o_fbarrive = off;
+    off = align_up(off + FB_GRID * sizeof(uint32_t), 256);
+    const size_t o_fbpart = off;
+    off = align_up(off + (size_t)fb_grid((int)B) * FB_PART_BYTES, 256);
     if (base) {
         w->cand = (uint64_t *)(base + o_cand);
         w->wcnt = (uint32_t *)(base + o_wcnt);
@@ -114,6 +118,8 @@ size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
         w->rowlo = (float *)(base + o_rowlo);
         w->fbcnt = (uint32_t *)(base + o_fbcnt);
         w->fblist = (uint32_t *)(base + o_fblist);
+        w->fbarrive = (uint32_t *)(base + o_fbarrive);
+        w->fbpart = base + o_fbpart;
     }
     return off;
 }

@@ -25,6 +25,16 @@ constexpr int K3_THREADS = 1024;
 constexpr int K3_BINS = 2048;      // value-space histogram bins
 constexpr int K3_COLLECT = 4096;   // bucket members sorted in LDS
 constexpr int K3_SEG = 65536;      // penalty-bitmap segment
+// Full-row search over several workgroups: the first histogram level of a
+// queued row is split into up to FB_TILES_MAX tiles of whole 4096-element
+// groups, when the queue is short enough for the grid of FB_GRID workgroups.
+constexpr int FB_GRID = 256;
+constexpr int FB_TILES_MAX = 16;
+constexpr int FB_GROUP = K3_THREADS * 4;  // elements of one step of the row passes
+// One tile's partial histogram: masses, race keys, counts of the K3_BINS
+// bins and the tile's total mass, padded to 256 bytes.
+constexpr size_t FB_PART_BYTES =
+    ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
 // Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
 constexpr int DGR_PER_TILE = 4;
 
@@ -128,6 +138,29 @@ constexpr int est_run_start(int s, int b, int V) {
     return (int)(seg0 + (int64_t)((s * 5 + b * 3) & 15) * step);
 }
 
+// Tiles per queued row of the full-row search and their length: with nq rows
+// queued and a grid of G workgroups, T = G / nq tiles per row (1 to
+// FB_TILES_MAX, no more than the row has 4096-element groups), each of TL
+// elements (a multiple of FB_GROUP) but the last; T = 1 keeps one workgroup
+// per row.  nq * T <= G whenever T > 1, so each workgroup takes one tile.
+struct FbTiling {
+    int T, TL;
+};
+constexpr FbTiling fb_tiling(uint32_t nq, uint32_t G, int V) {
+    FbTiling f{1, V};
+    if (nq == 0 || V <= 0) return f;
+    uint32_t t = G / nq;
+    if (t > (uint32_t)FB_TILES_MAX) t = FB_TILES_MAX;
+    const int groups = (V + FB_GROUP - 1) / FB_GROUP;
+    if (t > (uint32_t)groups) t = (uint32_t)groups;
+    if (t < 2) return f;
+    const int gpt = (groups + (int)t - 1) / (int)t;  // groups per tile
+    f.TL = gpt * FB_GROUP;
+    f.T = (V + f.TL - 1) / f.TL;
+    if (f.T < 2) f = FbTiling{1, V};
+    return f;
+}
+
 // Dynamic LDS words of the row merge: per-sub-slot candidate offsets, then
 // per-dense-tile counts of the kept list.
 constexpr int rows_lds_words(const KPlan &l) {
@@ -146,7 +179,15 @@ struct KWork {
     float *rowlo;     // [maxB] transformed smallest value of the estimate sample
     uint32_t *fbcnt;  // [1] rows queued for the full-row top-p search
     uint32_t *fblist; // [maxB] those rows
+    uint32_t *fbarrive; // [FB_GRID] tiles of queued row i done (zeroed by the pass)
+    char *fbpart;       // [fallback grid][FB_PART_BYTES] partial histograms of the tiles
 };
+
+// Workgroups of the full-row search for B rows: FB_GRID, or fewer when B rows
+// cannot use them all.
+constexpr int fb_grid(int B) {
+    return B <= 0 ? 1 : (int64_t)B * FB_TILES_MAX < FB_GRID ? B * FB_TILES_MAX : FB_GRID;
+}
 
 // Decode-step epilogue over all rows of a call (one workgroup).
 struct EpiParams {

@@ -988,6 +988,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
 //    row to the full-row search.
 
 constexpr int PASS_THREADS = 256;
+static_assert(PASS_THREADS >= FB_GRID, "the pass zeroes one arrival counter per thread");
 constexpr int PASS_WAVES = PASS_THREADS / 64;
 constexpr int PASS_D = 8;                      // groups of 4 in flight per thread
 constexpr int PGROUP = PASS_THREADS * 4;       // elements per group row
@@ -1448,7 +1449,11 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
             if (nv > 0) load4<DT, AL>(rowp, j, nv, ring[d]);
         }
     const Mode md = row_mode(P, b);
-    if (b == 0 && t == 0 && threadIdx.x == 0) *W.fbcnt = 0u;  // the full-row search queue
+    if (b == 0 && t == 0) {
+        // the full-row search queue and its tiles' arrival counters
+        if (threadIdx.x == 0) *W.fbcnt = 0u;
+        if (threadIdx.x < FB_GRID) W.fbarrive[threadIdx.x] = 0u;
+    }
     const bool filtering = P.top_k || P.top_p;  // the planning kernel ran
     const float traw = filtering ? W.rowthr[b] : 0.0f;
     const float ref = filtering ? W.rowref[b] : 0.0f;
@@ -2411,22 +2416,54 @@ __device__ __forceinline__ uint32_t race_key_id(uint64_t k) {
 }
 
 // Boundary bucket of a mass histogram: walking the bins from the top, the
-// bin where the running mass first reaches `need`.  Wave 0 sums 32 bins per
-// lane; lane 0 then walks lane sums and that lane's bins with one running
-// accumulator, so exactly one bin is chosen whatever the rounding.  Writes
-// found[0] = bin, fd[0] = mass of the bins above it.  If rounding leaves
-// `need` beyond the total, the lowest non-empty bin is chosen.
+// bin where the running mass first reaches `need`.  Writes found[0] = bin,
+// fd[0] = the mass of the bins above it, the running sum that the choice was
+// made with, so exactly one bin is chosen whatever the rounding.  Wave 0
+// sums 32 bins per lane and scans the lane sums; the first lane whose
+// inclusive sum reaches `need` scans its 32 bins on top of the lanes before
+// it, and the first bin of mass > 0 reaching `need` is the bucket.  When
+// rounding leaves no such bin in that lane, lane 0 walks the lane sums and
+// bins one by one instead, and if `need` lies beyond the total it takes the
+// lowest non-empty bin.
 __device__ void find_bucket(const double *hm, const uint32_t *hc, double need, double *lane_sum,
                             uint32_t *found, double *fd) {
     constexpr int PER = K3_BINS / 64;
+    static_assert(PER <= 64, "one lane per bin of a lane's share");
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         double s = 0.0;
         for (int t = 0; t < PER; ++t) s += hm[K3_BINS - 1 - lane * PER - t];
         lane_sum[lane] = s;
+        const double incl = wave_incl_scan_f64(s, lane);
+        const double excl = __shfl_up(incl, 1, 64);
+        const uint64_t reach = __ballot(incl >= need);
+        bool done = false;
+        if (reach) {
+            const int l = __builtin_ctzll(reach);
+            // shuffles run with every lane active (a lane outside the
+            // active set would read as 0), their results selected after
+            const double excl_l = __shfl(excl, l, 64);
+            const double acc0 = l == 0 ? 0.0 : excl_l;
+            const int bin = K3_BINS - 1 - l * PER - lane;
+            const double mb = lane < PER ? hm[bin] : 0.0;
+            const double bi = wave_incl_scan_f64(mb, lane);
+            const double bi_up = __shfl_up(bi, 1, 64);
+            const double be = lane == 0 ? 0.0 : bi_up;
+            const double acc = acc0 + be;
+            const uint64_t hit = __ballot(lane < PER && mb > 0.0 && acc + mb >= need);
+            if (hit) {
+                const int t = __builtin_ctzll(hit);
+                if (lane == t) {
+                    found[0] = (uint32_t)bin;
+                    fd[0] = acc;
+                }
+                done = true;
+            }
+        }
+        if (lane == 0) found[3] = done ? 1u : 0u;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && found[3] == 0u) {
         double acc = 0.0;
         int l = 0;
         for (; l < 63; ++l) {
@@ -2470,15 +2507,16 @@ __device__ __forceinline__ bool in_play(const FallbackShared &S, float x, uint32
     return true;
 }
 
-// Visit every element (x transformed, id j) of row b; f(x, j).  Groups of 4
-// per thread, the next group requested before the current one is visited,
-// so that each thread keeps a load in flight while its visitors run.
+// Visit every element (x transformed, id j) of elements [c0, c1) of row b;
+// f(x, j).  c0 is a multiple of 4.  Groups of 4 per thread, the next group
+// requested before the current one is visited, so that each thread keeps a
+// load in flight while its visitors run.
 template <int DT, bool AL, bool XF, class F>
-__device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
+__device__ __forceinline__ void range_pass(const KParams &P, int b, int c0, int c1, uint32_t *bm,
+                                           F &&f) {
     const void *rowp = row_ptr(P, DT, b);
-    const int V = P.V;
-    for (int s0 = 0; s0 < V; s0 += K3_SEG) {
-        const int s1 = min(s0 + K3_SEG, V);
+    for (int s0 = c0; s0 < c1; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, c1);
         if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
         int j = s0 + (int)threadIdx.x * 4;
         Raw4<DT> rx;
@@ -2502,17 +2540,22 @@ __device__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
     __syncthreads();
 }
 
-// row_pass with the row's q as well, f(x, q, j), in groups of 4: the 4
+template <int DT, bool AL, bool XF, class F>
+__device__ __forceinline__ void row_pass(const KParams &P, int b, uint32_t *bm, F &&f) {
+    range_pass<DT, AL, XF>(P, b, 0, P.V, bm, f);
+}
+
+// range_pass with the row's q as well, f(x, q, j), in groups of 4: the 4
 // logits and the 4 q of a group are requested as vectors one group ahead of
 // the visitors, so a visitor that needs q only for some elements does not
 // wait for each load in turn (and 4-wide groups keep the register count
 // down).
 template <int DT, bool AL, bool XF, class F>
-__device__ void row_pass_q(const KParams &P, int b, uint32_t *bm, const float *rowq, F &&f) {
+__device__ __forceinline__ void range_pass_q(const KParams &P, int b, int c0, int c1, uint32_t *bm,
+                                             const float *rowq, F &&f) {
     const void *rowp = row_ptr(P, DT, b);
-    const int V = P.V;
-    for (int s0 = 0; s0 < V; s0 += K3_SEG) {
-        const int s1 = min(s0 + K3_SEG, V);
+    for (int s0 = c0; s0 < c1; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, c1);
         if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
         // one group in flight ahead of the one being visited
         int j = s0 + (int)threadIdx.x * 4;
@@ -2547,16 +2590,70 @@ __device__ void row_pass_q(const KParams &P, int b, uint32_t *bm, const float *r
     __syncthreads();
 }
 
+template <int DT, bool AL, bool XF, class F>
+__device__ __forceinline__ void row_pass_q(const KParams &P, int b, uint32_t *bm, const float *rowq,
+                                           F &&f) {
+    range_pass_q<DT, AL, XF>(P, b, 0, P.V, bm, rowq, f);
+}
+
+// Bin function of the first histogram level of a row's search: bins over the
+// values that take part, from about the row minimum (or the floor's value)
+// to the maximum m, at most 128 below it; smaller values (whose mass is
+// below 1e-55 of the maximum's) fall in bin 0.
+__device__ __forceinline__ void level0_bins(float m, float rowlo, uint64_t cfloor, float &lo,
+                                            float &scale) {
+    lo = m - 128.0f;
+    if (rowlo <= m) lo = fmaxf(lo, rowlo);
+    if (cfloor != 0) lo = fmaxf(lo, key2f((uint32_t)(cfloor >> 32)));
+    const float w = m - lo;
+    scale = w > 0.0f ? (float)K3_BINS / w : 1.0f;
+    if (!(scale < INFINITY)) scale = 1.0f;  // a one-value range
+}
+
+// A tile's partial first level in the workspace: masses, race keys, counts
+// of the K3_BINS bins, then its total mass.
+struct FbPart {
+    double *hm;
+    uint64_t *rk;
+    uint32_t *hc;
+    double *z;
+};
+__device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
+    char *p = base + (size_t)slot * FB_PART_BYTES;
+    FbPart f;
+    f.hm = (double *)p;
+    f.rk = (uint64_t *)(p + (size_t)K3_BINS * 8);
+    f.hc = (uint32_t *)(p + (size_t)K3_BINS * 16);
+    f.z = (double *)(p + (size_t)K3_BINS * 20);
+    return f;
+}
+
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
-    // the rows the merge queued, spread over the workgroups
+    // The rows the merge queued, spread over the workgroups.  While the
+    // queue is short (T > 1), the first histogram level of the cut's search
+    // of a row is split into T tiles, one workgroup each: each writes its
+    // partial histogram, and the last to arrive merges them (in tile order)
+    // and carries on with the row alone.
     const uint32_t nq = *W.fbcnt;
-    for (uint32_t qi = blockIdx.x; qi < nq; qi += gridDim.x) {
+    const FbTiling ft = fb_tiling(nq, gridDim.x, P.V);
+    const uint32_t ntiles = (uint32_t)ft.T;
+    for (uint32_t it = blockIdx.x; it < nq * ntiles; it += gridDim.x) {
+    const uint32_t qi = it / ntiles, tile = it % ntiles;
     const int b = (int)W.fblist[qi];
     RowInfo info = W.info[b];
     const Mode md = row_mode(P, b);
+    // queued only for an inverse-CDF draw over the whole row
+    const bool whole = info.kind == KIND_UNFILTERED;
+    // tiles take the first level of the first search when that search is
+    // the cut's (or the whole-row draw's) at a positive level and the row's
+    // maximum is known
+    const bool tiled = ntiles > 1 && info.idx0 != NONE &&
+                       (whole ? P.u[b] > 0.0f
+                              : (md.tp && md.p > 0.0f && !(md.tk && info.T == 0)));
+    if (!tiled && tile != 0) continue;
     if (info.idx0 == NONE) {
         // a row the merge found incomplete: its maximum (the first element of
         // the order) from one pass over the row
@@ -2590,7 +2687,120 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     uint64_t rk_top = 0;
     uint32_t rk_fi = 0;
     const float *rowq = md.sm ? P.q + (int64_t)b * P.V : nullptr;
-    auto search = [&](double tval, bool frac, bool count, bool rk_on, uint64_t &Tst,
+
+    // The tiles of a tiled row: this workgroup's part of the first level of
+    // the first search (weights exp(x - m), race keys for a sampling row's
+    // cut), written to its slot it = qi * T + tile.  The last tile to arrive
+    // merges the T parts into S (masses, counts and totals summed in tile
+    // order, keys by maximum) for that search to use.
+    bool pre0 = false;
+    double pre_z = 0.0;
+    if (tiled) {
+        const bool rkt = md.sm && !whole;
+        float lo, scale;
+        level0_bins(info.m, rowlo, cfloor, lo, scale);
+        for (int i = tid; i < K3_BINS; i += K3_THREADS) {
+            S.hm[i] = 0.0;
+            S.hc[i] = 0u;
+            if (rkt) S.rk[i] = 0ull;
+        }
+        __syncthreads();
+        const int c0 = (int)tile * ft.TL, c1 = min(c0 + ft.TL, P.V);
+        double zt = 0.0;
+        auto visit = [&](float x, uint32_t j, float qj) {
+            if (!(x > -INFINITY) || mkcomp(x, j) < cfloor) return;
+            const double e = exp((double)x - m);
+            zt += e;
+            const uint32_t bi = bin_value(x, lo, scale);
+            atomicAdd(&S.hm[bi], e);
+            atomicAdd(&S.hc[bi], 1u);
+            if (rkt) atomicMax(&S.rk[bi], race_key(x, e, (double)qj + (double)P.eps, j));
+        };
+        if (rkt)
+            range_pass_q<DT, AL, XF>(P, b, c0, c1, S.bm, rowq,
+                                     [&](float x, float qj, uint32_t j) { visit(x, j, qj); });
+        else
+            range_pass<DT, AL, XF>(P, b, c0, c1, S.bm,
+                                   [&](float x, uint32_t j) { visit(x, j, 0.0f); });
+        const double zsum = wg_sum_f64<K3_THREADS>(zt, S.scd);
+        const FbPart mine = fb_part(W.fbpart, it);
+        for (int i = tid; i < K3_BINS; i += K3_THREADS) {
+            mine.hm[i] = S.hm[i];
+            mine.hc[i] = S.hc[i];
+            if (rkt) mine.rk[i] = S.rk[i];
+        }
+        if (tid == 0) *mine.z = zsum;
+        // One thread counts the arrival: its release (after the barrier that
+        // orders every thread's stores before it) publishes the whole part,
+        // and the last tile's acquire makes every part visible to the
+        // workgroup past the next barrier.  Only that thread touches the
+        // device-wide cache state.
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(&W.fbarrive[qi], 1u, __ATOMIC_RELEASE,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            if (old == ntiles - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            S.found[2] = old;
+        }
+        __syncthreads();
+        if (S.found[2] != ntiles - 1) continue;  // a later tile finishes the row
+        const uint32_t slot0 = qi * ntiles;
+        // each thread merges its K3_BINS / K3_THREADS bins, the loads of four
+        // tiles requested together; the sums still run in tile order
+        constexpr int BPT = K3_BINS / K3_THREADS;
+        static_assert(BPT * K3_THREADS == K3_BINS, "bins per thread");
+        double hm[BPT];
+        uint32_t hc[BPT];
+        uint64_t rk[BPT];
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            hm[u] = 0.0;
+            hc[u] = 0u;
+            rk[u] = 0ull;
+        }
+        for (uint32_t t0 = 0; t0 < ntiles; t0 += 4) {
+            double a[4][BPT];
+            uint32_t c[4][BPT];
+            uint64_t k[4][BPT];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const FbPart pt = fb_part(W.fbpart, slot0 + min(t0 + v, ntiles - 1));
+#pragma unroll
+                for (int u = 0; u < BPT; ++u) {
+                    const int i = tid + u * K3_THREADS;
+                    a[v][u] = pt.hm[i];
+                    c[v][u] = pt.hc[i];
+                    k[v][u] = rkt ? pt.rk[i] : 0ull;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (t0 + v < ntiles) {
+#pragma unroll
+                    for (int u = 0; u < BPT; ++u) {
+                        hm[u] += a[v][u];
+                        hc[u] += c[v][u];
+                        rk[u] = k[v][u] > rk[u] ? k[v][u] : rk[u];
+                    }
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = tid + u * K3_THREADS;
+            S.hm[i] = hm[u];
+            S.hc[i] = hc[u];
+            if (rkt) S.rk[i] = rk[u];
+            S.hlo[i] = NONE;
+            S.hhi[i] = 0u;
+        }
+        for (uint32_t t = 0; t < ntiles; ++t) pre_z += *fb_part(W.fbpart, slot0 + t).z;
+        pre0 = true;
+        __syncthreads();
+    }
+
+    // With pre (the first search of a tiled row) the first level's histogram
+    // is the tiles' merged one, and its total mass pre_z.
+    auto search = [&](double tval, bool frac, bool count, bool rk_on, bool pre, uint64_t &Tst,
                       double &ZKo) {
         double above = 0.0, target = 0.0;
         int nlev = 0;
@@ -2601,29 +2811,23 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             float lo = 0.0f, scale = 0.0f;
             uint32_t klo = 0, sh = 0;
             if (level == 0) {
-                // bins over the values that take part: from about the row
-                // minimum (or the floor's value) to the maximum, at most 128
-                // below it; smaller values (whose mass is below 1e-55 of the
-                // maximum's) fall in bin 0
-                lo = info.m - 128.0f;
-                if (rowlo <= info.m) lo = fmaxf(lo, rowlo);
-                if (cfloor != 0) lo = fmaxf(lo, key2f((uint32_t)(cfloor >> 32)));
-                const float w = info.m - lo;
-                scale = w > 0.0f ? (float)K3_BINS / w : 1.0f;
-                if (!(scale < INFINITY)) scale = 1.0f;  // a one-value range
+                level0_bins(info.m, rowlo, cfloor, lo, scale);
             } else {
                 klo = S.lv_klo[level];
                 sh = S.lv_sh[level];
             }
             const bool rkl = rk_on && level == 0;
-            for (int i = tid; i < K3_BINS; i += K3_THREADS) {
-                S.hm[i] = 0.0;
-                S.hc[i] = 0u;
-                S.hlo[i] = NONE;
-                S.hhi[i] = 0u;
-                if (rkl) S.rk[i] = 0ull;
+            const bool merged = pre && level == 0;
+            if (!merged) {
+                for (int i = tid; i < K3_BINS; i += K3_THREADS) {
+                    S.hm[i] = 0.0;
+                    S.hc[i] = 0u;
+                    S.hlo[i] = NONE;
+                    S.hhi[i] = 0u;
+                    if (rkl) S.rk[i] = 0ull;
+                }
+                __syncthreads();
             }
-            __syncthreads();
             double zt = 0.0;
             auto visit = [&](float x, uint32_t j, float qj) {
                 if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
@@ -2640,14 +2844,16 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 }
                 if (rkl) atomicMax(&S.rk[bi], race_key(x, e, (double)qj + (double)P.eps, j));
             };
-            if (rkl)
+            if (merged) {
+            } else if (rkl) {
                 row_pass_q<DT, AL, XF>(P, b, S.bm, rowq, [&](float x, float qj, uint32_t j) {
                     visit(x, j, qj);
                 });
-            else
+            } else {
                 row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) { visit(x, j, 0.0f); });
+            }
             if (level == 0) {
-                double Z = wg_sum_f64<K3_THREADS>(zt, S.scd);
+                const double Z = merged ? pre_z : wg_sum_f64<K3_THREADS>(zt, S.scd);
                 target = frac ? tval * Z : tval;
             }
             find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
@@ -2812,7 +3018,6 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
     // queued only for an inverse-CDF draw over the whole row, that draw at u;
     // (2) the draw inside the cut at u ZK.  A level <= 0 (or NaN) stands for
     // the first element of the order.
-    const bool whole = info.kind == KIND_UNFILTERED;
     const uint64_t top = mkcomp(info.m, info.idx0);
     uint64_t Tstar = top;  // the cut (or the whole-row draw)
     double ZK = 1.0;       // mass of the cut, exp(x - m) summed
@@ -2847,7 +3052,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
         uint64_t Tj;
         double Zj;
-        search(tval, frac, count, job == 1 && md.sm && !whole, Tj, Zj);
+        search(tval, frac, count, job == 1 && md.sm && !whole, job == 1 && pre0, Tj, Zj);
         if (job == 0) {
             cfloor = (P.flags & TOPK_TIES) ? (Tj >> 32) << 32 : Tj;
         } else if (job == 1) {
@@ -3233,9 +3438,9 @@ hipError_t launch_rows(const KParams &p, const KPlan &l, const KWork &w, hipStre
 hipError_t launch_fallback(const KParams &p, const KPlan &l, const KWork &w, int dtype, bool al,
                            hipStream_t s) {
     const bool xf = any_transform(p);
-    // one workgroup per CU (its LDS allows no more); queued rows are spread
-    // over them, none queued costs one read per workgroup
-    dim3 grid((unsigned)std::min(p.B, 256)), block(K3_THREADS);
+    // one workgroup per CU (its LDS allows no more); queued rows (or their
+    // tiles) are spread over them, none queued costs one read per workgroup
+    dim3 grid((unsigned)fb_grid(p.B)), block(K3_THREADS);
     return SMP_PICK(k_fallback, grid, block, 0);
 }
 

@@ -16,6 +16,12 @@
 //   est      the sample runs of the admission estimate lie inside the row,
 //            start on a multiple of VEC, inside their own segment, and do
 //            not overlap;
+//   tiles    the full-row search's tiling of a short queue: with T > 1
+//            tiles per row, the T tiles of TL elements (a multiple of the
+//            passes' 4096-element step) cover the row, none empty; T stays
+//            within FB_TILES_MAX; the tiles of all nq rows (slots qi T + t)
+//            fit the grid, hence the partial slots the workspace holds, and
+//            every queued row's arrival counter (index qi) is below FB_GRID;
 //   prefix   the six-ballot bit-plane prefix of the staged select gives
 //            every lane the exclusive prefix of the lanes' counts (at most
 //            4 PASS_D = 32 each), so entries land in [cnt, cnt + total).
@@ -134,6 +140,33 @@ static void check_estimate(int32_t V) {
 // A wave of 64 lanes, each with n_l <= 32 admitted entries: bit plane k of
 // the counts is one ballot; a lane's rank in it (set lanes below it) shifted
 // by k, summed over the six planes, is its exclusive prefix.
+static int64_t tilings = 0;
+static void check_tiling(int32_t V) {
+    static const int batches[] = {1, 2, 3, 4, 7, 15, 16, 17, 31, 64, 100, 255, 256, 257, 1024, 4096};
+    for (int B : batches) {
+        const int G = fb_grid(B);
+        CHECK(G >= 1 && G <= FB_GRID && (B * FB_TILES_MAX >= FB_GRID || G == B * FB_TILES_MAX),
+              "B=%d grid %d", B, G);
+        const int nqmax = B < 600 ? B : 600;
+        for (int nq = 0; nq <= nqmax; ++nq) {
+            const FbTiling f = fb_tiling((uint32_t)nq, (uint32_t)G, V);
+            ++tilings;
+            CHECK(f.T >= 1 && f.T <= FB_TILES_MAX, "V=%d B=%d nq=%d T=%d", V, B, nq, f.T);
+            if (f.T == 1) {
+                CHECK(f.TL == V, "V=%d nq=%d TL=%d", V, nq, f.TL);
+                continue;
+            }
+            CHECK(f.TL % FB_GROUP == 0, "V=%d nq=%d TL=%d", V, nq, f.TL);
+            CHECK((int64_t)(f.T - 1) * f.TL < V && (int64_t)f.T * f.TL >= V,
+                  "V=%d nq=%d T=%d TL=%d: a tile is empty or the row is not covered", V, nq, f.T,
+                  f.TL);
+            CHECK((int64_t)nq * f.T <= G, "V=%d B=%d nq=%d T=%d: slots beyond the grid", V, B,
+                  nq, f.T);
+            CHECK(nq - 1 < FB_GRID, "V=%d nq=%d: arrival counter out of range", V, nq);
+        }
+    }
+}
+
 static void check_prefix(std::mt19937 &rng) {
     std::uniform_int_distribution<int> cnt(0, 32), pick(0, 5);
     for (int trial = 0; trial < 20000; ++trial) {
@@ -168,6 +201,7 @@ int main() {
         check_dense(V);
         ++ndense;
         check_estimate(V);
+        if (i % 7 == 0 || V < 70000) check_tiling(V);
     }
     std::mt19937 rng(12345);
     check_prefix(rng);
@@ -175,7 +209,8 @@ int main() {
         fprintf(stderr, "%d failed checks\n", failures);
         return 1;
     }
-    printf("index checks ok: %zu vocab sizes, %d dense maps (%lld ids), %d tile lengths\n",
-           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN);
+    printf("index checks ok: %zu vocab sizes, %d dense maps (%lld ids), %d tile lengths, "
+           "%lld search tilings\n",
+           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN, (long long)tilings);
     return 0;
 }
