@@ -32,9 +32,11 @@ constexpr int FB_GRID = 256;
 constexpr int FB_TILES_MAX = 16;
 constexpr int FB_GROUP = K3_THREADS * 4;  // elements of one step of the row passes
 // One tile's partial histogram: masses, race keys, counts of the K3_BINS
-// bins and the tile's total mass, padded to 256 bytes.
-constexpr size_t FB_PART_BYTES =
-    ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
+// bins and the tile's total mass (padded to 256 bytes), then the mass sums
+// and largest race keys of FB_CHUNKS chunks of consecutive bins.
+constexpr int FB_CHUNKS = 64;
+constexpr size_t FB_PART_CHUNKS = ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
+constexpr size_t FB_PART_BYTES = (FB_PART_CHUNKS + (size_t)FB_CHUNKS * 16 + 255) / 256 * 256;
 // Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
 constexpr int DGR_PER_TILE = 4;
 

@@ -638,6 +638,31 @@ __device__ void bitonic_desc(uint64_t *s, int n) {
     }
 }
 
+// Descending bitonic sort of npad <= K3_THREADS composites, one per thread
+// (thread i holds place i afterwards): exchanges between lanes of a wave go
+// by shuffles, wider ones through s[0..K3_THREADS) in LDS (a barrier
+// pair each).  npad is a power of two; every thread of the workgroup calls.
+__device__ uint64_t bitonic_regs_desc(uint64_t c, int npad, uint64_t *s) {
+    const int tid = threadIdx.x;
+    for (int k = 2; k <= npad; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t o;
+            if (j >= 64) {
+                s[tid] = c;
+                __syncthreads();
+                o = s[tid ^ j];
+                __syncthreads();
+            } else {
+                o = shx64(c, j);
+            }
+            const bool lower = (tid & j) == 0;
+            const bool desc = (tid & k) == 0;
+            c = (lower == desc) ? (o > c ? o : c) : (o < c ? o : c);
+        }
+    }
+    return c;
+}
+
 __device__ __forceinline__ int pow2_ceil(int n) {
     int p = 1;
     while (p < n) p <<= 1;
@@ -2596,6 +2621,57 @@ __device__ __forceinline__ void row_pass_q(const KParams &P, int b, uint32_t *bm
     range_pass_q<DT, AL, XF>(P, b, 0, P.V, bm, rowq, f);
 }
 
+// Visit the elements of row b whose transformed key lies in [klo, khi]; f(x,
+// j).  A pass of one workgroup over a row is bound by its instruction count
+// and by the loads each thread keeps in flight, so the key test comes first
+// and whole chunks of KS_D groups of 4 per thread are requested at once
+// (unconditional loads); the tail of each bitmap segment goes one group per
+// thread.
+constexpr int KS_D = 4;
+template <int DT, bool AL, bool XF, class F>
+__device__ __forceinline__ void key_scan(const KParams &P, int b, uint32_t klo, uint32_t khi,
+                                         uint32_t *bm, F &&f) {
+    constexpr int STEP = K3_THREADS * 4;
+    constexpr int CHUNK = STEP * KS_D;
+    const void *rowp = row_ptr(P, DT, b);
+    const int t4 = (int)threadIdx.x * 4;
+    auto visit4 = [&](const Raw4<DT> &r, int j, int nv, int s0) {
+        float x[4];
+        unpack4<DT>(r, x);
+        uint32_t bits = 0;
+        if (P.pen) {
+            const int rr = j - s0;
+            bits = (bm[rr >> 5] >> (rr & 31)) & 0xfu;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < nv) {
+                const float y = xform<XF>(x[i], (bits >> i) & 1u, P);
+                const uint32_t k = f2key(y);
+                if (k >= klo && k <= khi) f(y, (uint32_t)(j + i));
+            }
+    };
+    for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, P.V);
+        if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
+        int base = s0;
+        for (; base + CHUNK <= s1; base += CHUNK) {
+            Raw4<DT> r[KS_D];
+#pragma unroll
+            for (int d = 0; d < KS_D; ++d) load4<DT, AL>(rowp, base + d * STEP + t4, 4, r[d]);
+#pragma unroll
+            for (int d = 0; d < KS_D; ++d) visit4(r[d], base + d * STEP + t4, 4, s0);
+        }
+        for (int j = base + t4; j < s1; j += STEP) {
+            Raw4<DT> r;
+            const int nv = nv4(j, s1);
+            load4<DT, AL>(rowp, j, nv, r);
+            visit4(r, j, nv, s0);
+        }
+    }
+    __syncthreads();
+}
+
 // Bin function of the first histogram level of a row's search: bins over the
 // values that take part, from about the row minimum (or the floor's value)
 // to the maximum m, at most 128 below it; smaller values (whose mass is
@@ -2611,12 +2687,18 @@ __device__ __forceinline__ void level0_bins(float m, float rowlo, uint64_t cfloo
 }
 
 // A tile's partial first level in the workspace: masses, race keys, counts
-// of the K3_BINS bins, then its total mass.
+// of the K3_BINS bins, its total mass, then per chunk of FB_CHUNK_BINS bins
+// (chunk c: bins K3_BINS - 1 - c FB_CHUNK_BINS down, the order in which the
+// bucket search sums them) the chunk's mass and its largest race key.
+constexpr int FB_CHUNK_BINS = K3_BINS / FB_CHUNKS;
+static_assert(FB_CHUNKS == 64 && FB_CHUNK_BINS <= 64, "one lane per chunk, one lane per bin");
 struct FbPart {
     double *hm;
     uint64_t *rk;
     uint32_t *hc;
     double *z;
+    double *csum;
+    uint64_t *crk;
 };
 __device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
     char *p = base + (size_t)slot * FB_PART_BYTES;
@@ -2625,6 +2707,8 @@ __device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
     f.rk = (uint64_t *)(p + (size_t)K3_BINS * 8);
     f.hc = (uint32_t *)(p + (size_t)K3_BINS * 16);
     f.z = (double *)(p + (size_t)K3_BINS * 20);
+    f.csum = (double *)(p + FB_PART_CHUNKS);
+    f.crk = (uint64_t *)(p + FB_PART_CHUNKS + (size_t)FB_CHUNKS * 8);
     return f;
 }
 
@@ -2730,6 +2814,24 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (rkt) mine.rk[i] = S.rk[i];
         }
         if (tid == 0) *mine.z = zsum;
+        // the chunk summaries: 32 lanes per chunk, summed by shuffles
+        static_assert(FB_CHUNK_BINS == 32, "a chunk is half a wave");
+        for (int c0 = 0; c0 < FB_CHUNKS; c0 += K3_THREADS / FB_CHUNK_BINS) {
+            const int c = c0 + tid / FB_CHUNK_BINS;
+            const int i = K3_BINS - 1 - c * FB_CHUNK_BINS - (tid % FB_CHUNK_BINS);
+            double cs = S.hm[i];
+            uint64_t ck = rkt ? S.rk[i] : 0ull;
+#pragma unroll
+            for (int sft = FB_CHUNK_BINS / 2; sft >= 1; sft >>= 1) {
+                cs += shxd(cs, sft);
+                const uint64_t o = shx64(ck, sft);
+                ck = o > ck ? o : ck;
+            }
+            if (tid % FB_CHUNK_BINS == 0) {
+                mine.csum[c] = cs;
+                mine.crk[c] = ck;
+            }
+        }
         // One thread counts the arrival: its release (after the barrier that
         // orders every thread's stores before it) publishes the whole part,
         // and the last tile's acquire makes every part visible to the
@@ -2744,6 +2846,18 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         }
         __syncthreads();
         if (S.found[2] != ntiles - 1) continue;  // a later tile finishes the row
+        // the tiles' totals, read at once and summed in tile order
+        static_assert(FB_TILES_MAX <= 16, "one scratch entry per tile");
+        if (tid < (int)ntiles) S.scd[tid] = *fb_part(W.fbpart, qi * ntiles + tid).z;
+        __syncthreads();
+        for (uint32_t t = 0; t < ntiles; ++t) pre_z += S.scd[t];
+        __syncthreads();
+        pre0 = true;
+    }
+
+    // The tiles' parts merged bin by bin, in tile order, into the first
+    // level's histogram in S (what a one-workgroup first level would hold).
+    auto merge_parts = [&](bool rkt) {
         const uint32_t slot0 = qi * ntiles;
         // each thread merges its K3_BINS / K3_THREADS bins, the loads of four
         // tiles requested together; the sums still run in tile order
@@ -2770,7 +2884,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                     const int i = tid + u * K3_THREADS;
                     a[v][u] = pt.hm[i];
                     c[v][u] = pt.hc[i];
-                    k[v][u] = rkt ? pt.rk[i] : 0ull;
+                    k[v][u] = pt.rk[i];  // read whether or not written: kept only with rkt
                 }
             }
 #pragma unroll
@@ -2793,10 +2907,103 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             S.hlo[i] = NONE;
             S.hhi[i] = 0u;
         }
-        for (uint32_t t = 0; t < ntiles; ++t) pre_z += *fb_part(W.fbpart, slot0 + t).z;
-        pre0 = true;
         __syncthreads();
-    }
+    };
+
+    // The boundary bucket of the merged first level from the tiles' chunk
+    // summaries and the bins of one chunk only: wave 0 merges the chunk masses
+    // (tile order), takes the first chunk whose running sum reaches need,
+    // merges that chunk's bins and takes the first bin of mass > 0 reaching
+    // need, as find_bucket would on the merged histogram.  Sets S.found[0],
+    // S.fd[0], S.hc of that bin and, with rkt, the best race key above it
+    // (S.sc64[0]).  Returns false (nothing set) when rounding leaves no such
+    // bin in that chunk; the caller then merges every bin.
+    auto chunk_bucket = [&](double need, bool rkt) -> bool {
+        const uint32_t slot0 = qi * ntiles;
+        // the bucket buffer is free here: the tiles' values gathered into it
+        // with one load per thread, then summed per lane in tile order
+        double *gs = reinterpret_cast<double *>(S.coll);  // [tile][FB_CHUNKS] or [tile][bin]
+        uint64_t *gk = S.coll + FB_TILES_MAX * FB_CHUNKS;
+        uint32_t *gc = reinterpret_cast<uint32_t *>(S.coll + 2 * FB_TILES_MAX * FB_CHUNKS);
+        static_assert(FB_TILES_MAX * FB_CHUNKS * 5 / 2 <= K3_COLLECT, "gather scratch");
+        for (int p = tid; p < (int)ntiles * FB_CHUNKS; p += K3_THREADS) {
+            const FbPart pt = fb_part(W.fbpart, slot0 + (uint32_t)(p / FB_CHUNKS));
+            gs[p] = pt.csum[p % FB_CHUNKS];
+            gk[p] = pt.crk[p % FB_CHUNKS];
+        }
+        __syncthreads();
+        const int lane = tid & 63;
+        uint64_t ck = 0ull;  // wave 0: the chunk's largest race key
+        if (tid < 64) {
+            double cs = 0.0;
+            for (uint32_t t = 0; t < ntiles; ++t) {
+                cs += gs[t * FB_CHUNKS + lane];
+                const uint64_t k = gk[t * FB_CHUNKS + lane];
+                ck = k > ck ? k : ck;
+            }
+            // shuffles with every lane active (an inactive lane reads as 0)
+            const double incl = wave_incl_scan_f64(cs, lane);
+            const double excl = __shfl_up(incl, 1, 64);
+            const uint64_t reach = __ballot(incl >= need);
+            const int l = reach ? __builtin_ctzll(reach) : 0;
+            const double excl_l = __shfl(excl, l, 64);
+            if (lane == 0) {
+                S.found[1] = reach ? (uint32_t)l : NONE;
+                S.fd[1] = l == 0 ? 0.0 : excl_l;
+            }
+        }
+        __syncthreads();
+        const uint32_t lsel = S.found[1];
+        if (lsel == NONE) return false;  // uniform
+        const double acc0 = S.fd[1];
+        __syncthreads();  // gs / gk reused below
+        for (int p = tid; p < (int)ntiles * FB_CHUNK_BINS; p += K3_THREADS) {
+            const FbPart pt = fb_part(W.fbpart, slot0 + (uint32_t)(p / FB_CHUNK_BINS));
+            const int bin = K3_BINS - 1 - (int)lsel * FB_CHUNK_BINS - p % FB_CHUNK_BINS;
+            gs[p] = pt.hm[bin];
+            gc[p] = pt.hc[bin];
+            gk[p] = pt.rk[bin];  // read whether or not written: used only with rkt
+        }
+        __syncthreads();
+        if (tid < 64) {
+            const int bin = K3_BINS - 1 - (int)lsel * FB_CHUNK_BINS - lane;
+            double mb = 0.0;
+            uint32_t cb = 0u;
+            uint64_t kb = 0ull;
+            if (lane < FB_CHUNK_BINS)
+                for (uint32_t t = 0; t < ntiles; ++t) {
+                    mb += gs[t * FB_CHUNK_BINS + lane];
+                    cb += gc[t * FB_CHUNK_BINS + lane];
+                    const uint64_t k = gk[t * FB_CHUNK_BINS + lane];
+                    kb = k > kb ? k : kb;
+                }
+            const double bi = wave_incl_scan_f64(mb, lane);
+            const double bi_up = __shfl_up(bi, 1, 64);
+            const double acc = acc0 + (lane == 0 ? 0.0 : bi_up);
+            const uint64_t hit = __ballot(lane < FB_CHUNK_BINS && mb > 0.0 && acc + mb >= need);
+            const int tb = hit ? __builtin_ctzll(hit) : 0;
+            // race keys of the chunks above and of the bins above it
+            uint64_t top = (lane < (int)lsel ? ck : 0ull);
+            const uint64_t kbin = lane < tb ? kb : 0ull;
+            top = kbin > top ? kbin : top;
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) {
+                const uint64_t o = shx64(top, sft);
+                top = o > top ? o : top;
+            }
+            if (hit && lane == tb) {
+                S.found[0] = (uint32_t)bin;
+                S.fd[0] = acc;
+                S.hc[bin] = cb;
+            }
+            if (lane == 0) {
+                if (rkt) S.sc64[0] = top;
+                S.found[3] = hit ? 1u : 0u;
+            }
+        }
+        __syncthreads();
+        return S.found[3] != 0u;
+    };
 
     // With pre (the first search of a tiled row) the first level's histogram
     // is the tiles' merged one, and its total mass pre_z.
@@ -2805,7 +3012,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         double above = 0.0, target = 0.0;
         int nlev = 0;
         int path = 0;  // 1 collect, 2 ties
-        uint32_t bsel = 0, bcnt = 0, bklo = 0;
+        uint32_t bsel = 0, bcnt = 0, bklo = 0, bkhi_sel = 0xffffffffu;
         for (int level = 0; level < 6; ++level) {
             // bin function of this level
             float lo = 0.0f, scale = 0.0f;
@@ -2856,10 +3063,16 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 const double Z = merged ? pre_z : wg_sum_f64<K3_THREADS>(zt, S.scd);
                 target = frac ? tval * Z : tval;
             }
-            find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
+            bool quick = false;  // the bucket found from the tiles' chunk summaries
+            if (merged) {
+                quick = chunk_bucket(target - above, rkl);
+                if (quick && rkl) rk_top = S.sc64[0];
+                if (!quick) merge_parts(rkl);
+            }
+            if (!quick) find_bucket(S.hm, S.hc, target - above, S.lane_sum, S.found, S.fd);
             const uint32_t fb = S.found[0];
             const double bbefore = S.fd[0];
-            if (rkl) {
+            if (rkl && !quick) {
                 // the best key of the bins above the boundary (all of them in K)
                 uint64_t t = 0;
                 for (int i = tid; i < K3_BINS; i += K3_THREADS)
@@ -2875,15 +3088,21 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (level == 0) {
                 // keys of the bin's value range, half a bin wider on each side
                 // than its edges (rounding in bin_value moves an edge by far
-                // less); bin 0 also holds everything below lo (-inf included),
-                // the last bin everything up to the maximum.  Membership is
-                // still decided by the bin itself, so a wider range is safe.
+                // less), and 64 keys more (adjacent floats have adjacent
+                // keys) for bins narrower than a unit in the last place of
+                // their values; bin 0 also holds everything below lo (-inf
+                // included), the last bin everything up to the maximum.
+                // Membership is still decided by the bin itself, so a wider
+                // range is safe: it only has to hold every member.
                 const float w = 1.0f / scale;
                 bklo = fb == 0 ? 0u : f2key(lo + ((float)fb - 0.5f) * w);
                 bkhi = fb == (uint32_t)(K3_BINS - 1) ? f2key(info.m)
                                                      : f2key(fminf(lo + ((float)fb + 1.5f) * w, info.m));
                 if (bkhi < bklo) bkhi = bklo;
+                bklo = bklo > 64u ? bklo - 64u : 0u;
+                bkhi = bkhi < 0xffffffffu - 64u ? bkhi + 64u : 0xffffffffu;
             }
+            bkhi_sel = bkhi;
             __syncthreads();
             if (tid == 0) {
                 if (level == 0) {
@@ -2913,7 +3132,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         if (path == 1) {
             if (tid == 0) S.counter = 0;
             __syncthreads();
-            row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
+            // the bucket's members lie in its key range [bklo, bkhi_sel]
+            key_scan<DT, AL, XF>(P, b, bklo, bkhi_sel, S.bm, [&](float x, uint32_t j) {
                 if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
@@ -2921,44 +3141,65 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 if (pos < (uint32_t)K3_COLLECT) S.coll[pos] = mkcomp(x, j);
             });
             const int n = (int)min(S.counter, (uint32_t)K3_COLLECT);
-            const int npad = pow2_ceil(n < 1 ? 1 : n);
-            for (int i = n + tid; i < npad; i += K3_THREADS) S.coll[i] = 0ull;
-            __syncthreads();
-            bitonic_desc<K3_THREADS>(S.coll, npad);
-            // masses of the sorted bucket members, 4 per thread
-            constexpr int PER = K3_COLLECT / K3_THREADS;
-            double ei[PER];
-            double loc = 0.0;
+            uint32_t fi;
+            if (n <= K3_THREADS) {
+                // one member per thread: sorted in registers, masses and
+                // their running sum from the top (above + the members before
+                // it + its own) one per thread
+                const int npad = pow2_ceil(n < 1 ? 1 : n);
+                uint64_t c = tid < n ? S.coll[tid] : 0ull;
+                __syncthreads();
+                c = bitonic_regs_desc(c, npad, S.coll);
+                if (tid < n) S.coll[tid] = c;
+                const double e1 = tid < n ? (count ? 1.0 : exp((double)cval(c) - m)) : 0.0;
+                double tot;
+                const double run = (above + wg_excl_scan_f64<K3_THREADS>(e1, S.scd, tot)) + e1;
+                fi = wg_min_u32<K3_THREADS>(tid < n && run >= target ? (uint32_t)tid : NONE, S.sc);
+                if (fi == NONE) fi = (uint32_t)(n > 0 ? n - 1 : 0);  // rounding: whole bucket
+                // ZK: mass of every kept element = the running sum through fi
+                if (tid == (int)fi) S.fd[1] = n > 0 ? run : above;
+                __syncthreads();
+                ZKo = S.fd[1];
+            } else {
+                const int npad = pow2_ceil(n);
+                for (int i = n + tid; i < npad; i += K3_THREADS) S.coll[i] = 0ull;
+                __syncthreads();
+                bitonic_desc<K3_THREADS>(S.coll, npad);
+                // masses of the sorted bucket members, 4 per thread
+                constexpr int PER = K3_COLLECT / K3_THREADS;
+                double ei[PER];
+                double loc = 0.0;
 #pragma unroll
-            for (int t = 0; t < PER; ++t) {
-                int i = tid * PER + t;
-                ei[t] = (i < n) ? (count ? 1.0 : exp((double)cval(S.coll[i]) - m)) : 0.0;
-                loc += ei[t];
-            }
-            double tot;
-            double run = above + wg_excl_scan_f64<K3_THREADS>(loc, S.scd, tot);
-            uint32_t first = NONE;
+                for (int t = 0; t < PER; ++t) {
+                    int i = tid * PER + t;
+                    ei[t] = (i < n) ? (count ? 1.0 : exp((double)cval(S.coll[i]) - m)) : 0.0;
+                    loc += ei[t];
+                }
+                double tot;
+                double run = above + wg_excl_scan_f64<K3_THREADS>(loc, S.scd, tot);
+                uint32_t first = NONE;
 #pragma unroll
-            for (int t = 0; t < PER; ++t) {
-                int i = tid * PER + t;
-                run += ei[t];
-                if (i < n && first == NONE && run >= target) first = (uint32_t)i;
+                for (int t = 0; t < PER; ++t) {
+                    int i = tid * PER + t;
+                    run += ei[t];
+                    if (i < n && first == NONE && run >= target) first = (uint32_t)i;
+                }
+                fi = wg_min_u32<K3_THREADS>(first, S.sc);
+                if (fi == NONE) fi = (uint32_t)(n - 1);  // rounding: whole bucket
+                // ZK: mass of every kept element = above + bucket prefix through fi
+                double sk = 0.0;
+#pragma unroll
+                for (int t = 0; t < PER; ++t) {
+                    int i = tid * PER + t;
+                    if (i <= (int)fi && i < n) sk += ei[t];
+                }
+                ZKo = above + wg_sum_f64<K3_THREADS>(sk, S.scd);
             }
-            uint32_t fi = wg_min_u32<K3_THREADS>(first, S.sc);
-            if (fi == NONE) fi = (uint32_t)(n > 0 ? n - 1 : 0);  // rounding: whole bucket
             Tst = (n > 0) ? S.coll[fi] : mkcomp(info.m, info.idx0);
             if (rk_level0 && n > 0) {
                 rk_done = true;
                 rk_fi = fi;
             }
-            // ZK: mass of every kept element = above + bucket prefix through fi
-            double s = 0.0;
-#pragma unroll
-            for (int t = 0; t < PER; ++t) {
-                int i = tid * PER + t;
-                if (i <= (int)fi && i < n) s += ei[t];
-            }
-            ZKo = above + wg_sum_f64<K3_THREADS>(s, S.scd);
         } else {
             // every bucket member has the same value: take the c members with
             // the smallest vocab ids
