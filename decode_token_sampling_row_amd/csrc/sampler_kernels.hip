@@ -2062,10 +2062,156 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     const double pZ = md.tp ? (double)md.p * Zc : 0.0;
     double at = 0.0, below = 0.0;
     bool found = false;
+    // ---- top-p without an inverse-CDF draw: K needs no order, only its
+    // least element T*, so the selection is binned by value instead of
+    // sorted.  256 bins from the top (bin 0 holds the largest values, -inf
+    // the last bin) take the masses; the first bin whose running mass
+    // reaches pZ holds T*; only its members are ranked, and K = { >= T* }
+    // is written to srt in thread order.  The bins add masses (each <= 1,
+    // the maximum's being 1) in fixed point, units of 2^-52, so that their
+    // sums do not depend on the order of the atomics: the choice of bin is
+    // then the same on every run, and off the double sums by at most nsel
+    // 2^-52.
+    const bool hist_cut = md.tp && !md.inv;
+    if (hist_cut) {
+        double e4[4];
+        uint32_t lo_key = ~0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t p = 4 * tid + i;
+            const float x = cval(v4[i]);
+            e4[i] = p < nsel ? exp((double)x - (double)x0) : 0.0;
+            if (p < nsel && x > -INFINITY) lo_key = min(lo_key, (uint32_t)(v4[i] >> 32));
+        }
+        const uint32_t kmin_sel = wg_min_u32<NT>(lo_key, S.sc);
+        const float span = kmin_sel == ~0u ? 0.0f : x0 - key2f(kmin_sel);
+        const float scale = span > 0.0f && span < INFINITY ? 256.0f / span : 0.0f;
+        uint64_t *hq = reinterpret_cast<uint64_t *>(S.addr);  // free by now
+        uint64_t *bl = reinterpret_cast<uint64_t *>(S.addr) + 256;
+        static_assert(sizeof(S.addr) >= (256 + KMAX) * sizeof(uint64_t), "bins and bucket");
+        for (int i = tid; i < 256; i += NT) {
+            hq[i] = 0ull;
+            S.hist[i] = 0u;
+        }
+        __syncthreads();
+        uint32_t bin4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = cval(v4[i]);
+            const float t = (x0 - x) * scale;
+            bin4[i] = !(x > -INFINITY) ? 255u : (t >= 255.0f ? 255u : (uint32_t)t);
+            if (4 * tid + i < nsel) {
+                atomicAdd((unsigned long long *)&hq[bin4[i]],
+                          (unsigned long long)(e4[i] * 0x1.0p52));
+                atomicAdd(&S.hist[bin4[i]], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane l sums bins 4 l .. 4 l + 3; the lane sums are scanned
+            // with every lane active, and the first lane reaching pZ walks
+            // its bins on top of the lanes before it
+            double h[4];
+            double ls = 0.0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                h[t] = (double)hq[4 * tid + t] * 0x1.0p-52;
+                ls += h[t];
+            }
+            const double incl = wave_incl_scan_f64(ls, tid);
+            const double excl = __shfl_up(incl, 1, 64);
+            const uint64_t reach = __ballot(incl >= pZ);
+            const int l = reach ? __builtin_ctzll(reach) : -1;
+            if (tid == (l < 0 ? 0 : l)) {
+                uint32_t pick = NONE;
+                double acc = tid == 0 ? 0.0 : excl, pa = 0.0;
+                if (l >= 0)
+                    for (int t = 0; t < 4; ++t) {
+                        if (h[t] > 0.0 && acc + h[t] >= pZ) {
+                            pick = (uint32_t)(4 * tid + t);
+                            pa = acc;
+                            break;
+                        }
+                        acc += h[t];
+                    }
+                S.sel[0] = pick;
+                S.fd[0] = pa;
+            }
+        }
+        __syncthreads();
+        const uint32_t bsel = S.sel[0];
+        const double above_b = S.fd[0];
+        if (bsel != NONE) {
+            // the bucket's members, ranked by the number above each
+            // (composites are distinct) into srt (the selection is in v4)
+            if (tid == 0) S.cnt = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * tid + i < nsel && bin4[i] == bsel) bl[atomicAdd(&S.cnt, 1u)] = v4[i];
+            __syncthreads();
+            const uint32_t nb = S.cnt;
+            for (uint32_t mi = tid; mi < nb; mi += NT) {
+                const uint64_t c = bl[mi];
+                uint32_t rank = 0;
+                for (uint32_t j = 0; j < nb; ++j) rank += bl[j] > c ? 1u : 0u;
+                S.srt[rank] = c;
+            }
+            __syncthreads();
+            // running mass over the sorted bucket, 4 positions per thread
+            double eb[4];
+            double lb = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                eb[i] = p < nb ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                lb += eb[i];
+            }
+            double tb;
+            double run = above_b + wg_excl_scan_f64<NT>(lb, S.scd, tb);
+            uint32_t first = NONE;
+            double a_ = 0.0, b_ = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = 4 * tid + i;
+                run += eb[i];
+                if (p < nb && first == NONE && run >= pZ) {
+                    first = p;
+                    a_ = run;
+                    b_ = run - eb[i];
+                }
+                if (p + 1 == nb && first == NONE) {  // rounding: the whole bucket
+                    a_ = run;
+                    b_ = run - eb[i];
+                }
+            }
+            const uint32_t mine = first;
+            first = wg_min_u32<NT>(first, S.sc);
+            const uint32_t fi = first == NONE ? nb - 1 : first;
+            if ((first != NONE && mine == first) || (first == NONE && fi / 4 == (uint32_t)tid)) {
+                S.fd[0] = a_;
+                S.fd[1] = b_;
+            }
+            __syncthreads();
+            const uint64_t tstar = S.srt[fi];
+            found = true;
+            at = S.fd[0];
+            below = S.fd[1];
+            __syncthreads();  // srt is rewritten below
+            uint32_t kc = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kc += (4 * tid + i < nsel && v4[i] >= tstar) ? 1u : 0u;
+            uint32_t off = wg_excl_scan_u32<NT>(kc, S.sc, nK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * tid + i < nsel && v4[i] >= tstar) S.srt[off++] = v4[i];
+            __syncthreads();
+        }
+    }
     // ---- top-p, step 1: a short prefix (the usual case).  Small selections
     // take their 4 largest from one wave reduction; larger ones up to
     // NUC_STEPS maxima, one at a time, by the workgroup.
-    if (md.tp) {
+    if (md.tp && !hist_cut) {
         if (small) {
             if (tid < 64) {
                 uint64_t t4[4];
@@ -2128,7 +2274,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // number of keys above it (a binary search; composite keys are distinct
     // and never 0, so 0 pads).  Then, for top-p, the shortest prefix whose
     // running mass (in double) reaches pZ.
-    if (md.tp ? !found : (md.inv && nsel > 1)) {
+    if (!hist_cut && (md.tp ? !found : (md.inv && nsel > 1))) {
         uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};
         wave_bitonic_desc256(w);
         if (small) {
