@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace smp {
@@ -138,6 +139,52 @@ constexpr int est_run_start(int s, int b, int V) {
     const int64_t room = seg1 - seg0 - EST_SEG;  // >= 0 when V > EST_N
     const int64_t step = (room / 16) & ~(int64_t)(VEC - 1);
     return (int)(seg0 + (int64_t)((s * 5 + b * 3) & 15) * step);
+}
+
+// exp(t) for finite t <= 0 in double, by the table-driven method of P. T. P.
+// Tang (ACM Trans. Math. Softw. 15(2), 1989): with n = rint(64 t / ln 2) =
+// 64 k + j (0 <= j < 64), t = n ln2 / 64 + r, |r| <= ln2 / 128, and
+// exp(t) = 2^k 2^(j/64) exp(r), exp(r) - 1 by its Taylor polynomial of
+// degree 5 (remainder below 4e-17).  ln2 / 64 is split into a 36-bit head, exact
+// times any |n| < 2^17, and a tail.  The 64 values 2^(j/64) are rounded to
+// nearest; t below -1000 (exp(t) = 0 in double) is clamped there.  Within a
+// few units in the last place of exp for results above the subnormal range;
+// the CPU checks measure it against long-double exp.  Host and device run
+// the same IEEE operations (fma, rint, ldexp) and get the same result.
+#define SMP_EXP2_J64_VALUES \
+    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0, \
+    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0, \
+    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0, \
+    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0, \
+    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0, \
+    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0, \
+    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0, \
+    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0, \
+    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0, \
+    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0, \
+    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0, \
+    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0, \
+    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0, \
+    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0, \
+    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0, \
+    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
+constexpr double EXP_INV_L = 0x1.71547652b82fep+6;  // 64 / ln 2
+constexpr double EXP_L1 = 0x1.62e42fefa0000p-7;     // ln 2 / 64, head
+constexpr double EXP_L2 = 0x1.cf79abc9e3b3ap-46;    // ln 2 / 64 - EXP_L1
+__host__ __device__ inline double exp_neg_tab(double t, const double *tab) {
+    t = t < -1000.0 ? -1000.0 : t;
+    const double n = rint(t * EXP_INV_L);
+    double r = fma(-n, EXP_L1, t);
+    r = fma(-n, EXP_L2, r);
+    // exp(r) - 1 = r + r^2 (1/2 + r/6 + r^2/24 + r^3/120), added to the table
+    // value by one fma so that its rounding is the last
+    double s = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    s = fma(s, r, 1.0 / 6.0);
+    s = fma(s, r, 0.5);
+    const double q = fma(s, r * r, r);
+    const int ni = (int)n;
+    const double tj = tab[ni & 63];
+    return ldexp(fma(tj, q, tj), ni >> 6);
 }
 
 // Tiles per queued row of the full-row search and their length: with nq rows

@@ -2532,6 +2532,7 @@ struct FallbackShared {
     uint32_t hhi[K3_BINS];
     uint64_t coll[K3_COLLECT];
     uint64_t rk[K3_BINS];  // first level: the best race key of each bin (race_key)
+    double etab[64];       // 2^(j/64) for exp_neg_tab
     uint32_t bm[K3_SEG / 32];
     // refinement levels: level 0 bins by value, later levels by key
     float lv_lo, lv_scale;
@@ -2550,9 +2551,9 @@ struct FallbackShared {
 };
 
 __device__ __forceinline__ uint32_t bin_value(float x, float lo, float scale) {
-    float t = (x - lo) * scale;
-    if (!(t >= 0.0f)) return 0u;
-    if (t >= (float)(K3_BINS - 1)) return K3_BINS - 1;
+    // below lo (and NaN) -> 0, from K3_BINS - 1 up -> K3_BINS - 1, without
+    // branches (fmaxf of NaN and 0 is 0)
+    const float t = fminf(fmaxf((x - lo) * scale, 0.0f), (float)(K3_BINS - 1));
     return (uint32_t)t;
 }
 // Key bins of a refinement level: keys from klo on, 2^sh keys per bin (sh
@@ -2574,11 +2575,17 @@ __device__ __forceinline__ uint32_t bin_shift(uint64_t span) {
 // denominator; a non-negative double orders like its bit pattern) cut to its
 // top 43 bits (relative steps of 2^-31), then ~id in the low 21 bits, so
 // that of two ratios that agree to that precision the smaller id wins.  Ids
-// are below SAMPLER_VOCAB_MAX = 2^21.
+// are below SAMPLER_VOCAB_MAX = 2^21.  The keys only choose each bin's
+// candidate: the winner is decided afresh by exact ratios.
 constexpr int RK_ID_BITS = 21;
 static_assert((1 << RK_ID_BITS) >= SAMPLER_VOCAB_MAX, "ids fit the key's low bits");
 __device__ __forceinline__ uint64_t race_key(float x, double e, double den, uint32_t j) {
-    const double r = race_ratio(x, e, den);
+    // e times the reciprocal of den (a hardware estimate and one Newton
+    // step, good to a few units in the last place: far inside the key's
+    // 2^-31 cut), not a division
+    double y = __builtin_amdgcn_rcp(den);
+    y = fma(fma(-den, y, 1.0), y, y);
+    const double r = !(x > -INFINITY) ? 0.0 : (den == 0.0 ? (double)INFINITY : e * y);
     const uint64_t hi = (uint64_t)__double_as_longlong(r) >> RK_ID_BITS;
     return (hi << RK_ID_BITS) | (uint64_t)(~j & ((1u << RK_ID_BITS) - 1u));
 }
@@ -2858,10 +2865,14 @@ __device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
     return f;
 }
 
+__device__ const double fb_exp2_j64[64] = {SMP_EXP2_J64_VALUES};
+
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
+    if (tid < 64) S.etab[tid] = fb_exp2_j64[tid];
+    __syncthreads();
     // The rows the merge queued, spread over the workgroups.  While the
     // queue is short (T > 1), the first histogram level of the cut's search
     // of a row is split into T tiles, one workgroup each: each writes its
@@ -2939,7 +2950,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         double zt = 0.0;
         auto visit = [&](float x, uint32_t j, float qj) {
             if (!(x > -INFINITY) || mkcomp(x, j) < cfloor) return;
-            const double e = exp((double)x - m);
+            const double e = exp_neg_tab((double)x - m, S.etab);
             zt += e;
             const uint32_t bi = bin_value(x, lo, scale);
             atomicAdd(&S.hm[bi], e);
@@ -3186,7 +3197,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
-                double e = count ? 1.0 : exp((double)x - m);
+                double e = count ? 1.0 : exp_neg_tab((double)x - m, S.etab);
                 if (level == 0) zt += e;
                 uint32_t bi = (level == 0) ? bin_value(x, lo, scale) : bin_key(k, klo, sh);
                 atomicAdd(&S.hm[bi], e);

@@ -22,9 +22,17 @@
 //            within FB_TILES_MAX; the tiles of all nq rows (slots qi T + t)
 //            fit the grid, hence the partial slots the workspace holds, and
 //            every queued row's arrival counter (index qi) is below FB_GRID;
+//   exp      the table-driven exp the full-row search weighs elements
+//            with (exp_neg_tab) against long-double exp: within 1.5 units in
+//            the last place above the subnormal range, over 4 million
+//            arguments in [-745, 0] (uniform, log-spaced towards 0, and
+//            the ends of each table interval), exactly 1 at 0, and tiny
+//            (below 2^-1000) from -745 down to -1000 and beyond;
 //   prefix   the six-ballot bit-plane prefix of the staged select gives
 //            every lane the exclusive prefix of the lanes' counts (at most
 //            4 PASS_D = 32 each), so entries land in [cnt, cnt + total).
+#include <float.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -167,6 +175,34 @@ static void check_tiling(int32_t V) {
     }
 }
 
+static double exp_worst_ulp = 0.0;
+static void check_exp(std::mt19937 &rng) {
+    static const double tab[64] = {SMP_EXP2_J64_VALUES};
+    auto one = [&](double t) {
+        const double got = exp_neg_tab(t, tab);
+        const long double ref = expl((long double)t);
+        if (ref >= (long double)DBL_MIN) {
+            const double ulp = ldexp(1.0, ilogb((double)ref) - 52);
+            const double err = (double)fabsl((long double)got - ref) / ulp;
+            if (err > exp_worst_ulp) exp_worst_ulp = err;
+            CHECK(err <= 1.5, "t=%.17g got=%.17g ref=%.17Lg err=%.3g ulp", t, got, ref, err);
+        } else {
+            CHECK(got >= 0.0 && got < 0x1p-1000, "t=%.17g got=%.17g", t, got);
+        }
+    };
+    std::uniform_real_distribution<double> uni(-745.0, 0.0), lg(-30.0, 3.0);
+    for (int i = 0; i < 2000000; ++i) one(uni(rng));
+    for (int i = 0; i < 2000000; ++i) one(-pow(10.0, lg(rng)));
+    for (int n = -47000; n <= 0; ++n) {  // table interval ends
+        const double c = n * (M_LN2 / 64.0);
+        one(nextafter(c + M_LN2 / 128.0, 0.0));
+        one(c - M_LN2 / 128.0);
+    }
+    CHECK(exp_neg_tab(0.0, tab) == 1.0, "exp(0)");
+    CHECK(exp_neg_tab(-0.0, tab) == 1.0, "exp(-0)");
+    for (double t : {-745.2, -800.0, -1000.0, -1e6, -1e300}) one(t);
+}
+
 static void check_prefix(std::mt19937 &rng) {
     std::uniform_int_distribution<int> cnt(0, 32), pick(0, 5);
     for (int trial = 0; trial < 20000; ++trial) {
@@ -205,12 +241,14 @@ int main() {
     }
     std::mt19937 rng(12345);
     check_prefix(rng);
+    check_exp(rng);
     if (failures) {
         fprintf(stderr, "%d failed checks\n", failures);
         return 1;
     }
     printf("index checks ok: %zu vocab sizes, %d dense maps (%lld ids), %d tile lengths, "
-           "%lld search tilings\n",
-           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN, (long long)tilings);
+           "%lld search tilings, table exp within %.2f ulp\n",
+           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN, (long long)tilings,
+           exp_worst_ulp);
     return 0;
 }
