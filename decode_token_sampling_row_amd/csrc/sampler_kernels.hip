@@ -644,20 +644,28 @@ __device__ void bitonic_desc(uint64_t *s, int n) {
 // pair each).  npad is a power of two; every thread of the workgroup calls.
 __device__ uint64_t bitonic_regs_desc(uint64_t c, int npad, uint64_t *s) {
     const int tid = threadIdx.x;
+    // a wave holding no place below npad only joins the barriers
+    const bool busy = (tid & ~63) < npad;
     for (int k = 2; k <= npad; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t o;
-            if (j >= 64) {
-                s[tid] = c;
-                __syncthreads();
-                o = s[tid ^ j];
-                __syncthreads();
-            } else {
-                o = shx64(c, j);
-            }
+        for (int j = k >> 1; j >= 64; j >>= 1) {
+            s[tid] = c;
+            __syncthreads();
+            const uint64_t o = s[tid ^ j];
+            __syncthreads();
             const bool lower = (tid & j) == 0;
             const bool desc = (tid & k) == 0;
             c = (lower == desc) ? (o > c ? o : c) : (o < c ? o : c);
+        }
+        if (busy) {
+            // within the wave: constant lane masks (every lane active)
+#pragma unroll
+            for (int j = 32; j >= 1; j >>= 1)
+                if (j < k) {
+                    const uint64_t o = shx64(c, j);
+                    const bool lower = (tid & j) == 0;
+                    const bool desc = (tid & k) == 0;
+                    c = (lower == desc) ? (o > c ? o : c) : (o < c ? o : c);
+                }
         }
     }
     return c;
@@ -2965,12 +2973,17 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                                    [&](float x, uint32_t j) { visit(x, j, 0.0f); });
         const double zsum = wg_sum_f64<K3_THREADS>(zt, S.scd);
         const FbPart mine = fb_part(W.fbpart, it);
+        // the part goes out by device-scope stores (written through to the
+        // level every workgroup reads), so that the release below has little
+        // left to write back
         for (int i = tid; i < K3_BINS; i += K3_THREADS) {
-            mine.hm[i] = S.hm[i];
-            mine.hc[i] = S.hc[i];
-            if (rkt) mine.rk[i] = S.rk[i];
+            __hip_atomic_store(&mine.hm[i], S.hm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&mine.hc[i], S.hc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (rkt)
+                __hip_atomic_store(&mine.rk[i], S.rk[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (tid == 0) *mine.z = zsum;
+        if (tid == 0) __hip_atomic_store(mine.z, zsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the chunk summaries: 32 lanes per chunk, summed by shuffles
         static_assert(FB_CHUNK_BINS == 32, "a chunk is half a wave");
         for (int c0 = 0; c0 < FB_CHUNKS; c0 += K3_THREADS / FB_CHUNK_BINS) {
@@ -2985,8 +2998,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 ck = o > ck ? o : ck;
             }
             if (tid % FB_CHUNK_BINS == 0) {
-                mine.csum[c] = cs;
-                mine.crk[c] = ck;
+                __hip_atomic_store(&mine.csum[c], cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&mine.crk[c], ck, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         // One thread counts the arrival: its release (after the barrier that
