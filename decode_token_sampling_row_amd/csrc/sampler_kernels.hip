@@ -2028,13 +2028,15 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         mxv = v4[i] > mxv ? v4[i] : mxv;
     }
     // a sampling row without top-p keeps the whole selection: q at its
-    // entries is requested now, so that the gather overlaps what follows
+    // entries is requested now, so that the gather overlaps what follows.
+    // Every lane loads (id 0 past the selection): a load under a condition
+    // would be waited for at once.
     const bool early_q = md.sm && !md.tp;
     float qv4[4];
     if (early_q) {
         const float *rowq = P.q + (int64_t)b * P.V;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv4[i] = (4 * tid + i < nsel) ? rowq[cidx(v4[i])] : 1.0f;
+        for (int i = 0; i < 4; ++i) qv4[i] = rowq[4 * tid + i < nsel ? cidx(v4[i]) : 0u];
     }
     const uint64_t top = wg_max_u64<NT>(mxv, S.sc64);
     const float x0 = cval(top);
@@ -2450,7 +2452,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const uint32_t p = (uint32_t)(r * NT + tid);
-            qv[r] = p < nK ? P.q[(int64_t)b * P.V + cidx(kp[p])] : 1.0f;
+            const uint32_t id = p < nK ? cidx(kp[p]) : 0u;  // every lane loads
+            qv[r] = P.q[(int64_t)b * P.V + id];
         }
     }
     if (early_q) {
