@@ -102,8 +102,8 @@ size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
     off = align_up(off + sizeof(uint32_t), 256);
     const size_t o_fblist = off;
     off = align_up(off + B * sizeof(uint32_t), 256);
-    const size_t o_fbarrive = off;
-    off = align_up(off + FB_GRID * sizeof(uint32_t), 256);
+    const size_t o_fbsync = off;
+    off = align_up(off + (size_t)FB_GRID * FB_SYNC_WORDS * sizeof(uint32_t), 256);
     const size_t o_fbpart = off;
     off = align_up(off + (size_t)fb_grid((int)B) * FB_PART_BYTES, 256);
     if (base) {
@@ -118,7 +118,7 @@ size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
         w->rowlo = (float *)(base + o_rowlo);
         w->fbcnt = (uint32_t *)(base + o_fbcnt);
         w->fblist = (uint32_t *)(base + o_fblist);
-        w->fbarrive = (uint32_t *)(base + o_fbarrive);
+        w->fbsync = (uint32_t *)(base + o_fbsync);
         w->fbpart = base + o_fbpart;
     }
     return off;

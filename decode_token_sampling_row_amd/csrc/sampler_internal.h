@@ -36,6 +36,13 @@ constexpr int FB_GROUP = K3_THREADS * 4;  // elements of one step of the row pas
 // bins and the tile's total mass (padded to 256 bytes), then the mass sums
 // and largest race keys of FB_CHUNKS chunks of consecutive bins.
 constexpr int FB_CHUNKS = 64;
+// Words of a queued row's synchronisation record (fbsync).
+constexpr int FB_SYNC_WORDS = 4;
+constexpr uint32_t FB_NO_BUCKET = 0xffffffffu;  // published: the tiles collect nothing
+// Polls (one load and a short sleep each, about 1 us) a tile spends waiting
+// for the row's bucket, and the last tile for the others' collections,
+// before it gives up; giving up only costs speed.
+constexpr int FB_POLLS = 200;
 constexpr size_t FB_PART_CHUNKS = ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
 constexpr size_t FB_PART_BYTES = (FB_PART_CHUNKS + (size_t)FB_CHUNKS * 16 + 255) / 256 * 256;
 // Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
@@ -228,7 +235,9 @@ struct KWork {
     float *rowlo;     // [maxB] transformed smallest value of the estimate sample
     uint32_t *fbcnt;  // [1] rows queued for the full-row top-p search
     uint32_t *fblist; // [maxB] those rows
-    uint32_t *fbarrive; // [FB_GRID] tiles of queued row i done (zeroed by the pass)
+    uint32_t *fbsync;   // [FB_GRID][4] per queued row i (zeroed by the pass): tiles arrived,
+                        // published bucket + 1 (or FB_NO_BUCKET), tiles done collecting,
+                        // members listed
     char *fbpart;       // [fallback grid][FB_PART_BYTES] partial histograms of the tiles
 };
 

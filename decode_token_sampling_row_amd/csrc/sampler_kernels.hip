@@ -1021,7 +1021,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
 //    row to the full-row search.
 
 constexpr int PASS_THREADS = 256;
-static_assert(PASS_THREADS >= FB_GRID, "the pass zeroes one arrival counter per thread");
 constexpr int PASS_WAVES = PASS_THREADS / 64;
 constexpr int PASS_D = 8;                      // groups of 4 in flight per thread
 constexpr int PGROUP = PASS_THREADS * 4;       // elements per group row
@@ -1483,9 +1482,9 @@ __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork
         }
     const Mode md = row_mode(P, b);
     if (b == 0 && t == 0) {
-        // the full-row search queue and its tiles' arrival counters
+        // the full-row search queue and its rows' synchronisation records
         if (threadIdx.x == 0) *W.fbcnt = 0u;
-        if (threadIdx.x < FB_GRID) W.fbarrive[threadIdx.x] = 0u;
+        for (int i = threadIdx.x; i < FB_GRID * FB_SYNC_WORDS; i += PASS_THREADS) W.fbsync[i] = 0u;
     }
     const bool filtering = P.top_k || P.top_p;  // the planning kernel ran
     const float traw = filtering ? W.rowthr[b] : 0.0f;
@@ -2785,16 +2784,16 @@ __device__ __forceinline__ void row_pass_q(const KParams &P, int b, uint32_t *bm
     range_pass_q<DT, AL, XF>(P, b, 0, P.V, bm, rowq, f);
 }
 
-// Visit the elements of row b whose transformed key lies in [klo, khi]; f(x,
-// j).  A pass of one workgroup over a row is bound by its instruction count
-// and by the loads each thread keeps in flight, so the key test comes first
-// and whole chunks of KS_D groups of 4 per thread are requested at once
-// (unconditional loads); the tail of each bitmap segment goes one group per
-// thread.
+// Visit the elements of [c0, c1) of row b (c0 a multiple of 4) whose
+// transformed key lies in [klo, khi]; f(x, j).  A pass of one workgroup over
+// a row is bound by its instruction count and by the loads each thread
+// keeps in flight, so the key test comes first and whole chunks of KS_D
+// groups of 4 per thread are requested at once (unconditional loads); the
+// tail of each bitmap segment goes one group per thread.
 constexpr int KS_D = 4;
 template <int DT, bool AL, bool XF, class F>
-__device__ __forceinline__ void key_scan(const KParams &P, int b, uint32_t klo, uint32_t khi,
-                                         uint32_t *bm, F &&f) {
+__device__ __forceinline__ void key_scan(const KParams &P, int b, int c0, int c1, uint32_t klo,
+                                         uint32_t khi, uint32_t *bm, F &&f) {
     constexpr int STEP = K3_THREADS * 4;
     constexpr int CHUNK = STEP * KS_D;
     const void *rowp = row_ptr(P, DT, b);
@@ -2815,8 +2814,8 @@ __device__ __forceinline__ void key_scan(const KParams &P, int b, uint32_t klo, 
                 if (k >= klo && k <= khi) f(y, (uint32_t)(j + i));
             }
     };
-    for (int s0 = 0; s0 < P.V; s0 += K3_SEG) {
-        const int s1 = min(s0 + K3_SEG, P.V);
+    for (int s0 = c0; s0 < c1; s0 += K3_SEG) {
+        const int s1 = min(s0 + K3_SEG, c1);
         if (P.pen) build_bitmap<K3_THREADS>(bm, s0, s1 - s0, P, b);
         int base = s0;
         for (; base + CHUNK <= s1; base += CHUNK) {
@@ -2850,6 +2849,23 @@ __device__ __forceinline__ void level0_bins(float m, float rowlo, uint64_t cfloo
     if (!(scale < INFINITY)) scale = 1.0f;  // a one-value range
 }
 
+// Keys of first-level bin fb's value range, half a bin wider on each side
+// than its edges (rounding in bin_value moves an edge by far less), and 64
+// keys more (adjacent floats have adjacent keys) for bins narrower than a
+// unit in the last place of their values; bin 0 also holds everything below
+// lo (-inf included), the last bin everything up to the maximum m.
+// Membership is decided by the bin itself; the range only has to hold every
+// member.
+__device__ __forceinline__ void level0_keys(uint32_t fb, float lo, float scale, float m,
+                                            uint32_t &klo, uint32_t &khi) {
+    const float w = 1.0f / scale;
+    klo = fb == 0 ? 0u : f2key(lo + ((float)fb - 0.5f) * w);
+    khi = fb == (uint32_t)(K3_BINS - 1) ? f2key(m) : f2key(fminf(lo + ((float)fb + 1.5f) * w, m));
+    if (khi < klo) khi = klo;
+    klo = klo > 64u ? klo - 64u : 0u;
+    khi = khi < 0xffffffffu - 64u ? khi + 64u : 0xffffffffu;
+}
+
 // A tile's partial first level in the workspace: masses, race keys, counts
 // of the K3_BINS bins, its total mass, then per chunk of FB_CHUNK_BINS bins
 // (chunk c: bins K3_BINS - 1 - c FB_CHUNK_BINS down, the order in which the
@@ -2864,6 +2880,12 @@ struct FbPart {
     double *csum;
     uint64_t *crk;
 };
+// The bucket members the tiles of a row list for its last tile: in the
+// row's first part slot, once the parts are merged.
+static_assert(FB_PART_BYTES >= (size_t)K3_COLLECT * 8, "member list fits a part slot");
+__device__ __forceinline__ uint64_t *fb_members(char *base, uint32_t slot0) {
+    return reinterpret_cast<uint64_t *>(base + (size_t)slot0 * FB_PART_BYTES);
+}
 __device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
     char *p = base + (size_t)slot * FB_PART_BYTES;
     FbPart f;
@@ -3011,14 +3033,58 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
         // workgroup past the next barrier.  Only that thread touches the
         // device-wide cache state.
         __syncthreads();
+        uint32_t *sy = W.fbsync + (size_t)qi * FB_SYNC_WORDS;
         if (tid == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&W.fbarrive[qi], 1u, __ATOMIC_RELEASE,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t old =
+                __hip_atomic_fetch_add(&sy[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             if (old == ntiles - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             S.found[2] = old;
         }
         __syncthreads();
-        if (S.found[2] != ntiles - 1) continue;  // a later tile finishes the row
+        if (S.found[2] != ntiles - 1) {
+            // A later tile finishes the row.  This one waits, for at most
+            // FB_POLLS polls, for the first-level bucket the last tile
+            // publishes, collects the bucket's members in its own range and
+            // lists them in the row's first part slot (the parts are merged
+            // by then).  Giving up only leaves the collection to the last
+            // tile, which then reads the whole row itself.
+            if (tid == 0) {
+                uint32_t v = 0u;
+                for (int it = 0; it < FB_POLLS; ++it) {
+                    v = __hip_atomic_load(&sy[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (v != 0u) break;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                S.found[3] = v;
+            }
+            __syncthreads();
+            const uint32_t pub = S.found[3];
+            if (pub == 0u || pub == FB_NO_BUCKET) continue;
+            const uint32_t fbp = pub - 1u;
+            uint32_t kl, kh;
+            level0_keys(fbp, lo, scale, info.m, kl, kh);
+            if (tid == 0) S.counter = 0u;
+            __syncthreads();
+            key_scan<DT, AL, XF>(P, b, c0, c1, kl, kh, S.bm, [&](float x, uint32_t j) {
+                if (!(x > -INFINITY) || mkcomp(x, j) < cfloor) return;
+                if (bin_value(x, lo, scale) != fbp) return;
+                const uint32_t pos = atomicAdd(&S.counter, 1u);
+                if (pos < (uint32_t)K3_COLLECT) S.coll[pos] = mkcomp(x, j);
+            });
+            const uint32_t nc = min(S.counter, (uint32_t)K3_COLLECT);
+            if (tid == 0)
+                S.found[1] = __hip_atomic_fetch_add(&sy[3], nc, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const uint32_t base = S.found[1];
+            uint64_t *mem = fb_members(W.fbpart, qi * ntiles);
+            for (uint32_t i = tid; i < nc; i += K3_THREADS)
+                if (base + i < (uint32_t)K3_COLLECT) mem[base + i] = S.coll[i];
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_fetch_add(&sy[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
         // the tiles' totals, read at once and summed in tile order
         static_assert(FB_TILES_MAX <= 16, "one scratch entry per tile");
         if (tid < (int)ntiles) S.scd[tid] = *fb_part(W.fbpart, qi * ntiles + tid).z;
@@ -3256,25 +3322,15 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             above += bbefore;
             bsel = fb;
             bcnt = S.hc[fb];
+            if (merged && tid == 0) {
+                // the waiting tiles collect this bucket (or nothing)
+                __hip_atomic_store(&W.fbsync[(size_t)qi * FB_SYNC_WORDS + 1],
+                                   bcnt <= (uint32_t)K3_COLLECT ? fb + 1u : FB_NO_BUCKET,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             bklo = S.hlo[fb];
             uint32_t bkhi = S.hhi[fb];
-            if (level == 0) {
-                // keys of the bin's value range, half a bin wider on each side
-                // than its edges (rounding in bin_value moves an edge by far
-                // less), and 64 keys more (adjacent floats have adjacent
-                // keys) for bins narrower than a unit in the last place of
-                // their values; bin 0 also holds everything below lo (-inf
-                // included), the last bin everything up to the maximum.
-                // Membership is still decided by the bin itself, so a wider
-                // range is safe: it only has to hold every member.
-                const float w = 1.0f / scale;
-                bklo = fb == 0 ? 0u : f2key(lo + ((float)fb - 0.5f) * w);
-                bkhi = fb == (uint32_t)(K3_BINS - 1) ? f2key(info.m)
-                                                     : f2key(fminf(lo + ((float)fb + 1.5f) * w, info.m));
-                if (bkhi < bklo) bkhi = bklo;
-                bklo = bklo > 64u ? bklo - 64u : 0u;
-                bkhi = bkhi < 0xffffffffu - 64u ? bkhi + 64u : 0xffffffffu;
-            }
+            if (level == 0) level0_keys(fb, lo, scale, info.m, bklo, bkhi);
             bkhi_sel = bkhi;
             __syncthreads();
             if (tid == 0) {
@@ -3306,13 +3362,52 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (tid == 0) S.counter = 0;
             __syncthreads();
             // the bucket's members lie in its key range [bklo, bkhi_sel]
-            key_scan<DT, AL, XF>(P, b, bklo, bkhi_sel, S.bm, [&](float x, uint32_t j) {
+            auto collect = [&](float x, uint32_t j) {
                 if ((!count && !(x > -INFINITY)) || mkcomp(x, j) < cfloor) return;
                 uint32_t k = f2key(x);
                 if (!in_play(S, x, k, nlev)) return;
                 uint32_t pos = atomicAdd(&S.counter, 1u);
                 if (pos < (uint32_t)K3_COLLECT) S.coll[pos] = mkcomp(x, j);
-            });
+            };
+            bool whole_row = true;
+            if (pre && nlev == 1) {
+                // the bucket was published: this tile collects its own range
+                // while the others collect theirs, then their lists follow
+                // its own in coll (at most FB_POLLS polls for them)
+                const int c0 = (int)tile * ft.TL, c1 = min(c0 + ft.TL, P.V);
+                key_scan<DT, AL, XF>(P, b, c0, c1, bklo, bkhi_sel, S.bm, collect);
+                uint32_t *sy = W.fbsync + (size_t)qi * FB_SYNC_WORDS;
+                if (tid == 0) {
+                    uint32_t d = 0u;
+                    for (int it = 0; it < FB_POLLS; ++it) {
+                        d = __hip_atomic_load(&sy[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (d >= ntiles - 1) break;
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    uint32_t nl = NONE;
+                    if (d >= ntiles - 1) {
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        nl = __hip_atomic_load(&sy[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    S.found[1] = nl;
+                }
+                __syncthreads();
+                const uint32_t nl = S.found[1];
+                if (nl != NONE) {
+                    const uint32_t own = min(S.counter, (uint32_t)K3_COLLECT);
+                    const uint64_t *mem = fb_members(W.fbpart, qi * ntiles);
+                    for (uint32_t i = tid; i < nl; i += K3_THREADS)
+                        if (own + i < (uint32_t)K3_COLLECT) S.coll[own + i] = mem[i];
+                    __syncthreads();
+                    if (tid == 0) S.counter = own + nl;
+                    __syncthreads();
+                    whole_row = false;
+                } else {
+                    if (tid == 0) S.counter = 0;  // gave up: the whole row below
+                    __syncthreads();
+                }
+            }
+            if (whole_row) key_scan<DT, AL, XF>(P, b, 0, P.V, bklo, bkhi_sel, S.bm, collect);
             const int n = (int)min(S.counter, (uint32_t)K3_COLLECT);
             uint32_t fi;
             if (n <= K3_THREADS) {

@@ -177,7 +177,7 @@ static void touch_workspace(const KPlan &l, const KWork &w, int rows, int kernel
         {"rowlo", w.rowlo, (size_t)rows * sizeof(float)},
         {"fbcnt", w.fbcnt, sizeof(uint32_t)},
         {"fblist", w.fblist, (size_t)rows * sizeof(uint32_t)},
-        {"fbarrive", w.fbarrive, (size_t)FB_GRID * sizeof(uint32_t)},
+        {"fbsync", w.fbsync, (size_t)FB_GRID * FB_SYNC_WORDS * sizeof(uint32_t)},
         {"fbpart", w.fbpart, (size_t)fb_grid(rows) * FB_PART_BYTES},
     };
     const int nr = (int)(sizeof r / sizeof r[0]);
