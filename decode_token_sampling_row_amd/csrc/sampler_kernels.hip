@@ -359,8 +359,11 @@ constexpr float LN2_LO = 0x1.7f7d1cp-20f;
 // exactly as a two-term sum, ln(qa / qb) as the exponent difference times
 // ln 2 (exact products) plus the log of the mantissa ratio, which lies in
 // (0.5, 2) so that its absolute error stays at a few 1e-8.  Equal -> the
-// smaller id.
-__device__ __forceinline__ bool race_ahead_exact(float xa, float qa, uint32_t ia, float xb, float qb,
+// smaller id.  Out of line: the fast test settles nearly every comparison,
+// and the close call, inlined at each of the pass's offers, made up a sixth
+// of the library's code (code that a call fetches again after its caches
+// are flushed).
+__device__ __attribute__((noinline)) bool race_ahead_exact(float xa, float qa, uint32_t ia, float xb, float qb,
                                                  uint32_t ib) {
     const bool za = qa == 0.0f, zb = qb == 0.0f;
     if (za || zb) return (za && zb) ? ia < ib : za;
