@@ -1,7 +1,7 @@
 """Benchmark of the batched logits sampler on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
-    python bench.py --latency [--steps K] [--warmup W]
+    python bench.py --latency [--warm] [--steps K] [--warmup W]
 
 A step is one sampler_run over one batch: the whole hot path (penalty,
 temperature, top-k, softmax, top-p, exponential race, dense filtered
@@ -18,7 +18,9 @@ sample of the same rows.
 vocab 4 x 32000 up to 1024 x 262144, each with its own stage mix) and prints
 one JSON line per workload: the median, p10 and p90 per-call time from HIP
 events around each call, with a 1 GiB buffer written between calls so that
-the small workloads' inputs are not served from the 256 MB last-level cache.
+the small workloads' inputs are not served from the 256 MB last-level cache
+(with --warm, calls back to back: inputs and kernel code stay cached, as in a
+decode loop).
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--latency", action="store_true",
                     help="per-call latency of every workload (one JSON line each)")
+    ap.add_argument("--warm", action="store_true",
+                    help="with --latency: no cache flush between calls")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) a few times: "
                          "the reference for scaling HBM byte counters")
@@ -170,7 +174,8 @@ def cpu_baseline(W, cpu_rows):
 
 
 def latency(args):
-    """Per-call latency of each workload, caches flushed between calls."""
+    """Per-call latency of each workload, caches flushed between calls (or
+    warm, back to back, with --warm)."""
     import torch
 
     from decode_token_sampling_row_amd import workloads as wl
@@ -203,7 +208,8 @@ def latency(args):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for i, (a, b) in enumerate(evs):
-            flush.fill_(float(i))
+            if not args.warm:
+                flush.fill_(float(i))
             a.record(stream)
             s.run(logits, out_idx, **kw)
             b.record(stream)
@@ -219,7 +225,8 @@ def latency(args):
             "rows_per_s": W.B / (med * 1e-6), "model_bytes": int(nbytes),
             "hbm_gbps": nbytes / (med * 1e-6) / 1e9,
             "hbm_frac": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-            "caches": "1 GiB written between calls"}), flush=True)
+            "caches": "warm, calls back to back" if args.warm
+                      else "1 GiB written between calls"}), flush=True)
         s.close()
         del out_l, logits
         torch.cuda.empty_cache()
