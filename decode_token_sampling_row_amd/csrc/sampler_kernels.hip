@@ -209,6 +209,41 @@ __device__ __forceinline__ uint64_t shx64(uint64_t v, int m) {
     uint32_t lo = shx((uint32_t)v, m), hi = shx((uint32_t)(v >> 32), m);
     return ((uint64_t)hi << 32) | lo;
 }
+// The same exchange with lane ^ m on the vector ALU where gfx950 has a
+// pattern for it (DPP quad permutes, the half-row mirror, a rotation of each
+// row of 16 by 8, and the row and half-wave swaps), which avoids the LDS
+// crossbar round trip of a shuffle.  m must be a constant once the caller's
+// loops are unrolled, and every lane of the wave must be active: each lane
+// reads its partner's register.
+__device__ __forceinline__ uint32_t xlane(uint32_t v, int m) {
+    const int lane = threadIdx.x & 63;
+    switch (m) {
+        case 1:  // quad_perm [1, 0, 3, 2]
+            return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+        case 2:  // quad_perm [2, 3, 0, 1]
+            return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+        case 4: {  // lane ^ 7 (half-row mirror), then lane ^ 3 (quad_perm [3, 2, 1, 0])
+            const int t = __builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false);
+            return (uint32_t)__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xf, 0xf, false);
+        }
+        case 8:  // each row of 16 rotated by 8
+            return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+        case 16: {  // odd rows swapped with even rows
+            const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            return (lane & 16) ? r[0] : r[1];
+        }
+        case 32: {  // upper half-wave swapped with the lower
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            return (lane & 32) ? r[0] : r[1];
+        }
+        default:
+            return shx(v, m);
+    }
+}
+__device__ __forceinline__ uint64_t xlane64(uint64_t v, int m) {
+    const uint32_t lo = xlane((uint32_t)v, m), hi = xlane((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ float shxf(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ double shxd(double v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -664,7 +699,7 @@ __device__ uint64_t bitonic_regs_desc(uint64_t c, int npad, uint64_t *s) {
 #pragma unroll
             for (int j = 32; j >= 1; j >>= 1)
                 if (j < k) {
-                    const uint64_t o = shx64(c, j);
+                    const uint64_t o = xlane64(c, j);
                     const bool lower = (tid & j) == 0;
                     const bool desc = (tid & k) == 0;
                     c = (lower == desc) ? (o > c ? o : c) : (o < c ? o : c);
@@ -1558,7 +1593,7 @@ __device__ __forceinline__ void wave_top4(const uint64_t (&v)[4], uint64_t (&t)[
     for (int m = 32; m >= 1; m >>= 1) {
         uint64_t o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = shx64(t[i], m);
+        for (int i = 0; i < 4; ++i) o[i] = xlane64(t[i], m);
 #pragma unroll
         for (int i = 0; i < 4; ++i) t[i] = t[i] > o[3 - i] ? t[i] : o[3 - i];
         cx_desc(t[0], t[2]);
@@ -1581,7 +1616,7 @@ __device__ __forceinline__ void wave_bitonic_desc256(uint64_t (&v)[4]) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int e = 4 * lane + r;
-                    const uint64_t o = shx64(v[r], j >> 2);
+                    const uint64_t o = xlane64(v[r], j >> 2);
                     // in a descending block the lower index keeps the larger key
                     const bool keep_max = ((e & k) == 0) == ((e & j) == 0);
                     v[r] = keep_max ? (o > v[r] ? o : v[r]) : (o < v[r] ? o : v[r]);
@@ -1935,6 +1970,12 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // k-th value); a group too large for the list goes to the full-row
     // search with the k-th value as its floor
     const bool ties = md.tk && (P.flags & TOPK_TIES) != 0;
+    // at most one wave's worth of candidates (the usual case for small k):
+    // each is placed by counting the candidates above it instead of the
+    // radix passes, and the selection, a prefix of the ordered candidates,
+    // comes out in the row's order, so top-p below is a single scan
+    const bool sorted = inreg && !ties && N <= (uint32_t)WAVE_TOPP;
+    static_assert(WAVE_TOPP <= NT && WAVE_TOPP + 8 <= KMAX, "one candidate per thread, padded list");
     bool to_search = false;
     uint32_t kmin = 0;  // value key of the k-th largest (ties rows)
     constexpr int R = RCAP / NT;
@@ -1965,7 +2006,29 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.ZK = Z;
     info.m = M;
     info.xmin = XMIN;
-    if (inreg) {
+    if (sorted) {
+        // candidate e is v[0] of thread e; its place in the order is the
+        // number of candidates above it (composites are distinct), counted
+        // over broadcast reads of all of them, 8 per step (zero pads count
+        // for nothing: no composite is 0)
+        const uint32_t n8 = (N + 7u) & ~7u;
+        if ((uint32_t)tid < N) S.srt[tid] = v[0];
+        else if ((uint32_t)tid < n8) S.srt[tid] = 0ull;
+        __syncthreads();
+        uint32_t place = 0;
+        if ((uint32_t)tid < N) {
+            const uint64_t c = v[0];
+            for (uint32_t j = 0; j < n8; j += 8) {
+                uint64_t u[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) u[i] = S.srt[j + i];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) place += u[i] > c ? 1u : 0u;
+            }
+        }
+        __syncthreads();
+        if ((uint32_t)tid < N && place < nsel) S.srt[place] = v[0];
+    } else if (inreg) {
         uint32_t km = vm;
         if (N > kk) {
             uint64_t prefix, pmask;
@@ -2084,7 +2147,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // sums do not depend on the order of the atomics: the choice of bin is
     // then the same on every run, and off the double sums by at most nsel
     // 2^-52.
-    const bool hist_cut = md.tp && !md.inv;
+    const bool hist_cut = md.tp && !md.inv && !sorted;
     if (hist_cut) {
         double e4[4];
         uint32_t lo_key = ~0u;
@@ -2223,7 +2286,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // ---- top-p, step 1: a short prefix (the usual case).  Small selections
     // take their 4 largest from one wave reduction; larger ones up to
     // NUC_STEPS maxima, one at a time, by the workgroup.
-    if (md.tp && !hist_cut) {
+    if (md.tp && !hist_cut && !sorted) {
         if (small) {
             if (tid < 64) {
                 uint64_t t4[4];
@@ -2288,7 +2351,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // running mass (in double) reaches pZ.
     if (!hist_cut && (md.tp ? !found : (md.inv && nsel > 1))) {
         uint64_t w[4] = {v4[0], v4[1], v4[2], v4[3]};
-        wave_bitonic_desc256(w);
+        if (!sorted) wave_bitonic_desc256(w);
         if (small) {
             if (tid < 64) {
 #pragma unroll
