@@ -25,7 +25,8 @@ struct Config {
     int32_t dtype;
     int32_t guess;
     int32_t seg;
-    int32_t cus;  // compute units of the device
+    bool seg_auto;  // the tile length is chosen per call (auto_seg)
+    int32_t cus;    // compute units of the device
 };
 
 struct sampler_s {
@@ -59,6 +60,7 @@ int make_config(Config &c, int32_t max_batch, int32_t vocab, int32_t dtype,
     c.dtype = dtype;
     c.guess = DEFAULT_GUESS;
     c.seg = SEG_DEFAULT;
+    c.seg_auto = true;
     c.rows_per_launch = 0;
     c.cus = 1;
     if (opts) {
@@ -69,23 +71,30 @@ int make_config(Config &c, int32_t max_batch, int32_t vocab, int32_t dtype,
             return SAMPLER_EINVAL;
         if (opts->rows_per_launch < 0) return SAMPLER_EINVAL;
         if (opts->topk_guess) c.guess = opts->topk_guess;
-        if (opts->segment_len) c.seg = opts->segment_len;
+        if (opts->segment_len) {
+            c.seg = opts->segment_len;
+            c.seg_auto = false;
+        }
         c.rows_per_launch = opts->rows_per_launch;
     }
     return SAMPLER_OK;
 }
 
-// The workspace of B rows laid out from base (null: only sized).  Returns its
-// size in bytes.
-size_t layout_workspace(size_t B, const KPlan &plan, char *base, KWork *w) {
+// The tile length of a call of batch rows.
+int32_t call_seg(const Config &c, int32_t batch) {
+    return c.seg_auto ? auto_seg(batch, c.vocab, c.cus) : c.seg;
+}
+
+// The workspace of B rows and `tiles` (row, tile) records laid out from base
+// (null: only sized).  Returns its size in bytes.
+size_t layout_workspace(size_t B, size_t tiles, const KPlan &plan, char *base, KWork *w) {
     size_t off = 0;
-    const size_t NTL = (size_t)plan.nt * 4;  // wave sub-slots per row
     const size_t o_cand = off;
     off = align_up(off + B * ROWCAP * sizeof(uint64_t), 256);
     const size_t o_wcnt = off;
-    off = align_up(off + B * NTL * sizeof(uint32_t), 256);
+    off = align_up(off + tiles * 4 * sizeof(uint32_t), 256);  // one per wave sub-slot
     const size_t o_cstat = off;
-    off = align_up(off + B * NTL * sizeof(ChunkStat), 256);
+    off = align_up(off + tiles * 4 * sizeof(ChunkStat), 256);
     const size_t o_info = off;
     off = align_up(off + B * sizeof(RowInfo), 256);
     const size_t o_klist = off;
@@ -186,7 +195,7 @@ int run_call(const Config &c, const KWork &ws, int32_t batch, const sampler_args
     p.guess = c.guess;
     p.pen = (a->repetition_penalty != 1.0f && a->penalty_ids != nullptr) ? 1 : 0;
 
-    const KPlan l = make_plan(c.vocab, c.seg, c.cus);
+    const KPlan l = make_plan(c.vocab, call_seg(c, batch), c.cus);
     const int esize = c.dtype == SAMPLER_BF16 ? 2 : 4;
     const bool al = aligned16(a->logits) && ((a->ld * esize) % 16) == 0 &&
                     (c.vocab % 4) == 0 && (a->q == nullptr || aligned16(a->q)) &&
@@ -289,8 +298,12 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
     }
     if (cfg.cus < 1) cfg.cus = 1;
     s->cfg = cfg;
+    // tile records for every batch up to max_batch, at the fixed tile length
+    // or at any the call may choose (auto_seg)
     const KPlan plan = make_plan(vocab, cfg.seg, cfg.cus);
-    const size_t bytes = layout_workspace((size_t)max_batch, plan, nullptr, nullptr);
+    size_t tiles = (size_t)max_batch * (size_t)plan.nt;
+    if (cfg.seg_auto) tiles = std::max(tiles, (size_t)AUTO_WG_PER_CU * (size_t)cfg.cus);
+    const size_t bytes = layout_workspace((size_t)max_batch, tiles, plan, nullptr, nullptr);
     void *base = nullptr;
     hipError_t e = hipMalloc(&base, bytes);
     if (e != hipSuccess) {
@@ -299,7 +312,7 @@ int sampler_create(sampler_t **h, int32_t max_batch, int32_t vocab, int32_t dtyp
         return e == hipErrorOutOfMemory ? SAMPLER_ENOMEM : SAMPLER_EHIP;
     }
     s->ws_base = base;
-    (void)layout_workspace((size_t)max_batch, plan, (char *)base, &s->ws);
+    (void)layout_workspace((size_t)max_batch, tiles, plan, (char *)base, &s->ws);
     s->events_made = false;
     s->events_ok = false;
     s->nprof = 0;
@@ -355,13 +368,14 @@ int sampler_run_static(int32_t batch, int32_t vocab, int32_t dtype, const sample
             hipSuccess)
         return SAMPLER_EHIP;
     if (cfg.cus < 1) cfg.cus = 1;
-    const KPlan plan = make_plan(vocab, cfg.seg, cfg.cus);
-    const size_t bytes = layout_workspace((size_t)batch, plan, nullptr, nullptr);
+    const KPlan plan = make_plan(vocab, call_seg(cfg, batch), cfg.cus);
+    const size_t tiles = (size_t)batch * (size_t)plan.nt;
+    const size_t bytes = layout_workspace((size_t)batch, tiles, plan, nullptr, nullptr);
     if (bytes > (size_t)SAMPLER_STATIC_SCRATCH_BYTES) return SAMPLER_EINVAL;
     void *base = nullptr;
     if (static_scratch(device, &base) != hipSuccess) return SAMPLER_EHIP;
     KWork ws;
-    (void)layout_workspace((size_t)batch, plan, (char *)base, &ws);
+    (void)layout_workspace((size_t)batch, tiles, plan, (char *)base, &ws);
     Marks mk;
     mk.ev = nullptr;
     mk.launched = nullptr;

@@ -127,6 +127,27 @@ constexpr KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
     return l;
 }
 
+// The tile length of a call whose handle leaves it automatic: the shortest
+// multiple of SEG_MIN below SEG_DEFAULT whose grid of batch x tiles stays
+// within AUTO_WG_PER_CU workgroups per compute unit with at most
+// AUTO_TILES_MAX tiles per row; SEG_DEFAULT when none does.  Small batches
+// then spread each row over more compute units (the pass of a row of 32000
+// runs on 32 workgroups instead of 4).  With at most AUTO_TILES_MAX tiles, a
+// wave's share of the row's candidate capacity stays at least
+// ROWCAP / (4 AUTO_TILES_MAX) = 32 entries.  Below SEG_DEFAULT a call has at
+// most AUTO_WG_PER_CU cus tile records, so a workspace laid out for
+// max(max_batch x tiles at SEG_DEFAULT, AUTO_WG_PER_CU cus) records serves
+// every batch up to max_batch.
+constexpr int AUTO_WG_PER_CU = 4;
+constexpr int AUTO_TILES_MAX = 64;
+constexpr int32_t auto_seg(int32_t batch, int32_t vocab, int32_t cus) {
+    for (int32_t s = SEG_MIN; s < SEG_DEFAULT; s += SEG_MIN) {
+        const int64_t nt = ((int64_t)vocab + s - 1) / s;
+        if (nt <= AUTO_TILES_MAX && (int64_t)batch * nt <= (int64_t)AUTO_WG_PER_CU * cus) return s;
+    }
+    return SEG_DEFAULT;
+}
+
 // Dense writer tiles: group-row g (DGR elements) of a row belongs to tile
 // g mod ntd, at position (g / ntd) DGR inside it.
 constexpr int DGR_LOG2 = 11;

@@ -97,8 +97,11 @@ typedef struct sampler_opts {
      * runs).  0 = default (256); otherwise 1..1024. */
     int32_t topk_guess;
     /* Elements per tile of the streaming pass (one workgroup per tile; the
-     * Ascend page's rolling top-k uses segments of 8192).  0 = default
-     * (8192); otherwise a multiple of 1024 in [1024, 32768]. */
+     * Ascend page's rolling top-k uses segments of 8192).  0 = automatic:
+     * each call takes the shortest multiple of 1024 below 8192 for which
+     * batch x tiles stays within 4 workgroups per compute unit and a row has
+     * at most 64 tiles, else 8192 (small batches spread their rows over more
+     * of the device); otherwise a multiple of 1024 in [1024, 32768]. */
     int32_t segment_len;
     /* Most rows per kernel launch: a call with more rows runs each kernel
      * over consecutive chunks of rows (in order, on the same stream).  0 =
@@ -175,7 +178,7 @@ typedef struct sampler_args {
  * Create a handle for batches of at most max_batch rows of vocab V logits of
  * the given storage type on the current HIP device (the Ascend page's
  * parameter list: logits [batch, voc_size] of float32 or bfloat16).  Allocates the device
- * workspace (about 80 KiB per row at the default segment length).  opts
+ * workspace (about 80 KiB per row at 8192-element tiles).  opts
  * may be NULL.
  * Returns SAMPLER_OK and sets *h, SAMPLER_EINVAL for bad arguments
  * (max_batch < 1, V < 1 or > SAMPLER_VOCAB_MAX, unknown dtype, bad opts),

@@ -437,7 +437,8 @@ static void run_case(int B, int V, int dtype, const sampler_opts *opts, bool fil
             if (rc == SAMPLER_EINVAL) {
                 // only when the workspace of B rows exceeds the static area
                 const KPlan l = make_plan(V, opts && opts->segment_len ? opts->segment_len
-                                                                       : SEG_DEFAULT, cus);
+                                                                       : auto_seg(B, V, cus),
+                                          cus);
                 CHECK((size_t)B * ROWCAP * 8 > (size_t)SAMPLER_STATIC_SCRATCH_BYTES / 2 ||
                           l.nt > 64,
                       "static path refused B=%d V=%d", B, V);

@@ -37,6 +37,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <random>
 #include <vector>
 
@@ -99,6 +100,40 @@ static void check_plans(const std::vector<int32_t> &vs) {
             CHECK(rows_lds_words(l) >= 4 * l.nt + 1 && rows_lds_words(l) >= l.ntd + 1,
                   "V=%d seg=%d", V, seg);
         }
+}
+
+// The automatic tile length: a multiple of SEG_MIN up to SEG_DEFAULT; below
+// SEG_DEFAULT the grid stays within AUTO_WG_PER_CU workgroups per CU with at
+// most AUTO_TILES_MAX tiles per row, it is the shortest such length, and the
+// call's tile records fit the handle's workspace bound.
+static int64_t auto_cases = 0;
+
+static void check_auto_seg(const std::vector<int32_t> &vs) {
+    const int32_t batches[] = {1, 2, 3, 4, 7, 16, 64, 100, 256, 1000, 1024, 4096};
+    const int32_t cuss[] = {1, 80, 256, 304};
+    for (int32_t cu : cuss)
+        for (int32_t V : vs)
+            for (int32_t B : batches) {
+                const int32_t s = auto_seg(B, V, cu);
+                CHECK(s >= SEG_MIN && s <= SEG_DEFAULT && s % SEG_MIN == 0, "B=%d V=%d seg=%d", B,
+                      V, s);
+                const KPlan l = make_plan(V, s, cu);
+                if (s < SEG_DEFAULT) {
+                    CHECK(l.nt <= AUTO_TILES_MAX && (int64_t)B * l.nt <= (int64_t)AUTO_WG_PER_CU * cu,
+                          "B=%d V=%d seg=%d nt=%d", B, V, s, l.nt);
+                    CHECK(l.wcap >= ROWCAP / (4 * AUTO_TILES_MAX), "B=%d V=%d wcap=%d", B, V, l.wcap);
+                }
+                for (int32_t t = SEG_MIN; t < s; t += SEG_MIN) {
+                    const KPlan lt = make_plan(V, t, cu);
+                    CHECK(lt.nt > AUTO_TILES_MAX || (int64_t)B * lt.nt > (int64_t)AUTO_WG_PER_CU * cu,
+                          "B=%d V=%d: %d fits before %d", B, V, t, s);
+                }
+                // the handle's bound, for any max_batch >= B
+                const KPlan ld = make_plan(V, SEG_DEFAULT, cu);
+                const int64_t bound = std::max((int64_t)B * ld.nt, (int64_t)AUTO_WG_PER_CU * cu);
+                CHECK((int64_t)B * l.nt <= bound, "B=%d V=%d records", B, V);
+                ++auto_cases;
+            }
 }
 
 // Every id of a row of V maps into its tile, inside DTILE, and no two ids
@@ -231,6 +266,7 @@ static void check_prefix(std::mt19937 &rng) {
 int main() {
     const std::vector<int32_t> vs = vocab_set();
     check_plans(vs);
+    check_auto_seg(vs);
     int ndense = 0;
     for (size_t i = 0; i < vs.size(); ++i) {
         const int32_t V = vs[i];
@@ -247,8 +283,8 @@ int main() {
         return 1;
     }
     printf("index checks ok: %zu vocab sizes, %d dense maps (%lld ids), %d tile lengths, "
-           "%lld search tilings, table exp within %.2f ulp\n",
-           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN, (long long)tilings,
-           exp_worst_ulp);
+           "%lld automatic tile choices, %lld search tilings, table exp within %.2f ulp\n",
+           vs.size(), ndense, (long long)dense_ids, SEG_MAX / SEG_MIN, (long long)auto_cases,
+           (long long)tilings, exp_worst_ulp);
     return 0;
 }
