@@ -2103,7 +2103,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
 #pragma unroll
         for (int i = 0; i < 4; ++i) qv4[i] = rowq[4 * tid + i < nsel ? cidx(v4[i]) : 0u];
     }
-    const uint64_t top = wg_max_u64<NT>(mxv, S.sc64);
+    // (an ordered selection starts with its maximum)
+    const uint64_t top = sorted ? S.srt[0] : wg_max_u64<NT>(mxv, S.sc64);
     const float x0 = cval(top);
     if (to_search) {
         info.kind = KIND_FALLBACK;
@@ -2117,9 +2118,12 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         return;
     }
     double loc = 0.0;
+    double e4s[4];  // the masses of this thread's positions (0 past nsel)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (4 * tid + i < nsel) loc += exp((double)cval(v4[i]) - (double)x0);
+    for (int i = 0; i < 4; ++i) {
+        e4s[i] = 4 * tid + i < nsel ? exp((double)cval(v4[i]) - (double)x0) : 0.0;
+        loc += e4s[i];
+    }
     const double tot_e = wg_sum_f64<NT>(loc, S.scd);
     double Zc;
     if (md.tk) Zc = tot_e;
@@ -2391,7 +2395,9 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 double l = 0.0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e[i] = 4 * tid + i < nsel ? exp((double)cval(w[i]) - (double)x0) : 0.0;
+                    // an ordered selection has these masses already
+                    e[i] = sorted ? e4s[i]
+                                  : (4 * tid + i < nsel ? exp((double)cval(w[i]) - (double)x0) : 0.0);
                     l += e[i];
                 }
                 double inc = l;
