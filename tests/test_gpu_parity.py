@@ -102,7 +102,7 @@ def _all_combos(B):
     return (np.arange(B) % 8).astype(np.uint8)
 
 
-@pytest.mark.parametrize("V", [1, 2, 5, 63, 64, 65, 1000, 2047, 2048, 2049])
+@pytest.mark.parametrize("V", [1, 2, 5, 63, 64, 65, 256, 257, 1000, 2047, 2048, 2049])
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 def test_tiny_and_ragged_vocab(V, dtype):
     rng = np.random.default_rng(V)
@@ -189,6 +189,46 @@ def test_knobs_do_not_change_results(guess, seg):
     # probabilities are a floating-point output: the row normaliser is summed
     # in a tile-dependent order
     np.testing.assert_allclose(base["probs"], other["probs"], rtol=1e-6, atol=1e-12)
+
+
+@pytest.mark.parametrize("B", [1, 32, 33, 200])
+def test_automatic_tile_length_across_batches(B):
+    """With the tile length left automatic, a call's batch picks it: at
+    V = 32000 on a 256-CU device, tiles of 1024 up to 32 rows, 2048 at 33
+    rows, 7168 at 200 rows (a length that is not a power of two).  Every row against the
+    oracle, and bit-identical to fixed 8192-element tiles."""
+    rng = np.random.default_rng(300 + B)
+    V = 32000
+    x = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+    k = rng.integers(0, 1025, size=B)
+    p = rng.uniform(0.3, 1.0, size=B)
+    W = _custom(x, top_k=k, top_p=p, flags=_all_combos(B), seed=301)
+    hip, _ = _check(W, f"automatic tiles B={B}")
+    fixed = run_hip(W, need_logits=True, need_probs=True, seg=8192)
+    np.testing.assert_array_equal(hip["idx"], fixed["idx"])
+    np.testing.assert_array_equal(hip["logits"].view(np.uint32), fixed["logits"].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("draw", ["race", "inverse"])
+def test_small_candidate_sets_with_ties(dtype, draw):
+    """Small k, where the row merge places at most 256 candidates by
+    counting: values on a coarse grid put many equal values around the k-th
+    and inside the nucleus, so the order among them is the vocab id's."""
+    rng = np.random.default_rng(77 if dtype == wl.F32 else 78)
+    ks = [1, 2, 3, 17, 50, 120]
+    ps = [0.3, 0.8, 0.97, 1.0]
+    B, V = len(ks) * len(ps), 12000
+    x = np.round(rng.standard_normal((B, V)) * 4.0) / 4.0
+    k = np.repeat(ks, len(ps))
+    p = np.tile(ps, len(ks)).astype(np.float32)
+    W = _custom(x.astype(np.float32), top_k=k, top_p=p, flags=7, dtype=dtype, seed=79)
+    u = rng.random(B).astype(np.float32) if draw == "inverse" else None
+    print(f"[case] small candidate sets with ties {dtype} {draw} B={B} V={V}", flush=True)
+    hip = run_hip(W, need_logits=True, need_probs=True, u=u, drop_q=u is not None)
+    ref = run_oracle(W, need_logits=True, need_probs=True, u=u)
+    _log(f"small sets {dtype} {draw}", compare(W, hip, ref, label="small sets",
+                                               inverse=u is not None))
 
 
 @pytest.mark.parametrize("rpl", [1, 5])
