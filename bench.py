@@ -111,15 +111,28 @@ def model_bytes(W, kept):
             "k_epilogue": 0}
 
 
+def device_source_sha():
+    """sha256 over the sources the kernels are compiled from, in this order:
+    csrc/sampler_kernels.hip, csrc/sampler_internal.h, include/sampler.h."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in (("decode_token_sampling_row_amd", "csrc", "sampler_kernels.hip"),
+                ("decode_token_sampling_row_amd", "csrc", "sampler_internal.h"),
+                ("include", "sampler.h")):
+        with open(os.path.join(ROOT, *rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def counted_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading), or
-    None when no summary covers it or the kernel source changed since."""
+    None when no summary covers it or the device code changed since (the
+    hash covers every source the kernels are compiled from)."""
     import glob
-    import hashlib
 
-    src = os.path.join(ROOT, "decode_token_sampling_row_amd", "csrc", "sampler_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = device_source_sha()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         txt = open(path).read()
         m_sha = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", txt, re.M)

@@ -46,7 +46,7 @@ constexpr int FB_POLLS = 200;
 constexpr size_t FB_PART_CHUNKS = ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
 constexpr size_t FB_PART_BYTES = (FB_PART_CHUNKS + (size_t)FB_CHUNKS * 16 + 255) / 256 * 256;
 // Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
-constexpr int DGR_PER_TILE = 4;
+constexpr int DGR_PER_TILE = 2;
 
 // Row kinds written by the merge kernel.
 enum RowKind : int32_t {
