@@ -1558,7 +1558,12 @@ constexpr int NUC_STEPS = 16;    // top-p prefixes found without a sort, at most
 constexpr int WAVE_TOPP = 256;   // selections this small: top-p by one wave, in registers
 constexpr int WAVE_NUC = 4;      // maxima the wave looks at before it sorts (fixed: 4)
 
+// 2^(j/64), j = 0..63: the table of exp_neg_tab, copied to LDS by the
+// kernels that use it
+__device__ const double exp2_j64_tab[64] = {SMP_EXP2_J64_VALUES};
+
 struct RowsShared {
+    double etab[64];          // exp2_j64_tab
     uint32_t addr[RCAP];      // slot address of each candidate (in-register path)
     uint64_t srt[KMAX];       // the kk selected
     uint64_t nuc[NUC_STEPS];  // a short top-p prefix, in order
@@ -1724,14 +1729,14 @@ __device__ __forceinline__ void radix_select_any(uint32_t n, uint32_t kk, G &&ge
 // total short of the target.  Every thread returns it.
 template <int NT>
 __device__ __forceinline__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t n, float x0, float u, double *scd,
-                                    uint32_t *sc) {
+                                    uint32_t *sc, const double *etab) {
     if (!(u > 0.0f) || n <= 1) return 0u;
     double e[4];
     double loc = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t p = 4 * threadIdx.x + i;
-        e[i] = p < n ? exp((double)cval(a[p]) - (double)x0) : 0.0;
+        e[i] = p < n ? exp_neg_tab((double)cval(a[p]) - (double)x0, etab) : 0.0;
         loc += e[i];
     }
     double tot;
@@ -1843,6 +1848,8 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     constexpr int NT = ROWS_THREADS;
     const int tid = threadIdx.x;
     const int b = P.b0 + xcd_row(blockIdx.x, gridDim.x);
+    // (read after the barriers that precede every use)
+    if (tid < 64) S.etab[tid] = exp2_j64_tab[tid];
     const Mode md = row_mode(P, b);
     const bool filtered = md.tk || md.tp;
     const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
@@ -1877,7 +1884,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         double z_loc = 0.0;
         for (int t = tid; t < nt; t += NT) {
             const ChunkStat cs = cst[t];
-            if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
+            if (cs.z != 0.0) z_loc += cs.z * exp_neg_tab((double)cs.m - (double)M, S.etab);
         }
         Z = wg_sum_f64<NT>(z_loc, S.scd);
     };
@@ -2121,13 +2128,13 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     double e4s[4];  // the masses of this thread's positions (0 past nsel)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        e4s[i] = 4 * tid + i < nsel ? exp((double)cval(v4[i]) - (double)x0) : 0.0;
+        e4s[i] = 4 * tid + i < nsel ? exp_neg_tab((double)cval(v4[i]) - (double)x0, S.etab) : 0.0;
         loc += e4s[i];
     }
     const double tot_e = wg_sum_f64<NT>(loc, S.scd);
     double Zc;
     if (md.tk) Zc = tot_e;
-    else Zc = (Z != 0.0) ? Z * exp((double)M - (double)x0) : tot_e;
+    else Zc = (Z != 0.0) ? Z * exp_neg_tab((double)M - (double)x0, S.etab) : tot_e;
 
     // ---- top-p.  The kept set is the shortest prefix, in the order, whose
     // mass reaches p Zc.  Selections of at most WAVE_TOPP entries are sorted
@@ -2159,7 +2166,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         for (int i = 0; i < 4; ++i) {
             const uint32_t p = 4 * tid + i;
             const float x = cval(v4[i]);
-            e4[i] = p < nsel ? exp((double)x - (double)x0) : 0.0;
+            e4[i] = e4s[i];  // the softmax total's masses (0 past nsel)
             if (p < nsel && x > -INFINITY) lo_key = min(lo_key, (uint32_t)(v4[i] >> 32));
         }
         const uint32_t kmin_sel = wg_min_u32<NT>(lo_key, S.sc);
@@ -2243,7 +2250,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t p = 4 * tid + i;
-                eb[i] = p < nb ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                eb[i] = p < nb ? exp_neg_tab((double)cval(S.srt[p]) - (double)x0, S.etab) : 0.0;
                 lb += eb[i];
             }
             double tb;
@@ -2301,7 +2308,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 for (int it = 0; it < WAVE_NUC; ++it) {
                     if (nfound || (uint32_t)it >= nsel) break;
                     prev = cum;
-                    cum += exp((double)cval(t4[it]) - (double)x0);
+                    cum += exp_neg_tab((double)cval(t4[it]) - (double)x0, S.etab);
                     if (tid == 0) S.nuc[it] = t4[it];
                     if (cum >= pZ) nfound = it + 1;
                 }
@@ -2331,7 +2338,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (v4[i] == mx && 4 * tid + i < nsel) rem |= 1u << i;
-                const double em = exp((double)cval(mx) - (double)x0);
+                const double em = exp_neg_tab((double)cval(mx) - (double)x0, S.etab);
                 below = cum;
                 cum += em;
                 if (tid == 0) S.nuc[it] = mx;
@@ -2397,7 +2404,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                 for (int i = 0; i < 4; ++i) {
                     // an ordered selection has these masses already
                     e[i] = sorted ? e4s[i]
-                                  : (4 * tid + i < nsel ? exp((double)cval(w[i]) - (double)x0) : 0.0);
+                                  : (4 * tid + i < nsel ? exp_neg_tab((double)cval(w[i]) - (double)x0, S.etab) : 0.0);
                     l += e[i];
                 }
                 double inc = l;
@@ -2443,7 +2450,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t p = 4 * tid + i;
-                e[i] = p < nsel ? exp((double)cval(S.srt[p]) - (double)x0) : 0.0;
+                e[i] = p < nsel ? exp_neg_tab((double)cval(S.srt[p]) - (double)x0, S.etab) : 0.0;
                 l2 += e[i];
             }
             double t2;
@@ -2507,7 +2514,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     // the sorted selection, or the short prefix in S.nuc)
     uint32_t inv_pos = 0;
     if (md.inv)
-        inv_pos = inverse_cdf_pos<NT>(use_nuc ? S.nuc : S.srt, nK, x0, P.u[b], S.scd, S.sc);
+        inv_pos = inverse_cdf_pos<NT>(use_nuc ? S.nuc : S.srt, nK, x0, P.u[b], S.scd, S.sc, S.etab);
 
     // ---- exponential race over K (or greedy), and the kept list
     const uint64_t *kp = use_nuc ? S.nuc : S.srt;
@@ -2533,7 +2540,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         for (int i = 0; i < 4; ++i)
             if (4 * tid + i < nsel) {
                 const uint32_t id = cidx(v4[i]);
-                const double ei = exp((double)cval(v4[i]) - (double)x0);
+                const double ei = e4s[i];
                 const double rr = race_ratio(cval(v4[i]), ei, (double)qv4[i] + (double)P.eps);
                 if (rr > rbest || (rr == rbest && id < ibest)) {
                     rbest = rr;
@@ -2582,7 +2589,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
         if (p < nK) {
             const uint64_t v = kp[p];
             const uint32_t id = cidx(v);
-            const double ei = exp((double)cval(v) - (double)x0);
+            const double ei = exp_neg_tab((double)cval(v) - (double)x0, S.etab);
             zk += ei;
             if (md.sm && !early_q) {
                 const double rr = race_ratio(cval(v), ei, (double)qv[r] + (double)P.eps);
@@ -2970,13 +2977,12 @@ __device__ __forceinline__ FbPart fb_part(char *base, uint32_t slot) {
     return f;
 }
 
-__device__ const double fb_exp2_j64[64] = {SMP_EXP2_J64_VALUES};
 
 template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWork W) {
     __shared__ FallbackShared S;
     const int tid = threadIdx.x;
-    if (tid < 64) S.etab[tid] = fb_exp2_j64[tid];
+    if (tid < 64) S.etab[tid] = exp2_j64_tab[tid];
     __syncthreads();
     // The rows the merge queued, spread over the workgroups.  While the
     // queue is short (T > 1), the first histogram level of the cut's search
