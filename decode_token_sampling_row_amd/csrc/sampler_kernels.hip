@@ -1761,7 +1761,7 @@ __device__ __forceinline__ uint32_t inverse_cdf_pos(const uint64_t *a, uint32_t 
 template <int NT>
 __device__ __forceinline__ void merge_unfiltered(const KParams &P, const KPlan &L, const KWork &W, int b,
                                  const Mode &md, double *scd, uint64_t *sc64, float *scx,
-                                 float *scq, uint32_t *sci) {
+                                 float *scq, uint32_t *sci, const double *etab) {
     static_assert(NT / 64 <= 16, "scratch of 16 entries");
     const int tid = threadIdx.x;
     const int nt = L.nt * PASS_WAVES;  // wave records (sub-slots) of the row
@@ -1791,7 +1791,7 @@ __device__ __forceinline__ void merge_unfiltered(const KParams &P, const KPlan &
     double z_loc = 0.0;
     for (int t = tid; t < nt; t += NT) {
         const ChunkStat cs = cst[t];
-        if (cs.z != 0.0) z_loc += cs.z * exp((double)cs.m - (double)M);
+        if (cs.z != 0.0) z_loc += cs.z * exp_neg_tab((double)cs.m - (double)M, etab);
     }
     const double Z = wg_sum_f64<NT>(z_loc, scd);
     RowInfo info;
@@ -1900,7 +1900,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
     info.pad = 0;
 
     if (!filtered) {
-        merge_unfiltered<NT>(P, L, W, b, md, S.scd, S.sc64, S.scx, S.scq, S.sci);
+        merge_unfiltered<NT>(P, L, W, b, md, S.scd, S.sc64, S.scx, S.scq, S.sci, S.etab);
         return;
     }
 
@@ -3497,7 +3497,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 __syncthreads();
                 c = bitonic_regs_desc(c, npad, S.coll);
                 if (tid < n) S.coll[tid] = c;
-                const double e1 = tid < n ? (count ? 1.0 : exp((double)cval(c) - m)) : 0.0;
+                const double e1 = tid < n ? (count ? 1.0 : exp_neg_tab((double)cval(c) - m, S.etab)) : 0.0;
                 double tot;
                 const double run = (above + wg_excl_scan_f64<K3_THREADS>(e1, S.scd, tot)) + e1;
                 fi = wg_min_u32<K3_THREADS>(tid < n && run >= target ? (uint32_t)tid : NONE, S.sc);
@@ -3518,7 +3518,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 #pragma unroll
                 for (int t = 0; t < PER; ++t) {
                     int i = tid * PER + t;
-                    ei[t] = (i < n) ? (count ? 1.0 : exp((double)cval(S.coll[i]) - m)) : 0.0;
+                    ei[t] = (i < n) ? (count ? 1.0 : exp_neg_tab((double)cval(S.coll[i]) - m, S.etab)) : 0.0;
                     loc += ei[t];
                 }
                 double tot;
@@ -3550,7 +3550,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             // every bucket member has the same value: take the c members with
             // the smallest vocab ids
             const float xt = key2f(bklo);
-            const double et = count ? 1.0 : exp((double)xt - m);
+            const double et = count ? 1.0 : exp_neg_tab((double)xt - m, S.etab);
             double cnt_need = ceil((target - above) / et);
             uint32_t cneed = (cnt_need < 1.0) ? 1u : (cnt_need > (double)bcnt ? bcnt : (uint32_t)cnt_need);
             // c-th smallest index among elements equal to xt: scan in index order
@@ -3623,7 +3623,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 Tstar = cfloor;
                 double z = 0.0;
                 row_pass<DT, AL, XF>(P, b, S.bm, [&](float x, uint32_t j) {
-                    if (mkcomp(x, j) >= cfloor) z += exp((double)x - m);
+                    if (mkcomp(x, j) >= cfloor) z += exp_neg_tab((double)x - m, S.etab);
                 });
                 ZK = wg_sum_f64<K3_THREADS>(z, S.scd);
                 continue;
@@ -3666,7 +3666,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             const uint64_t c = S.coll[i];
             const uint32_t id = cidx(c);
             const float x = cval(c);
-            const double r = race_ratio(x, exp((double)x - m), (double)rowq[id] + (double)P.eps);
+            const double r = race_ratio(x, exp_neg_tab((double)x - m, S.etab), (double)rowq[id] + (double)P.eps);
             if (r > rr || (r == rr && id < ri)) {
                 rr = r;
                 ri = id;
@@ -3691,7 +3691,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             if (tid == 0) {
                 const float x = xform<XF>(ld1<DT>(row_ptr(P, DT, b), id), hit ? 1u : 0u, P);
                 const double r =
-                    race_ratio(x, exp((double)x - m), (double)rowq[id] + (double)P.eps);
+                    race_ratio(x, exp_neg_tab((double)x - m, S.etab), (double)rowq[id] + (double)P.eps);
                 if (r > rr || (r == rr && id < ri)) {
                     rr = r;
                     ri = id;
@@ -3737,6 +3737,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 // unfiltered rows re-read the tile's logits.
 
 struct DenseShared {
+    double etab[64];            // exp2_j64_tab (probabilities only)
     float lval[KMAX];           // the tile's kept values by rank
     uint32_t tb[DTILE / 32];    // kept positions (or penalised positions) of the tile
     uint32_t wpre[DTILE / 32];  // set bits before each word
@@ -3850,7 +3851,7 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    o[e] = ((bits >> e) & 1u) ? (float)(exp((double)xv[e] - m) / ZK) : 0.0f;
+                    o[e] = ((bits >> e) & 1u) ? (float)(exp_neg_tab((double)xv[e] - m, S.etab) / ZK) : 0.0f;
                 store8<AL>(op, j, nv, o);
             }
         }
@@ -3898,7 +3899,7 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
             const float xi = xform<XF>(x[e], (bits >> e) & 1u, P);
             const bool in = mkcomp(xi, (uint32_t)(j + e)) >= T;
             lo[e] = in ? xi : -INFINITY;
-            po[e] = in ? (float)(exp((double)xi - m) / ZK) : 0.0f;
+            po[e] = in ? (float)(exp_neg_tab((double)xi - m, S.etab) / ZK) : 0.0f;
         }
         if (ol) store8<AL>(ol, j, nv, lo);
         if (op) store8<AL>(op, j, nv, po);
@@ -3912,6 +3913,10 @@ __global__ __launch_bounds__(DENSE_THREADS) void k_dense(KParams P, KPlan L, KWo
     __shared__ DenseShared S;
     const int ntd = L.ntd;
     const int i = (int)blockIdx.x;
+    if (P.out_probs) {  // the same for the whole grid
+        if (threadIdx.x < 64) S.etab[threadIdx.x] = exp2_j64_tab[threadIdx.x];
+        __syncthreads();
+    }
     dense_tile_write<DT, AL, XF>(P, W, ntd, P.b0 + i / ntd, i % ntd, dense_meta(P, W, ntd, i), S);
 }
 
