@@ -3731,17 +3731,14 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 // DGR_PER_TILE group-rows of DGR elements spaced ntd group-rows apart: group-
 // row g of the row belongs to tile g mod ntd.  Spreading a workgroup's
 // stores over the row in this way writes faster than one contiguous span per
-// workgroup.  Rows with a kept list place the tile's kept values through a
-// bitmap of their tile positions and their ranks among the set bits, without
-// reading the logits; threshold rows (after the full-row search) and
-// unfiltered rows re-read the tile's logits.
+// workgroup.  Rows with a kept list compose the tile in LDS (-inf, then each
+// kept value at its place) without reading the logits; threshold rows (after
+// the full-row search) and unfiltered rows re-read the tile's logits.
 
 struct DenseShared {
     double etab[64];            // exp2_j64_tab (probabilities only)
-    float lval[KMAX];           // the tile's kept values by rank
-    uint32_t tb[DTILE / 32];    // kept positions (or penalised positions) of the tile
-    uint32_t wpre[DTILE / 32];  // set bits before each word
-    uint32_t sc[16];
+    float tv[DTILE];            // a listed row's tile, composed
+    uint32_t tb[DTILE / 32];    // penalised positions of the tile (threshold rows)
 };
 
 // What a dense tile needs before its stores: the row's kind and the range of
@@ -3789,41 +3786,16 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
             const int i = k0 + r * NT + tid;
             kv[r] = i < k1 ? kl[i] : 0ull;
         }
-        for (int w = tid; w < NW; w += NT) S.tb[w] = 0u;
+        // the tile composed in LDS: -inf everywhere, then each kept value at
+        // its place
+        static_assert(DTILE % (4 * NT) == 0, "the fill is whole vectors per thread");
+        const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int w = tid; w < DTILE / 4; w += NT) reinterpret_cast<f32x4 *>(S.tv)[w] = ninf;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KR; ++r)
-            if (k0 + r * NT + tid < k1) {
-                const uint32_t rr = dense_pos(cidx(kv[r]), (uint32_t)ntd);
-                atomicOr(&S.tb[rr >> 5], 1u << (rr & 31));
-            }
-        __syncthreads();
-        // ranks: set bits before each word (words split evenly over threads)
-        constexpr int PER = (NW + NT - 1) / NT;
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int w = tid * PER + i;
-            if (w < NW) cnt += __popc(S.tb[w]);
-        }
-        uint32_t tot;
-        uint32_t run = wg_excl_scan_u32<NT>(cnt, S.sc, tot);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int w = tid * PER + i;
-            if (w < NW) {
-                S.wpre[w] = run;
-                run += __popc(S.tb[w]);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < KR; ++r)
-            if (k0 + r * NT + tid < k1) {
-                const uint32_t rr = dense_pos(cidx(kv[r]), (uint32_t)ntd);
-                const uint32_t below = S.tb[rr >> 5] & ((1u << (rr & 31)) - 1u);
-                S.lval[S.wpre[rr >> 5] + __popc(below)] = cval(kv[r]);
-            }
+            if (k0 + r * NT + tid < k1) S.tv[dense_pos(cidx(kv[r]), (uint32_t)ntd)] = cval(kv[r]);
         __syncthreads();
         // each lane writes 8 consecutive floats (two 16-byte stores) of each
         // of the tile's group-rows
@@ -3835,28 +3807,20 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
             const int j = g * DGR + tid * VEC;
             const int nv = group_nv(j, P.V);
             if (nv == 0) continue;
-            const uint32_t word = S.tb[r0 >> 5];
-            const uint32_t bits = (word >> (r0 & 31)) & 0xffu;
-            float xv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[e] = -INFINITY;
-            if (bits) {
-                uint32_t k = S.wpre[r0 >> 5] + __popc(word & ((1u << (r0 & 31)) - 1u));
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if ((bits >> e) & 1u) xv[e] = S.lval[k++];
-            }
+            const f32x4 a = reinterpret_cast<const f32x4 *>(S.tv + r0)[0];
+            const f32x4 c = reinterpret_cast<const f32x4 *>(S.tv + r0)[1];
+            const float xv[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
             if (ol) store8<AL>(ol, j, nv, xv);
             if (op) {
+                // a kept -inf has probability 0, as a dropped entry
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    o[e] = ((bits >> e) & 1u) ? (float)(exp_neg_tab((double)xv[e] - m, S.etab) / ZK) : 0.0f;
+                    o[e] = xv[e] > -INFINITY ? (float)(exp_neg_tab((double)xv[e] - m, S.etab) / ZK)
+                                             : 0.0f;
                 store8<AL>(op, j, nv, o);
             }
         }
-        // the next tile rewrites the bitmap, ranks and values
-        __syncthreads();
         return;
     }
     if (info.kind != KIND_THRESH && info.kind != KIND_UNFILTERED) return;
