@@ -3741,6 +3741,8 @@ struct DenseShared {
     uint32_t tb[DTILE / 32];    // penalised positions of the tile (threshold rows)
 };
 
+static_assert(DGR == 8 * DENSE_THREADS, "a group-row is 8 floats per lane (tv_slot)");
+
 // What a dense tile needs before its stores: the row's kind and the range of
 // the kept list, requested one tile ahead.
 struct DenseMeta {
@@ -3795,7 +3797,7 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KR; ++r)
-            if (k0 + r * NT + tid < k1) S.tv[dense_pos(cidx(kv[r]), (uint32_t)ntd)] = cval(kv[r]);
+            if (k0 + r * NT + tid < k1) S.tv[tv_slot(dense_pos(cidx(kv[r]), (uint32_t)ntd))] = cval(kv[r]);
         __syncthreads();
         // each lane writes 8 consecutive floats (two 16-byte stores) of each
         // of the tile's group-rows
@@ -3803,12 +3805,11 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
         for (int i = 0; i < DGR_PER_TILE; ++i) {
             const int g = t + i * ntd;
             if (g >= ngr) break;
-            const int r0 = i * DGR + tid * VEC;
             const int j = g * DGR + tid * VEC;
             const int nv = group_nv(j, P.V);
             if (nv == 0) continue;
-            const f32x4 a = reinterpret_cast<const f32x4 *>(S.tv + r0)[0];
-            const f32x4 c = reinterpret_cast<const f32x4 *>(S.tv + r0)[1];
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(S.tv + i * DGR + 4 * tid);
+            const f32x4 c = *reinterpret_cast<const f32x4 *>(S.tv + i * DGR + DGR / 2 + 4 * tid);
             const float xv[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
             if (ol) store8<AL>(ol, j, nv, xv);
             if (op) {
