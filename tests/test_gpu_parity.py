@@ -171,6 +171,25 @@ def test_signed_zero_and_neg_inf():
     assert not np.signbit(hip["logits"][np.isfinite(hip["logits"]) & (hip["logits"] == 0)]).any()
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_kept_neg_inf_entries(dtype):
+    """Rows with only 30 finite logits: a top-k larger than that keeps -inf
+    entries, whose dense logit stays -inf and whose probability is 0 (the
+    dense writer composes listed tiles from the kept values alone)."""
+    rng = np.random.default_rng(88 if dtype == wl.F32 else 89)
+    B, V = 16, 4096
+    x = np.full((B, V), -np.inf, np.float32)
+    for r in range(B):
+        x[r, rng.choice(V, size=30, replace=False)] = rng.standard_normal(30).astype(np.float32)
+    k = np.array([1, 30, 31, 100, 1024, 0, 64, 500] * 2)
+    p = np.array([1.0] * 8 + [0.5] * 8, np.float32)
+    W = _custom(x, top_k=k, top_p=p, flags=_all_combos(B), dtype=dtype, seed=90)
+    hip, ref = _check(W, f"kept -inf {dtype}")
+    # some rows keep more entries than they have finite logits
+    assert (ref["nkept"] > 30).any()
+    assert np.array_equal(np.isneginf(hip["logits"]), np.isneginf(ref["logits"]))
+
+
 @pytest.mark.parametrize("pad", [8, 3])
 def test_padded_row_stride(pad):
     W = wl.make(5, B=16, V=20000, seed=2)
