@@ -3105,11 +3105,14 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
                 __hip_atomic_store(&mine.crk[c], ck, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        // One thread counts the arrival: its release (after the barrier that
-        // orders every thread's stores before it) publishes the whole part,
+        // One thread counts the arrival: its release publishes the whole part,
         // and the last tile's acquire makes every part visible to the
-        // workgroup past the next barrier.  Only that thread touches the
-        // device-wide cache state.
+        // workgroup past the next barrier.  Each wave first waits for its own
+        // stores to complete (requests of different waves to different
+        // memory channels are not ordered by the barrier), so that they
+        // precede the release; only that thread touches the device-wide
+        // cache state.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         uint32_t *sy = W.fbsync + (size_t)qi * FB_SYNC_WORDS;
         if (tid == 0) {
@@ -3158,6 +3161,8 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
             uint64_t *mem = fb_members(W.fbpart, qi * ntiles);
             for (uint32_t i = tid; i < nc; i += K3_THREADS)
                 if (base + i < (uint32_t)K3_COLLECT) mem[base + i] = S.coll[i];
+            // every wave's list stores complete before the release (as above)
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (tid == 0)
                 __hip_atomic_fetch_add(&sy[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
