@@ -45,8 +45,11 @@ constexpr uint32_t FB_NO_BUCKET = 0xffffffffu;  // published: the tiles collect 
 constexpr int FB_POLLS = 200;
 constexpr size_t FB_PART_CHUNKS = ((size_t)K3_BINS * (8 + 8 + 4) + 8 + 255) / 256 * 256;
 constexpr size_t FB_PART_BYTES = (FB_PART_CHUNKS + (size_t)FB_CHUNKS * 16 + 255) / 256 * 256;
-// Dense writer: a tile is DGR_PER_TILE group-rows of 2048 elements.
+// Dense writer: a tile is DGR_PER_TILE group-rows of DGR elements (8 per
+// lane of its workgroup).
 constexpr int DGR_PER_TILE = 2;
+constexpr int DGR_LOG2 = 11;
+constexpr int DGR = 1 << DGR_LOG2;
 
 // Row kinds written by the merge kernel.
 enum RowKind : int32_t {
@@ -107,7 +110,7 @@ struct KPlan {
     int32_t seg;   // elements per pass tile (a multiple of 1024)
     int32_t nt;    // tiles per row
     int32_t wcap;  // candidate entries per wave sub-slot (4 nt wcap <= ROWCAP)
-    int32_t ntd;   // dense tiles per row: ceil(ceil(V / 2048) / DGR_PER_TILE)
+    int32_t ntd;   // dense tiles per row: ceil(ceil(V / DGR) / DGR_PER_TILE)
     int32_t cus;   // compute units of the device
 };
 
@@ -122,7 +125,7 @@ constexpr KPlan make_plan(int32_t vocab, int32_t seg, int32_t cus) {
     l.nt = (int32_t)(((int64_t)vocab + seg - 1) / seg);
     const int64_t tc = ROWCAP / l.nt;
     l.wcap = (int32_t)((tc < TCAP_MAX ? tc : TCAP_MAX) / 4);
-    const int64_t ngr = ((int64_t)vocab + 2047) / 2048;  // dense group-rows
+    const int64_t ngr = ((int64_t)vocab + DGR - 1) / DGR;  // dense group-rows
     l.ntd = (int32_t)((ngr + DGR_PER_TILE - 1) / DGR_PER_TILE);
     return l;
 }
@@ -150,8 +153,6 @@ constexpr int32_t auto_seg(int32_t batch, int32_t vocab, int32_t cus) {
 
 // Dense writer tiles: group-row g (DGR elements) of a row belongs to tile
 // g mod ntd, at position (g / ntd) DGR inside it.
-constexpr int DGR_LOG2 = 11;
-constexpr int DGR = 1 << DGR_LOG2;
 constexpr int DTILE = DGR * DGR_PER_TILE;
 constexpr uint32_t dense_tile(uint32_t j, uint32_t ntd) { return (j >> DGR_LOG2) % ntd; }
 constexpr uint32_t dense_pos(uint32_t j, uint32_t ntd) {
