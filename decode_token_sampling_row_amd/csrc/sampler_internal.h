@@ -20,7 +20,7 @@ constexpr int VEC = 8;             // elements per group of the row helpers
 constexpr int EST_SEGS = 16;
 constexpr int EST_SEG = 512;
 constexpr int EST_N = EST_SEGS * EST_SEG;
-constexpr int K1_THREADS = 256;    // estimate workgroup
+constexpr int K1_THREADS = 512;    // estimate workgroup
 // Row kernels.
 constexpr int K3_THREADS = 1024;
 constexpr int K3_BINS = 2048;      // value-space histogram bins
