@@ -244,23 +244,46 @@ __device__ __forceinline__ uint64_t xlane64(uint64_t v, int m) {
     const uint32_t lo = xlane((uint32_t)v, m), hi = xlane((uint32_t)(v >> 32), m);
     return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ double xlaned(double v, int m) {
+    return __longlong_as_double((long long)xlane64((uint64_t)__double_as_longlong(v), m));
+}
 __device__ __forceinline__ float shxf(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ double shxd(double v, int m) { return __shfl_xor(v, m, 64); }
 
+// Inclusive scans over the wave on the VALU: within each row of 16 lanes by
+// DPP row shifts of 1, 2, 4 and 8 (a lane shifted in from outside the row
+// adds 0), then the last lane of row 0 is added into row 1 and row 3's
+// predecessor, and lane 31 into rows 2 and 3 (row broadcasts).  The lane
+// layout was checked on the GPU against a serial prefix sum.  Every lane of
+// the wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_in0(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_in0d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp_in0<CTRL, ROWS>((uint32_t)u), hi = dpp_in0<CTRL, ROWS>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t t = (uint32_t)__shfl_up((int)v, d, 64);
-        if (lane >= d) v += t;
-    }
+    (void)lane;
+    v += dpp_in0<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_in0<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_in0<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_in0<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_in0<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_in0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 __device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        double t = __shfl_up(v, d, 64);
-        if (lane >= d) v += t;
-    }
+    (void)lane;
+    v += dpp_in0d<0x111, 0xf>(v);
+    v += dpp_in0d<0x112, 0xf>(v);
+    v += dpp_in0d<0x114, 0xf>(v);
+    v += dpp_in0d<0x118, 0xf>(v);
+    v += dpp_in0d<0x142, 0xa>(v);
+    v += dpp_in0d<0x143, 0xc>(v);
     return v;
 }
 
@@ -305,7 +328,7 @@ __device__ __forceinline__ double wg_excl_scan_f64(double v, double *sc, double 
 template <int NT>
 __device__ __forceinline__ double wg_sum_f64(double v, double *sc) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += shxd(v, m);
+    for (int m = 32; m >= 1; m >>= 1) v += xlaned(v, m);
     if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
     __syncthreads();
     double t = 0.0;
@@ -319,7 +342,7 @@ template <int NT>
 __device__ __forceinline__ uint64_t wg_max_u64(uint64_t v, uint64_t *sc) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shx64(v, m);
+        uint64_t o = xlane64(v, m);
         v = o > v ? o : v;
     }
     if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
@@ -335,7 +358,7 @@ template <int NT>
 __device__ __forceinline__ uint64_t wg_min_u64(uint64_t v, uint64_t *sc) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shx64(v, m);
+        uint64_t o = xlane64(v, m);
         v = o < v ? o : v;
     }
     if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
@@ -350,7 +373,7 @@ __device__ __forceinline__ uint64_t wg_min_u64(uint64_t v, uint64_t *sc) {
 template <int NT>
 __device__ __forceinline__ uint32_t wg_min_u32(uint32_t v, uint32_t *sc) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = min(v, shx(v, m));
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, xlane(v, m));
     if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t t = NONE;
@@ -499,12 +522,9 @@ __device__ __forceinline__ void wave0_find_bin(const uint32_t *hist, uint32_t ne
         uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
         uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
         uint32_t s = h0 + h1 + h2 + h3;
-        uint32_t S = s;  // suffix sum over lanes >= lane
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            uint32_t t = (uint32_t)__shfl_down((int)S, d, 64);
-            if (lane + d < 64) S += t;
-        }
+        // suffix sum over lanes >= lane: the total less the prefix before
+        const uint32_t inc = wave_incl_scan_u32(s, lane);
+        const uint32_t S = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc + s;
         uint32_t above = S - s;
         if (above < need && S >= need) {
             uint32_t acc = above, d, c;
@@ -531,7 +551,7 @@ __device__ __forceinline__ void wg_min_max_or_and(uint64_t &mn, uint64_t &mx, ui
                                                   uint64_t &a, uint64_t *sc) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t x0 = shx64(mn, m), x1 = shx64(mx, m), x2 = shx64(o, m), x3 = shx64(a, m);
+        const uint64_t x0 = xlane64(mn, m), x1 = xlane64(mx, m), x2 = xlane64(o, m), x3 = xlane64(a, m);
         mn = x0 < mn ? x0 : mn;
         mx = x1 > mx ? x1 : mx;
         o |= x2;
@@ -1649,8 +1669,8 @@ __device__ __forceinline__ uint32_t wg_best_ratio(double r, uint32_t idx, double
                                                   uint32_t *sci) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        double ro = shxd(r, m);
-        uint32_t io = shx(idx, m);
+        double ro = xlaned(r, m);
+        uint32_t io = xlane(idx, m);
         if (ro > r || (ro == r && io < idx)) {
             r = ro;
             idx = io;
@@ -2407,12 +2427,7 @@ __global__ __launch_bounds__(ROWS_THREADS) void k_rows(KParams P, KPlan L, KWork
                                   : (4 * tid + i < nsel ? exp_neg_tab((double)cval(w[i]) - (double)x0, S.etab) : 0.0);
                     l += e[i];
                 }
-                double inc = l;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const double o = __shfl_up(inc, d, 64);
-                    if (tid >= d) inc += o;
-                }
+                const double inc = wave_incl_scan_f64(l, tid);
                 double run = inc - l, a_ = 0.0, b_ = 0.0;
                 uint32_t first = NONE;
 #pragma unroll
