@@ -190,6 +190,54 @@ def test_kept_neg_inf_entries(dtype):
     assert np.array_equal(np.isneginf(hip["logits"]), np.isneginf(ref["logits"]))
 
 
+def test_randomized_sweep():
+    """300 seeded random calls, every row against the oracle: batch 1..100,
+    vocabularies from 7 to 70001 (both sides of 256 and of the tile
+    lengths), fp32 / bf16, near-flat, Gumbel, coarse-grid (tied) and spiky
+    rows, any k (including 0 and past min(V, 1024)), any p, every stage
+    combination, temperature and repetition penalty (history ids partly out
+    of range), top-k ties kept or not, race or inverse-CDF draws, automatic
+    or fixed tile lengths.  Random rows can land on near ties, so up to a
+    tenth of a call's rows (at least one) may be exempted from the id check
+    by the oracle's own margins."""
+    rng = np.random.default_rng(20241203)
+    for case in range(300):
+        B = int(rng.choice([1, 3, 8, 17, 40, 100]))
+        V = int(rng.choice([7, 64, 255, 256, 257, 1000, 4097, 6400, 20000, 32000, 70001]))
+        dtype = wl.BF16 if rng.random() < 0.5 else wl.F32
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            x = rng.standard_normal((B, V)) * rng.choice([0.05, 1.0, 3.0])
+        elif kind == 1:
+            x = rng.gumbel(size=(B, V)) * 4.0
+        elif kind == 2:
+            x = np.round(rng.standard_normal((B, V)) * 4.0) / 4.0
+        else:
+            x = rng.standard_normal((B, V))
+            for r in range(B):
+                x[r, rng.choice(V, size=min(V, 10), replace=False)] += rng.uniform(5, 15)
+        k = rng.integers(0, min(V, 1024) + 2, size=B)
+        p = np.where(rng.random(B) < 0.3, 1.0, rng.uniform(0.05, 1.0, size=B))
+        flags = rng.integers(0, 8, size=B)
+        kw = dict(temperature=float(rng.choice([1.0, 0.7, 1.3])),
+                  penalty=float(rng.choice([1.0, 1.2])))
+        if kw["penalty"] != 1.0:
+            kw["ids"] = rng.integers(-5, V + 5, size=B * 20).astype(np.int32)
+            kw["offsets"] = np.arange(B + 1, dtype=np.int64) * 20
+        W = _custom(x.astype(np.float32), top_k=k, top_p=p, flags=flags, dtype=dtype,
+                    seed=case, **kw)
+        inverse = bool(rng.random() < 0.25)
+        ties = bool(rng.random() < 0.2)
+        u = rng.random(B).astype(np.float32) if inverse else None
+        seg = int(rng.choice([0, 0, 0, 1024, 3072]))
+        label = (f"sweep {case}: B={B} V={V} {dtype} rows={kind} inverse={inverse} "
+                 f"ties={ties} seg={seg} {kw.get('temperature')} {kw.get('penalty')}")
+        hip = run_hip(W, need_logits=True, need_probs=True, u=u, drop_q=inverse, ties=ties,
+                      seg=seg)
+        ref = run_oracle(W, need_logits=True, need_probs=True, u=u, ties=ties)
+        compare(W, hip, ref, label=label, inverse=inverse, max_exempt=max(1, B // 10))
+
+
 @pytest.mark.parametrize("pad", [8, 3])
 def test_padded_row_stride(pad):
     W = wl.make(5, B=16, V=20000, seed=2)
