@@ -158,16 +158,6 @@ constexpr uint32_t dense_tile(uint32_t j, uint32_t ntd) { return (j >> DGR_LOG2)
 constexpr uint32_t dense_pos(uint32_t j, uint32_t ntd) {
     return (((j >> DGR_LOG2) / ntd) << DGR_LOG2) | (j & (uint32_t)(DGR - 1));
 }
-// The LDS place of tile position pos when the dense writer composes a tile:
-// within each group-row (DGR positions, 8 per lane), lane l's 8 floats are
-// two 16-byte vectors at 4 l, one in each half of the group-row's slots, so
-// that a wave's vector reads are contiguous (no bank conflicts) while each
-// lane still stores 8 consecutive floats.
-constexpr uint32_t tv_slot(uint32_t pos) {
-    return (pos & ~(uint32_t)(DGR - 1)) | ((pos & 4u) ? (uint32_t)(DGR / 2) : 0u) |
-           (((pos & (uint32_t)(DGR - 1)) >> 3) << 2) | (pos & 3u);
-}
-
 // First element of sample run s (of EST_SEGS) of row b of a row of V >
 // EST_N elements: inside the s-th of EST_SEGS equal segments, at one of 16
 // offsets that depend on s and b, a multiple of VEC.

@@ -183,23 +183,6 @@ __device__ __forceinline__ void load8(const void *p, int64_t j, int nv, float (&
     }
 }
 
-// Plain write-back stores: each lane writes 32 contiguous bytes as two 16-byte
-// stores, and L2 merges the two half lines of a wave before they reach HBM
-// (streaming stores of half lines write at a fraction of the bandwidth).
-template <bool AL>
-__device__ __forceinline__ void store8(float *p, int64_t j, int nv, const float (&x)[8]) {
-    if (AL && nv == 8) {
-        f32x4 a = {x[0], x[1], x[2], x[3]};
-        f32x4 c = {x[4], x[5], x[6], x[7]};
-        *(f32x4 *)(p + j) = a;
-        *((f32x4 *)(p + j) + 1) = c;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < nv) p[j + i] = x[i];
-    }
-}
-
 // ---------------------------------------------------------------- wave / WG primitives
 
 __device__ __forceinline__ uint32_t shx(uint32_t v, int m) {
@@ -1145,6 +1128,9 @@ __device__ __forceinline__ void unpack4(const Raw4<DT> &r, float (&x)[4]) {
     }
 }
 
+// Plain write-back stores of 16 bytes per lane; lanes of a wave write
+// consecutive vectors, so a wave's store covers whole lines (streaming stores
+// write at a fraction of the bandwidth here).
 template <bool AL>
 __device__ __forceinline__ void store4(float *p, int j, int nv, const float (&x)[4]) {
     if (AL && nv == 4) {
@@ -3761,7 +3747,7 @@ struct DenseShared {
     uint32_t tb[DTILE / 32];    // penalised positions of the tile (threshold rows)
 };
 
-static_assert(DGR == 8 * DENSE_THREADS, "a group-row is 8 floats per lane (tv_slot)");
+static_assert(DGR == 8 * DENSE_THREADS, "a group-row is two vectors of 4 floats per lane");
 
 // What a dense tile needs before its stores: the row's kind and the range of
 // the kept list, requested one tile ahead.
@@ -3817,29 +3803,32 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KR; ++r)
-            if (k0 + r * NT + tid < k1) S.tv[tv_slot(dense_pos(cidx(kv[r]), (uint32_t)ntd))] = cval(kv[r]);
+            if (k0 + r * NT + tid < k1) S.tv[dense_pos(cidx(kv[r]), (uint32_t)ntd)] = cval(kv[r]);
         __syncthreads();
-        // each lane writes 8 consecutive floats (two 16-byte stores) of each
-        // of the tile's group-rows
+        // each lane writes the 4 floats at 4 tid and the 4 at DGR/2 + 4 tid of
+        // each group-row, so that a wave's store covers 1 KB without gaps (as
+        // the pass's stores do)
 #pragma unroll
         for (int i = 0; i < DGR_PER_TILE; ++i) {
             const int g = t + i * ntd;
             if (g >= ngr) break;
-            const int j = g * DGR + tid * VEC;
-            const int nv = group_nv(j, P.V);
-            if (nv == 0) continue;
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(S.tv + i * DGR + 4 * tid);
-            const f32x4 c = *reinterpret_cast<const f32x4 *>(S.tv + i * DGR + DGR / 2 + 4 * tid);
-            const float xv[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-            if (ol) store8<AL>(ol, j, nv, xv);
-            if (op) {
-                // a kept -inf has probability 0, as a dropped entry
-                float o[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o[e] = xv[e] > -INFINITY ? (float)(exp_neg_tab((double)xv[e] - m, S.etab) / ZK)
-                                             : 0.0f;
-                store8<AL>(op, j, nv, o);
+            for (int h = 0; h < 2; ++h) {
+                const int r = i * DGR + h * (DGR / 2) + 4 * tid;
+                const int j = g * DGR + h * (DGR / 2) + 4 * tid;
+                const int nv = nv4(j, P.V);
+                if (nv == 0) continue;
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(S.tv + r);
+                const float xv[4] = {a[0], a[1], a[2], a[3]};
+                if (ol) store4<AL>(ol, j, nv, xv);
+                if (op) {
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = xv[e] > -INFINITY ? (float)(exp_neg_tab((double)xv[e] - m, S.etab) / ZK)
+                                                 : 0.0f;
+                    store4<AL>(op, j, nv, o);
+                }
             }
         }
         return;
@@ -3871,23 +3860,28 @@ __device__ __forceinline__ void dense_tile_write(const KParams &P, const KWork &
     for (int i = 0; i < DGR_PER_TILE; ++i) {
         const int g = t + i * ntd;
         if (g >= ngr) break;
-        const int r0 = i * DGR + tid * VEC;
-        const int j = g * DGR + tid * VEC;
-        const int nv = group_nv(j, P.V);
-        if (nv == 0) continue;
-        float x[8];
-        load8<DT, AL>(rowp, j, nv, x);
-        const uint32_t bits = (XF && P.pen) ? (S.tb[r0 >> 5] >> (r0 & 31)) & 0xffu : 0u;
-        float lo[8], po[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xi = xform<XF>(x[e], (bits >> e) & 1u, P);
-            const bool in = mkcomp(xi, (uint32_t)(j + e)) >= T;
-            lo[e] = in ? xi : -INFINITY;
-            po[e] = in ? (float)(exp_neg_tab((double)xi - m, S.etab) / ZK) : 0.0f;
+        for (int h = 0; h < 2; ++h) {
+            const int r = i * DGR + h * (DGR / 2) + 4 * tid;
+            const int j = g * DGR + h * (DGR / 2) + 4 * tid;
+            const int nv = nv4(j, P.V);
+            if (nv == 0) continue;
+            Raw4<DT> raw;
+            load4<DT, AL>(rowp, j, nv, raw);
+            float x[4];
+            unpack4<DT>(raw, x);
+            const uint32_t bits = (XF && P.pen) ? (S.tb[r >> 5] >> (r & 31)) & 0xfu : 0u;
+            float lo[4], po[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xi = xform<XF>(x[e], (bits >> e) & 1u, P);
+                const bool in = mkcomp(xi, (uint32_t)(j + e)) >= T;
+                lo[e] = in ? xi : -INFINITY;
+                po[e] = in ? (float)(exp_neg_tab((double)xi - m, S.etab) / ZK) : 0.0f;
+            }
+            if (ol) store4<AL>(ol, j, nv, lo);
+            if (op) store4<AL>(op, j, nv, po);
         }
-        if (ol) store8<AL>(ol, j, nv, lo);
-        if (op) store8<AL>(op, j, nv, po);
     }
     if (XF && P.pen) __syncthreads();  // the next tile rewrites the bitmap
 }

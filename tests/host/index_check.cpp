@@ -108,19 +108,6 @@ static void check_plans(const std::vector<int32_t> &vs) {
 // call's tile records fit the handle's workspace bound.
 static int64_t auto_cases = 0;
 
-// The composed tile's LDS slots: a permutation of the tile's positions, lane
-// l's two vectors of a group-row at slots 4 l and DGR / 2 + 4 l.
-static void check_tv_slots() {
-    std::vector<uint8_t> seen(DTILE, 0);
-    for (uint32_t pos = 0; pos < (uint32_t)DTILE; ++pos) {
-        const uint32_t t = tv_slot(pos);
-        CHECK(t < (uint32_t)DTILE && !seen[t], "pos=%u slot=%u", pos, t);
-        if (t < (uint32_t)DTILE) seen[t] = 1;
-        const uint32_t g = pos / DGR, lane = (pos % DGR) / 8, e = pos % 8;
-        CHECK(t == g * DGR + (e / 4) * (DGR / 2) + 4 * lane + e % 4, "pos=%u slot=%u", pos, t);
-    }
-}
-
 static void check_auto_seg(const std::vector<int32_t> &vs) {
     const int32_t batches[] = {1, 2, 3, 4, 7, 16, 64, 100, 256, 1000, 1024, 4096};
     const int32_t cuss[] = {1, 80, 256, 304};
@@ -168,8 +155,10 @@ static void check_dense(int32_t V) {
         s = 1;
         // the bitmap word and bit of the position stay inside the tile's words
         CHECK((pos >> 5) < (uint32_t)(DTILE / 32), "V=%d j=%u", V, j);
-        // its LDS slot when the tile is composed stays inside the tile
-        CHECK(tv_slot(pos) < (uint32_t)DTILE, "V=%d j=%u slot=%u", V, j, tv_slot(pos));
+        // the writer of tile t stores position pos of its LDS copy at element
+        // (t + (pos / DGR) ntd) DGR + pos % DGR of the row: j itself
+        const uint32_t back = (t + (pos / DGR) * ntd) * DGR + pos % DGR;
+        CHECK(back == j, "V=%d j=%u written at %u", V, j, back);
     }
     dense_ids += V;
 }
@@ -282,7 +271,6 @@ int main() {
     const std::vector<int32_t> vs = vocab_set();
     check_plans(vs);
     check_auto_seg(vs);
-    check_tv_slots();
     int ndense = 0;
     for (size_t i = 0; i < vs.size(); ++i) {
         const int32_t V = vs[i];
