@@ -1128,13 +1128,20 @@ __device__ __forceinline__ void unpack4(const Raw4<DT> &r, float (&x)[4]) {
     }
 }
 
-// Plain write-back stores of 16 bytes per lane; lanes of a wave write
-// consecutive vectors, so a wave's store covers whole lines (streaming stores
-// write at a fraction of the bandwidth here).
-template <bool AL>
+// Stores of 16 bytes per lane; the lanes of a wave write consecutive
+// vectors, so a wave's store covers whole lines.  NT: streaming
+// (non-temporal) stores, for the pass, whose dense output is written once
+// and not read again; its write-back lines would otherwise still be draining
+// into HBM while the next kernels run.  The dense writer keeps write-back
+// stores, which it issues faster.
+template <bool AL, bool NT = false>
 __device__ __forceinline__ void store4(float *p, int j, int nv, const float (&x)[4]) {
     if (AL && nv == 4) {
-        *(f32x4 *)(p + j) = f32x4{x[0], x[1], x[2], x[3]};
+        const f32x4 v = {x[0], x[1], x[2], x[3]};
+        if (NT)
+            __builtin_nontemporal_store(v, (f32x4 *)(p + j));
+        else
+            *(f32x4 *)(p + j) = v;
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1315,7 +1322,7 @@ __device__ __forceinline__ void stream_group(const Raw4<DT> &raw, const Raw4<0> 
     const uint32_t bits = (FULL || nv > 0) ? pen_bits4<XF>(bm, j - c0, P) : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[0][i] = xform<XF>(y[0][i], (bits >> i) & 1u, P);
-    if (rowo && (FULL || nv > 0)) store4<AL>(rowo, j, FULL ? 4 : nv, y[0]);
+    if (rowo && (FULL || nv > 0)) store4<AL, true>(rowo, j, FULL ? 4 : nv, y[0]);
     if (STATS) {
         int nvv[1] = {FULL ? 4 : nv};
         stats_batch<1, 4>(ss.st, y, nvv);
