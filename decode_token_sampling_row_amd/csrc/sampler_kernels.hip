@@ -3748,9 +3748,11 @@ __global__ __launch_bounds__(K3_THREADS) void k_fallback(KParams P, KPlan L, KWo
 // kept value at its place) without reading the logits; threshold rows (after
 // the full-row search) and unfiltered rows re-read the tile's logits.
 
-struct DenseShared {
-    double etab[64];            // exp2_j64_tab (probabilities only)
+// tv first and 16-byte aligned, so that its vector accesses compile to
+// single 16-byte LDS operations (two 8-byte halves conflict on the banks).
+struct alignas(16) DenseShared {
     float tv[DTILE];            // a listed row's tile, composed
+    double etab[64];            // exp2_j64_tab (probabilities only)
     uint32_t tb[DTILE / 32];    // penalised positions of the tile (threshold rows)
 };
 
