@@ -1063,7 +1063,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
 
 constexpr int PASS_THREADS = 256;
 constexpr int PASS_WAVES = PASS_THREADS / 64;
-constexpr int PASS_D = 8;                      // groups of 4 in flight per thread
+// Groups of 4 in flight per thread in the pass: 8 for fp32 logits (16
+// bytes a group), 6 for bf16 (8 bytes a group), whose fewer registers let
+// more waves share a CU.
+template <int DT>
+constexpr int pass_depth() { return DT == 1 ? 6 : 8; }
+constexpr int PASS_D_MAX = 8;
 constexpr int PGROUP = PASS_THREADS * 4;       // elements per group row
 
 template <int DT>
@@ -1364,14 +1369,15 @@ __device__ __forceinline__ double lane_sum_again(const KParams &P, const uint32_
     return z;
 }
 
-// The group loop of a tile: PASS_D groups in flight per thread (q for racing
+// The group loop of a tile: pass_depth<DT>() groups in flight per thread (q for racing
 // rows QD groups ahead), each group processed as soon as it arrives.
 template <int DT, bool AL, bool XF, int KIND, bool FULL, bool STATS>
 __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, int c0, int c1,
                                           int ng, int j0, const void *rowp, const float *rowq,
-                                          float *rowo, Raw4<DT> (&ring)[PASS_D], StreamState &ss,
+                                          float *rowo, Raw4<DT> (&ring)[pass_depth<DT>()], StreamState &ss,
                                           RefSum &rs, WaveSel &ws, Raw4<DT> *stage, uint64_t *dst,
                                           uint32_t wcap, float ref, float traw, float yt) {
+    constexpr int PASS_D = pass_depth<DT>();
     constexpr int QD = KIND == 1 ? PASS_D / 2 : 1;
     Raw4<0> qring[QD];
     if (KIND == 1) {
@@ -1423,7 +1429,7 @@ __device__ __forceinline__ void tile_loop(const uint32_t *bm, const KParams &P, 
 template <int DT, bool AL, bool XF, int KIND>
 __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, const KPlan &L,
                                           const KWork &W, const Mode &md, int b, int t,
-                                          float traw, float ref, Raw4<DT> (&ring)[PASS_D],
+                                          float traw, float ref, Raw4<DT> (&ring)[pass_depth<DT>()],
                                           Raw4<DT> *stage) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int c0 = t * L.seg;
@@ -1439,7 +1445,7 @@ __device__ __forceinline__ void pass_tile(const uint32_t *bm, const KParams &P, 
     const int j0 = c0 + tid * 4;
     const int wslot = (b * L.nt + t) * PASS_WAVES + (tid >> 6);
     const uint32_t wcap = (uint32_t)L.wcap;
-    Raw4<DT> *wstage = stage ? stage + (tid >> 6) * (PASS_D * 64) : nullptr;
+    Raw4<DT> *wstage = stage ? stage + (tid >> 6) * (pass_depth<DT>() * 64) : nullptr;
     uint64_t *dst = W.cand + (int64_t)b * ROWCAP + (int64_t)(t * PASS_WAVES + (tid >> 6)) * wcap;
     const float yt = KIND == 2 ? xform<XF>(traw, 0u, P) : 0.0f;
     StreamState ss;
@@ -1514,6 +1520,7 @@ template <int DT, bool AL, bool XF>
 __global__ __launch_bounds__(PASS_THREADS) void k_pass(KParams P, KPlan L, KWork W) {
     // each wave's staging slots: the raw groups in which a lane admitted
     // something, read back when the chunk is handed over
+    constexpr int PASS_D = pass_depth<DT>();
     __shared__ Raw4<DT> stage[PASS_WAVES][PASS_D * 64];
     extern __shared__ uint32_t bm[];  // penalty bitmap of the tile
     const int b = P.b0 + (int)(blockIdx.x / L.nt), t = (int)(blockIdx.x % L.nt);
@@ -3999,7 +4006,7 @@ hipError_t launch_pass(const KParams &p, const KPlan &l, const KWork &w, int dty
     const bool xf = any_transform(p);
     dim3 grid((unsigned)((int64_t)p.B * l.nt)), block(PASS_THREADS);
     size_t sh = p.pen ? (size_t)((l.seg + 31) / 32) * 4 : 0;
-    static_assert(sizeof(Raw4<0>) * PASS_WAVES * PASS_D * 64 + (SEG_MAX / 32) * 4 <= 65536,
+    static_assert(sizeof(Raw4<0>) * PASS_WAVES * PASS_D_MAX * 64 + (SEG_MAX / 32) * 4 <= 65536,
                   "pass LDS: staging and the penalty bitmap of the longest tile");
     return SMP_PICK(k_pass, grid, block, sh);
 }
