@@ -1048,9 +1048,10 @@ __global__ __launch_bounds__(K1_THREADS) void k_plan(KParams P, KPlan L, KWork W
 // The one streaming pass over the logits: one workgroup per tile of
 // L.seg elements (the segment length v of the Ascend page's rolling top-k by
 // default), every tile of every row in one grid, so the hardware dispatcher
-// spreads rows of every kind over all CUs.  Each thread keeps its whole share
-// of the tile in flight: groups of 4 consecutive elements, one 16-byte store
-// per group, consecutive lanes on consecutive groups.
+// spreads rows of every kind over all CUs.  Each thread keeps pass_depth
+// groups of its share of the tile in flight (the whole share of an fp32 tile
+// of 8192): groups of 4 consecutive elements, one 16-byte streaming store per
+// group of dense output, consecutive lanes on consecutive groups.
 //  * rows without top-k / top-p: the dense output gets the transformed
 //    logits; the exponential race over the tile runs with q read in the same
 //    pass, or the greedy argmax; optional statistics for the probabilities;
