@@ -1070,6 +1070,8 @@ constexpr int PASS_WAVES = PASS_THREADS / 64;
 template <int DT>
 constexpr int pass_depth() { return DT == 1 ? 6 : 8; }
 constexpr int PASS_D_MAX = 8;
+static_assert(pass_depth<0>() <= PASS_D_MAX && pass_depth<1>() <= PASS_D_MAX,
+              "a lane's admissions of a chunk are one bit each of a 32-bit mask (4 per group)");
 constexpr int PGROUP = PASS_THREADS * 4;       // elements per group row
 
 template <int DT>
